@@ -1,0 +1,187 @@
+"""CPU oracle for the W4A16 MoE expert layer (ctypes wrapper over moe_oracle.c).
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package. It never imports the GPU package and
+the GPU package never imports it; the two share only the seeded input
+generators, which hold none of the layer's arithmetic.
+
+bf16 tensors are passed as numpy uint16 bit patterns. Every function here is a
+thin marshalling layer; the arithmetic lives in moe_oracle.c, whose header
+cites the pages each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+
+W13_SWIGLU, W2, RAW = 0, 1, 2
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.oracle_bf16_from_double.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_from_double.restype = ctypes.c_uint16
+    lib.oracle_set_threads.argtypes = [I]
+    lib.oracle_get_threads.restype = I
+    lib.oracle_route.argtypes = [I, I, I, P, P, P]
+    lib.oracle_permute.argtypes = [I, I, I, I, P, P, P, P, P]
+    lib.oracle_grouped_gemm.argtypes = [I, I, I, I, I, P, P, I, P, P, P, P, P, I]
+    lib.oracle_finalize.argtypes = [I, I, I, P, I, P, P, P, P, I]
+    lib.oracle_layer.argtypes = [I] * 8 + [P] * 7 + [P] * 9
+    lib.oracle_layer_bruteforce.argtypes = [I] * 7 + [P] * 9
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().oracle_get_threads())
+
+
+def bf16_from_double(d: float) -> int:
+    """Single round-to-nearest-even of a double to a bf16 bit pattern."""
+    return int(_load().oracle_bf16_from_double(float(d)))
+
+
+def route(logits: np.ndarray, top_k: int):
+    """Top-k routing: returns (topk_ids int32 [T,k], topk_w float32 [T,k])."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, top_k), np.int32)
+    w = np.empty((T, top_k), np.float32)
+    _load().oracle_route(T, E, top_k, _ptr(logits), _ptr(ids), _ptr(w))
+    return ids, w
+
+
+def permute(topk_ids: np.ndarray, num_local_experts: int, expert_begin: int = 0):
+    """Stable expert bucketing: returns counts, offsets, perm, inv_perm."""
+    topk_ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    T, k = topk_ids.shape
+    counts = np.empty(num_local_experts, np.int32)
+    offsets = np.empty(num_local_experts + 1, np.int32)
+    perm = np.empty(T * k, np.int32)
+    inv_perm = np.empty((T, k), np.int32)
+    _load().oracle_permute(T, k, expert_begin, num_local_experts, _ptr(topk_ids), _ptr(counts),
+                           _ptr(offsets), _ptr(perm), _ptr(inv_perm))
+    return counts, offsets, perm, inv_perm
+
+
+def grouped_gemm(kind: int, a: np.ndarray, offsets: np.ndarray, wq: np.ndarray, s: np.ndarray,
+                 *, rows: int, a_row_index: np.ndarray | None = None, top_k: int = 1,
+                 out_f32: bool = False, row_sel: np.ndarray | None = None, group: int = 128,
+                 out: np.ndarray | None = None):
+    """Grouped GEMM over expert slabs (see oracle_grouped_gemm in moe_oracle.c).
+
+    wq: uint8 [E_loc, N, K/2]; s: uint16 (bf16) [E_loc, N, K/group]; a: uint16 [*, K].
+    Returns c [rows, out_cols] as float32 or uint16 (bf16); rows not computed stay 0.
+    """
+    E_loc, N, K2 = wq.shape
+    K = 2 * K2
+    out_cols = N // 2 if kind == W13_SWIGLU else N
+    if out is None:
+        out = np.zeros((rows, out_cols), np.float32 if out_f32 else np.uint16)
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    assert a.shape[-1] == K
+    idx = None if a_row_index is None else np.ascontiguousarray(a_row_index, dtype=np.int32)
+    sel = None if row_sel is None else np.ascontiguousarray(row_sel, dtype=np.uint8)
+    _load().oracle_grouped_gemm(kind, E_loc, N, K, group, _ptr(a), _ptr(idx), top_k,
+                                _ptr(np.ascontiguousarray(offsets, dtype=np.int32)),
+                                _ptr(np.ascontiguousarray(wq)), _ptr(np.ascontiguousarray(s)),
+                                _ptr(sel), _ptr(out), 1 if out_f32 else 0)
+    return out
+
+
+def finalize(y: np.ndarray, topk_w: np.ndarray, inv_perm: np.ndarray, *, out_f32: bool,
+             tok_sel: np.ndarray | None = None):
+    """Slot-ordered combine. y: float32 or uint16 (bf16) [R, H]."""
+    topk_w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    inv_perm = np.ascontiguousarray(inv_perm, dtype=np.int32)
+    T, k = topk_w.shape
+    H = y.shape[-1]
+    y_f32 = y.dtype == np.float32
+    assert y_f32 or y.dtype == np.uint16
+    out = np.zeros((T, H), np.float32 if out_f32 else np.uint16)
+    sel = None if tok_sel is None else np.ascontiguousarray(tok_sel, dtype=np.uint8)
+    _load().oracle_finalize(T, k, H, _ptr(np.ascontiguousarray(y)), 1 if y_f32 else 0, _ptr(topk_w),
+                            _ptr(inv_perm), _ptr(sel), _ptr(out), 1 if out_f32 else 0)
+    return out
+
+
+def layer(x, logits, w13_q, s13, w2_q, s2, *, top_k: int, expert_begin: int = 0,
+          tok_sel: np.ndarray | None = None, group: int = 128):
+    """The whole layer through the permutation; returns a dict of every stage."""
+    T, H = x.shape
+    E_g = logits.shape[1]
+    E_loc, N13, _ = w13_q.shape
+    I = N13 // 2
+    S = T * top_k
+    r = dict(
+        topk_ids=np.empty((T, top_k), np.int32), topk_w=np.empty((T, top_k), np.float32),
+        counts=np.empty(E_loc, np.int32), offsets=np.empty(E_loc + 1, np.int32),
+        perm=np.empty(S, np.int32), inv_perm=np.empty((T, top_k), np.int32),
+        h=np.zeros((S, I), np.uint16), y=np.zeros((S, H), np.uint16), out=np.zeros((T, H), np.uint16))
+    sel = None if tok_sel is None else np.ascontiguousarray(tok_sel, dtype=np.uint8)
+    _load().oracle_layer(T, E_g, top_k, expert_begin, E_loc, H, I, group,
+                         _ptr(np.ascontiguousarray(x, dtype=np.uint16)),
+                         _ptr(np.ascontiguousarray(logits, dtype=np.float32)),
+                         _ptr(np.ascontiguousarray(w13_q)), _ptr(np.ascontiguousarray(s13)),
+                         _ptr(np.ascontiguousarray(w2_q)), _ptr(np.ascontiguousarray(s2)), _ptr(sel),
+                         _ptr(r["topk_ids"]), _ptr(r["topk_w"]), _ptr(r["counts"]), _ptr(r["offsets"]),
+                         _ptr(r["perm"]), _ptr(r["inv_perm"]), _ptr(r["h"]), _ptr(r["y"]), _ptr(r["out"]))
+    return r
+
+
+def layer_bruteforce(x, topk_ids, topk_w, w13_q, s13, w2_q, s2, *, expert_begin: int = 0,
+                     tok_sel: np.ndarray | None = None, group: int = 128):
+    """Naive per-(token, slot) expert MLPs + ordered combine; no permutation."""
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    E_loc, N13, _ = w13_q.shape
+    I = N13 // 2
+    out = np.zeros((T, H), np.uint16)
+    sel = None if tok_sel is None else np.ascontiguousarray(tok_sel, dtype=np.uint8)
+    _load().oracle_layer_bruteforce(T, k, expert_begin, E_loc, H, I, group,
+                                    _ptr(np.ascontiguousarray(x, dtype=np.uint16)),
+                                    _ptr(np.ascontiguousarray(topk_ids, dtype=np.int32)),
+                                    _ptr(np.ascontiguousarray(topk_w, dtype=np.float32)),
+                                    _ptr(np.ascontiguousarray(w13_q)), _ptr(np.ascontiguousarray(s13)),
+                                    _ptr(np.ascontiguousarray(w2_q)), _ptr(np.ascontiguousarray(s2)),
+                                    _ptr(sel), _ptr(out))
+    return out
