@@ -1,0 +1,194 @@
+/*
+ * moe_w4a16.h -- C ABI of the MI355X (gfx950) W4A16 Mixture-of-Experts
+ * expert layer: top-k routing, stable expert permutation, grouped GEMM over
+ * expert slabs on int4 group-scaled weights with bf16 activations (gate/up
+ * with fused SwiGLU, then down), and the slot-ordered finalize combine.
+ *
+ * Pages that define the operations (cited by title and section):
+ *   [FI] "FlashInfer, CuTe DSL W4A16 MoE optimization and bitwise-exactness
+ *        tests" (FlashInfer PR #7196 analysis): section 1 `moe_finalize.py`
+ *        (combine: fp32 multiply for the first slot, fp32 FMA for later slots
+ *        in slot order, no flush-to-zero); section 2 `moe_w4a16_kernel.py`
+ *        (runtime MMA N from the routed-token count, skipping inactive
+ *        subtiles; valid-rows-only bf16 permutation; SwiGLU); section 3
+ *        (zero-tolerance checks).
+ *   [IL] "T2-1-3 Qwen3-MoE inference optimization report" (InfiniLM PR #500):
+ *        section 2.2 (bucket the routing ids into per-expert counts and a
+ *        permutation, gather, grouped GEMMs gate/up/down + SwiGLU, weighted
+ *        scatter back to tokens; grouped_gemm takes group sizes); section
+ *        2.3 (the host-side count passthrough that skips a device-to-host
+ *        sync -- here counts never leave the device at all).
+ *   [GC] "GC-MoE: Overlapping Expert-Parallel Token Dispatch with FP8/FP4
+ *        Grouped GEMM via CUDA Green Contexts" (abstract): decode holds 1-256
+ *        tokens per rank and is dominated by weight traffic; operand-swapped
+ *        MMA; in-register 4-bit decode fed to the matrix unit; fused SwiGLU.
+ *   [FI2] "FlashInfer, NVFP4 SVDQuant GEMM kernel optimization: per-
+ *        architecture dispatch" (FlashInfer PR #6986 analysis), section 1:
+ *        `is_supported` answers a shape query without raising; `run` raises.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are caller-owned DEVICE memory, 16-byte aligned
+ *     (workspace: 256-byte aligned). The library never allocates, frees or
+ *     synchronises and never reads device data on the host.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and the call returns after launching, so the calls can be
+ *     captured into a HIP graph. No memset nodes are issued.
+ *   - Host-side validation failures return an error BEFORE any launch, so
+ *     outputs are untouched. A launch failure returns MOE_ERR_HIP. Faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - The library is stateless; calls are thread-safe.
+ *
+ * Storage formats (row-major, contiguous):
+ *   bf16 values are 16-bit patterns (uint16_t here).
+ *   int4 weights: two's-complement codes in [-8, 7], element k of a row in
+ *   byte k/2, even k in the low nibble, K contiguous; no zero point.
+ *   Scales: one bf16 per (weight row, 128-wide K group): W[n][k] =
+ *   q[n][k] * s[n][k/128].
+ *   w13_q  uint8 [E_loc][2*I][H/2], s13 bf16 [E_loc][2*I][H/128]: rows
+ *          [0, I) are the gate projection, [I, 2I) the up projection.
+ *   w2_q   uint8 [E_loc][H][I/2],   s2  bf16 [E_loc][H][I/128].
+ *   Weight arrays start at local expert 0 (global id expert_begin).
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    MOE_ERR_SHAPE = 2,       /* sizes inconsistent or out of range             */
+    MOE_ERR_UNSUPPORTED = 3, /* valid but not supported (group != 128, ...)    */
+    MOE_ERR_ALIGN = 4,       /* a pointer violates its alignment requirement   */
+    MOE_ERR_WORKSPACE = 5,   /* workspace too small                            */
+    MOE_ERR_HIP = 6          /* a kernel launch failed                         */
+} moe_status;
+
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
+
+typedef enum {
+    MOE_GEMM_W13_SWIGLU = 0, /* a[R][H] x w13^T -> h[R][I] = bf16(silu(g) * u)  */
+    MOE_GEMM_W2 = 1,         /* a[R][I] x w2^T  -> c[R][H] (bf16 or f32)         */
+    MOE_GEMM_W13_RAW = 2     /* a[R][H] x w13^T -> c[R][2I] (no activation)      */
+} moe_gemm_kind;
+
+typedef struct {
+    int32_t num_tokens;        /* T >= 0                                         */
+    int32_t hidden;            /* H, multiple of 128, <= 16384                   */
+    int32_t inter;             /* I, multiple of 128, <= 16384                   */
+    int32_t num_experts;       /* E_g: router logit columns, 1..1024             */
+    int32_t expert_begin;      /* global id of local expert 0                    */
+    int32_t num_local_experts; /* E_loc, 1..1024, expert_begin+E_loc <= E_g      */
+    int32_t top_k;             /* 1..min(E_g, 16)                                */
+    int32_t group_size;        /* quantisation group along K: 128 only           */
+} moe_shape;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *moe_status_str(moe_status s);
+
+/* Validate a shape without raising: MOE_OK if every entry point supports it,
+ * else the status forward() would return ([FI2] section 1: is_supported). */
+moe_status moe_w4a16_check_shape(const moe_shape *shape);
+
+/* 1 if moe_w4a16_check_shape(shape) == MOE_OK, else 0. Never an error. */
+int moe_w4a16_is_supported(const moe_shape *shape);
+
+/* Bytes of workspace moe_w4a16_forward needs for this shape (0 if the shape
+ * is invalid). Layout is private to the library. */
+size_t moe_w4a16_workspace_size(const moe_shape *shape);
+
+/*
+ * The whole layer: route -> permute -> GEMM1 (w13, SwiGLU) -> GEMM2 (w2) ->
+ * finalize, all on `stream`, no host synchronisation.
+ *   x             bf16  [T][H]        activations
+ *   router_logits f32   [T][E_g]
+ *   w13_q, s13, w2_q, s2              local experts' weights (formats above)
+ *   out           bf16  [T][H]        written for every token; a token with no
+ *                                     local slot gets +0.0
+ *   workspace     >= moe_w4a16_workspace_size(shape) bytes, 256-B aligned
+ * T == 0 is a no-op returning MOE_OK.
+ */
+moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const float *router_logits,
+                             const uint8_t *w13_q, const uint16_t *s13, const uint8_t *w2_q,
+                             const uint16_t *s2, uint16_t *out, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * Top-k routing ([FI] section 2; the layer definition: softmax over all E_g
+ * experts, keep the top-k, renormalise). Selection order: larger logit first,
+ * lower expert index first among equal logits (-0 == +0); the i-th selected
+ * expert is slot i. topk_w[t][i] = exp(l_i - l_0) / sum_{j<k} exp(l_j - l_0)
+ * in fp32 (equal to the renormalised softmax up to rounding).
+ *   logits f32 [T][E_g] -> topk_ids int32 [T][k] (global ids), topk_w f32 [T][k]
+ */
+moe_status moe_route(const moe_shape *shape, const float *logits, int32_t *topk_ids,
+                     float *topk_w, void *stream);
+
+/* Workspace bytes moe_permute needs (0 if the shape is invalid). */
+size_t moe_permute_workspace_size(const moe_shape *shape);
+
+/*
+ * Stable expert permutation ([IL] section 2.2; [FI] section 2 permutation).
+ * Slots (t, j) routed to local experts [expert_begin, expert_begin+E_loc) are
+ * bucketed by expert, token-ascending within each expert.
+ *   topk_ids int32 [T][k] ->
+ *   counts   int32 [E_loc]      slots per local expert
+ *   offsets  int32 [E_loc+1]    exclusive scan of counts; R = offsets[E_loc]
+ *   perm     int32 [T*k]        row r < R holds slot id t*k+j; rows >= R get -1
+ *   inv_perm int32 [T][k]       row of slot (t, j), or -1 if not local
+ *   x / x_perm (both NULL, or both set): x bf16 [T][H] gathered into
+ *                x_perm bf16 [T*k][H], row r = x[perm[r] / k] (rows >= R
+ *                untouched)
+ * Bit-exact and deterministic (no atomics decide a position).
+ */
+moe_status moe_permute(const moe_shape *shape, const int32_t *topk_ids, const uint16_t *x,
+                       int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
+                       uint16_t *x_perm, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Grouped GEMM over expert slabs with int4 group-scaled weights and bf16
+ * activations ([IL] section 2.2 grouped_gemm with group sizes; [FI] section
+ * 2 runtime N; [GC] abstract: in-register 4-bit decode fed to the matrix
+ * unit). For local expert e and rows r in [offsets[e], offsets[e+1]):
+ *   A row r = a[a_row_index[r] / top_k]   if a_row_index != NULL (gather
+ *             straight from the unpermuted activations through perm)
+ *           = a[r]                         otherwise.
+ *   W13_SWIGLU: K = H, weights w13 (2I rows); c = h bf16 [T*k][I] with
+ *               h = bf16(silu(g) * u), g = A.W_gate^T, u = A.W_up^T.
+ *   W13_RAW:    K = H, c [T*k][2I] = A.w13^T, bf16 or f32 (c_dtype).
+ *   W2:         K = I, c [T*k][H]  = A.w2^T,  bf16 or f32 (c_dtype).
+ * Accumulation is fp32 over exact int4 codes; the scale of each 128-wide
+ * group is applied in fp32. Rows >= R of c are untouched. `offsets` stays on
+ * the device: the grid never depends on the counts.
+ */
+moe_status moe_grouped_gemm_w4a16(const moe_shape *shape, moe_gemm_kind kind, const uint16_t *a,
+                                  const int32_t *a_row_index, const int32_t *offsets,
+                                  const uint8_t *wq, const uint16_t *s, void *c, moe_dtype c_dtype,
+                                  void *stream);
+
+/*
+ * Finalize: weighted unpermute / combine ([FI] section 1 `moe_finalize.py`).
+ * For every token t and column c < H: the first slot j (slot order) with
+ * inv_perm[t][j] >= 0 gives acc = y[r][c] * w[t][j] (IEEE binary32 multiply,
+ * round to nearest even); each later present slot gives
+ * acc = fma(y[r][c], w[t][j], acc) (IEEE binary32 FMA); no slot -> +0.0.
+ * No flush-to-zero: subnormal inputs, products and sums are kept.
+ *   y       [T*k][H]  bf16 or f32 (y_dtype)
+ *   topk_w  f32 [T][k], inv_perm int32 [T][k]
+ *   out     [T][H]    f32 (the accumulator) or bf16 (its RNE rounding)
+ * Bit-exact against the IEEE definition.
+ */
+moe_status moe_finalize(const moe_shape *shape, const void *y, moe_dtype y_dtype,
+                        const float *topk_w, const int32_t *inv_perm, void *out,
+                        moe_dtype out_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

@@ -1,0 +1,55 @@
+"""Shared test helpers: device transfer of numpy inputs and the layer tolerance."""
+import sys
+
+import numpy as np
+
+# Full-layer tolerance (floating point; MFMA accumulation order, the exp
+# implementation and bf16 rounding points differ from the fp64 oracle):
+#   max |gpu - ref| <= 2e-2 * max |ref|   and   sum |gpu - ref| / sum |ref| <= 5e-3
+MAX_ABS_FRAC = 2e-2
+MEAN_REL = 5e-3
+
+
+def say(*a):
+    """Name the case before a GPU step (unbuffered)."""
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(a, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def bf16_dev(a_u16):
+    import torch
+    return to_dev(np.ascontiguousarray(a_u16, dtype=np.uint16)).view(torch.bfloat16)
+
+
+def to_np_u16(t):
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_to_f64(a_u16):
+    return (np.asarray(a_u16, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def layer_errors(got_u16, ref_u16):
+    g = bf16_to_f64(got_u16)
+    r = bf16_to_f64(ref_u16)
+    d = np.abs(g - r)
+    max_ref = float(np.abs(r).max()) if r.size else 0.0
+    max_err = float(d.max()) if d.size else 0.0
+    mean_rel = float(d.sum() / max(np.abs(r).sum(), 1e-300)) if r.size else 0.0
+    return max_err, max_ref, mean_rel
+
+
+def assert_layer_close(got_u16, ref_u16, what=""):
+    max_err, max_ref, mean_rel = layer_errors(got_u16, ref_u16)
+    say(f"  {what}: max|d|={max_err:.3e} max|ref|={max_ref:.3e} ({max_err / max(max_ref, 1e-300):.2e}) "
+        f"mean_rel={mean_rel:.2e}")
+    assert max_err <= MAX_ABS_FRAC * max_ref, (what, max_err, max_ref)
+    assert mean_rel <= MEAN_REL, (what, mean_rel)

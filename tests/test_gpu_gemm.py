@@ -1,0 +1,118 @@
+"""GPU grouped W4A16 GEMM vs the oracle.
+
+- Integer-exact pin: activations in {-2..2}, codes in [-8, 7], every scale
+  2^-6: every partial sum is exact in fp32 under any order, so the GPU result
+  (W13_RAW and W2 with fp32 output) must equal the oracle and numpy's int64
+  matmul bit for bit. Ragged expert loads (empty experts, counts above one
+  chunk) and the gather through a permutation are covered.
+- One-hot activations read single weight columns back exactly.
+- W13 + SwiGLU and W2 (bf16) against the oracle within a rounding bound.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import bf16_dev, say, to_dev, to_np_u16, bf16_to_f64
+from w4a16_grouped_gemm_amd.inputs import bf16_bits, make_layer_inputs, pack_int4
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [0, 1, 17, 40, 3, 0, 70, 16, 33, 128]
+
+
+def _offsets(counts):
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+def _gpu_gemm(kind, a, offsets, wq, s, *, T, k, a_row_index=None, out_f32=True):
+    import torch
+    from w4a16_grouped_gemm_amd import ops
+    out = ops.grouped_gemm_w4a16(kind, bf16_dev(a), to_dev(offsets), to_dev(wq), bf16_dev(s), num_tokens=T,
+                                 top_k=k, a_row_index=None if a_row_index is None else to_dev(a_row_index),
+                                 out_dtype=torch.float32 if out_f32 else torch.bfloat16)
+    torch.cuda.synchronize()
+    return out.cpu().numpy() if out_f32 else to_np_u16(out)
+
+
+@pytest.mark.parametrize("kind,H,I", [(2, 2048, 768), (1, 2048, 768), (2, 7168, 256), (1, 256, 2048),
+                                      (2, 256, 512), (1, 256, 512)])
+@pytest.mark.parametrize("gather", [False, True])
+def test_integer_exact(kind, H, I, gather):
+    from w4a16_grouped_gemm_amd import ops
+    say(f"gemm integer-exact kind={kind} H={H} I={I} gather={gather}")
+    rng = np.random.default_rng(H + I + kind)
+    counts = np.array(RAGGED)
+    E = len(counts)
+    N, K = (2 * I, H) if kind == ops.W13_RAW else (H, I)
+    q = rng.integers(-8, 8, size=(E, N, K), dtype=np.int8)
+    s = np.full((E, N, K // 128), bf16_bits(np.float32(2.0 ** -6)), np.uint16)
+    offsets = _offsets(counts)
+    R = int(offsets[-1])
+    k = 4
+    T = (R + k - 1) // k + 1
+    xi = rng.integers(-2, 3, size=(T if gather else R, K))
+    a = bf16_bits(xi.astype(np.float32))
+    idx = None
+    if gather:
+        idx = np.full(T * k, -1, np.int32)
+        idx[:R] = rng.permutation(T * k)[:R].astype(np.int32)
+    wq = pack_int4(q)
+    got = _gpu_gemm(kind, a, offsets, wq, s, T=T, k=k, a_row_index=idx)
+    ref = oracle.grouped_gemm(oracle.RAW, a, offsets, wq, s, rows=T * k, a_row_index=idx, top_k=k,
+                              out_f32=True)
+    assert np.array_equal(got[:R].view(np.uint32), ref[:R].view(np.uint32))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        rows = xi[idx[r0:r1] // k] if gather else xi[r0:r1]
+        want = (rows.astype(np.int64) @ q[e].T.astype(np.int64)).astype(np.float64) * 2.0 ** -6
+        assert np.array_equal(got[r0:r1].astype(np.float64), want), e
+
+
+def test_one_hot_columns():
+    from w4a16_grouped_gemm_amd import ops
+    say("gemm one-hot")
+    rng = np.random.default_rng(77)
+    E, N, K = 4, 256, 1024
+    q = rng.integers(-8, 8, size=(E, N, K), dtype=np.int8)
+    sexp = rng.integers(-9, -3, size=(E, N, K // 128))
+    s = bf16_bits((2.0 ** sexp).astype(np.float32))
+    counts = np.array([5, 0, 37, 22])
+    offsets = _offsets(counts)
+    R = int(offsets[-1])
+    ks = rng.integers(0, K, size=R)
+    a = bf16_bits(np.eye(K, dtype=np.float32)[ks])
+    got = _gpu_gemm(ops.W13_RAW, a, offsets, pack_int4(q), s, T=R, k=1)
+    for e in range(E):
+        for r in range(offsets[e], offsets[e + 1]):
+            want = q[e, :, ks[r]].astype(np.float64) * 2.0 ** sexp[e, :, ks[r] // 128]
+            assert np.array_equal(got[r].astype(np.float64), want), (e, r)
+
+
+def _close_bf16(got_u16, ref_u16, what):
+    g, r = bf16_to_f64(got_u16), bf16_to_f64(ref_u16)
+    bound = 2.0 ** -7 * np.abs(r) + 1e-3 * np.abs(r).max()
+    bad = np.abs(g - r) > bound
+    exact = float((got_u16 == ref_u16).mean())
+    say(f"  {what}: exact bf16 matches {exact:.3f}, out of bound {int(bad.sum())}")
+    assert not bad.any(), what
+    assert exact > 0.5, what
+
+
+@pytest.mark.parametrize("wl,T", [("tiny", 16), ("qwen3_decode", 64), ("qwen3_prefill", 256)])
+def test_swiglu_and_down_vs_oracle(wl, T):
+    from w4a16_grouped_gemm_amd import ops
+    say(f"gemm w13+swiglu / w2 {wl} T={T}")
+    inp = make_layer_inputs(wl, T)
+    k = inp.workload.top_k
+    ids, _ = oracle.route(inp.logits, k)
+    _, offsets, perm, _ = oracle.permute(ids, inp.workload.num_local_experts, 0)
+    R = int(offsets[-1])
+    h_ref = oracle.grouped_gemm(oracle.W13_SWIGLU, inp.x, offsets, inp.w13_q, inp.s13, rows=T * k,
+                                a_row_index=perm, top_k=k)
+    h = _gpu_gemm(ops.W13_SWIGLU, inp.x, offsets, inp.w13_q, inp.s13, T=T, k=k, a_row_index=perm,
+                  out_f32=False)
+    _close_bf16(h[:R], h_ref[:R], "h")
+    # down projection on the oracle's h (inputs never come from the GPU path)
+    y_ref = oracle.grouped_gemm(oracle.W2, h_ref, offsets, inp.w2_q, inp.s2, rows=T * k)
+    y = _gpu_gemm(ops.W2, h_ref, offsets, inp.w2_q, inp.s2, T=T, k=k, out_f32=False)
+    _close_bf16(y[:R], y_ref[:R], "y")

@@ -1,0 +1,55 @@
+"""The C-ABI library loads and exports every symbol include/moe_w4a16.h declares (no GPU, no compute)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from w4a16_grouped_gemm_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.fail("libmoe_w4a16.so is not built; run __graft_entry__.build()")
+    return ctypes.CDLL(ops.LIB_PATH)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(ops.EXPORTED)
+
+
+def test_shape_queries_without_gpu():
+    # pure host-side validation: no device needed
+    ok = ops.make_shape(16, 256, 512, 8, 8, 2)
+    assert ops.is_supported(ok) and ops.check_shape(ok) == 0
+    assert ops.workspace_size(ok) > 0
+    bad = [ops.make_shape(16, 200, 512, 8, 8, 2),          # H % 128
+           ops.make_shape(16, 256, 512, 8, 8, 9),          # k > E
+           ops.make_shape(16, 256, 512, 8, 8, 17),         # k > 16
+           ops.make_shape(-1, 256, 512, 8, 8, 2),
+           ops.make_shape(16, 256, 512, 8, 4, 2, expert_begin=6),
+           ops.make_shape(16, 256, 512, 2000, 8, 2)]
+    for b in bad:
+        assert not ops.is_supported(b)
+        assert ops.check_shape(b) == 2
+        assert ops.workspace_size(b) == 0
+    g64 = ops.make_shape(16, 256, 512, 8, 8, 2, group_size=64)
+    assert ops.check_shape(g64) == 3
+    assert ops.status_str(0) == "MOE_OK"

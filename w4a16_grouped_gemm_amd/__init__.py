@@ -7,14 +7,12 @@ marshalling only). PyTorch provides device memory and streams.
 Importing the package does not load the native library; the first call into
 ``ops`` does, and raises if the library is missing.
 """
+import importlib
+
 __all__ = ["ops", "inputs"]
 
 
 def __getattr__(name):
-    if name == "ops":
-        from . import ops as _ops
-        return _ops
-    if name == "inputs":
-        from . import inputs as _inputs
-        return _inputs
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

@@ -1,0 +1,301 @@
+// api.hip -- the C ABI: argument validation, workspace layout and the launch
+// sequence of the whole layer. No allocation, no synchronisation, no device
+// reads on the host: every call only enqueues kernels on the caller's stream.
+//
+// Error convention after the FlashInfer PR #6986 analysis, section 1:
+// shape queries (check_shape / is_supported) answer without failing; the run
+// entry points return a status and launch nothing when validation fails.
+#include <mutex>
+
+#include "common.hpp"
+
+namespace moe {
+
+int device_cu_count()
+{
+    static int cache[64];
+    static std::once_flag once[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    std::call_once(once[dev], [dev] {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    });
+    return cache[dev];
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status check_shape(const moe_shape *sh)
+{
+    if (!sh)
+        return MOE_ERR_NULL;
+    if (sh->group_size != kGroup)
+        return MOE_ERR_UNSUPPORTED;
+    if (sh->num_tokens < 0 || sh->num_tokens > kMaxTokens)
+        return MOE_ERR_SHAPE;
+    if (sh->hidden < kGroup || sh->hidden > kMaxDim || sh->hidden % kGroup)
+        return MOE_ERR_SHAPE;
+    if (sh->inter < kGroup || sh->inter > kMaxDim || sh->inter % kGroup)
+        return MOE_ERR_SHAPE;
+    if (sh->num_experts < 1 || sh->num_experts > kMaxExperts)
+        return MOE_ERR_SHAPE;
+    if (sh->num_local_experts < 1 || sh->num_local_experts > kMaxExperts)
+        return MOE_ERR_SHAPE;
+    if (sh->expert_begin < 0 || sh->expert_begin + sh->num_local_experts > sh->num_experts)
+        return MOE_ERR_SHAPE;
+    if (sh->top_k < 1 || sh->top_k > kMaxTopK || sh->top_k > sh->num_experts)
+        return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+// Forward workspace layout (each region 256-byte aligned).
+struct Workspace {
+    int32_t *ids;
+    float *w;
+    int32_t *counts;
+    int32_t *offsets;
+    int32_t *perm;
+    int32_t *inv_perm;
+    uint16_t *h;
+    uint16_t *y;
+    size_t bytes;
+};
+
+Workspace carve(const moe_shape &sh, void *base)
+{
+    const size_t S = (size_t)sh.num_tokens * sh.top_k;
+    const size_t E = (size_t)sh.num_local_experts;
+    char *p = static_cast<char *>(base);
+    size_t off = 0;
+    Workspace ws{};
+    auto take = [&](size_t bytes) {
+        char *r = p ? p + off : nullptr;
+        off += align_up(bytes);
+        return r;
+    };
+    ws.ids = reinterpret_cast<int32_t *>(take(S * 4));
+    ws.w = reinterpret_cast<float *>(take(S * 4));
+    ws.counts = reinterpret_cast<int32_t *>(take(E * 4));
+    ws.offsets = reinterpret_cast<int32_t *>(take((E + 1) * 4));
+    ws.perm = reinterpret_cast<int32_t *>(take(S * 4));
+    ws.inv_perm = reinterpret_cast<int32_t *>(take(S * 4));
+    ws.h = reinterpret_cast<uint16_t *>(take(S * (size_t)sh.inter * 2));
+    ws.y = reinterpret_cast<uint16_t *>(take(S * (size_t)sh.hidden * 2));
+    ws.bytes = off;
+    return ws;
+}
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+GemmLaunch gemm_args(const moe_shape &sh, moe_gemm_kind kind)
+{
+    GemmLaunch g{};
+    g.kind = kind;
+    g.top_k = sh.top_k;
+    g.num_experts = sh.num_local_experts;
+    g.max_rows = sh.num_tokens * sh.top_k;
+    // expected local rows: the routed slots that land on this GPU's experts
+    g.expected_rows = (int)((long long)g.max_rows * sh.num_local_experts / sh.num_experts);
+    if (kind == MOE_GEMM_W2) {
+        g.K = sh.inter;
+        g.N = sh.hidden;
+    } else {
+        g.K = sh.hidden;
+        g.N = 2 * sh.inter;
+    }
+    return g;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char *moe_status_str(moe_status s)
+{
+    switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: sizes inconsistent or out of range";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: configuration not supported";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: pointer misaligned";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: kernel launch failed";
+    }
+    return "unknown moe_status";
+}
+
+moe_status moe_w4a16_check_shape(const moe_shape *shape) { return check_shape(shape); }
+
+int moe_w4a16_is_supported(const moe_shape *shape) { return check_shape(shape) == MOE_OK ? 1 : 0; }
+
+size_t moe_w4a16_workspace_size(const moe_shape *shape)
+{
+    if (check_shape(shape) != MOE_OK)
+        return 0;
+    return carve(*shape, nullptr).bytes;
+}
+
+size_t moe_permute_workspace_size(const moe_shape *shape)
+{
+    if (check_shape(shape) != MOE_OK)
+        return 0;
+    return 0;
+}
+
+moe_status moe_route(const moe_shape *shape, const float *logits, int32_t *topk_ids, float *topk_w,
+                     void *stream)
+{
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK)
+        return st;
+    if (shape->num_tokens == 0)
+        return MOE_OK;
+    if (!logits || !topk_ids || !topk_w)
+        return MOE_ERR_NULL;
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+        return MOE_ERR_ALIGN;
+    return from_hip(launch_route(*shape, logits, topk_ids, topk_w, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_permute(const moe_shape *shape, const int32_t *topk_ids, const uint16_t *x,
+                       int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
+                       uint16_t *x_perm, void *workspace, size_t workspace_bytes, void *stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK)
+        return st;
+    if (!counts || !offsets)
+        return MOE_ERR_NULL;
+    if ((x == nullptr) != (x_perm == nullptr))
+        return MOE_ERR_NULL;
+    if (shape->num_tokens > 0 && (!topk_ids || !perm || !inv_perm))
+        return MOE_ERR_NULL;
+    if (x && (!aligned(x, 16) || !aligned(x_perm, 16)))
+        return MOE_ERR_ALIGN;
+    if (!aligned(counts, 4) || !aligned(offsets, 4) || !aligned(topk_ids, 4) || !aligned(perm, 4) ||
+        !aligned(inv_perm, 4))
+        return MOE_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_permute(*shape, topk_ids, counts, offsets, perm, inv_perm, s);
+    if (e == hipSuccess && x && shape->num_tokens > 0)
+        e = launch_gather(*shape, x, perm, offsets, x_perm, s);
+    return from_hip(e);
+}
+
+moe_status moe_grouped_gemm_w4a16(const moe_shape *shape, moe_gemm_kind kind, const uint16_t *a,
+                                  const int32_t *a_row_index, const int32_t *offsets,
+                                  const uint8_t *wq, const uint16_t *s, void *c, moe_dtype c_dtype,
+                                  void *stream)
+{
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK)
+        return st;
+    if (kind != MOE_GEMM_W13_SWIGLU && kind != MOE_GEMM_W2 && kind != MOE_GEMM_W13_RAW)
+        return MOE_ERR_UNSUPPORTED;
+    if (c_dtype != MOE_BF16 && c_dtype != MOE_F32)
+        return MOE_ERR_UNSUPPORTED;
+    if (kind == MOE_GEMM_W13_SWIGLU && c_dtype != MOE_BF16)
+        return MOE_ERR_UNSUPPORTED;
+    if (shape->num_tokens == 0)
+        return MOE_OK;
+    if (!a || !offsets || !wq || !s || !c)
+        return MOE_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(wq, 16) || !aligned(c, 16) || !aligned(s, 2) ||
+        !aligned(offsets, 4) || (a_row_index && !aligned(a_row_index, 4)))
+        return MOE_ERR_ALIGN;
+    GemmLaunch g = gemm_args(*shape, kind);
+    g.a = a;
+    g.a_row_index = a_row_index;
+    g.offsets = offsets;
+    g.wq = wq;
+    g.s = s;
+    g.c = c;
+    g.c_f32 = c_dtype == MOE_F32;
+    return from_hip(launch_grouped_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_finalize(const moe_shape *shape, const void *y, moe_dtype y_dtype,
+                        const float *topk_w, const int32_t *inv_perm, void *out, moe_dtype out_dtype,
+                        void *stream)
+{
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK)
+        return st;
+    if ((y_dtype != MOE_BF16 && y_dtype != MOE_F32) || (out_dtype != MOE_BF16 && out_dtype != MOE_F32))
+        return MOE_ERR_UNSUPPORTED;
+    if (shape->num_tokens == 0)
+        return MOE_OK;
+    if (!y || !topk_w || !inv_perm || !out)
+        return MOE_ERR_NULL;
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_w, 4) || !aligned(inv_perm, 4))
+        return MOE_ERR_ALIGN;
+    return from_hip(launch_finalize(*shape, y, y_dtype == MOE_F32, topk_w, inv_perm, out,
+                                    out_dtype == MOE_F32, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const float *router_logits,
+                             const uint8_t *w13_q, const uint16_t *s13, const uint8_t *w2_q,
+                             const uint16_t *s2, uint16_t *out, void *workspace,
+                             size_t workspace_bytes, void *stream)
+{
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK)
+        return st;
+    const moe_shape &sh = *shape;
+    if (sh.num_tokens == 0)
+        return MOE_OK;
+    if (!x || !router_logits || !w13_q || !s13 || !w2_q || !s2 || !out || !workspace)
+        return MOE_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w13_q, 16) || !aligned(w2_q, 16) ||
+        !aligned(s13, 2) || !aligned(s2, 2) || !aligned(router_logits, 4) || !aligned(workspace, kAlign))
+        return MOE_ERR_ALIGN;
+    Workspace ws = carve(sh, workspace);
+    if (workspace_bytes < ws.bytes)
+        return MOE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_route(sh, router_logits, ws.ids, ws.w, s);
+    if (e == hipSuccess)
+        e = launch_permute(sh, ws.ids, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s);
+    if (e == hipSuccess) {
+        GemmLaunch g = gemm_args(sh, MOE_GEMM_W13_SWIGLU);
+        g.a = x;
+        g.a_row_index = ws.perm;
+        g.offsets = ws.offsets;
+        g.wq = w13_q;
+        g.s = s13;
+        g.c = ws.h;
+        g.c_f32 = false;
+        e = launch_grouped_gemm(g, s);
+    }
+    if (e == hipSuccess) {
+        GemmLaunch g = gemm_args(sh, MOE_GEMM_W2);
+        g.a = ws.h;
+        g.a_row_index = nullptr;
+        g.offsets = ws.offsets;
+        g.wq = w2_q;
+        g.s = s2;
+        g.c = ws.y;
+        g.c_f32 = false;
+        e = launch_grouped_gemm(g, s);
+    }
+    if (e == hipSuccess)
+        e = launch_finalize(sh, ws.y, false, ws.w, ws.inv_perm, out, false, s);
+    return from_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// common.hpp -- shared device helpers and the internal launcher interface of
+// the gfx950 W4A16 MoE library. Everything here is gfx950-only HIP.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_w4a16.h"
+
+namespace moe {
+
+constexpr int kGroup = 128;          // quantisation group along K
+constexpr int kMaxExperts = 1024;    // E_g and E_loc limit (LDS tables)
+constexpr int kMaxTopK = 16;
+constexpr int kMaxDim = 16384;       // H and I limit
+constexpr int kMaxTokens = 1 << 18;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// binary32 -> bf16, round to nearest even on the bit pattern (exact for
+// normals, subnormals and overflow; bf16 shares binary32's exponent range so
+// there is nothing to flush). NaN -> quiet NaN with the same sign.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return (u >> 16) | 0x0040u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Wave-level (64-lane) exclusive prefix sum of an int; also returns the total.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int &total)
+{
+    const int lane = threadIdx.x & 63;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int o = __shfl_up(inc, d, 64);
+        if (lane >= d)
+            inc += o;
+    }
+    total = __shfl(inc, 63, 64);
+    return inc - v;
+}
+
+// ---- launchers (host side, one per kernel family) ------------------------
+
+struct GemmLaunch {
+    moe_gemm_kind kind;
+    const uint16_t *a;
+    const int32_t *a_row_index;
+    int top_k;
+    const int32_t *offsets;
+    int num_experts;          // E_loc
+    const uint8_t *wq;
+    const uint16_t *s;
+    void *c;
+    bool c_f32;
+    int K;                    // reduction length
+    int N;                    // weight rows per expert
+    int max_rows;             // T * k: upper bound on R
+    int expected_rows;        // expected R (routed slots on local experts)
+};
+
+hipError_t launch_route(const moe_shape &sh, const float *logits, int32_t *ids, float *w,
+                        hipStream_t st);
+hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *counts,
+                          int32_t *offsets, int32_t *perm, int32_t *inv_perm, hipStream_t st);
+hipError_t launch_gather(const moe_shape &sh, const uint16_t *x, const int32_t *perm,
+                         const int32_t *offsets, uint16_t *x_perm, hipStream_t st);
+hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st);
+hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const float *w,
+                           const int32_t *inv_perm, void *out, bool out_f32, hipStream_t st);
+
+int device_cu_count();
+
+}  // namespace moe

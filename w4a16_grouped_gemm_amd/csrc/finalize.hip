@@ -1,0 +1,109 @@
+// finalize.hip -- weighted unpermute / combine of the expert outputs.
+//
+// FlashInfer PR #7196 analysis, section 1 (`moe_finalize.py`): per output
+// element the first slot is a plain fp32 multiply (so a signed zero survives),
+// every later slot an fp32 FMA in slot order, and the FMA no longer flushes
+// subnormals to zero; section 2 ("Arithmetic Alignment") restates the order.
+// InfiniLM PR #500 report, section 2.2 scatters with index_add_ atomics, which
+// its section 3 blames for run-to-run differences; here the combine is a
+// gather over the token's slots instead, so it is deterministic.
+//
+// gfx950 notes: this file is compiled without FP contraction and with fp32
+// denormals preserved (the kernel descriptor's f32 denorm mode is "keep"),
+// so v_mul_f32 / v_fma_f32 are exactly IEEE binary32 multiply / FMA with
+// round-to-nearest-even. One thread owns 8 consecutive columns of one token:
+// 16-byte (bf16) or 2x16-byte (fp32) coalesced row loads per slot.
+#include "common.hpp"
+
+namespace moe {
+
+namespace {
+
+template <bool Y_F32, bool OUT_F32>
+__global__ __launch_bounds__(256) void finalize_kernel(int T, int k, int H,
+                                                       const void *__restrict__ y,
+                                                       const float *__restrict__ w,
+                                                       const int32_t *__restrict__ inv,
+                                                       void *__restrict__ out)
+{
+    const int vec_per_row = H >> 3;
+    const long long total = (long long)T * vec_per_row;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (long long)gridDim.x * blockDim.x) {
+        const int t = (int)(i / vec_per_row);
+        const int c0 = (int)(i - (long long)t * vec_per_row) * 8;
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            acc[q] = 0.0f;
+        bool first = true;
+        for (int j = 0; j < k; ++j) {
+            const int32_t r = inv[(size_t)t * k + j];
+            if (r < 0)
+                continue;
+            const float wt = w[(size_t)t * k + j];
+            float v[8];
+            if (Y_F32) {
+                const float *src = static_cast<const float *>(y) + (size_t)r * H + c0;
+                const floatx4 a = *reinterpret_cast<const floatx4 *>(src);
+                const floatx4 b = *reinterpret_cast<const floatx4 *>(src + 4);
+                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+                v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+            } else {
+                const uint16_t *src = static_cast<const uint16_t *>(y) + (size_t)r * H + c0;
+                const u32x4 d = *reinterpret_cast<const u32x4 *>(src);
+                v[0] = bf16_to_f32(d.x & 0xFFFFu); v[1] = bf16_to_f32(d.x >> 16);
+                v[2] = bf16_to_f32(d.y & 0xFFFFu); v[3] = bf16_to_f32(d.y >> 16);
+                v[4] = bf16_to_f32(d.z & 0xFFFFu); v[5] = bf16_to_f32(d.z >> 16);
+                v[6] = bf16_to_f32(d.w & 0xFFFFu); v[7] = bf16_to_f32(d.w >> 16);
+            }
+            if (first) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    acc[q] = __fmul_rn(v[q], wt);
+                first = false;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    acc[q] = __fmaf_rn(v[q], wt, acc[q]);
+            }
+        }
+        if (OUT_F32) {
+            float *dst = static_cast<float *>(out) + (size_t)t * H + c0;
+            *reinterpret_cast<floatx4 *>(dst) = floatx4{acc[0], acc[1], acc[2], acc[3]};
+            *reinterpret_cast<floatx4 *>(dst + 4) = floatx4{acc[4], acc[5], acc[6], acc[7]};
+        } else {
+            uint16_t *dst = static_cast<uint16_t *>(out) + (size_t)t * H + c0;
+            *reinterpret_cast<u32x4 *>(dst) =
+                u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                      pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const float *w,
+                           const int32_t *inv_perm, void *out, bool out_f32, hipStream_t st)
+{
+    const long long total = (long long)sh.num_tokens * (sh.hidden / 8);
+    long long blocks = (total + 255) / 256;
+    const long long cap = (long long)device_cu_count() * 32;
+    if (blocks > cap)
+        blocks = cap;
+    if (blocks < 1)
+        blocks = 1;
+    const dim3 grid((unsigned)blocks), block(256);
+    const int T = sh.num_tokens, k = sh.top_k, H = sh.hidden;
+    if (y_f32 && out_f32)
+        hipLaunchKernelGGL((finalize_kernel<true, true>), grid, block, 0, st, T, k, H, y, w, inv_perm, out);
+    else if (y_f32)
+        hipLaunchKernelGGL((finalize_kernel<true, false>), grid, block, 0, st, T, k, H, y, w, inv_perm, out);
+    else if (out_f32)
+        hipLaunchKernelGGL((finalize_kernel<false, true>), grid, block, 0, st, T, k, H, y, w, inv_perm, out);
+    else
+        hipLaunchKernelGGL((finalize_kernel<false, false>), grid, block, 0, st, T, k, H, y, w, inv_perm, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

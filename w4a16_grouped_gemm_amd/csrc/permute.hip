@@ -1,0 +1,191 @@
+// permute.hip -- stable expert permutation: histogram, exclusive scan,
+// token-stable scatter; plus the optional bf16 row gather.
+//
+// InfiniLM PR #500 report, section 2.2: bucket the routing ids into per-expert
+// counts and a permutation, then gather rows by it. Here the bucketing runs on
+// the device (no device-to-host copy, section 2.3's concern disappears) and is
+// deterministic: atomics only count, and a slot's position is
+//   offsets[e] + #{earlier tokens routed to e},
+// computed from per-expert token bitmaps with popcounts. A token's k experts
+// are distinct, so token order alone fixes every position.
+//
+// FlashInfer PR #7196 analysis, section 2 ("specialized BF16 permutation"):
+// copy only the valid rows, with wide vectors; rows are 16-byte aligned here
+// because H is a multiple of 128.
+#include "common.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kPermThreads = 1024;
+constexpr int kMaskBytes = 32 * 1024;   // LDS budget for the token bitmaps
+
+// One workgroup does the whole permutation: T*k <= 16M slots, E_loc <= 1024.
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+    int T, int k, int begin, int E, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm,
+    int chunk_tokens)
+{
+    __shared__ int s_count[kMaxExperts];
+    __shared__ int s_cursor[kMaxExperts];
+    __shared__ int s_wave_tot[kPermThreads / 64];
+    extern __shared__ uint32_t s_mask[];          // [E][words], words = chunk_tokens / 32
+    const int tid = threadIdx.x;
+    const int words = chunk_tokens >> 5;
+    int *s_wprefix = reinterpret_cast<int *>(s_mask + (size_t)E * words);   // [E][words]
+
+    for (int e = tid; e < E; e += kPermThreads)
+        s_count[e] = 0;
+    __syncthreads();
+
+    // 1. histogram of local slots
+    const long long S = (long long)T * k;
+    for (long long i = tid; i < S; i += kPermThreads) {
+        int e = ids[i] - begin;
+        if (e >= 0 && e < E)
+            atomicAdd(&s_count[e], 1);
+    }
+    __syncthreads();
+
+    // 2. exclusive scan over experts (one element per thread per pass)
+    int carry = 0;
+    for (int base = 0; base < E; base += kPermThreads) {
+        int e = base + tid;
+        int v = e < E ? s_count[e] : 0;
+        int wtot;
+        int ex = wave_exclusive_scan(v, wtot);
+        if ((tid & 63) == 0)
+            s_wave_tot[tid >> 6] = wtot;
+        __syncthreads();
+        int wbase = 0, all = 0;
+        for (int w = 0; w < kPermThreads / 64; ++w) {
+            int t = s_wave_tot[w];
+            if (w < (tid >> 6))
+                wbase += t;
+            all += t;
+        }
+        if (e < E) {
+            int off = carry + wbase + ex;
+            offsets[e] = off;
+            counts[e] = v;
+            s_cursor[e] = off;
+        }
+        carry += all;
+        __syncthreads();
+    }
+    if (tid == 0)
+        offsets[E] = carry;
+    const int R = carry;
+
+    // 3. stable scatter, chunk by chunk of tokens
+    for (int t0 = 0; t0 < T; t0 += chunk_tokens) {
+        for (int i = tid; i < E * words; i += kPermThreads)
+            s_mask[i] = 0u;
+        __syncthreads();
+        const int nt = min(chunk_tokens, T - t0);
+        for (int tl = tid; tl < nt; tl += kPermThreads) {
+            const int t = t0 + tl;
+            for (int j = 0; j < k; ++j) {
+                int e = ids[(size_t)t * k + j] - begin;
+                if (e >= 0 && e < E)
+                    atomicOr(&s_mask[e * words + (tl >> 5)], 1u << (tl & 31));
+            }
+        }
+        __syncthreads();
+        // per-expert prefix popcounts over the chunk's words
+        for (int e = tid; e < E; e += kPermThreads) {
+            int run = 0;
+            for (int wd = 0; wd < words; ++wd) {
+                s_wprefix[e * words + wd] = run;
+                run += __popc(s_mask[e * words + wd]);
+            }
+        }
+        __syncthreads();
+        for (int tl = tid; tl < nt; tl += kPermThreads) {
+            const int t = t0 + tl;
+            for (int j = 0; j < k; ++j) {
+                const size_t slot = (size_t)t * k + j;
+                int e = ids[slot] - begin;
+                int32_t row = -1;
+                if (e >= 0 && e < E) {
+                    const uint32_t m = s_mask[e * words + (tl >> 5)];
+                    const int rank = s_wprefix[e * words + (tl >> 5)] +
+                                     __popc(m & ((1u << (tl & 31)) - 1u));
+                    row = s_cursor[e] + rank;
+                    perm[row] = (int32_t)slot;
+                }
+                inv_perm[slot] = row;
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += kPermThreads)
+            s_cursor[e] += s_wprefix[e * words + words - 1] + __popc(s_mask[e * words + words - 1]);
+        __syncthreads();
+    }
+    // rows past R hold no slot
+    for (long long r = R + tid; r < S; r += kPermThreads)
+        perm[r] = -1;
+}
+
+// x_perm[r] = x[perm[r] / k] for r < R; 16 bytes per thread.
+__global__ __launch_bounds__(256) void gather_kernel(int H, int k, int E,
+                                                     const uint16_t *__restrict__ x,
+                                                     const int32_t *__restrict__ perm,
+                                                     const int32_t *__restrict__ offsets,
+                                                     uint16_t *__restrict__ x_perm, long long max_rows)
+{
+    const int R = offsets[E];
+    const int vec_per_row = H >> 3;
+    const long long total = (long long)R * vec_per_row;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (long long)gridDim.x * blockDim.x) {
+        const long long r = i / vec_per_row;
+        const int v = (int)(i - r * vec_per_row);
+        if (r >= max_rows)
+            break;
+        const int src = perm[r] / k;
+        const u32x4 d = *reinterpret_cast<const u32x4 *>(x + (size_t)src * H + (size_t)v * 8);
+        *reinterpret_cast<u32x4 *>(x_perm + (size_t)r * H + (size_t)v * 8) = d;
+    }
+}
+
+}  // namespace
+
+static int chunk_tokens_for(int E)
+{
+    // bitmaps + prefix words: 8 bytes per (expert, 32 tokens)
+    int c = 1024;
+    while (c > 32 && (size_t)E * (c / 32) * 8 > (size_t)kMaskBytes)
+        c >>= 1;
+    return c;
+}
+
+hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *counts,
+                          int32_t *offsets, int32_t *perm, int32_t *inv_perm, hipStream_t st)
+{
+    const int E = sh.num_local_experts;
+    const int chunk = chunk_tokens_for(E);
+    const size_t lds = (size_t)E * (chunk / 32) * 8;
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, st, sh.num_tokens,
+                       sh.top_k, sh.expert_begin, E, ids, counts, offsets, perm, inv_perm, chunk);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const moe_shape &sh, const uint16_t *x, const int32_t *perm,
+                         const int32_t *offsets, uint16_t *x_perm, hipStream_t st)
+{
+    const long long rows = (long long)sh.num_tokens * sh.top_k;
+    const long long total = rows * (sh.hidden / 8);
+    long long blocks = (total + 255) / 256;
+    const long long cap = (long long)device_cu_count() * 16;
+    if (blocks > cap)
+        blocks = cap;
+    if (blocks < 1)
+        blocks = 1;
+    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(256), 0, st, sh.hidden,
+                       sh.top_k, sh.num_local_experts, x, perm, offsets, x_perm, rows);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -132,7 +132,11 @@ class LayerInputs:
     s2: np.ndarray       # uint16 (bf16) [E_loc, H, I/128]
 
 
-def make_layer_inputs(workload: str | Workload, tokens: int, seed: int | None = None) -> LayerInputs:
+def make_layer_inputs(workload: str | Workload, tokens: int, seed: int | None = None,
+                      weights: bool = True) -> LayerInputs:
+    """Draw x, logits and (unless weights=False) the four weight arrays.
+
+    Weights are drawn last, so skipping them leaves x and logits unchanged."""
     wl = WORKLOADS[workload] if isinstance(workload, str) else workload
     T, H, I, E, El = tokens, wl.hidden, wl.inter, wl.num_experts, wl.num_local_experts
     rng = np.random.Generator(np.random.PCG64(seed_for(wl.index, T) if seed is None else seed))
@@ -141,6 +145,8 @@ def make_layer_inputs(workload: str | Workload, tokens: int, seed: int | None = 
         logits = zipf_logits(rng, T, E)
     else:
         logits = rng.standard_normal((T, E), dtype=np.float32)
+    if not weights:
+        return LayerInputs(wl, T, x, logits, None, None, None, None)
     w13_q = random_int4_packed(rng, (El, 2 * I, H // 2))
     s13 = random_scales(rng, (El, 2 * I, H // GROUP))
     w2_q = random_int4_packed(rng, (El, H, I // 2))

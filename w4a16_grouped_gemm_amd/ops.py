@@ -1,0 +1,275 @@
+"""ctypes binding of libmoe_w4a16.so (argument marshalling only).
+
+Every function takes torch tensors on a gfx950 device, checks dtypes and
+shapes, and passes data pointers plus the current (or given) HIP stream to the
+C ABI declared in include/moe_w4a16.h. All arithmetic runs in the library's
+HIP kernels; nothing here computes on the host. If the library is missing the
+first call raises; there is no fallback path.
+
+Status codes map to exceptions: NULL / SHAPE / UNSUPPORTED / ALIGN / WORKSPACE
+raise ValueError, a failed launch raises RuntimeError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
+
+MOE_BF16, MOE_F32 = 0, 1
+W13_SWIGLU, W2, W13_RAW = 0, 1, 2
+_STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
+           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP"}
+EXPORTED = ["moe_status_str", "moe_w4a16_check_shape", "moe_w4a16_is_supported",
+            "moe_w4a16_workspace_size", "moe_w4a16_forward", "moe_route", "moe_permute_workspace_size",
+            "moe_permute", "moe_grouped_gemm_w4a16", "moe_finalize"]
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("expert_begin", ctypes.c_int32),
+                ("num_local_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("group_size", ctypes.c_int32)]
+
+
+class MoeError(ValueError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the C ABI library (once). Raises RuntimeError if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} not found: build it first (python -m w4a16_grouped_gemm_amd.build "
+                               "or __graft_entry__.build())")
+        lib = ctypes.CDLL(path)
+        P, I, S, Z = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(MoeShape), ctypes.c_size_t
+        lib.moe_status_str.argtypes = [I]
+        lib.moe_status_str.restype = ctypes.c_char_p
+        lib.moe_w4a16_check_shape.argtypes = [S]
+        lib.moe_w4a16_check_shape.restype = I
+        lib.moe_w4a16_is_supported.argtypes = [S]
+        lib.moe_w4a16_is_supported.restype = I
+        lib.moe_w4a16_workspace_size.argtypes = [S]
+        lib.moe_w4a16_workspace_size.restype = Z
+        lib.moe_permute_workspace_size.argtypes = [S]
+        lib.moe_permute_workspace_size.restype = Z
+        lib.moe_w4a16_forward.argtypes = [S, P, P, P, P, P, P, P, P, Z, P]
+        lib.moe_w4a16_forward.restype = I
+        lib.moe_route.argtypes = [S, P, P, P, P]
+        lib.moe_route.restype = I
+        lib.moe_permute.argtypes = [S, P, P, P, P, P, P, P, P, Z, P]
+        lib.moe_permute.restype = I
+        lib.moe_grouped_gemm_w4a16.argtypes = [S, I, P, P, P, P, P, P, I, P]
+        lib.moe_grouped_gemm_w4a16.restype = I
+        lib.moe_finalize.argtypes = [S, P, I, P, P, P, I, P]
+        lib.moe_finalize.restype = I
+        _lib = lib
+        return lib
+
+
+def make_shape(num_tokens, hidden, inter, num_experts, num_local_experts, top_k, expert_begin=0,
+               group_size=128) -> MoeShape:
+    return MoeShape(int(num_tokens), int(hidden), int(inter), int(num_experts), int(expert_begin),
+                    int(num_local_experts), int(top_k), int(group_size))
+
+
+def status_str(code: int) -> str:
+    return load_library().moe_status_str(int(code)).decode()
+
+
+def _check(code: int):
+    if code == 0:
+        return
+    msg = status_str(code)
+    if code == 6:
+        raise RuntimeError(msg)
+    raise MoeError(code, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t, dtype, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def check_shape(shape: MoeShape) -> int:
+    return int(load_library().moe_w4a16_check_shape(ctypes.byref(shape)))
+
+
+def is_supported(shape: MoeShape) -> bool:
+    return bool(load_library().moe_w4a16_is_supported(ctypes.byref(shape)))
+
+
+def workspace_size(shape: MoeShape) -> int:
+    return int(load_library().moe_w4a16_workspace_size(ctypes.byref(shape)))
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def route(logits: torch.Tensor, top_k: int, *, stream=None):
+    """Top-k routing -> (topk_ids int32 [T,k], topk_w float32 [T,k])."""
+    _need(logits, torch.float32, "logits")
+    T, E = logits.shape
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    sh = make_shape(T, 128, 128, E, E, top_k)
+    _check(load_library().moe_route(ctypes.byref(sh), _ptr(logits), _ptr(ids), _ptr(w), _stream(stream)))
+    return ids, w
+
+
+def permute(topk_ids: torch.Tensor, num_local_experts: int, *, num_experts: int | None = None,
+            expert_begin: int = 0, x: torch.Tensor | None = None, stream=None):
+    """Stable expert permutation -> (counts, offsets, perm, inv_perm, x_perm or None)."""
+    _need(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    E_g = num_experts if num_experts is not None else expert_begin + num_local_experts
+    H = 128
+    x_perm = None
+    if x is not None:
+        _need(x, torch.bfloat16, "x")
+        H = x.shape[1]
+        x_perm = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    sh = make_shape(T, H, 128, E_g, num_local_experts, k, expert_begin)
+    counts = torch.empty(num_local_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(num_local_experts + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv_perm = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _check(load_library().moe_permute(ctypes.byref(sh), _ptr(topk_ids), _ptr(x), _ptr(counts), _ptr(offsets),
+                                      _ptr(perm), _ptr(inv_perm), _ptr(x_perm), None, 0, _stream(stream)))
+    return counts, offsets, perm, inv_perm, x_perm
+
+
+def grouped_gemm_w4a16(kind: int, a: torch.Tensor, offsets: torch.Tensor, wq: torch.Tensor,
+                       s: torch.Tensor, *, num_tokens: int, top_k: int,
+                       a_row_index: torch.Tensor | None = None, out_dtype=torch.bfloat16,
+                       num_experts: int | None = None, out: torch.Tensor | None = None, stream=None):
+    """Grouped W4A16 GEMM over expert slabs; returns c [num_tokens*top_k, cols]."""
+    _need(a, torch.bfloat16, "a")
+    _need(offsets, torch.int32, "offsets")
+    _need(wq, torch.uint8, "wq")
+    _need(s, torch.bfloat16, "s")
+    if a_row_index is not None:
+        _need(a_row_index, torch.int32, "a_row_index")
+    E_loc, N, K2 = wq.shape
+    K = 2 * K2
+    if kind == W2:
+        H, I = N, K
+        cols = N
+    else:
+        H, I = K, N // 2
+        cols = I if kind == W13_SWIGLU else N
+    if a.shape[-1] != K:
+        raise ValueError(f"a has {a.shape[-1]} columns, weights expect K={K}")
+    if s.shape != (E_loc, N, K // 128):
+        raise ValueError(f"scales shape {tuple(s.shape)} != {(E_loc, N, K // 128)}")
+    rows = num_tokens * top_k
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=a.device)
+    dt = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}.get(out.dtype)
+    if dt is None:
+        raise ValueError("out dtype must be bfloat16 or float32")
+    sh = make_shape(num_tokens, H, I, num_experts or E_loc, E_loc, top_k)
+    _check(load_library().moe_grouped_gemm_w4a16(ctypes.byref(sh), int(kind), _ptr(a), _ptr(a_row_index),
+                                                 _ptr(offsets), _ptr(wq), _ptr(s), _ptr(out), dt,
+                                                 _stream(stream)))
+    return out
+
+
+def finalize(y: torch.Tensor, topk_w: torch.Tensor, inv_perm: torch.Tensor, *,
+             out_dtype=torch.bfloat16, out: torch.Tensor | None = None, stream=None):
+    """Slot-ordered combine -> out [T, H] (float32 accumulator or its bf16 RNE)."""
+    _need(topk_w, torch.float32, "topk_w")
+    _need(inv_perm, torch.int32, "inv_perm")
+    if y.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("y must be bfloat16 or float32")
+    _need(y, y.dtype, "y")
+    T, k = topk_w.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=y.device)
+    sh = make_shape(T, H, 128, k, k, k)
+    ydt = MOE_F32 if y.dtype == torch.float32 else MOE_BF16
+    odt = MOE_F32 if out.dtype == torch.float32 else MOE_BF16
+    _check(load_library().moe_finalize(ctypes.byref(sh), _ptr(y), ydt, _ptr(topk_w), _ptr(inv_perm),
+                                       _ptr(out), odt, _stream(stream)))
+    return out
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    key = (device.index if device.index is not None else torch.cuda.current_device())
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def moe_w4a16_forward(x: torch.Tensor, router_logits: torch.Tensor, w13_q: torch.Tensor,
+                      s13: torch.Tensor, w2_q: torch.Tensor, s2: torch.Tensor, top_k: int,
+                      out: torch.Tensor | None = None, stream=None, *, expert_begin: int = 0,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The whole quantized MoE expert layer (route, permute, GEMM1+SwiGLU, GEMM2, finalize)."""
+    _need(x, torch.bfloat16, "x")
+    _need(router_logits, torch.float32, "router_logits")
+    _need(w13_q, torch.uint8, "w13_q")
+    _need(s13, torch.bfloat16, "s13")
+    _need(w2_q, torch.uint8, "w2_q")
+    _need(s2, torch.bfloat16, "s2")
+    T, H = x.shape
+    E_g = router_logits.shape[1]
+    E_loc, N13, H2 = w13_q.shape
+    I = N13 // 2
+    if H2 * 2 != H or w2_q.shape != (E_loc, H, I // 2):
+        raise ValueError("weight shapes do not match x")
+    if s13.shape != (E_loc, 2 * I, H // 128) or s2.shape != (E_loc, H, I // 128):
+        raise ValueError("scale shapes do not match the weights")
+    if router_logits.shape[0] != T:
+        raise ValueError("router_logits rows != tokens")
+    sh = make_shape(T, H, I, E_g, E_loc, top_k, expert_begin)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    lib = load_library()
+    nbytes = int(lib.moe_w4a16_workspace_size(ctypes.byref(sh)))
+    if nbytes == 0:
+        _check(int(lib.moe_w4a16_check_shape(ctypes.byref(sh))) or 2)
+    if workspace is None:
+        workspace = _workspace(nbytes, x.device)
+    _check(lib.moe_w4a16_forward(ctypes.byref(sh), _ptr(x), _ptr(router_logits), _ptr(w13_q), _ptr(s13),
+                                 _ptr(w2_q), _ptr(s2), _ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
