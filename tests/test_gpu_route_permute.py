@@ -1,7 +1,8 @@
 """GPU routing and permutation vs the oracle: ids, counts, offsets, perm, inv_perm bit-exact.
 
 Routing weights are not in the bit-exact set (fp32 exp vs the oracle's fp64
-softmax); they must lie within 2 ulp of the oracle and sum to 1.
+softmax); they must lie within the forward error bound derived below and
+sum to 1.
 """
 import numpy as np
 import pytest
@@ -33,10 +34,14 @@ def test_route_matches_oracle(wl, T):
     torch.cuda.synchronize()
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
     got_w = wt.cpu().numpy()
-    # fp32 exp / sum / divide vs the oracle's fp64 softmax rounded once: a few ulp
+    # Forward error of the fp32 path against the exact weight, with u = 2^-24:
+    # each exp term carries <= 2u (1 ulp of expf) + u (the residual fma);
+    # the k-term sum adds (k-1)u; the divide adds u; the oracle's single
+    # rounding adds u. Relative error <= 2*3u + (k-1)u + u + u = (k+7)u, and
+    # one ulp of a binary32 value is at least u relative, so <= k+7 ulp.
     ulps = np.abs(got_w.astype(np.float64) - ref_w) / np.spacing(ref_w).astype(np.float64)
     say(f"  max weight error {ulps.max():.1f} ulp")
-    assert ulps.max() <= 4
+    assert ulps.max() <= w.top_k + 7
     assert np.all(np.abs(got_w.astype(np.float64).sum(axis=1) - 1.0) <= w.top_k * 2.0 ** -23)
 
 

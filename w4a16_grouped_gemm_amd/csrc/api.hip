@@ -55,6 +55,11 @@ moe_status check_shape(const moe_shape *sh)
         return MOE_ERR_SHAPE;
     if (sh->top_k < 1 || sh->top_k > kMaxTopK || sh->top_k > sh->num_experts)
         return MOE_ERR_SHAPE;
+    // activation-sized arrays are addressed with 32-bit buffer offsets
+    const long long rows = (long long)sh->num_tokens * sh->top_k;
+    const long long widest = sh->hidden > sh->inter ? sh->hidden : sh->inter;
+    if (rows * widest * 2 >= (1LL << 31))
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -113,6 +118,7 @@ GemmLaunch gemm_args(const moe_shape &sh, moe_gemm_kind kind)
         g.K = sh.hidden;
         g.N = 2 * sh.inter;
     }
+    g.a_bytes = (size_t)g.max_rows * g.K * 2;
     return g;
 }
 
@@ -221,6 +227,8 @@ moe_status moe_grouped_gemm_w4a16(const moe_shape *shape, moe_gemm_kind kind, co
     GemmLaunch g = gemm_args(*shape, kind);
     g.a = a;
     g.a_row_index = a_row_index;
+    if (a_row_index)
+        g.a_bytes = (size_t)shape->num_tokens * g.K * 2;
     g.offsets = offsets;
     g.wq = wq;
     g.s = s;
@@ -275,6 +283,7 @@ moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const fl
         GemmLaunch g = gemm_args(sh, MOE_GEMM_W13_SWIGLU);
         g.a = x;
         g.a_row_index = ws.perm;
+        g.a_bytes = (size_t)sh.num_tokens * sh.hidden * 2;
         g.offsets = ws.offsets;
         g.wq = w13_q;
         g.s = s13;

@@ -72,6 +72,7 @@ struct GemmLaunch {
     int N;                    // weight rows per expert
     int max_rows;             // T * k: upper bound on R
     int expected_rows;        // expected R (routed slots on local experts)
+    size_t a_bytes;           // bytes of the activation array `a`
 };
 
 hipError_t launch_route(const moe_shape &sh, const float *logits, int32_t *ids, float *w,

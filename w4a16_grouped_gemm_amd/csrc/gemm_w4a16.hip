@@ -4,49 +4,60 @@
 // Method (pages): InfiniLM PR #500 report, section 2.2 (one grouped GEMM
 // covers every expert slab given the group sizes; gate/up, SwiGLU, down);
 // FlashInfer PR #7196 analysis, section 2 (the MMA N extent follows the
-// routed-token count at run time, inactive subtiles are skipped;
-// activations sit in operand B of an operand-swapped MMA); GC-MoE abstract
-// (4-bit weights decoded in registers and fed straight to the matrix unit;
-// decode is bound by weight traffic); Cloudflare "Unweight" post, section on
-// the reconstructive matmul (weights are reconstructed on chip and never
+// routed-token count at run time and inactive subtiles are skipped; the
+// activations sit in operand B of an operand-swapped MMA; valid rows only);
+// GC-MoE abstract (4-bit weights decoded in registers and fed straight to the
+// matrix unit; decode is bound by weight traffic); Cloudflare "Unweight" post,
+// section on the reconstructive matmul (weights are rebuilt on chip and never
 // written back to HBM).
 //
 // gfx950 design (ours):
 //  * MFMA v_mfma_f32_16x16x32_bf16. Operand A = 16 routed tokens of one
-//    expert (a 16-token N-subtile of the expert's rows), operand B = 16 weight
+//    expert (a 16-token subtile of the expert's rows), operand B = 16 weight
 //    rows. Lane l supplies token / weight row l%16 and one 8-element K slice
-//    chosen by l/16; the result lane holds 4 tokens x 1 weight row, so each
-//    lane needs exactly one scale per 128-wide group: the scale of its own row.
-//  * Weights stream HBM -> VGPR, 16 bytes per lane per group (= 32 int4 of one
-//    row), no LDS: in decode nothing is reused. Within a lane the 32 codes of
-//    a group feed 4 MFMAs (K = 4 x 8 per lane x 4 lane slices = 128).
-//  * Unpack is one bit-op per pair of codes: (w ^ 0x8888) & 0x000F000F |
-//    0x43004300 turns two nibbles into the bf16 values 128 + (q + 8), which are
-//    exact. The K order inside each 8-code dword comes out as
-//    (0,4,1,5,2,6,3,7); the activation fragment is permuted the same way
-//    (any common K permutation leaves the dot product unchanged).
-//  * The +136 offset is removed inside the matrix unit: a second MFMA with a
-//    constant -136 operand accumulates -136 * sum(x) into the same chain, so
-//    the chain holds sum(x * q) exactly up to fp32 rounding (exactly, for
-//    integer-valued activations). The row's fp32 scale is then applied once
-//    per group: total += s * chain. Codes are never rounded.
-//  * K is split over the waves of a workgroup (contiguous group ranges), the
-//    partial sums are reduced through LDS in wave order (deterministic), then
-//    the epilogue applies SwiGLU (gate rows 0..7 and up rows 8..15 of the
-//    same 16-row tile, i.e. 8 features) or stores the plain result.
-//  * Work items = (expert chunk of up to 16*NSUB rows, weight-row tile). The
-//    item list is derived on the device from `offsets` by every workgroup of
-//    a persistent grid, so the grid never depends on the counts and the host
-//    never synchronises. Subtiles past the chunk's valid rows are skipped
-//    (runtime N); rows past the last valid token are neither read nor written.
+//    chosen by l/16; the result lane holds 4 tokens x 1 weight row, so a lane
+//    needs one scale per 128-wide group: the scale of its own row.
+//  * Weights stream HBM -> VGPR through buffer loads (SGPR descriptor per
+//    expert, 32-bit lane offsets, group offsets folded into the instruction),
+//    16 bytes per lane per group and 16-row tile (= 32 int4 codes of one row).
+//    A lane's 32 codes feed 4 MFMAs.
+//  * Unpack: ((w >> 4j) & 0x000F000F) ^ 0x43084308 turns two nibbles into the
+//    bf16 values 128 + (q + 8) -- exact -- in one v_bitop3_b32 (plus a shift
+//    shared by the 8 codes of the dword). The K order inside each dword comes
+//    out as (0,4,1,5,2,6,3,7); activation fragments are permuted the same way
+//    when they are staged (a common K permutation leaves the dot product
+//    unchanged).
+//  * The +136 offset is removed inside the matrix unit: per 16-token subtile
+//    and group a chain of MFMAs against a constant -136 operand gives
+//    -136 * sum(x); every weight tile's chain starts from it, so the chain
+//    ends at sum(x * q) (exact for integer-valued activations). The row's
+//    fp32 scale is applied once per group: total += s * chain. Codes are
+//    never rounded.
+//  * gemm_stream_kernel (the common case): a workgroup owns a block of
+//    4 waves x TPW tiles x 16 weight rows over the full K for one chunk of up
+//    to 16*NSUB rows of one expert. The chunk's activations are staged per
+//    K-segment of KSEG groups into LDS (double buffered, one barrier per
+//    segment), already in MFMA fragment order, and shared by the four waves,
+//    each reusing them across its TPW tiles; weights are prefetched one
+//    group ahead in registers. Tokens past the chunk are loaded as zeros by
+//    the buffer unit's range check, so no lane branches on them.
+//  * gemm_splitk_kernel (about one routed row per active expert, e.g. one
+//    decode token): one 16-row tile per workgroup, K split over the waves,
+//    partial sums reduced through LDS in wave order (deterministic). It keeps
+//    many more workgroups in flight when only a few experts are active.
+//  * Work items = (expert chunk, weight-row block). Every workgroup of a
+//    persistent grid derives the item list on the device from `offsets`, so
+//    the grid never depends on the counts and the host never synchronises.
+//    Subtiles past the chunk's valid rows are skipped (runtime N); rows past
+//    the last valid token are neither read nor written.
 #include "common.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr uint32_t kMagic = 0x43004300u;   // bf16 pair (128, 128)
 constexpr uint32_t kNeg136 = 0xC308C308u;  // bf16 pair (-136, -136)
+constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every descriptor
 
 struct GemmArgs {
     const uint16_t *a;
@@ -55,282 +66,520 @@ struct GemmArgs {
     const uint8_t *wq;
     const uint16_t *s;
     void *c;
+    uint32_t a_bytes;  // bytes of `a` reachable through the buffer descriptor (< 2^31)
     int top_k;
     int num_experts;
     int K;
     int N;          // weight rows per expert
     int ldc;        // output row stride (elements)
-    int row_tiles;  // 16-row weight tiles per expert
     int half;       // SwiGLU: row offset of the up projection (= I)
     int c_f32;
 };
 
-// Two nibbles per 16-bit half -> four bf16 pairs holding 136 + q, K order
-// (0,4,1,5,2,6,3,7) within the dword.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Raw bf16 bits of a scale; converted where it is used, so that the load can
+// stay in flight until then (a conversion next to the load would wait for it).
+__device__ __forceinline__ uint32_t bload_scale(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
+// Two nibbles per 16-bit half -> bf16 pair (128 + (q+8)); K order (0,4,1,5,..).
 __device__ __forceinline__ bf16x8 unpack8(uint32_t w)
 {
-    const uint32_t t = w ^ 0x88888888u;
     u32x4 o;
-    o.x = (t & 0x000F000Fu) | kMagic;
-    o.y = ((t >> 4) & 0x000F000Fu) | kMagic;
-    o.z = ((t >> 8) & 0x000F000Fu) | kMagic;
-    o.w = ((t >> 12) & 0x000F000Fu) | kMagic;
+    o.x = (w & 0x000F000Fu) ^ 0x43084308u;
+    o.y = ((w >> 4) & 0x000F000Fu) ^ 0x43084308u;
+    o.z = ((w >> 8) & 0x000F000Fu) ^ 0x43084308u;
+    o.w = ((w >> 12) & 0x000F000Fu) ^ 0x43084308u;
     return __builtin_bit_cast(bf16x8, o);
 }
 
 // Eight consecutive bf16 activations -> the same (0,4,1,5,2,6,3,7) order.
-__device__ __forceinline__ bf16x8 permute_act(u32x4 d)
+__device__ __forceinline__ u32x4 permute_act(u32x4 d)
 {
     u32x4 o;
     o.x = __builtin_amdgcn_perm(d.z, d.x, 0x05040100u);
     o.y = __builtin_amdgcn_perm(d.z, d.x, 0x07060302u);
     o.z = __builtin_amdgcn_perm(d.w, d.y, 0x05040100u);
     o.w = __builtin_amdgcn_perm(d.w, d.y, 0x07060302u);
-    return __builtin_bit_cast(bf16x8, o);
+    return o;
+}
+
+__device__ __forceinline__ floatx4 mfma(u32x4 a, bf16x8 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-template <int KIND, int NWAVES, int NSUB, int GB>
-__global__ __launch_bounds__(NWAVES * 64) void gemm_w4a16_kernel(GemmArgs p)
+__device__ __forceinline__ bf16x8 neg136_operand()
 {
-    constexpr int CS = 16 * NSUB;                 // rows per chunk
-    __shared__ int s_prefix[kMaxExperts + 1];     // chunk prefix per expert
-    __shared__ int s_wtot[NWAVES];
-    __shared__ float s_red[NWAVES][CS][17];
+    const u32x4 v = {kNeg136, kNeg136, kNeg136, kNeg136};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Chunk prefix over experts: s_prefix[e] = chunks of experts < e (chunk =
+// up to CS rows of one expert), s_prefix[E] = total. Block-wide.
+template <int NT>
+__device__ void build_chunk_prefix(const int32_t *offsets, int E, int CS, int *s_prefix, int *s_wtot)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int carry = 0;
+    for (int base = 0; base < E; base += NT) {
+        const int e = base + tid;
+        int v = 0;
+        if (e < E) {
+            const int cnt = offsets[e + 1] - offsets[e];
+            v = (cnt + CS - 1) / CS;
+        }
+        int wt;
+        const int ex = wave_exclusive_scan(v, wt);
+        if (lane == 0)
+            s_wtot[wave] = wt;
+        __syncthreads();
+        int wbase = 0, all = 0;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) {
+            wbase += (w < wave) ? s_wtot[w] : 0;
+            all += s_wtot[w];
+        }
+        if (e < E)
+            s_prefix[e] = carry + wbase + ex;
+        carry += all;
+        __syncthreads();
+    }
+    if (tid == 0)
+        s_prefix[E] = carry;
+    __syncthreads();
+}
+
+// Expert owning chunk `chunk`: the last e with s_prefix[e] <= chunk.
+__device__ __forceinline__ int chunk_expert(const int *s_prefix, int E, int chunk)
+{
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_prefix[mid] <= chunk)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// Weight row of lane n16 in 16-row tile `tile`: for SwiGLU rows 0..7 are gate
+// rows of features 8*tile.., rows 8..15 the matching up rows.
+template <int KIND>
+__device__ __forceinline__ int tile_row(const GemmArgs &p, int tile, int n16)
+{
+    if (KIND == MOE_GEMM_W13_SWIGLU)
+        return (n16 < 8) ? tile * 8 + n16 : p.half + tile * 8 + (n16 - 8);
+    return tile * 16 + n16;
+}
+
+// Store one lane's 4 results (tokens 4*kq+i of the subtile, row n16 of tile).
+template <int KIND>
+__device__ __forceinline__ void store_tile(const GemmArgs &p, floatx4 v, int tile, int row0, int mbase,
+                                           int nvalid, int n16)
+{
+    float r[4] = {v.x, v.y, v.z, v.w};
+    if (KIND == MOE_GEMM_W13_SWIGLU) {
+        float u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            u[i] = __shfl_xor(r[i], 8, 64);            // partner lane holds the up row
+        if (n16 < 8) {
+            uint16_t *c = static_cast<uint16_t *>(p.c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = mbase + i;
+                if (m < nvalid)
+                    c[(size_t)(row0 + m) * p.ldc + tile * 8 + n16] = (uint16_t)f32_to_bf16_rne(silu(r[i]) * u[i]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = mbase + i;
+            if (m < nvalid) {
+                const size_t off = (size_t)(row0 + m) * p.ldc + tile * 16 + n16;
+                if (p.c_f32)
+                    static_cast<float *>(p.c)[off] = r[i];
+                else
+                    static_cast<uint16_t *>(p.c)[off] = (uint16_t)f32_to_bf16_rne(r[i]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gemm_stream_kernel
+// ---------------------------------------------------------------------------
+template <int KIND, int TPW, int NSUB, int KSEG, int RING>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
+{
+    static_assert(KSEG % RING == 0, "the weight ring index follows the group index within a segment");
+    constexpr int CS = 16 * NSUB;
+    constexpr int BT = 4 * TPW;                         // tiles per block
+    __shared__ int s_prefix[kMaxExperts + 1];
+    __shared__ int s_wtot[4];
+    __shared__ u32x4 s_act[2][KSEG][NSUB][4][64];     // [buf][group][subtile][step][lane]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int n16 = lane & 15;
+    const int kq = lane >> 4;
     const int E = p.num_experts;
+    build_chunk_prefix<256>(p.offsets, E, CS, s_prefix, s_wtot);
 
-    // ---- chunk prefix over experts (device-side work list) ----
-    {
-        int carry = 0;
-        for (int base = 0; base < E; base += NWAVES * 64) {
-            const int e = base + tid;
-            int v = 0;
-            if (e < E) {
-                const int cnt = p.offsets[e + 1] - p.offsets[e];
-                v = (cnt + CS - 1) / CS;
-            }
-            int wt;
-            const int ex = wave_exclusive_scan(v, wt);
-            if (lane == 0)
-                s_wtot[wave] = wt;
-            __syncthreads();
-            int wbase = 0, all = 0;
+    const int ntiles = p.N >> 4;
+    const int nblocks = (ntiles + BT - 1) / BT;
+    const int total_items = s_prefix[E] * nblocks;
+    const int G = p.K / kGroup;
+    const int nseg = G / KSEG;                         // host guarantees KSEG | G
+    const uint32_t row_bytes = (uint32_t)(p.K >> 1);
+    // staging: thread -> (token of the subtile, 16-byte chunk of a group)
+    const int st_tok = tid >> 4;
+    const int st_c16 = tid & 15;
+    const int st_lane = st_tok + 16 * (st_c16 >> 2);
+    const int st_step = st_c16 & 3;
+    const bf16x8 neg136 = neg136_operand();
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+
+    for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+        const int chunk = item / nblocks;
+        const int block = item - chunk * nblocks;
+        const int e = uniform(chunk_expert(s_prefix, E, chunk));
+        const int row0 = uniform(p.offsets[e] + (chunk - s_prefix[e]) * CS);
+        const int nvalid = uniform(min(CS, p.offsets[e + 1] - row0));
+        const int nsub = (nvalid + 15) >> 4;
+        const int tile0 = block * BT + wave * TPW;
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (size_t)e * p.N * row_bytes, (uint32_t)p.N * row_bytes);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s + (size_t)e * p.N * G, (uint32_t)p.N * G * 2);
+
+        bool tval[TPW];
+        uint32_t voff_w[TPW], voff_s[TPW];
 #pragma unroll
-            for (int w = 0; w < NWAVES; ++w) {
-                wbase += (w < wave) ? s_wtot[w] : 0;
-                all += s_wtot[w];
-            }
-            if (e < E)
-                s_prefix[e] = carry + wbase + ex;
-            carry += all;
-            __syncthreads();
+        for (int t = 0; t < TPW; ++t) {
+            tval[t] = tile0 + t < ntiles;
+            const uint32_t row = (uint32_t)tile_row<KIND>(p, tval[t] ? tile0 + t : 0, n16);
+            voff_w[t] = row * row_bytes + kq * 16;
+            voff_s[t] = row * (uint32_t)G * 2;
         }
-        if (tid == 0)
-            s_prefix[E] = carry;
-        __syncthreads();
+        uint32_t voff_x[NSUB];
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb) {
+            const int m = sb * 16 + st_tok;
+            voff_x[sb] = kOutOfRange;
+            if (m < nvalid) {
+                const int r = row0 + m;
+                const uint32_t src = p.a_row_index ? (uint32_t)(p.a_row_index[r] / p.top_k) : (uint32_t)r;
+                voff_x[sb] = src * (uint32_t)p.K * 2 + st_c16 * 16;
+            }
+        }
+
+        floatx4 tot[TPW][NSUB];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb)
+                tot[t][sb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+        u32x4 xr[KSEG][NSUB];
+        u32x4 wv[RING][TPW];              // weights of groups g .. g+RING-1
+        uint32_t sv[RING][TPW];
+
+        auto load_act = [&](int seg) {
+            const uint32_t soff = (uint32_t)seg * KSEG * kGroup * 2;
+#pragma unroll
+            for (int j = 0; j < KSEG; ++j)
+#pragma unroll
+                for (int sb = 0; sb < NSUB; ++sb)
+                    if (sb < nsub)
+                        xr[j][sb] = bload16(ra, voff_x[sb] + j * kGroup * 2, soff);
+        };
+        auto write_act = [&](int buf) {
+#pragma unroll
+            for (int j = 0; j < KSEG; ++j)
+#pragma unroll
+                for (int sb = 0; sb < NSUB; ++sb)
+                    if (sb < nsub)
+                        s_act[buf][j][sb][st_step][st_lane] = permute_act(xr[j][sb]);
+        };
+        auto load_w = [&](int g, int b) {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                if (tval[t]) {
+                    wv[b][t] = bload16(rw, voff_w[t], (uint32_t)g * 64);
+                    sv[b][t] = bload_scale(rs, voff_s[t], (uint32_t)g * 2);
+                }
+            }
+        };
+        // One group: the -136*sum(x) chain per subtile, then every tile's
+        // chain of 4 MFMAs starting from it; the group scale is applied to
+        // the chain result.
+        auto compute = [&](int buf, int j, int b) {
+            u32x4 a[NSUB][4];
+            floatx4 corr[NSUB];
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb) {
+                if (sb < nsub) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        a[sb][i] = s_act[buf][j][sb][i][lane];
+                    floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        c = mfma(a[sb][i], neg136, c);
+                    corr[sb] = c;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                if (!tval[t])
+                    continue;
+                const bf16x8 wf0 = unpack8(wv[b][t].x);
+                const bf16x8 wf1 = unpack8(wv[b][t].y);
+                const bf16x8 wf2 = unpack8(wv[b][t].z);
+                const bf16x8 wf3 = unpack8(wv[b][t].w);
+                const float sc = bf16_to_f32(sv[b][t]);
+#pragma unroll
+                for (int sb = 0; sb < NSUB; ++sb) {
+                    if (sb < nsub) {
+                        floatx4 acc = corr[sb];
+                        acc = mfma(a[sb][0], wf0, acc);
+                        acc = mfma(a[sb][1], wf1, acc);
+                        acc = mfma(a[sb][2], wf2, acc);
+                        acc = mfma(a[sb][3], wf3, acc);
+                        tot[t][sb].x = __builtin_fmaf(sc, acc.x, tot[t][sb].x);
+                        tot[t][sb].y = __builtin_fmaf(sc, acc.y, tot[t][sb].y);
+                        tot[t][sb].z = __builtin_fmaf(sc, acc.z, tot[t][sb].z);
+                        tot[t][sb].w = __builtin_fmaf(sc, acc.w, tot[t][sb].w);
+                    }
+                }
+            }
+        };
+
+        __syncthreads();                                  // previous item done with s_act
+        load_act(0);
+#pragma unroll
+        for (int r = 0; r < RING - 1; ++r)
+            if (r < G)
+                load_w(r, r);
+        write_act(0);
+        for (int seg = 0; seg < nseg; ++seg) {
+            __syncthreads();                              // segment seg staged; the other buffer free
+            if (seg + 1 < nseg)
+                load_act(seg + 1);
+#pragma unroll
+            for (int j = 0; j < KSEG; ++j) {
+                const int g = seg * KSEG + j;
+                if (g + RING - 1 < G)
+                    load_w(g + RING - 1, (j + RING - 1) % RING);
+                compute(seg & 1, j, j % RING);
+            }
+            if (seg + 1 < nseg)
+                write_act((seg + 1) & 1);
+        }
+
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+            if (tval[t])
+#pragma unroll
+                for (int sb = 0; sb < NSUB; ++sb)
+                    if (sb < nsub)
+                        store_tile<KIND>(p, tot[t][sb], tile0 + t, row0, sb * 16 + kq * 4, nvalid, n16);
     }
-    const int total_items = s_prefix[E] * p.row_tiles;
+}
+
+// ---------------------------------------------------------------------------
+// gemm_splitk_kernel: one 16-row tile per workgroup, K split over NWAVES
+// waves (contiguous group ranges), LDS reduction in wave order. For about one
+// row per active expert: activations come straight from global memory.
+// ---------------------------------------------------------------------------
+template <int KIND, int NWAVES, int GB>
+__global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
+{
+    constexpr int CS = 16;
+    __shared__ int s_prefix[kMaxExperts + 1];
+    __shared__ int s_wtot[NWAVES];
+    __shared__ floatx4 s_red[NWAVES][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int n16 = lane & 15;
+    const int kq = lane >> 4;
+    const int E = p.num_experts;
+    build_chunk_prefix<NWAVES * 64>(p.offsets, E, CS, s_prefix, s_wtot);
+
+    const int ntiles = p.N >> 4;
+    const int total_items = s_prefix[E] * ntiles;
     const int G = p.K / kGroup;
     const int g0 = wave * G / NWAVES;
     const int g1 = (wave + 1) * G / NWAVES;
-    const int n16 = lane & 15;
-    const int kq = lane >> 4;
-    const u32x4 neg136v = {kNeg136, kNeg136, kNeg136, kNeg136};
-    const bf16x8 neg136 = __builtin_bit_cast(bf16x8, neg136v);
+    const uint32_t row_bytes = (uint32_t)(p.K >> 1);
+    const bf16x8 neg136 = neg136_operand();
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
 
     for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
-        const int chunk = item / p.row_tiles;
-        const int tile = item - chunk * p.row_tiles;
-        // expert owning this chunk: last e with s_prefix[e] <= chunk
-        int lo = 0, hi = E - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_prefix[mid] <= chunk)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        const int e = lo;
-        const int row0 = p.offsets[e] + (chunk - s_prefix[e]) * CS;
-        const int nvalid = min(CS, p.offsets[e + 1] - row0);
-
-        // this lane's weight row
-        int wrow;
-        if (KIND == MOE_GEMM_W13_SWIGLU)
-            wrow = (n16 < 8) ? tile * 8 + n16 : p.half + tile * 8 + (n16 - 8);
-        else
-            wrow = tile * 16 + n16;
-        const size_t wrow_index = (size_t)e * p.N + wrow;
-        const uint8_t *wptr = p.wq + wrow_index * (size_t)(p.K >> 1) + kq * 16;
-        const uint16_t *sptr = p.s + wrow_index * (size_t)G;
-
-        // this lane's activation rows (one per subtile)
-        const uint16_t *aptr[NSUB];
-        bool aval[NSUB];
-#pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb) {
-            const int m = sb * 16 + n16;
-            aval[sb] = m < nvalid;
-            size_t src = 0;
-            if (aval[sb]) {
-                const int r = row0 + m;
-                src = p.a_row_index ? (size_t)(p.a_row_index[r] / p.top_k) : (size_t)r;
-            }
-            aptr[sb] = p.a + src * (size_t)p.K + kq * 32;
+        const int chunk = item / ntiles;
+        const int tile = item - chunk * ntiles;
+        const int e = uniform(chunk_expert(s_prefix, E, chunk));
+        const int row0 = uniform(p.offsets[e] + (chunk - s_prefix[e]) * CS);
+        const int nvalid = uniform(min(CS, p.offsets[e + 1] - row0));
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (size_t)e * p.N * row_bytes, (uint32_t)p.N * row_bytes);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s + (size_t)e * p.N * G, (uint32_t)p.N * G * 2);
+        const uint32_t row = (uint32_t)tile_row<KIND>(p, tile, n16);
+        const uint32_t voff_w = row * row_bytes + kq * 16;
+        const uint32_t voff_s = row * (uint32_t)G * 2;
+        uint32_t voff_x = kOutOfRange;
+        if (n16 < nvalid) {
+            const int r = row0 + n16;
+            const uint32_t src = p.a_row_index ? (uint32_t)(p.a_row_index[r] / p.top_k) : (uint32_t)r;
+            voff_x = src * (uint32_t)p.K * 2 + kq * 64;
         }
 
-        floatx4 tot[NSUB];
-#pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb)
-            tot[sb] = floatx4{0.f, 0.f, 0.f, 0.f};
-
+        floatx4 tot = {0.f, 0.f, 0.f, 0.f};
         for (int gb = g0; gb < g1; gb += GB) {
             u32x4 wv[GB];
-            float sc[GB];
+            uint32_t sc[GB];
+            u32x4 xa[GB][4];
 #pragma unroll
             for (int j = 0; j < GB; ++j) {
                 if (gb + j < g1) {
-                    wv[j] = *reinterpret_cast<const u32x4 *>(wptr + (size_t)(gb + j) * 64);
-                    sc[j] = bf16_to_f32(sptr[gb + j]);
+                    const uint32_t g = gb + j;
+                    wv[j] = bload16(rw, voff_w, g * 64);
+                    sc[j] = bload_scale(rs, voff_s, g * 2);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        xa[j][i] = bload16(ra, voff_x + i * 16, g * kGroup * 2);
                 }
             }
 #pragma unroll
             for (int j = 0; j < GB; ++j) {
                 if (gb + j >= g1)
                     break;
-                const int g = gb + j;
-                const bf16x8 wf0 = unpack8(wv[j].x);
-                const bf16x8 wf1 = unpack8(wv[j].y);
-                const bf16x8 wf2 = unpack8(wv[j].z);
-                const bf16x8 wf3 = unpack8(wv[j].w);
+                u32x4 a[4];
 #pragma unroll
-                for (int sb = 0; sb < NSUB; ++sb) {
-                    if (sb * 16 >= nvalid)
-                        break;                      // inactive subtile (wave-uniform)
-                    u32x4 xa[4];
+                for (int i = 0; i < 4; ++i)
+                    a[i] = permute_act(xa[j][i]);
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        xa[i] = u32x4{0u, 0u, 0u, 0u};
-                        if (aval[sb])
-                            xa[i] = *reinterpret_cast<const u32x4 *>(aptr[sb] + (size_t)g * kGroup + i * 8);
-                    }
-                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                    bf16x8 af;
-                    af = permute_act(xa[0]);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wf0, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, neg136, acc, 0, 0, 0);
-                    af = permute_act(xa[1]);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wf1, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, neg136, acc, 0, 0, 0);
-                    af = permute_act(xa[2]);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wf2, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, neg136, acc, 0, 0, 0);
-                    af = permute_act(xa[3]);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wf3, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, neg136, acc, 0, 0, 0);
-                    tot[sb].x = __builtin_fmaf(sc[j], acc.x, tot[sb].x);
-                    tot[sb].y = __builtin_fmaf(sc[j], acc.y, tot[sb].y);
-                    tot[sb].z = __builtin_fmaf(sc[j], acc.z, tot[sb].z);
-                    tot[sb].w = __builtin_fmaf(sc[j], acc.w, tot[sb].w);
-                }
+                for (int i = 0; i < 4; ++i)
+                    acc = mfma(a[i], neg136, acc);
+                acc = mfma(a[0], unpack8(wv[j].x), acc);
+                acc = mfma(a[1], unpack8(wv[j].y), acc);
+                acc = mfma(a[2], unpack8(wv[j].z), acc);
+                acc = mfma(a[3], unpack8(wv[j].w), acc);
+                const float scale = bf16_to_f32(sc[j]);
+                tot.x = __builtin_fmaf(scale, acc.x, tot.x);
+                tot.y = __builtin_fmaf(scale, acc.y, tot.y);
+                tot.z = __builtin_fmaf(scale, acc.z, tot.z);
+                tot.w = __builtin_fmaf(scale, acc.w, tot.w);
             }
         }
-
-        // ---- cross-wave reduction through LDS ----
-        // result lane layout: token (within subtile) = 4*kq + i, weight row = n16
-#pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb) {
-            s_red[wave][sb * 16 + kq * 4 + 0][n16] = tot[sb].x;
-            s_red[wave][sb * 16 + kq * 4 + 1][n16] = tot[sb].y;
-            s_red[wave][sb * 16 + kq * 4 + 2][n16] = tot[sb].z;
-            s_red[wave][sb * 16 + kq * 4 + 3][n16] = tot[sb].w;
-        }
+        s_red[wave][lane] = tot;
         __syncthreads();
-        if (KIND == MOE_GEMM_W13_SWIGLU) {
-            for (int m = tid; m < nvalid; m += NWAVES * 64) {
-                uint32_t packed[4];
+        if (wave == 0) {
+            floatx4 sum = s_red[0][lane];
 #pragma unroll
-                for (int jp = 0; jp < 4; ++jp) {
-                    float hv[2];
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int f = jp * 2 + q;
-                        float gsum = 0.f, usum = 0.f;
-#pragma unroll
-                        for (int w = 0; w < NWAVES; ++w) {
-                            gsum += s_red[w][m][f];
-                            usum += s_red[w][m][8 + f];
-                        }
-                        hv[q] = silu(gsum) * usum;
-                    }
-                    packed[jp] = pack_bf16x2(hv[0], hv[1]);
-                }
-                uint16_t *dst = static_cast<uint16_t *>(p.c) + (size_t)(row0 + m) * p.ldc + tile * 8;
-                *reinterpret_cast<u32x4 *>(dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+            for (int w = 1; w < NWAVES; ++w) {
+                const floatx4 v = s_red[w][lane];
+                sum.x += v.x;
+                sum.y += v.y;
+                sum.z += v.z;
+                sum.w += v.w;
             }
-        } else {
-            for (int idx = tid; idx < nvalid * 2; idx += NWAVES * 64) {
-                const int m = idx >> 1;
-                const int h8 = (idx & 1) * 8;
-                float v[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    float sum = 0.f;
-#pragma unroll
-                    for (int w = 0; w < NWAVES; ++w)
-                        sum += s_red[w][m][h8 + q];
-                    v[q] = sum;
-                }
-                const size_t off = (size_t)(row0 + m) * p.ldc + tile * 16 + h8;
-                if (p.c_f32) {
-                    float *dst = static_cast<float *>(p.c) + off;
-                    *reinterpret_cast<floatx4 *>(dst) = floatx4{v[0], v[1], v[2], v[3]};
-                    *reinterpret_cast<floatx4 *>(dst + 4) = floatx4{v[4], v[5], v[6], v[7]};
-                } else {
-                    uint16_t *dst = static_cast<uint16_t *>(p.c) + off;
-                    *reinterpret_cast<u32x4 *>(dst) =
-                        u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-                }
-            }
+            store_tile<KIND>(p, sum, tile, row0, kq * 4, nvalid, n16);
         }
         __syncthreads();
     }
 }
 
-template <int KIND, int NWAVES, int NSUB>
-hipError_t launch_cfg(const GemmArgs &a, int max_rows, hipStream_t st)
+// ---------------------------------------------------------------------------
+// launch selection
+// ---------------------------------------------------------------------------
+
+long long grid_for(long long items, int wg_per_cu)
+{
+    const long long cap = (long long)device_cu_count() * wg_per_cu;
+    long long g = items < cap ? items : cap;
+    return g < 1 ? 1 : g;
+}
+
+// Workgroups of `kernel` (256 threads) one CU holds at once, per instance.
+template <typename F>
+int resident_per_cu(F kernel)
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess || n < 1)
+        n = 1;
+    return n;
+}
+
+template <int KIND, int TPW, int NSUB, int KSEG, int RING>
+hipError_t launch_stream(const GemmArgs &a, int max_rows, hipStream_t st)
 {
     constexpr int CS = 16 * NSUB;
-    // upper bound on chunks: every non-empty expert adds at most one partial chunk
+    auto kernel = gemm_stream_kernel<KIND, TPW, NSUB, KSEG, RING>;
+    static const int per_cu = resident_per_cu(kernel);
+    // persistent grid: at most the resident slots, at most the item bound
+    const int nblocks = ((a.N >> 4) + 4 * TPW - 1) / (4 * TPW);
     const long long chunks = (long long)min(a.num_experts, max_rows) + max_rows / CS;
-    const long long items = chunks * a.row_tiles;
-    const long long cap = (long long)device_cu_count() * (NWAVES >= 8 ? 2 : 16 / NWAVES);
-    long long grid = items < cap ? items : cap;
-    if (grid < 1)
-        grid = 1;
-    hipLaunchKernelGGL((gemm_w4a16_kernel<KIND, NWAVES, NSUB, 4>), dim3((unsigned)grid),
-                       dim3(NWAVES * 64), 0, st, a);
+    const long long grid = grid_for(chunks * nblocks, per_cu);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int KIND, int NWAVES>
+hipError_t launch_splitk(const GemmArgs &a, int max_rows, hipStream_t st)
+{
+    const long long chunks = (long long)min(a.num_experts, max_rows) + max_rows / 16;
+    const long long grid = grid_for(chunks * (a.N >> 4), 16 / NWAVES > 0 ? 16 / NWAVES : 1);
+    hipLaunchKernelGGL((gemm_splitk_kernel<KIND, NWAVES, 4>), dim3((unsigned)grid), dim3(NWAVES * 64), 0, st, a);
     return hipGetLastError();
 }
 
 template <int KIND>
-hipError_t launch_kind(const GemmArgs &a, int max_rows, int nwaves, int nsub, hipStream_t st)
+hipError_t launch_kind(const GemmArgs &a, int max_rows, int mode, int tpw, int nsub, int kseg, int ring,
+                       hipStream_t st)
 {
-#define MOE_CFG(W, S)                                              \
-    if (nwaves == W && nsub == S)                                  \
-        return launch_cfg<KIND, W, S>(a, max_rows, st);
-    MOE_CFG(1, 1) MOE_CFG(1, 2) MOE_CFG(1, 4)
-    MOE_CFG(2, 1) MOE_CFG(2, 2) MOE_CFG(2, 4)
-    MOE_CFG(4, 1) MOE_CFG(4, 2) MOE_CFG(4, 4)
-    MOE_CFG(8, 1) MOE_CFG(8, 2) MOE_CFG(8, 4)
-#undef MOE_CFG
-    return hipErrorInvalidValue;
+    if (mode == 0) {
+        const int G = a.K / kGroup;
+        if (G >= 24)
+            return launch_splitk<KIND, 8>(a, max_rows, st);
+        if (G >= 8)
+            return launch_splitk<KIND, 4>(a, max_rows, st);
+        if (G >= 4)
+            return launch_splitk<KIND, 2>(a, max_rows, st);
+        return launch_splitk<KIND, 1>(a, max_rows, st);
+    }
+#define MOE_STREAM(T, S, B, R)                                \
+    if (tpw == T && nsub == S && kseg == B && ring == R)      \
+        return launch_stream<KIND, T, S, B, R>(a, max_rows, st);
+    MOE_STREAM(1, 1, 2, 2) MOE_STREAM(1, 1, 4, 2) MOE_STREAM(1, 1, 4, 4) MOE_STREAM(1, 1, 8, 4) MOE_STREAM(1, 2, 2, 2)
+    MOE_STREAM(1, 4, 2, 2)
+    MOE_STREAM(2, 1, 2, 2) MOE_STREAM(2, 1, 4, 2) MOE_STREAM(2, 1, 4, 4) MOE_STREAM(2, 1, 8, 4)
+    MOE_STREAM(2, 2, 2, 2) MOE_STREAM(2, 2, 4, 2) MOE_STREAM(2, 2, 4, 4) MOE_STREAM(2, 4, 2, 2)
+    MOE_STREAM(4, 1, 2, 2) MOE_STREAM(4, 1, 4, 2) MOE_STREAM(4, 1, 4, 4) MOE_STREAM(4, 1, 8, 4)
+    MOE_STREAM(4, 2, 2, 2) MOE_STREAM(4, 2, 4, 2) MOE_STREAM(4, 2, 4, 4) MOE_STREAM(4, 4, 2, 2)
+#undef MOE_STREAM
+    // no streaming instance for this combination: the split-K kernel takes any shape
+    return launch_kind<KIND>(a, max_rows, 0, tpw, nsub, kseg, ring, st);
 }
 
 }  // namespace
@@ -344,34 +593,57 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     a.wq = g.wq;
     a.s = g.s;
     a.c = g.c;
+    a.a_bytes = (uint32_t)g.a_bytes;
     a.top_k = g.top_k;
     a.num_experts = g.num_experts;
     a.K = g.K;
     a.N = g.N;
     a.c_f32 = g.c_f32 ? 1 : 0;
     a.half = g.N / 2;
-    if (g.kind == MOE_GEMM_W13_SWIGLU) {
-        a.ldc = g.N / 2;
-        a.row_tiles = g.N / 16;   // 8 features = 16 rows (8 gate + 8 up) per tile
-    } else {
-        a.ldc = g.N;
-        a.row_tiles = g.N / 16;
-    }
+    a.ldc = (g.kind == MOE_GEMM_W13_SWIGLU) ? g.N / 2 : g.N;
+
+    // Expected rows per active expert (uniform routing estimate) picks the
+    // kernel and the tile shape. Only the launch shape depends on it, never
+    // the result.
+    const double E = g.num_experts > 0 ? g.num_experts : 1;
+    const double R = g.expected_rows > 0 ? g.expected_rows : 1;
+    const double T = g.max_rows / (double)(g.top_k > 0 ? g.top_k : 1);
+    const double p_slot = R / (T * E);                   // P(token routes to a given expert)
+    const double active = E * (1.0 - pow(1.0 - (p_slot < 1.0 ? p_slot : 1.0), T));
+    const double m = R / (active > 1.0 ? active : 1.0);
     const int G = g.K / kGroup;
-    // K split: about four 128-groups per wave
-    int nwaves = 1;
-    while (nwaves < 8 && G / (nwaves * 2) >= 3)
-        nwaves *= 2;
-    // token subtiles per chunk from the mean rows per active expert
-    const int mean_rows = g.expected_rows / (g.num_experts > 0 ? g.num_experts : 1);
-    int nsub = mean_rows > 24 ? 4 : (mean_rows > 8 ? 2 : 1);
+    const int ntiles = g.N / 16;
+    // Measured on MI355X (Qwen3-30B-A3B and EP-shard decode shapes, 1..256
+    // tokens): two 16-row tiles per wave and one 16-token subtile, 4-group K
+    // segments; a 4-deep weight ring for long K or few rows per expert, else
+    // 2. More subtiles per wave lose at every decode size measured.
+    int mode = m < 1.25 ? 0 : 1;
+    int nsub = 1;
+    int tpw = 2;
+    int kseg = 4;
+    int ring = (g.K >= 4096 || m < 3.0) ? 4 : 2;
+    if (const char *env = getenv("MOE_GEMM_MODE"))
+        mode = atoi(env);
+    if (const char *env = getenv("MOE_GEMM_TPW"))
+        tpw = atoi(env);
     if (const char *env = getenv("MOE_GEMM_NSUB"))
         nsub = atoi(env);
-    if (const char *env = getenv("MOE_GEMM_NWAVES"))
-        nwaves = atoi(env);
+    if (const char *env = getenv("MOE_GEMM_KSEG"))
+        kseg = atoi(env);
+    if (const char *env = getenv("MOE_GEMM_RING"))
+        ring = atoi(env);
+    while (tpw > 1 && ntiles % (4 * tpw) != 0)
+        tpw >>= 1;
+    // LDS: 2 buffers x KSEG groups x NSUB subtiles x 4 KiB <= 64 KiB
+    while (kseg > 2 && (G % kseg != 0 || 2 * kseg * nsub * 4 > 64))
+        kseg >>= 1;
+    if (kseg % ring != 0)
+        ring = 2;
+    if (mode != 0 && (ntiles % (4 * tpw) != 0 || G % kseg != 0))
+        mode = 0;                                         // shapes the streaming tiles do not divide
     if (g.kind == MOE_GEMM_W13_SWIGLU)
-        return launch_kind<MOE_GEMM_W13_SWIGLU>(a, g.max_rows, nwaves, nsub, st);
-    return launch_kind<MOE_GEMM_W2>(a, g.max_rows, nwaves, nsub, st);
+        return launch_kind<MOE_GEMM_W13_SWIGLU>(a, g.max_rows, mode, tpw, nsub, kseg, ring, st);
+    return launch_kind<MOE_GEMM_W2>(a, g.max_rows, mode, tpw, nsub, kseg, ring, st);
 }
 
 }  // namespace moe

@@ -77,7 +77,10 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(int T, int E, i
             if (lane + 64 * i == e)
                 key[i] = 0;
     }
-    // renormalised softmax over the k selected logits (fp32)
+    // renormalised softmax over the k selected logits (fp32). The difference
+    // l_j - l_0 is formed error-free (TwoSum: d + r == l_j - l_0 exactly) and
+    // exp(d + r) ~= exp(d) * (1 + r), so wide logit ranges lose no accuracy
+    // before the exponential.
     const float l0 = sel_v[0];
     float z = 0.0f;
     float ex[kMaxTopK];
@@ -85,7 +88,13 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(int T, int E, i
     for (int j = 0; j < kMaxTopK; ++j) {
         if (j >= k)
             break;
-        ex[j] = expf(sel_v[j] - l0);
+        const float a = sel_v[j], b = -l0;
+        const float d = a + b;
+        const float ap = d - b;
+        const float bp = d - ap;
+        const float r = (a - ap) + (b - bp);
+        const float e = expf(d);
+        ex[j] = __builtin_fmaf(e, r, e);
         z += ex[j];
     }
 #pragma unroll
