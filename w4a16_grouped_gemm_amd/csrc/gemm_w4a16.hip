@@ -52,6 +52,10 @@
 //    the last valid token are neither read nor written.
 #include "common.hpp"
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 namespace moe {
 
 namespace {
@@ -132,8 +136,10 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 // Chunk prefix over experts: s_prefix[e] = chunks of experts < e (chunk =
 // up to CS rows of one expert), s_prefix[E] = total. Block-wide.
+// When s_off is given it receives offsets[0..E] as well.
 template <int NT>
-__device__ void build_chunk_prefix(const int32_t *offsets, int E, int CS, int *s_prefix, int *s_wtot)
+__device__ void build_chunk_prefix(const int32_t *offsets, int E, int CS, int *s_prefix, int *s_wtot,
+                                   int *s_off = nullptr)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int carry = 0;
@@ -141,7 +147,13 @@ __device__ void build_chunk_prefix(const int32_t *offsets, int E, int CS, int *s
         const int e = base + tid;
         int v = 0;
         if (e < E) {
-            const int cnt = offsets[e + 1] - offsets[e];
+            const int o0 = offsets[e], o1 = offsets[e + 1];
+            if (s_off) {
+                s_off[e] = o0;
+                if (e == E - 1)
+                    s_off[E] = o1;
+            }
+            const int cnt = o1 - o0;
             v = (cnt + CS - 1) / CS;
         }
         int wt;
@@ -226,27 +238,45 @@ __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx4 v, int til
 
 // ---------------------------------------------------------------------------
 // gemm_stream_kernel
+//
+// No load sits under a branch: tiles past N never occur (the host launches
+// this kernel only when 4*TPW tiles divide N), tokens past the chunk, groups
+// past K and the segment after the last are all loaded through out-of-range
+// buffer offsets (zeros, no memory traffic). The waitcnt insertion then sees
+// one straight sequence of loads, so each wait names exactly the load it
+// needs and the weight ring stays in flight across groups.
 // ---------------------------------------------------------------------------
+template <int NSUB, int KSEG>
+constexpr size_t stream_act_bytes()
+{
+    return sizeof(u32x4) * 2 * KSEG * NSUB * 4 * 64;
+}
+
 template <int KIND, int TPW, int NSUB, int KSEG, int RING>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
 {
     static_assert(KSEG % RING == 0, "the weight ring index follows the group index within a segment");
+    static_assert(KSEG % 2 == 0, "scales are loaded as dwords of two groups");
     constexpr int CS = 16 * NSUB;
     constexpr int BT = 4 * TPW;                         // tiles per block
-    __shared__ int s_prefix[kMaxExperts + 1];
-    __shared__ int s_wtot[4];
-    __shared__ u32x4 s_act[2][KSEG][NSUB][4][64];     // [buf][group][subtile][step][lane]
+    extern __shared__ __align__(16) unsigned char s_dyn[];
+    // [buf][group][subtile][step][lane] activation fragments, then the chunk
+    // prefix, the expert offsets and the scan scratch
+    auto s_act = reinterpret_cast<u32x4(*)[KSEG][NSUB][4][64]>(s_dyn);
+    const int E = p.num_experts;
+    int *s_prefix = reinterpret_cast<int *>(s_dyn + stream_act_bytes<NSUB, KSEG>());
+    int *s_off = s_prefix + (E + 1);
+    int *s_wtot = s_off + (E + 1);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int n16 = lane & 15;
     const int kq = lane >> 4;
-    const int E = p.num_experts;
-    build_chunk_prefix<256>(p.offsets, E, CS, s_prefix, s_wtot);
+    build_chunk_prefix<256>(p.offsets, E, CS, s_prefix, s_wtot, s_off);
 
     const int ntiles = p.N >> 4;
-    const int nblocks = (ntiles + BT - 1) / BT;
+    const int nblocks = ntiles / BT;
     const int total_items = s_prefix[E] * nblocks;
     const int G = p.K / kGroup;
     const int nseg = G / KSEG;                         // host guarantees KSEG | G
@@ -263,19 +293,17 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         const int chunk = item / nblocks;
         const int block = item - chunk * nblocks;
         const int e = uniform(chunk_expert(s_prefix, E, chunk));
-        const int row0 = uniform(p.offsets[e] + (chunk - s_prefix[e]) * CS);
-        const int nvalid = uniform(min(CS, p.offsets[e + 1] - row0));
+        const int row0 = uniform(s_off[e] + (chunk - s_prefix[e]) * CS);
+        const int nvalid = uniform(min(CS, s_off[e + 1] - row0));
         const int nsub = (nvalid + 15) >> 4;
         const int tile0 = block * BT + wave * TPW;
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (size_t)e * p.N * row_bytes, (uint32_t)p.N * row_bytes);
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s + (size_t)e * p.N * G, (uint32_t)p.N * G * 2);
 
-        bool tval[TPW];
         uint32_t voff_w[TPW], voff_s[TPW];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            tval[t] = tile0 + t < ntiles;
-            const uint32_t row = (uint32_t)tile_row<KIND>(p, tval[t] ? tile0 + t : 0, n16);
+            const uint32_t row = (uint32_t)tile_row<KIND>(p, tile0 + t, n16);
             voff_w[t] = row * row_bytes + kq * 16;
             voff_s[t] = row * (uint32_t)G * 2;
         }
@@ -283,12 +311,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb) {
             const int m = sb * 16 + st_tok;
-            voff_x[sb] = kOutOfRange;
-            if (m < nvalid) {
-                const int r = row0 + m;
-                const uint32_t src = p.a_row_index ? (uint32_t)(p.a_row_index[r] / p.top_k) : (uint32_t)r;
-                voff_x[sb] = src * (uint32_t)p.K * 2 + st_c16 * 16;
-            }
+            const int r = row0 + min(m, nvalid - 1);       // always a valid row: no branch around the load
+            const uint32_t src = p.a_row_index ? (uint32_t)(p.a_row_index[r] / p.top_k) : (uint32_t)r;
+            voff_x[sb] = (m < nvalid) ? src * (uint32_t)p.K * 2 + st_c16 * 16 : kOutOfRange;
         }
 
         floatx4 tot[TPW][NSUB];
@@ -299,71 +324,64 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
                 tot[t][sb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
         u32x4 xr[KSEG][NSUB];
-        u32x4 wv[RING][TPW];              // weights of groups g .. g+RING-1
-        uint32_t sv[RING][TPW];
+        u32x4 wv[RING][TPW];                  // weights of groups g .. g+RING-1
+        uint32_t sv[2][TPW][KSEG / 2];        // scales of the current and next segment
 
-        auto load_act = [&](int seg) {
-            const uint32_t soff = (uint32_t)seg * KSEG * kGroup * 2;
+        // Activations and scales of segment `seg`; the segment after the last
+        // is read out of range (zeros, no traffic).
+        auto load_seg = [&](int seg, int buf) {
+            const uint32_t oor = seg < nseg ? 0u : kOutOfRange;
+            const uint32_t soff = (uint32_t)(seg < nseg ? seg : 0) * KSEG * kGroup * 2;
 #pragma unroll
             for (int j = 0; j < KSEG; ++j)
 #pragma unroll
                 for (int sb = 0; sb < NSUB; ++sb)
-                    if (sb < nsub)
-                        xr[j][sb] = bload16(ra, voff_x[sb] + j * kGroup * 2, soff);
+                    xr[j][sb] = bload16(ra, (voff_x[sb] | oor) + j * kGroup * 2, soff);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int h = 0; h < KSEG / 2; ++h)
+                    sv[buf][t][h] = __builtin_amdgcn_raw_buffer_load_b32(
+                        rs, (voff_s[t] | oor) + h * 4, (uint32_t)(seg < nseg ? seg : 0) * KSEG * 2, 0);
         };
         auto write_act = [&](int buf) {
 #pragma unroll
             for (int j = 0; j < KSEG; ++j)
 #pragma unroll
                 for (int sb = 0; sb < NSUB; ++sb)
-                    if (sb < nsub)
-                        s_act[buf][j][sb][st_step][st_lane] = permute_act(xr[j][sb]);
+                    s_act[buf][j][sb][st_step][st_lane] = permute_act(xr[j][sb]);
         };
         auto load_w = [&](int g, int b) {
+            const uint32_t oor = g < G ? 0u : kOutOfRange;
+            const uint32_t soff = (uint32_t)(g < G ? g : 0) * 64;
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                if (tval[t]) {
-                    wv[b][t] = bload16(rw, voff_w[t], (uint32_t)g * 64);
-                    sv[b][t] = bload_scale(rs, voff_s[t], (uint32_t)g * 2);
-                }
-            }
+            for (int t = 0; t < TPW; ++t)
+                wv[b][t] = bload16(rw, voff_w[t] | oor, soff);
         };
         // One group: the -136*sum(x) chain per subtile, then every tile's
         // chain of 4 MFMAs starting from it; the group scale is applied to
         // the chain result.
-        auto compute = [&](int buf, int j, int b) {
-            u32x4 a[NSUB][4];
-            floatx4 corr[NSUB];
+        auto compute = [&](int buf, int sbuf, int j, int b) {
 #pragma unroll
             for (int sb = 0; sb < NSUB; ++sb) {
                 if (sb < nsub) {
+                    u32x4 a[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        a[sb][i] = s_act[buf][j][sb][i][lane];
-                    floatx4 c = {0.f, 0.f, 0.f, 0.f};
+                        a[i] = s_act[buf][j][sb][i][lane];
+                    floatx4 corr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        c = mfma(a[sb][i], neg136, c);
-                    corr[sb] = c;
-                }
-            }
+                        corr = mfma(a[i], neg136, corr);
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                if (!tval[t])
-                    continue;
-                const bf16x8 wf0 = unpack8(wv[b][t].x);
-                const bf16x8 wf1 = unpack8(wv[b][t].y);
-                const bf16x8 wf2 = unpack8(wv[b][t].z);
-                const bf16x8 wf3 = unpack8(wv[b][t].w);
-                const float sc = bf16_to_f32(sv[b][t]);
-#pragma unroll
-                for (int sb = 0; sb < NSUB; ++sb) {
-                    if (sb < nsub) {
-                        floatx4 acc = corr[sb];
-                        acc = mfma(a[sb][0], wf0, acc);
-                        acc = mfma(a[sb][1], wf1, acc);
-                        acc = mfma(a[sb][2], wf2, acc);
-                        acc = mfma(a[sb][3], wf3, acc);
+                    for (int t = 0; t < TPW; ++t) {
+                        floatx4 acc = corr;
+                        acc = mfma(a[0], unpack8(wv[b][t].x), acc);
+                        acc = mfma(a[1], unpack8(wv[b][t].y), acc);
+                        acc = mfma(a[2], unpack8(wv[b][t].z), acc);
+                        acc = mfma(a[3], unpack8(wv[b][t].w), acc);
+                        const uint32_t d = sv[sbuf][t][j >> 1];
+                        const float sc = __uint_as_float((j & 1) ? (d & 0xFFFF0000u) : (d << 16));
                         tot[t][sb].x = __builtin_fmaf(sc, acc.x, tot[t][sb].x);
                         tot[t][sb].y = __builtin_fmaf(sc, acc.y, tot[t][sb].y);
                         tot[t][sb].z = __builtin_fmaf(sc, acc.z, tot[t][sb].z);
@@ -374,22 +392,19 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         };
 
         __syncthreads();                                  // previous item done with s_act
-        load_act(0);
+        load_seg(0, 0);
 #pragma unroll
         for (int r = 0; r < RING - 1; ++r)
-            if (r < G)
-                load_w(r, r);
+            load_w(r, r);
         write_act(0);
         for (int seg = 0; seg < nseg; ++seg) {
             __syncthreads();                              // segment seg staged; the other buffer free
-            if (seg + 1 < nseg)
-                load_act(seg + 1);
+            load_seg(seg + 1, (seg + 1) & 1);
 #pragma unroll
             for (int j = 0; j < KSEG; ++j) {
                 const int g = seg * KSEG + j;
-                if (g + RING - 1 < G)
-                    load_w(g + RING - 1, (j + RING - 1) % RING);
-                compute(seg & 1, j, j % RING);
+                load_w(g + RING - 1, (j + RING - 1) % RING);
+                compute(seg & 1, seg & 1, j, j % RING);
             }
             if (seg + 1 < nseg)
                 write_act((seg + 1) & 1);
@@ -397,11 +412,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
 
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
-            if (tval[t])
 #pragma unroll
-                for (int sb = 0; sb < NSUB; ++sb)
-                    if (sb < nsub)
-                        store_tile<KIND>(p, tot[t][sb], tile0 + t, row0, sb * 16 + kq * 4, nvalid, n16);
+            for (int sb = 0; sb < NSUB; ++sb)
+                if (sb < nsub)
+                    store_tile<KIND>(p, tot[t][sb], tile0 + t, row0, sb * 16 + kq * 4, nvalid, n16);
     }
 }
 
@@ -522,12 +536,21 @@ long long grid_for(long long items, int wg_per_cu)
 }
 
 // Workgroups of `kernel` (256 threads) one CU holds at once, per instance.
+// Cached per (kernel, dynamic LDS size): the occupancy query is not free.
 template <typename F>
-int resident_per_cu(F kernel)
+int resident_per_cu(F kernel, size_t lds = 0)
 {
+    static std::mutex mu;
+    static std::map<std::pair<const void *, size_t>, int> cache;
+    const auto key = std::make_pair(reinterpret_cast<const void *>(kernel), lds);
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end())
+        return it->second;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, lds) != hipSuccess || n < 1)
         n = 1;
+    cache[key] = n;
     return n;
 }
 
@@ -536,12 +559,13 @@ hipError_t launch_stream(const GemmArgs &a, int max_rows, hipStream_t st)
 {
     constexpr int CS = 16 * NSUB;
     auto kernel = gemm_stream_kernel<KIND, TPW, NSUB, KSEG, RING>;
-    static const int per_cu = resident_per_cu(kernel);
+    const size_t lds = stream_act_bytes<NSUB, KSEG>() + sizeof(int) * (2 * (a.num_experts + 1) + 4);
+    const int per_cu = resident_per_cu(kernel, lds);
     // persistent grid: at most the resident slots, at most the item bound
-    const int nblocks = ((a.N >> 4) + 4 * TPW - 1) / (4 * TPW);
+    const int nblocks = (a.N >> 4) / (4 * TPW);
     const long long chunks = (long long)min(a.num_experts, max_rows) + max_rows / CS;
     const long long grid = grid_for(chunks * nblocks, per_cu);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
 
@@ -615,13 +639,16 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     const int ntiles = g.N / 16;
     // Measured on MI355X (Qwen3-30B-A3B and EP-shard decode shapes, 1..256
     // tokens): two 16-row tiles per wave and one 16-token subtile, 4-group K
-    // segments; a 4-deep weight ring for long K or few rows per expert, else
-    // 2. More subtiles per wave lose at every decode size measured.
+    // segments (8 for K >= 4096); a 4-deep weight ring for long K or few rows
+    // per expert, else 2. More subtiles per wave lose at every decode size
+    // measured.
     int mode = m < 1.25 ? 0 : 1;
     int nsub = 1;
     int tpw = 2;
     int kseg = 4;
     int ring = (g.K >= 4096 || m < 3.0) ? 4 : 2;
+    if (g.K >= 4096)
+        kseg = 8;
     if (const char *env = getenv("MOE_GEMM_MODE"))
         mode = atoi(env);
     if (const char *env = getenv("MOE_GEMM_TPW"))
