@@ -2,7 +2,8 @@
 
 Flags: gfx950 only; -O3; no FP contraction (the combine must be exactly the
 IEEE multiply / FMA it names); fp32 denormals preserved (no flush-to-zero);
-packed-fp32 instructions disabled.
+packed-fp32 instructions disabled; MFMA accumulators in ordinary VGPRs
+(the epilogue reads them with plain VALU instructions, no AGPR copies).
 """
 from __future__ import annotations
 
@@ -22,6 +23,7 @@ SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm_w4a16.hip", "finalize.hi
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-fno-gpu-flush-denormals-to-zero", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wall", "-Wno-unused-function", "-I" + INCLUDE, "-I" + CSRC]
 
 

@@ -12,14 +12,18 @@
 // denormals preserved (the kernel descriptor's f32 denorm mode is "keep"),
 // so v_mul_f32 / v_fma_f32 are exactly IEEE binary32 multiply / FMA with
 // round-to-nearest-even. One thread owns 8 consecutive columns of one token:
-// 16-byte (bf16) or 2x16-byte (fp32) coalesced row loads per slot.
+// 16-byte (bf16) or 2x16-byte (fp32) coalesced row loads per slot, all of a
+// token's slots in flight at once.
 #include "common.hpp"
 
 namespace moe {
 
 namespace {
 
-template <bool Y_F32, bool OUT_F32>
+// KMAX >= k. All of a token's row indices and weights are read first, then
+// all of its expert rows, so a thread waits for two memory round trips
+// instead of two per slot; the combine then runs in slot order.
+template <bool Y_F32, bool OUT_F32, int KMAX>
 __global__ __launch_bounds__(256) void finalize_kernel(int T, int k, int H,
                                                        const void *__restrict__ y,
                                                        const float *__restrict__ w,
@@ -32,40 +36,51 @@ __global__ __launch_bounds__(256) void finalize_kernel(int T, int k, int H,
          i += (long long)gridDim.x * blockDim.x) {
         const int t = (int)(i / vec_per_row);
         const int c0 = (int)(i - (long long)t * vec_per_row) * 8;
+        int32_t r[KMAX];
+        float wt[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            r[j] = j < k ? inv[(size_t)t * k + j] : -1;
+            wt[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
+        }
+        float v[KMAX][8];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            if (r[j] < 0)
+                continue;
+            if (Y_F32) {
+                const float *src = static_cast<const float *>(y) + (size_t)r[j] * H + c0;
+                const floatx4 a = *reinterpret_cast<const floatx4 *>(src);
+                const floatx4 b = *reinterpret_cast<const floatx4 *>(src + 4);
+                v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
+                v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
+            } else {
+                const uint16_t *src = static_cast<const uint16_t *>(y) + (size_t)r[j] * H + c0;
+                const u32x4 d = *reinterpret_cast<const u32x4 *>(src);
+                v[j][0] = bf16_to_f32(d.x & 0xFFFFu); v[j][1] = bf16_to_f32(d.x >> 16);
+                v[j][2] = bf16_to_f32(d.y & 0xFFFFu); v[j][3] = bf16_to_f32(d.y >> 16);
+                v[j][4] = bf16_to_f32(d.z & 0xFFFFu); v[j][5] = bf16_to_f32(d.z >> 16);
+                v[j][6] = bf16_to_f32(d.w & 0xFFFFu); v[j][7] = bf16_to_f32(d.w >> 16);
+            }
+        }
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             acc[q] = 0.0f;
         bool first = true;
-        for (int j = 0; j < k; ++j) {
-            const int32_t r = inv[(size_t)t * k + j];
-            if (r < 0)
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            if (r[j] < 0)
                 continue;
-            const float wt = w[(size_t)t * k + j];
-            float v[8];
-            if (Y_F32) {
-                const float *src = static_cast<const float *>(y) + (size_t)r * H + c0;
-                const floatx4 a = *reinterpret_cast<const floatx4 *>(src);
-                const floatx4 b = *reinterpret_cast<const floatx4 *>(src + 4);
-                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-                v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-            } else {
-                const uint16_t *src = static_cast<const uint16_t *>(y) + (size_t)r * H + c0;
-                const u32x4 d = *reinterpret_cast<const u32x4 *>(src);
-                v[0] = bf16_to_f32(d.x & 0xFFFFu); v[1] = bf16_to_f32(d.x >> 16);
-                v[2] = bf16_to_f32(d.y & 0xFFFFu); v[3] = bf16_to_f32(d.y >> 16);
-                v[4] = bf16_to_f32(d.z & 0xFFFFu); v[5] = bf16_to_f32(d.z >> 16);
-                v[6] = bf16_to_f32(d.w & 0xFFFFu); v[7] = bf16_to_f32(d.w >> 16);
-            }
             if (first) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q)
-                    acc[q] = __fmul_rn(v[q], wt);
+                    acc[q] = __fmul_rn(v[j][q], wt[j]);
                 first = false;
             } else {
 #pragma unroll
                 for (int q = 0; q < 8; ++q)
-                    acc[q] = __fmaf_rn(v[q], wt, acc[q]);
+                    acc[q] = __fmaf_rn(v[j][q], wt[j], acc[q]);
             }
         }
         if (OUT_F32) {
@@ -79,6 +94,21 @@ __global__ __launch_bounds__(256) void finalize_kernel(int T, int k, int H,
                       pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
         }
     }
+}
+
+template <bool Y_F32, bool OUT_F32>
+void launch_fin(dim3 grid, dim3 block, hipStream_t st, int T, int k, int H, const void *y, const float *w,
+                const int32_t *inv, void *out)
+{
+    if (k <= 2)
+        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 2>), grid, block, 0, st, T, k, H, y, w, inv, out);
+    else if (k <= 4)
+        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 4>), grid, block, 0, st, T, k, H, y, w, inv, out);
+    else if (k <= 8)
+        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 8>), grid, block, 0, st, T, k, H, y, w, inv, out);
+    else
+        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, kMaxTopK>), grid, block, 0, st, T, k, H, y, w, inv,
+                           out);
 }
 
 }  // namespace
@@ -96,13 +126,13 @@ hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const
     const dim3 grid((unsigned)blocks), block(256);
     const int T = sh.num_tokens, k = sh.top_k, H = sh.hidden;
     if (y_f32 && out_f32)
-        hipLaunchKernelGGL((finalize_kernel<true, true>), grid, block, 0, st, T, k, H, y, w, inv_perm, out);
+        launch_fin<true, true>(grid, block, st, T, k, H, y, w, inv_perm, out);
     else if (y_f32)
-        hipLaunchKernelGGL((finalize_kernel<true, false>), grid, block, 0, st, T, k, H, y, w, inv_perm, out);
+        launch_fin<true, false>(grid, block, st, T, k, H, y, w, inv_perm, out);
     else if (out_f32)
-        hipLaunchKernelGGL((finalize_kernel<false, true>), grid, block, 0, st, T, k, H, y, w, inv_perm, out);
+        launch_fin<false, true>(grid, block, st, T, k, H, y, w, inv_perm, out);
     else
-        hipLaunchKernelGGL((finalize_kernel<false, false>), grid, block, 0, st, T, k, H, y, w, inv_perm, out);
+        launch_fin<false, false>(grid, block, st, T, k, H, y, w, inv_perm, out);
     return hipGetLastError();
 }
 

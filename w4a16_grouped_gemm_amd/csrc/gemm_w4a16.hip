@@ -53,6 +53,7 @@
 #include "common.hpp"
 
 #include <map>
+#include <type_traits>
 #include <mutex>
 #include <utility>
 
@@ -252,6 +253,15 @@ constexpr size_t stream_act_bytes()
     return sizeof(u32x4) * 2 * KSEG * NSUB * 4 * 64;
 }
 
+// LDS slot of MFMA step `step`, lane `lane` inside one 64-slot row: the low
+// four lane bits are XORed with (4*step + lane/16) so that the staging
+// writes (16 lanes of one token, all steps) and the MFMA reads (16 lanes of
+// one step) both hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int act_slot(int step, int lane)
+{
+    return lane ^ ((4 * step + (lane >> 4)) & 15);
+}
+
 template <int KIND, int TPW, int NSUB, int KSEG, int RING>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
 {
@@ -260,7 +270,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
     constexpr int CS = 16 * NSUB;
     constexpr int BT = 4 * TPW;                         // tiles per block
     extern __shared__ __align__(16) unsigned char s_dyn[];
-    // [buf][group][subtile][step][lane] activation fragments, then the chunk
+    // [buf][group][subtile][step][slot] activation fragments, then the chunk
     // prefix, the expert offsets and the scan scratch
     auto s_act = reinterpret_cast<u32x4(*)[KSEG][NSUB][4][64]>(s_dyn);
     const int E = p.num_experts;
@@ -281,11 +291,15 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
     const int G = p.K / kGroup;
     const int nseg = G / KSEG;                         // host guarantees KSEG | G
     const uint32_t row_bytes = (uint32_t)(p.K >> 1);
-    // staging: thread -> (token of the subtile, 16-byte chunk of a group)
+    // staging: thread -> 16 bytes (8 K positions) of one token of a group:
+    // token st_tok, chunk st_c16 = 4*kq + step of the MFMA fragment layout
     const int st_tok = tid >> 4;
     const int st_c16 = tid & 15;
-    const int st_lane = st_tok + 16 * (st_c16 >> 2);
-    const int st_step = st_c16 & 3;
+    const int st_idx = (st_c16 & 3) * 64 + act_slot(st_c16 & 3, st_tok + 16 * (st_c16 >> 2));
+    int rd_idx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        rd_idx[i] = i * 64 + act_slot(i, lane);
     const bf16x8 neg136 = neg136_operand();
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
 
@@ -327,29 +341,32 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         u32x4 wv[RING][TPW];                  // weights of groups g .. g+RING-1
         uint32_t sv[2][TPW][KSEG / 2];        // scales of the current and next segment
 
-        // Activations and scales of segment `seg`; the segment after the last
-        // is read out of range (zeros, no traffic).
-        auto load_seg = [&](int seg, int buf) {
+        // Activations and scales of segment `seg` into xr / sv[buf]; the
+        // segment after the last is read out of range (zeros, no traffic).
+        auto load_seg = [&](int seg, auto bufc) {
+            constexpr int buf = decltype(bufc)::value;
             const uint32_t oor = seg < nseg ? 0u : kOutOfRange;
-            const uint32_t soff = (uint32_t)(seg < nseg ? seg : 0) * KSEG * kGroup * 2;
+            const uint32_t sg = (uint32_t)(seg < nseg ? seg : 0);
 #pragma unroll
             for (int j = 0; j < KSEG; ++j)
 #pragma unroll
                 for (int sb = 0; sb < NSUB; ++sb)
-                    xr[j][sb] = bload16(ra, (voff_x[sb] | oor) + j * kGroup * 2, soff);
+                    xr[j][sb] = bload16(ra, (voff_x[sb] | oor) + j * kGroup * 2, sg * KSEG * kGroup * 2);
 #pragma unroll
             for (int t = 0; t < TPW; ++t)
 #pragma unroll
                 for (int h = 0; h < KSEG / 2; ++h)
-                    sv[buf][t][h] = __builtin_amdgcn_raw_buffer_load_b32(
-                        rs, (voff_s[t] | oor) + h * 4, (uint32_t)(seg < nseg ? seg : 0) * KSEG * 2, 0);
+                    sv[buf][t][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, (voff_s[t] | oor) + h * 4,
+                                                                        sg * KSEG * 2, 0);
         };
-        auto write_act = [&](int buf) {
+        auto write_act = [&](auto bufc) {
+            constexpr int buf = decltype(bufc)::value;
+            u32x4 *dst = &s_act[buf][0][0][0][0];
 #pragma unroll
             for (int j = 0; j < KSEG; ++j)
 #pragma unroll
                 for (int sb = 0; sb < NSUB; ++sb)
-                    s_act[buf][j][sb][st_step][st_lane] = permute_act(xr[j][sb]);
+                    dst[(j * NSUB + sb) * 256 + st_idx] = permute_act(xr[j][sb]);
         };
         auto load_w = [&](int g, int b) {
             const uint32_t oor = g < G ? 0u : kOutOfRange;
@@ -361,14 +378,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         // One group: the -136*sum(x) chain per subtile, then every tile's
         // chain of 4 MFMAs starting from it; the group scale is applied to
         // the chain result.
-        auto compute = [&](int buf, int sbuf, int j, int b) {
+        auto compute = [&](auto bufc, int j, int b) {
+            constexpr int buf = decltype(bufc)::value;
+            const u32x4 *src = &s_act[buf][0][0][0][0];
 #pragma unroll
             for (int sb = 0; sb < NSUB; ++sb) {
                 if (sb < nsub) {
                     u32x4 a[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        a[i] = s_act[buf][j][sb][i][lane];
+                        a[i] = src[(j * NSUB + sb) * 256 + rd_idx[i]];
                     floatx4 corr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -380,7 +399,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
                         acc = mfma(a[1], unpack8(wv[b][t].y), acc);
                         acc = mfma(a[2], unpack8(wv[b][t].z), acc);
                         acc = mfma(a[3], unpack8(wv[b][t].w), acc);
-                        const uint32_t d = sv[sbuf][t][j >> 1];
+                        const uint32_t d = sv[buf][t][j >> 1];
                         const float sc = __uint_as_float((j & 1) ? (d & 0xFFFF0000u) : (d << 16));
                         tot[t][sb].x = __builtin_fmaf(sc, acc.x, tot[t][sb].x);
                         tot[t][sb].y = __builtin_fmaf(sc, acc.y, tot[t][sb].y);
@@ -390,25 +409,37 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
                 }
             }
         };
-
-        __syncthreads();                                  // previous item done with s_act
-        load_seg(0, 0);
-#pragma unroll
-        for (int r = 0; r < RING - 1; ++r)
-            load_w(r, r);
-        write_act(0);
-        for (int seg = 0; seg < nseg; ++seg) {
+        // Segment `seg` staged in buffer BUF: prefetch the next segment,
+        // run its groups, stage the next segment into the other buffer.
+        // BUF is a constant so that register double buffers are indexed
+        // statically (no selects).
+        auto segment = [&](auto bufc, int seg) {
+            constexpr int buf = decltype(bufc)::value;
             __syncthreads();                              // segment seg staged; the other buffer free
-            load_seg(seg + 1, (seg + 1) & 1);
+            load_seg(seg + 1, std::integral_constant<int, buf ^ 1>());
 #pragma unroll
             for (int j = 0; j < KSEG; ++j) {
                 const int g = seg * KSEG + j;
                 load_w(g + RING - 1, (j + RING - 1) % RING);
-                compute(seg & 1, seg & 1, j, j % RING);
+                compute(bufc, j, j % RING);
             }
             if (seg + 1 < nseg)
-                write_act((seg + 1) & 1);
+                write_act(std::integral_constant<int, buf ^ 1>());
+        };
+
+        __syncthreads();                                  // previous item done with s_act
+        load_seg(0, std::integral_constant<int, 0>());
+#pragma unroll
+        for (int r = 0; r < RING - 1; ++r)
+            load_w(r, r);
+        write_act(std::integral_constant<int, 0>());
+        int seg = 0;
+        for (; seg + 2 <= nseg; seg += 2) {
+            segment(std::integral_constant<int, 0>(), seg);
+            segment(std::integral_constant<int, 1>(), seg + 1);
         }
+        if (seg < nseg)
+            segment(std::integral_constant<int, 0>(), seg);
 
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
@@ -638,12 +669,12 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     const int G = g.K / kGroup;
     const int ntiles = g.N / 16;
     // Measured on MI355X (Qwen3-30B-A3B and EP-shard decode shapes, 1..256
-    // tokens): two 16-row tiles per wave and one 16-token subtile, 4-group K
-    // segments (8 for K >= 4096); a 4-deep weight ring for long K or few rows
-    // per expert, else 2. More subtiles per wave lose at every decode size
-    // measured.
+    // tokens): two 16-row tiles per wave, 4-group K segments (8 for
+    // K >= 4096); a 4-deep weight ring for long K or few rows per expert,
+    // else 2; a second 16-token subtile once experts average more than 12
+    // rows (each expert's weights are then streamed once instead of twice).
     int mode = m < 1.25 ? 0 : 1;
-    int nsub = 1;
+    int nsub = m > 12.0 ? 2 : 1;
     int tpw = 2;
     int kseg = 4;
     int ring = (g.K >= 4096 || m < 3.0) ? 4 : 2;

@@ -20,8 +20,13 @@ namespace {
 
 constexpr int kPermThreads = 1024;
 constexpr int kMaskBytes = 32 * 1024;   // LDS budget for the token bitmaps
+constexpr size_t kDynLdsMax = 64 * 1024; // dynamic LDS of one launch: bitmaps + staged ids
 
 // One workgroup does the whole permutation: T*k <= 16M slots, E_loc <= 1024.
+// IDS_IN_LDS: the routing ids are read from global memory once, coalesced,
+// and every later pass reads LDS (each pass over global ids would cost a
+// memory round trip per slot of a thread).
+template <bool IDS_IN_LDS>
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int T, int k, int begin, int E, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm,
@@ -30,20 +35,35 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     __shared__ int s_count[kMaxExperts];
     __shared__ int s_cursor[kMaxExperts];
     __shared__ int s_wave_tot[kPermThreads / 64];
-    extern __shared__ uint32_t s_mask[];          // [E][words], words = chunk_tokens / 32
+    extern __shared__ uint32_t s_dyn[];
     const int tid = threadIdx.x;
     const int words = chunk_tokens >> 5;
+    const long long S = (long long)T * k;
+    uint32_t *s_mask = s_dyn;                                           // [E][words]
     int *s_wprefix = reinterpret_cast<int *>(s_mask + (size_t)E * words);   // [E][words]
+    int *s_ids = s_wprefix + (size_t)E * words;                         // [S] local expert or -1
 
     for (int e = tid; e < E; e += kPermThreads)
         s_count[e] = 0;
+    if (IDS_IN_LDS) {
+        // local expert index (or -1) of every slot
+        for (int i = tid; i < (int)S; i += kPermThreads) {
+            const int e = ids[i] - begin;
+            s_ids[i] = (e >= 0 && e < E) ? e : -1;
+        }
+    }
     __syncthreads();
+    auto local_expert = [&](long long slot) -> int {
+        if (IDS_IN_LDS)
+            return s_ids[slot];
+        const int e = ids[slot] - begin;
+        return (e >= 0 && e < E) ? e : -1;
+    };
 
     // 1. histogram of local slots
-    const long long S = (long long)T * k;
     for (long long i = tid; i < S; i += kPermThreads) {
-        int e = ids[i] - begin;
-        if (e >= 0 && e < E)
+        const int e = local_expert(i);
+        if (e >= 0)
             atomicAdd(&s_count[e], 1);
     }
     __syncthreads();
@@ -86,11 +106,14 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
         const int nt = min(chunk_tokens, T - t0);
         for (int tl = tid; tl < nt; tl += kPermThreads) {
             const int t = t0 + tl;
-            for (int j = 0; j < k; ++j) {
-                int e = ids[(size_t)t * k + j] - begin;
-                if (e >= 0 && e < E)
-                    atomicOr(&s_mask[e * words + (tl >> 5)], 1u << (tl & 31));
-            }
+            int le[kMaxTopK];                 // all of the token's ids first: one round trip
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j)
+                le[j] = j < k ? local_expert((long long)t * k + j) : -1;
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j)
+                if (le[j] >= 0)
+                    atomicOr(&s_mask[le[j] * words + (tl >> 5)], 1u << (tl & 31));
         }
         __syncthreads();
         // per-expert prefix popcounts over the chunk's words
@@ -104,11 +127,18 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
         __syncthreads();
         for (int tl = tid; tl < nt; tl += kPermThreads) {
             const int t = t0 + tl;
-            for (int j = 0; j < k; ++j) {
-                const size_t slot = (size_t)t * k + j;
-                int e = ids[slot] - begin;
+            int le[kMaxTopK];
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j)
+                le[j] = j < k ? local_expert((long long)t * k + j) : -1;
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j) {
+                if (j >= k)
+                    break;
+                const long long slot = (long long)t * k + j;
+                const int e = le[j];
                 int32_t row = -1;
-                if (e >= 0 && e < E) {
+                if (e >= 0) {
                     const uint32_t m = s_mask[e * words + (tl >> 5)];
                     const int rank = s_wprefix[e * words + (tl >> 5)] +
                                      __popc(m & ((1u << (tl & 31)) - 1u));
@@ -165,10 +195,18 @@ hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *coun
                           int32_t *offsets, int32_t *perm, int32_t *inv_perm, hipStream_t st)
 {
     const int E = sh.num_local_experts;
-    const int chunk = chunk_tokens_for(E);
+    int chunk = chunk_tokens_for(E);
+    while (chunk > 32 && chunk / 2 >= sh.num_tokens)      // no wider than the token count needs
+        chunk >>= 1;
     const size_t lds = (size_t)E * (chunk / 32) * 8;
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, st, sh.num_tokens,
-                       sh.top_k, sh.expert_begin, E, ids, counts, offsets, perm, inv_perm, chunk);
+    const long long S = (long long)sh.num_tokens * sh.top_k;
+    if (lds + (size_t)S * 4 <= kDynLdsMax)
+        hipLaunchKernelGGL(permute_kernel<true>, dim3(1), dim3(kPermThreads), lds + (size_t)S * 4, st,
+                           sh.num_tokens, sh.top_k, sh.expert_begin, E, ids, counts, offsets, perm, inv_perm,
+                           chunk);
+    else
+        hipLaunchKernelGGL(permute_kernel<false>, dim3(1), dim3(kPermThreads), lds, st, sh.num_tokens,
+                           sh.top_k, sh.expert_begin, E, ids, counts, offsets, perm, inv_perm, chunk);
     return hipGetLastError();
 }
 
