@@ -87,6 +87,13 @@ def make_replicas(wl, T, L, torch, seed_base=7):
     return inp, reps
 
 
+def pack_replicas(reps, ops):
+    """Reorder every replica's codes into the tiled layout (a once-per-model step, untimed)."""
+    for r in reps:
+        r["w13"] = ops.pack_weights(ops.W13_SWIGLU, r["w13"])
+        r["w2"] = ops.pack_weights(ops.W2, r["w2"])
+
+
 def new_batch(wl, T, reps, torch, seed):
     """Fresh activations / logits of T tokens for every replica (weights kept)."""
     dev = torch.device("cuda")
@@ -99,19 +106,19 @@ def new_batch(wl, T, reps, torch, seed):
     return out
 
 
-def time_layer(ops, wl, reps, steps, warmup, torch):
+def time_layer(ops, wl, reps, steps, warmup, torch, layout=0):
     """Capture L forwards in one graph; replay; return (seconds for `steps` steps, outs)."""
     L = len(reps)
     T = reps[0]["x"].shape[0]
     outs = [torch.empty((T, wl.hidden), dtype=torch.bfloat16, device="cuda") for _ in reps]
     wsz = ops.workspace_size(ops.make_shape(T, wl.hidden, wl.inter, wl.num_experts, wl.num_local_experts,
-                                            wl.top_k, wl.expert_begin))
+                                            wl.top_k, wl.expert_begin, weight_layout=layout))
     ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device="cuda")
 
     def fwd(i):
         r = reps[i]
         ops.moe_w4a16_forward(r["x"], r["logits"], r["w13"], r["s13"], r["w2"], r["s2"], wl.top_k,
-                              out=outs[i], expert_begin=wl.expert_begin, workspace=ws)
+                              out=outs[i], expert_begin=wl.expert_begin, workspace=ws, weight_layout=layout)
 
     for i in range(L):          # eager pass (also loads kernels)
         fwd(i)
@@ -161,7 +168,7 @@ def routing_stats(ops, wl, reps, torch):
     return res
 
 
-def time_gemm1(ops, wl, reps, stats, reps_n, torch):
+def time_gemm1(ops, wl, reps, stats, reps_n, torch, layout=0):
     """Average duration of one GEMM1 (w13 + SwiGLU) launch, HIP events on its stream."""
     L = len(reps)
     T = reps[0]["x"].shape[0]
@@ -170,7 +177,7 @@ def time_gemm1(ops, wl, reps, stats, reps_n, torch):
     def g1(i):
         ops.grouped_gemm_w4a16(ops.W13_SWIGLU, reps[i]["x"], stats[i]["offsets"], reps[i]["w13"],
                                reps[i]["s13"], num_tokens=T, top_k=wl.top_k, a_row_index=stats[i]["perm"],
-                               num_experts=wl.num_experts, out=hs[i])
+                               num_experts=wl.num_experts, out=hs[i], weight_layout=layout)
 
     for i in range(L):
         g1(i)
@@ -239,6 +246,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weights", choices=["tiled", "plain"], default="tiled",
+                    help="int4 code layout the layer reads (tiled: packed once before timing)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (scale reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -259,10 +268,13 @@ def main():
     T, L = args.tokens, args.replicas
     log(f"generating {L} replicas of {wl.name} (T={T})")
     inp, reps = make_replicas(wl, T, L, torch)
+    layout = ops.WEIGHTS_TILED if args.weights == "tiled" else ops.WEIGHTS_PLAIN
+    if layout == ops.WEIGHTS_TILED:
+        pack_replicas(reps, ops)
     stats = routing_stats(ops, wl, reps, torch)
     w13b, w2b = weight_bytes_per_expert(wl.hidden, wl.inter)
     log("timing the layer")
-    dt, _ = time_layer(ops, wl, reps, args.steps, args.warmup, torch)
+    dt, _ = time_layer(ops, wl, reps, args.steps, args.warmup, torch, layout)
     ms = dt / args.steps * 1e3
     tok_s = T * args.steps / dt
     mean_active = sum(s["active"] for s in stats) / L
@@ -270,7 +282,7 @@ def main():
     layer_gbps = layer_bytes / (ms * 1e-3) / 1e9
 
     log("timing GEMM1 alone")
-    g1 = time_gemm1(ops, wl, reps, stats, max(4, args.steps // L), torch)
+    g1 = time_gemm1(ops, wl, reps, stats, max(4, args.steps // L), torch, layout)
     g1_bytes = sum(gemm1_algorithmic_bytes(wl, T, s["active"], s["rows"]) for s in stats) / L
     achieved = g1_bytes / g1 / 1e9
     traffic, traffic_note = load_traffic(kernel_source_hash())
@@ -288,7 +300,7 @@ def main():
             reps_t = new_batch(wl, ts, reps, torch, seed=ts)
             st = routing_stats(ops, wl, reps_t, torch)
             n = max(args.steps, 200)
-            dts, _ = time_layer(ops, wl, reps_t, n, args.warmup, torch)
+            dts, _ = time_layer(ops, wl, reps_t, n, args.warmup, torch, layout)
             act = sum(s["active"] for s in st) / L
             us = dts / n * 1e6
             sweep.append({"tokens": ts, "us_per_layer": round(us, 2), "tokens_per_s": round(ts * n / dts, 1),
@@ -309,7 +321,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{wl.name} (Qwen3-30B-A3B MoE layer, decode)", "tokens": T,
                    "experts": wl.num_experts, "top_k": wl.top_k, "hidden": wl.hidden, "inter": wl.inter,
-                   "weights": "int4 group-128, bf16 scales", "activations": "bf16", "replicas": L,
+                   "weights": f"int4 group-128 ({args.weights} code layout), bf16 scales",
+                   "activations": "bf16", "replicas": L,
                    "parallelism": "single GPU"},
         "layer_weight_GBps": round(layer_gbps, 1), "layer_hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"kernel": "gemm_stream_kernel<W13_SWIGLU> (GEMM1 + SwiGLU)", "bound": "hbm",

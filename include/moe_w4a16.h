@@ -48,6 +48,18 @@
  *          [0, I) are the gate projection, [I, 2I) the up projection.
  *   w2_q   uint8 [E_loc][H][I/2],   s2  bf16 [E_loc][H][I/128].
  *   Weight arrays start at local expert 0 (global id expert_begin).
+ *
+ * Tiled code layout (moe_shape.weight_layout == MOE_WEIGHTS_TILED; scales
+ * keep the plain layout above). The same bytes as the plain codes of a
+ * weight matrix with N rows and K columns, reordered so that one 64-lane
+ * load of 16 bytes per lane reads 1 KiB contiguously:
+ *   tiled[e][b][g][i][l][0..16) = plain[e][row(16*(8*b+i), l%16)][64*g + 16*(l/16) .. +16)
+ *   b < N/128 (blocks of 8 sixteen-row tiles), g < K/128, i < 8, l < 64,
+ *   row(t0, n) = t0 + n                           for MOE_GEMM_W2 / W13_RAW,
+ *   row(16*t, n) = 8*t + n (n < 8), I + 8*t + n - 8 (n >= 8)
+ *                                                 for MOE_GEMM_W13_SWIGLU
+ *   (a gate row and its up row share a tile). moe_w4a16_pack_weights writes
+ *   it; it is an offline, once-per-model step.
  */
 #ifndef MOE_W4A16_H
 #define MOE_W4A16_H
@@ -77,6 +89,11 @@ typedef enum {
     MOE_GEMM_W13_RAW = 2     /* a[R][H] x w13^T -> c[R][2I] (no activation)      */
 } moe_gemm_kind;
 
+typedef enum {
+    MOE_WEIGHTS_PLAIN = 0,     /* row-major codes (the storage format above)     */
+    MOE_WEIGHTS_TILED = 1      /* codes reordered by moe_w4a16_pack_weights      */
+} moe_weight_layout;
+
 typedef struct {
     int32_t num_tokens;        /* T >= 0                                         */
     int32_t hidden;            /* H, multiple of 128, <= 16384                   */
@@ -86,6 +103,7 @@ typedef struct {
     int32_t num_local_experts; /* E_loc, 1..1024, expert_begin+E_loc <= E_g      */
     int32_t top_k;             /* 1..min(E_g, 16)                                */
     int32_t group_size;        /* quantisation group along K: 128 only           */
+    int32_t weight_layout;     /* moe_weight_layout of w13_q / w2_q / wq         */
 } moe_shape;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -107,7 +125,8 @@ size_t moe_w4a16_workspace_size(const moe_shape *shape);
  * finalize, all on `stream`, no host synchronisation.
  *   x             bf16  [T][H]        activations
  *   router_logits f32   [T][E_g]
- *   w13_q, s13, w2_q, s2              local experts' weights (formats above)
+ *   w13_q, s13, w2_q, s2              local experts' weights (formats above;
+ *                                     codes plain or tiled per weight_layout)
  *   out           bf16  [T][H]        written for every token; a token with no
  *                                     local slot gets +0.0
  *   workspace     >= moe_w4a16_workspace_size(shape) bytes, 256-B aligned
@@ -186,6 +205,22 @@ moe_status moe_grouped_gemm_w4a16(const moe_shape *shape, moe_gemm_kind kind, co
 moe_status moe_finalize(const moe_shape *shape, const void *y, moe_dtype y_dtype,
                         const float *topk_w, const int32_t *inv_perm, void *out,
                         moe_dtype out_dtype, void *stream);
+
+/*
+ * Reorder one weight matrix's int4 codes from the plain layout into the tiled
+ * layout described above (an internal layout of the grouped GEMM, like the
+ * kernel layout [FI] section 3 inverts back to a plain one in its tests).
+ *   kind    MOE_GEMM_W13_SWIGLU (w13, gate/up rows paired in tiles),
+ *           MOE_GEMM_W13_RAW (w13, rows in order) or MOE_GEMM_W2 (w2)
+ *   wq      uint8 plain codes of the shape's E_loc experts
+ *   wq_tiled uint8, same size, must not overlap wq
+ * shape->weight_layout is ignored. The GEMM and the layer then take
+ * wq_tiled with weight_layout = MOE_WEIGHTS_TILED (w13 packed with
+ * MOE_GEMM_W13_SWIGLU for the layer and for W13_SWIGLU GEMMs, with
+ * MOE_GEMM_W13_RAW for W13_RAW GEMMs). Bit-exact byte permutation.
+ */
+moe_status moe_w4a16_pack_weights(const moe_shape *shape, moe_gemm_kind kind, const uint8_t *wq,
+                                  uint8_t *wq_tiled, void *stream);
 
 #ifdef __cplusplus
 }

@@ -53,3 +53,25 @@ def assert_layer_close(got_u16, ref_u16, what=""):
         f"mean_rel={mean_rel:.2e}")
     assert max_err <= MAX_ABS_FRAC * max_ref, (what, max_err, max_ref)
     assert mean_rel <= MEAN_REL, (what, mean_rel)
+
+
+def tiled_codes(wq, kind, inter):
+    """The tiled code layout written out from its definition in the C header:
+    tiled[e][b][g][i][l] = plain[e][row(16*(8b+i), l%16)][64g + 16(l//16) : +16].
+    kind 0 (W13_SWIGLU) pairs gate row 8t+n with up row I+8t+n in tile t."""
+    wq = np.asarray(wq, np.uint8)
+    E, N, K2 = wq.shape
+    G = (2 * K2) // 128
+    out = np.empty((E, N // 128, G, 8, 64, 16), np.uint8)
+    for b in range(N // 128):
+        for i in range(8):
+            t = 8 * b + i
+            for n in range(16):
+                if kind == 0:
+                    row = 8 * t + n if n < 8 else inter + 8 * t + n - 8
+                else:
+                    row = 16 * t + n
+                for g in range(G):
+                    for kq in range(4):
+                        out[:, b, g, i, 16 * kq + n, :] = wq[:, row, 64 * g + 16 * kq: 64 * g + 16 * kq + 16]
+    return out.reshape(E, N, K2)

@@ -15,12 +15,16 @@ from w4a16_grouped_gemm_amd.inputs import make_layer_inputs
 pytestmark = pytest.mark.gpu
 
 
-def _forward(inp, out=None):
+def _forward(inp, out=None, tiled=False):
     import torch
     from w4a16_grouped_gemm_amd import ops
-    o = ops.moe_w4a16_forward(bf16_dev(inp.x), to_dev(inp.logits), to_dev(inp.w13_q), bf16_dev(inp.s13),
-                              to_dev(inp.w2_q), bf16_dev(inp.s2), inp.workload.top_k, out=out,
-                              expert_begin=inp.workload.expert_begin)
+    w13, w2 = to_dev(inp.w13_q), to_dev(inp.w2_q)
+    if tiled:
+        w13, w2 = ops.pack_weights(ops.W13_SWIGLU, w13), ops.pack_weights(ops.W2, w2)
+    o = ops.moe_w4a16_forward(bf16_dev(inp.x), to_dev(inp.logits), w13, bf16_dev(inp.s13),
+                              w2, bf16_dev(inp.s2), inp.workload.top_k, out=out,
+                              expert_begin=inp.workload.expert_begin,
+                              weight_layout=ops.WEIGHTS_TILED if tiled else ops.WEIGHTS_PLAIN)
     torch.cuda.synchronize()
     return to_np_u16(o)
 
@@ -83,3 +87,13 @@ def test_zero_tokens_is_noop_and_errors_touch_nothing():
                               workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     assert bool((sentinel == 7.0).all())
+
+
+@pytest.mark.parametrize("wl,T", [("tiny", 16), ("qwen3_decode", 1), ("qwen3_decode", 256),
+                                  ("ep_shard_decode", 64)])
+def test_tiled_layout_gives_identical_layer(wl, T):
+    # the tiled codes feed the same MFMA sequence in the same order: the
+    # layer output must match the plain-layout run bit for bit
+    say(f"layer tiled vs plain {wl} T={T}")
+    inp = make_layer_inputs(wl, T)
+    assert np.array_equal(_forward(inp, tiled=True), _forward(inp))

@@ -53,3 +53,19 @@ def test_shape_queries_without_gpu():
     g64 = ops.make_shape(16, 256, 512, 8, 8, 2, group_size=64)
     assert ops.check_shape(g64) == 3
     assert ops.status_str(0) == "MOE_OK"
+
+
+def test_layout_validation_without_gpu():
+    # an unknown weight layout is rejected on the host
+    bad = ops.make_shape(16, 256, 512, 8, 8, 2, weight_layout=2)
+    assert ops.check_shape(bad) == 3
+    assert not ops.is_supported(bad)
+    tiled = ops.make_shape(16, 256, 512, 8, 8, 2, weight_layout=ops.WEIGHTS_TILED)
+    assert ops.check_shape(tiled) == 0
+    # packing in place is refused before any launch (host-side check only)
+    lib = ops.load_library()
+    sh = ops.make_shape(0, 256, 512, 8, 8, 1)
+    p = ctypes.c_void_p(1 << 20)
+    assert lib.moe_w4a16_pack_weights(ctypes.byref(sh), 0, p, p, None) == 3
+    assert lib.moe_w4a16_pack_weights(ctypes.byref(sh), 7, p, p, None) == 3
+    assert lib.moe_w4a16_pack_weights(ctypes.byref(sh), 0, None, p, None) == 1

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libmoe_w4a16.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm_w4a16.hip", "finalize.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm_w4a16.hip", "finalize.hip", "pack.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

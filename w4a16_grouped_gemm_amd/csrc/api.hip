@@ -55,6 +55,8 @@ moe_status check_shape(const moe_shape *sh)
         return MOE_ERR_SHAPE;
     if (sh->top_k < 1 || sh->top_k > kMaxTopK || sh->top_k > sh->num_experts)
         return MOE_ERR_SHAPE;
+    if (sh->weight_layout != MOE_WEIGHTS_PLAIN && sh->weight_layout != MOE_WEIGHTS_TILED)
+        return MOE_ERR_UNSUPPORTED;
     // activation-sized arrays are addressed with 32-bit buffer offsets
     const long long rows = (long long)sh->num_tokens * sh->top_k;
     const long long widest = sh->hidden > sh->inter ? sh->hidden : sh->inter;
@@ -119,6 +121,7 @@ GemmLaunch gemm_args(const moe_shape &sh, moe_gemm_kind kind)
         g.N = 2 * sh.inter;
     }
     g.a_bytes = (size_t)g.max_rows * g.K * 2;
+    g.w_tiled = sh.weight_layout == MOE_WEIGHTS_TILED;
     return g;
 }
 
@@ -254,6 +257,29 @@ moe_status moe_finalize(const moe_shape *shape, const void *y, moe_dtype y_dtype
         return MOE_ERR_ALIGN;
     return from_hip(launch_finalize(*shape, y, y_dtype == MOE_F32, topk_w, inv_perm, out,
                                     out_dtype == MOE_F32, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_w4a16_pack_weights(const moe_shape *shape, moe_gemm_kind kind, const uint8_t *wq,
+                                  uint8_t *wq_tiled, void *stream)
+{
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK)
+        return st;
+    if (kind != MOE_GEMM_W13_SWIGLU && kind != MOE_GEMM_W2 && kind != MOE_GEMM_W13_RAW)
+        return MOE_ERR_UNSUPPORTED;
+    if (!wq || !wq_tiled)
+        return MOE_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(wq_tiled, 16))
+        return MOE_ERR_ALIGN;
+    const int N = kind == MOE_GEMM_W2 ? shape->hidden : 2 * shape->inter;
+    const int K = kind == MOE_GEMM_W2 ? shape->inter : shape->hidden;
+    const size_t bytes = (size_t)shape->num_local_experts * N * (K / 2);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(wq), b = reinterpret_cast<uintptr_t>(wq_tiled);
+    if (a < b + bytes && b < a + bytes)
+        return MOE_ERR_UNSUPPORTED;                       // in place or overlapping
+    return from_hip(launch_pack_weights(shape->num_local_experts, N, K, shape->inter,
+                                        kind == MOE_GEMM_W13_SWIGLU, wq, wq_tiled,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const float *router_logits,

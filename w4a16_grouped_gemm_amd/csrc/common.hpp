@@ -73,6 +73,7 @@ struct GemmLaunch {
     int max_rows;             // T * k: upper bound on R
     int expected_rows;        // expected R (routed slots on local experts)
     size_t a_bytes;           // bytes of the activation array `a`
+    bool w_tiled;             // codes in the tiled layout (1 KiB per tile and group)
 };
 
 hipError_t launch_route(const moe_shape &sh, const float *logits, int32_t *ids, float *w,
@@ -82,6 +83,8 @@ hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *coun
 hipError_t launch_gather(const moe_shape &sh, const uint16_t *x, const int32_t *perm,
                          const int32_t *offsets, uint16_t *x_perm, hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st);
+hipError_t launch_pack_weights(int E, int N, int K, int half, bool pair_rows, const uint8_t *wq,
+                               uint8_t *wq_tiled, hipStream_t st);
 hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const float *w,
                            const int32_t *inv_perm, void *out, bool out_f32, hipStream_t st);
 

@@ -79,7 +79,19 @@ struct GemmArgs {
     int ldc;        // output row stride (elements)
     int half;       // SwiGLU: row offset of the up projection (= I)
     int c_f32;
+    int w_tiled;    // codes in the tiled layout: tile t, group g at ((t/8)*G*8 + t%8)*1 KiB + g*8 KiB
 };
+
+// Lane offset of a tile's codes and the byte step from one group to the next.
+__device__ __forceinline__ uint32_t code_offset(const GemmArgs &p, int tile, uint32_t row, int G, uint32_t row_bytes,
+                                                int lane)
+{
+    if (p.w_tiled)
+        return (uint32_t)((tile >> 3) * G * 8 + (tile & 7)) * 1024u + (uint32_t)lane * 16u;
+    return row * row_bytes + (uint32_t)(lane >> 4) * 16u;
+}
+
+__device__ __forceinline__ uint32_t group_stride(const GemmArgs &p) { return p.w_tiled ? 8192u : 64u; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -302,6 +314,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         rd_idx[i] = i * 64 + act_slot(i, lane);
     const bf16x8 neg136 = neg136_operand();
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+    const uint32_t gstride = group_stride(p);
 
     for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
         const int chunk = item / nblocks;
@@ -318,7 +331,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const uint32_t row = (uint32_t)tile_row<KIND>(p, tile0 + t, n16);
-            voff_w[t] = row * row_bytes + kq * 16;
+            voff_w[t] = code_offset(p, tile0 + t, row, G, row_bytes, lane);
             voff_s[t] = row * (uint32_t)G * 2;
         }
         uint32_t voff_x[NSUB];
@@ -370,7 +383,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         };
         auto load_w = [&](int g, int b) {
             const uint32_t oor = g < G ? 0u : kOutOfRange;
-            const uint32_t soff = (uint32_t)(g < G ? g : 0) * 64;
+            const uint32_t soff = (uint32_t)(g < G ? g : 0) * gstride;
 #pragma unroll
             for (int t = 0; t < TPW; ++t)
                 wv[b][t] = bload16(rw, voff_w[t] | oor, soff);
@@ -479,6 +492,7 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
     const uint32_t row_bytes = (uint32_t)(p.K >> 1);
     const bf16x8 neg136 = neg136_operand();
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+    const uint32_t gstride = group_stride(p);
 
     for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
         const int chunk = item / ntiles;
@@ -489,7 +503,7 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (size_t)e * p.N * row_bytes, (uint32_t)p.N * row_bytes);
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s + (size_t)e * p.N * G, (uint32_t)p.N * G * 2);
         const uint32_t row = (uint32_t)tile_row<KIND>(p, tile, n16);
-        const uint32_t voff_w = row * row_bytes + kq * 16;
+        const uint32_t voff_w = code_offset(p, tile, row, G, row_bytes, lane);
         const uint32_t voff_s = row * (uint32_t)G * 2;
         uint32_t voff_x = kOutOfRange;
         if (n16 < nvalid) {
@@ -507,7 +521,7 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
             for (int j = 0; j < GB; ++j) {
                 if (gb + j < g1) {
                     const uint32_t g = gb + j;
-                    wv[j] = bload16(rw, voff_w, g * 64);
+                    wv[j] = bload16(rw, voff_w, g * gstride);
                     sc[j] = bload_scale(rs, voff_s, g * 2);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -654,6 +668,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     a.K = g.K;
     a.N = g.N;
     a.c_f32 = g.c_f32 ? 1 : 0;
+    a.w_tiled = g.w_tiled ? 1 : 0;
     a.half = g.N / 2;
     a.ldc = (g.kind == MOE_GEMM_W13_SWIGLU) ? g.N / 2 : g.N;
 

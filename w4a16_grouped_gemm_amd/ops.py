@@ -22,18 +22,19 @@ LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
 
 MOE_BF16, MOE_F32 = 0, 1
 W13_SWIGLU, W2, W13_RAW = 0, 1, 2
+WEIGHTS_PLAIN, WEIGHTS_TILED = 0, 1
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
            4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP"}
 EXPORTED = ["moe_status_str", "moe_w4a16_check_shape", "moe_w4a16_is_supported",
             "moe_w4a16_workspace_size", "moe_w4a16_forward", "moe_route", "moe_permute_workspace_size",
-            "moe_permute", "moe_grouped_gemm_w4a16", "moe_finalize"]
+            "moe_permute", "moe_grouped_gemm_w4a16", "moe_finalize", "moe_w4a16_pack_weights"]
 
 
 class MoeShape(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("expert_begin", ctypes.c_int32),
                 ("num_local_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("group_size", ctypes.c_int32)]
+                ("group_size", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
 
 
 class MoeError(ValueError):
@@ -77,14 +78,16 @@ def load_library(path: str = LIB_PATH):
         lib.moe_grouped_gemm_w4a16.restype = I
         lib.moe_finalize.argtypes = [S, P, I, P, P, P, I, P]
         lib.moe_finalize.restype = I
+        lib.moe_w4a16_pack_weights.argtypes = [S, I, P, P, P]
+        lib.moe_w4a16_pack_weights.restype = I
         _lib = lib
         return lib
 
 
 def make_shape(num_tokens, hidden, inter, num_experts, num_local_experts, top_k, expert_begin=0,
-               group_size=128) -> MoeShape:
+               group_size=128, weight_layout=WEIGHTS_PLAIN) -> MoeShape:
     return MoeShape(int(num_tokens), int(hidden), int(inter), int(num_experts), int(expert_begin),
-                    int(num_local_experts), int(top_k), int(group_size))
+                    int(num_local_experts), int(top_k), int(group_size), int(weight_layout))
 
 
 def status_str(code: int) -> str:
@@ -171,10 +174,28 @@ def permute(topk_ids: torch.Tensor, num_local_experts: int, *, num_experts: int 
     return counts, offsets, perm, inv_perm, x_perm
 
 
+def pack_weights(kind: int, wq: torch.Tensor, *, stream=None) -> torch.Tensor:
+    """Plain -> tiled int4 codes of one weight matrix (same shape and dtype).
+
+    kind: W13_SWIGLU (w13 for the layer / SwiGLU GEMM), W13_RAW or W2."""
+    _need(wq, torch.uint8, "wq")
+    E_loc, N, K2 = wq.shape
+    if kind == W2:
+        H, I = N, 2 * K2
+    else:
+        H, I = 2 * K2, N // 2
+    out = torch.empty_like(wq)
+    sh = make_shape(0, H, I, E_loc, E_loc, 1)
+    _check(load_library().moe_w4a16_pack_weights(ctypes.byref(sh), int(kind), _ptr(wq), _ptr(out),
+                                                 _stream(stream)))
+    return out
+
+
 def grouped_gemm_w4a16(kind: int, a: torch.Tensor, offsets: torch.Tensor, wq: torch.Tensor,
                        s: torch.Tensor, *, num_tokens: int, top_k: int,
                        a_row_index: torch.Tensor | None = None, out_dtype=torch.bfloat16,
-                       num_experts: int | None = None, out: torch.Tensor | None = None, stream=None):
+                       num_experts: int | None = None, out: torch.Tensor | None = None, stream=None,
+                       weight_layout: int = WEIGHTS_PLAIN):
     """Grouped W4A16 GEMM over expert slabs; returns c [num_tokens*top_k, cols]."""
     _need(a, torch.bfloat16, "a")
     _need(offsets, torch.int32, "offsets")
@@ -200,7 +221,7 @@ def grouped_gemm_w4a16(kind: int, a: torch.Tensor, offsets: torch.Tensor, wq: to
     dt = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}.get(out.dtype)
     if dt is None:
         raise ValueError("out dtype must be bfloat16 or float32")
-    sh = make_shape(num_tokens, H, I, num_experts or E_loc, E_loc, top_k)
+    sh = make_shape(num_tokens, H, I, num_experts or E_loc, E_loc, top_k, weight_layout=weight_layout)
     _check(load_library().moe_grouped_gemm_w4a16(ctypes.byref(sh), int(kind), _ptr(a), _ptr(a_row_index),
                                                  _ptr(offsets), _ptr(wq), _ptr(s), _ptr(out), dt,
                                                  _stream(stream)))
@@ -242,8 +263,12 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 def moe_w4a16_forward(x: torch.Tensor, router_logits: torch.Tensor, w13_q: torch.Tensor,
                       s13: torch.Tensor, w2_q: torch.Tensor, s2: torch.Tensor, top_k: int,
                       out: torch.Tensor | None = None, stream=None, *, expert_begin: int = 0,
-                      workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """The whole quantized MoE expert layer (route, permute, GEMM1+SwiGLU, GEMM2, finalize)."""
+                      workspace: torch.Tensor | None = None,
+                      weight_layout: int = WEIGHTS_PLAIN) -> torch.Tensor:
+    """The whole quantized MoE expert layer (route, permute, GEMM1+SwiGLU, GEMM2, finalize).
+
+    weight_layout=WEIGHTS_TILED takes codes from pack_weights (w13 packed
+    with W13_SWIGLU, w2 with W2)."""
     _need(x, torch.bfloat16, "x")
     _need(router_logits, torch.float32, "router_logits")
     _need(w13_q, torch.uint8, "w13_q")
@@ -260,7 +285,7 @@ def moe_w4a16_forward(x: torch.Tensor, router_logits: torch.Tensor, w13_q: torch
         raise ValueError("scale shapes do not match the weights")
     if router_logits.shape[0] != T:
         raise ValueError("router_logits rows != tokens")
-    sh = make_shape(T, H, I, E_g, E_loc, top_k, expert_begin)
+    sh = make_shape(T, H, I, E_g, E_loc, top_k, expert_begin, weight_layout=weight_layout)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     lib = load_library()
