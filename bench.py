@@ -52,6 +52,28 @@ def weight_bytes_per_expert(H: int, I: int):
     return w13, w2
 
 
+MFMA_PEAK_TFLOPS = 2500.0
+
+
+def time_prefill(ops, reps, torch, layout, steps, warmup):
+    """The same layer shape in prefill: 2048 tokens whose routing follows Zipf(1.1)
+    expert popularity, weights of the decode replicas. Reported against the
+    dense bf16 MFMA peak (algorithmic flops 6 * I * H per routed row)."""
+    from w4a16_grouped_gemm_amd.inputs import WORKLOADS, make_layer_inputs
+    wl = WORKLOADS["qwen3_prefill"]
+    T = 2048
+    inp = make_layer_inputs(wl, T, weights=False)
+    dev = torch.device("cuda")
+    x = torch.from_numpy(inp.x).to(dev).view(torch.bfloat16)
+    lg = torch.from_numpy(inp.logits).to(dev)
+    reps_p = [dict(r, x=x, logits=lg) for r in reps]
+    dt, _ = time_layer(ops, wl, reps_p, steps, warmup, torch, layout)
+    us = dt / steps * 1e6
+    flops = 6.0 * wl.inter * wl.hidden * T * wl.top_k
+    return {"tokens": T, "routing": "zipf(1.1)", "us_per_layer": round(us, 1), "tokens_per_s": round(T / (us * 1e-6), 1),
+            "tflops": round(flops / (us * 1e-6) / 1e12, 1), "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
+
+
 def gemm1_algorithmic_bytes(wl, T, active, rows):
     """Bytes GEMM1 must move at least once: the weights and scales of every
     active expert, the T input rows, the rows x I SwiGLU outputs, the offsets
@@ -310,6 +332,11 @@ def main():
                       "active_experts": mean_active, "weight_GBps": round(layer_gbps, 1),
                       "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4)})
 
+    prefill = None
+    if not args.no_sweep:
+        log("prefill T=2048 (Zipf routing)")
+        prefill = time_prefill(ops, reps, torch, layout, max(8, args.steps // 50), args.warmup // 10 + 1)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
@@ -333,6 +360,7 @@ def main():
                      "traffic_note": traffic_note},
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "prefill": prefill,
     }
     print(json.dumps(rec), flush=True)
 
