@@ -139,3 +139,45 @@ def test_pack_matches_layout_definition(kind, wl):
     torch.cuda.synchronize()
     want = tiled_codes(wq, 0 if kind == ops.W13_SWIGLU else 1, inp.workload.inter)
     assert np.array_equal(got.cpu().numpy(), want)
+
+
+# Launch shapes chosen by the host heuristic depend on the expected load; the
+# integer-exact pin must hold for every kernel variant, so each is forced here
+# (MOE_GEMM_* environment overrides are read at every launch).
+VARIANTS = [
+    {"MOE_GEMM_MODE": "0"},
+    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "2", "MOE_GEMM_NSUB": "1", "MOE_GEMM_KSEG": "4", "MOE_GEMM_RING": "4"},
+    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "2", "MOE_GEMM_NSUB": "2", "MOE_GEMM_KSEG": "2", "MOE_GEMM_RING": "2"},
+    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "2", "MOE_GEMM_NSUB": "4", "MOE_GEMM_KSEG": "1", "MOE_GEMM_RING": "2"},
+    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "4", "MOE_GEMM_NSUB": "1", "MOE_GEMM_KSEG": "8", "MOE_GEMM_RING": "4"},
+]
+
+
+@pytest.mark.parametrize("variant", range(len(VARIANTS)))
+@pytest.mark.parametrize("kind,H,I", [(2, 2048, 768), (1, 1024, 1024)])
+@pytest.mark.parametrize("tiled", [False, True])
+def test_integer_exact_every_launch_shape(variant, kind, H, I, tiled, monkeypatch):
+    from w4a16_grouped_gemm_amd import ops
+    for k_, v_ in VARIANTS[variant].items():
+        monkeypatch.setenv(k_, v_)
+    say(f"gemm integer-exact variant={VARIANTS[variant]} kind={kind} H={H} I={I} tiled={tiled}")
+    rng = np.random.default_rng(variant * 7 + kind)
+    counts = np.array([0, 1, 17, 40, 3, 0, 70, 16, 33, 128, 65, 200])
+    E = len(counts)
+    N, K = (2 * I, H) if kind == ops.W13_RAW else (H, I)
+    q = rng.integers(-8, 8, size=(E, N, K), dtype=np.int8)
+    s = np.full((E, N, K // 128), bf16_bits(np.float32(2.0 ** -6)), np.uint16)
+    offsets = _offsets(counts)
+    R = int(offsets[-1])
+    k = 4
+    T = (R + k - 1) // k + 1
+    xi = rng.integers(-2, 3, size=(T, K))
+    a = bf16_bits(xi.astype(np.float32))
+    idx = np.full(T * k, -1, np.int32)
+    idx[:R] = rng.permutation(T * k)[:R].astype(np.int32)
+    wq = pack_int4(q)
+    got = _gpu_gemm(kind, a, offsets, wq, s, T=T, k=k, a_row_index=idx, tiled=tiled)
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        want = (xi[idx[r0:r1] // k].astype(np.int64) @ q[e].T.astype(np.int64)).astype(np.float64) * 2.0 ** -6
+        assert np.array_equal(got[r0:r1].astype(np.float64), want), e

@@ -277,8 +277,9 @@ __device__ __forceinline__ int act_slot(int step, int lane)
 template <int KIND, int TPW, int NSUB, int KSEG, int RING>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
 {
-    static_assert(KSEG % RING == 0, "the weight ring index follows the group index within a segment");
-    static_assert(KSEG % 2 == 0, "scales are loaded as dwords of two groups");
+    static_assert((2 * KSEG) % RING == 0, "the weight ring slot of group g is g % RING, static per segment parity");
+    static_assert(KSEG == 1 || KSEG % 2 == 0, "scales are loaded as dwords of two groups");
+    constexpr int SD = (KSEG + 1) / 2;                 // scale dwords per tile and segment
     constexpr int CS = 16 * NSUB;
     constexpr int BT = 4 * TPW;                         // tiles per block
     extern __shared__ __align__(16) unsigned char s_dyn[];
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
 
         u32x4 xr[KSEG][NSUB];
         u32x4 wv[RING][TPW];                  // weights of groups g .. g+RING-1
-        uint32_t sv[2][TPW][KSEG / 2];        // scales of the current and next segment
+        uint32_t sv[2][TPW][SD];              // scales of the current and next segment
 
         // Activations and scales of segment `seg` into xr / sv[buf]; the
         // segment after the last is read out of range (zeros, no traffic).
@@ -365,12 +366,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
 #pragma unroll
                 for (int sb = 0; sb < NSUB; ++sb)
                     xr[j][sb] = bload16(ra, (voff_x[sb] | oor) + j * kGroup * 2, sg * KSEG * kGroup * 2);
+            // KSEG == 1: the dword of groups (seg & ~1, seg | 1); seg has the parity of buf
+            const uint32_t s_soff = KSEG == 1 ? (sg & ~1u) * 2 : sg * KSEG * 2;
 #pragma unroll
             for (int t = 0; t < TPW; ++t)
 #pragma unroll
-                for (int h = 0; h < KSEG / 2; ++h)
-                    sv[buf][t][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, (voff_s[t] | oor) + h * 4,
-                                                                        sg * KSEG * 2, 0);
+                for (int h = 0; h < SD; ++h)
+                    sv[buf][t][h] = __builtin_amdgcn_raw_buffer_load_b32(rs, (voff_s[t] | oor) + h * 4, s_soff, 0);
         };
         auto write_act = [&](auto bufc) {
             constexpr int buf = decltype(bufc)::value;
@@ -413,7 +415,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
                         acc = mfma(a[2], unpack8(wv[b][t].z), acc);
                         acc = mfma(a[3], unpack8(wv[b][t].w), acc);
                         const uint32_t d = sv[buf][t][j >> 1];
-                        const float sc = __uint_as_float((j & 1) ? (d & 0xFFFF0000u) : (d << 16));
+                        const int hi = KSEG == 1 ? buf : (j & 1);
+                        const float sc = __uint_as_float(hi ? (d & 0xFFFF0000u) : (d << 16));
                         tot[t][sb].x = __builtin_fmaf(sc, acc.x, tot[t][sb].x);
                         tot[t][sb].y = __builtin_fmaf(sc, acc.y, tot[t][sb].y);
                         tot[t][sb].z = __builtin_fmaf(sc, acc.z, tot[t][sb].z);
@@ -433,8 +436,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
 #pragma unroll
             for (int j = 0; j < KSEG; ++j) {
                 const int g = seg * KSEG + j;
-                load_w(g + RING - 1, (j + RING - 1) % RING);
-                compute(bufc, j, j % RING);
+                load_w(g + RING - 1, (buf * KSEG + j + RING - 1) % RING);
+                compute(bufc, j, (buf * KSEG + j) % RING);
             }
             if (seg + 1 < nseg)
                 write_act(std::integral_constant<int, buf ^ 1>());
@@ -646,6 +649,8 @@ hipError_t launch_kind(const GemmArgs &a, int max_rows, int mode, int tpw, int n
     MOE_STREAM(2, 2, 2, 2) MOE_STREAM(2, 2, 4, 2) MOE_STREAM(2, 2, 4, 4) MOE_STREAM(2, 4, 2, 2)
     MOE_STREAM(4, 1, 2, 2) MOE_STREAM(4, 1, 4, 2) MOE_STREAM(4, 1, 4, 4) MOE_STREAM(4, 1, 8, 4)
     MOE_STREAM(4, 2, 2, 2) MOE_STREAM(4, 2, 4, 2) MOE_STREAM(4, 2, 4, 4) MOE_STREAM(4, 4, 2, 2)
+    MOE_STREAM(2, 8, 1, 2) MOE_STREAM(4, 8, 1, 2) MOE_STREAM(2, 4, 1, 2) MOE_STREAM(4, 4, 1, 2)
+    MOE_STREAM(2, 8, 2, 2) MOE_STREAM(4, 8, 2, 2)
 #undef MOE_STREAM
     // no streaming instance for this combination: the split-K kernel takes any shape
     return launch_kind<KIND>(a, max_rows, 0, tpw, nsub, kseg, ring, st);
@@ -687,14 +692,19 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     // tokens): two 16-row tiles per wave, 4-group K segments (8 for
     // K >= 4096); a 4-deep weight ring for long K or few rows per expert,
     // else 2; a second 16-token subtile once experts average more than 12
-    // rows (each expert's weights are then streamed once instead of twice).
+    // rows (each expert's weights are then streamed once instead of twice),
+    // four (64 tokens, one group per segment) once they average more than 48.
     int mode = m < 1.25 ? 0 : 1;
-    int nsub = m > 12.0 ? 2 : 1;
+    int nsub = m > 48.0 ? 4 : (m > 12.0 ? 2 : 1);
     int tpw = 2;
     int kseg = 4;
     int ring = (g.K >= 4096 || m < 3.0) ? 4 : 2;
     if (g.K >= 4096)
         kseg = 8;
+    if (nsub == 4) {                                     // prefill: 64-token chunks, one group per segment
+        kseg = 1;
+        ring = 2;
+    }
     if (const char *env = getenv("MOE_GEMM_MODE"))
         mode = atoi(env);
     if (const char *env = getenv("MOE_GEMM_TPW"))
@@ -710,7 +720,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     // LDS: 2 buffers x KSEG groups x NSUB subtiles x 4 KiB <= 64 KiB
     while (kseg > 2 && (G % kseg != 0 || 2 * kseg * nsub * 4 > 64))
         kseg >>= 1;
-    if (kseg % ring != 0)
+    if ((2 * kseg) % ring != 0)
         ring = 2;
     if (mode != 0 && (ntiles % (4 * tpw) != 0 || G % kseg != 0))
         mode = 0;                                         // shapes the streaming tiles do not divide
