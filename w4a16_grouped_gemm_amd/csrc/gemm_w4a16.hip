@@ -139,6 +139,19 @@ __device__ __forceinline__ floatx4 mfma(u32x4 a, bf16x8 b, floatx4 c)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// silu for a value that is rounded to bf16 next: hardware exp2 and reciprocal
+// (errors of a few fp32 ulp, far below the bf16 rounding step).
+__device__ __forceinline__ float silu_fast(float g)
+{
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
+// Value of lane (l ^ 8) within each 16-lane row (DPP row rotate by 8).
+__device__ __forceinline__ float row_swap8(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ bf16x8 neg136_operand()
 {
     const u32x4 v = {kNeg136, kNeg136, kNeg136, kNeg136};
@@ -457,12 +470,59 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         if (seg < nseg)
             segment(std::integral_constant<int, 0>(), seg);
 
+        // ---- epilogue: bf16 results pass through the LDS buffer the last
+        // segment did not use (every wave is past that segment's barrier), so
+        // each lane stores one 16-byte run of an output row instead of four
+        // scattered 2-byte values ----
+        constexpr bool SWI = KIND == MOE_GEMM_W13_SWIGLU;
+        constexpr int COLS = SWI ? 8 : 16;                 // output columns per tile
+        constexpr int NBLK = TPW * NSUB;                   // (tile, subtile) blocks of a wave
+        constexpr bool VIA_LDS = 4 * NBLK * 16 * COLS * 2 <= KSEG * NSUB * 4096;
+        if (VIA_LDS && (SWI || !p.c_f32)) {
+            uint16_t *so = reinterpret_cast<uint16_t *>(&s_act[nseg & 1][0][0][0][0]) + wave * (NBLK * 16 * COLS);
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
+            for (int t = 0; t < TPW; ++t)
 #pragma unroll
-            for (int sb = 0; sb < NSUB; ++sb)
-                if (sb < nsub)
-                    store_tile<KIND>(p, tot[t][sb], tile0 + t, row0, sb * 16 + kq * 4, nvalid, n16);
+                for (int sb = 0; sb < NSUB; ++sb) {
+                    const floatx4 v = tot[t][sb];
+                    const float r4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = kq * 4 + i;
+                        if (SWI) {
+                            const float up = row_swap8(r4[i]);     // lane n16 + 8 holds the up row
+                            if (n16 < 8)
+                                so[((t * NSUB + sb) * 16 + rr) * COLS + n16] =
+                                    (uint16_t)f32_to_bf16_rne(silu_fast(r4[i]) * up);
+                        } else {
+                            so[((t * NSUB + sb) * 16 + rr) * COLS + n16] = (uint16_t)f32_to_bf16_rne(r4[i]);
+                        }
+                    }
+                }
+            __builtin_amdgcn_wave_barrier();
+            uint16_t *c = static_cast<uint16_t *>(p.c);
+            constexpr int LPR = COLS * 2 / 16;                 // lanes per row (16 bytes each)
+            constexpr int BPP = 64 / (16 * LPR);               // blocks per pass
+#pragma unroll
+            for (int b0 = 0; b0 < NBLK; b0 += BPP) {
+                const int b = b0 + lane / (16 * LPR);
+                const int rr = (lane / LPR) & 15;
+                const int part = lane % LPR;
+                const int t = b / NSUB, sb = b - (b / NSUB) * NSUB;
+                const int m = sb * 16 + rr;
+                if (b < NBLK && sb < nsub && m < nvalid) {
+                    const u32x4 d = *reinterpret_cast<const u32x4 *>(so + (b * 16 + rr) * COLS + part * 8);
+                    *reinterpret_cast<u32x4 *>(c + (size_t)(row0 + m) * p.ldc + (tile0 + t) * COLS + part * 8) = d;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int sb = 0; sb < NSUB; ++sb)
+                    if (sb < nsub)
+                        store_tile<KIND>(p, tot[t][sb], tile0 + t, row0, sb * 16 + kq * 4, nvalid, n16);
+        }
     }
 }
 
@@ -720,7 +780,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     // LDS: 2 buffers x KSEG groups x NSUB subtiles x 4 KiB <= 64 KiB
     while (kseg > 2 && (G % kseg != 0 || 2 * kseg * nsub * 4 > 64))
         kseg >>= 1;
-    if ((2 * kseg) % ring != 0)
+    if (kseg % ring != 0 && !(kseg == 1 && ring == 2))   // instantiated ring depths
         ring = 2;
     if (mode != 0 && (ntiles % (4 * tpw) != 0 || G % kseg != 0))
         mode = 0;                                         // shapes the streaming tiles do not divide

@@ -14,13 +14,15 @@
 // because H is a multiple of 128.
 #include "common.hpp"
 
+#include <mutex>
+
 namespace moe {
 
 namespace {
 
 constexpr int kPermThreads = 1024;
 constexpr int kMaskBytes = 32 * 1024;   // LDS budget for the token bitmaps
-constexpr size_t kDynLdsMax = 64 * 1024; // dynamic LDS of one launch: bitmaps + staged ids
+constexpr size_t kDynLdsMax = 144 * 1024; // dynamic LDS of one launch: bitmaps + staged ids (160 KiB per CU)
 
 // One workgroup does the whole permutation: T*k <= 16M slots, E_loc <= 1024.
 // IDS_IN_LDS: the routing ids are read from global memory once, coalesced,
@@ -200,11 +202,19 @@ hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *coun
         chunk >>= 1;
     const size_t lds = (size_t)E * (chunk / 32) * 8;
     const long long S = (long long)sh.num_tokens * sh.top_k;
-    if (lds + (size_t)S * 4 <= kDynLdsMax)
-        hipLaunchKernelGGL(permute_kernel<true>, dim3(1), dim3(kPermThreads), lds + (size_t)S * 4, st,
+    if (lds + (size_t)S * 4 <= kDynLdsMax) {
+        const size_t dyn = lds + (size_t)S * 4;
+        if (dyn > 64 * 1024) {
+            static std::once_flag once;
+            std::call_once(once, [] {
+                (void)hipFuncSetAttribute(reinterpret_cast<const void *>(permute_kernel<true>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDynLdsMax);
+            });
+        }
+        hipLaunchKernelGGL(permute_kernel<true>, dim3(1), dim3(kPermThreads), dyn, st,
                            sh.num_tokens, sh.top_k, sh.expert_begin, E, ids, counts, offsets, perm, inv_perm,
                            chunk);
-    else
+    } else
         hipLaunchKernelGGL(permute_kernel<false>, dim3(1), dim3(kPermThreads), lds, st, sh.num_tokens,
                            sh.top_k, sh.expert_begin, E, ids, counts, offsets, perm, inv_perm, chunk);
     return hipGetLastError();
