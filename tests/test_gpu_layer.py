@@ -97,3 +97,29 @@ def test_tiled_layout_gives_identical_layer(wl, T):
     say(f"layer tiled vs plain {wl} T={T}")
     inp = make_layer_inputs(wl, T)
     assert np.array_equal(_forward(inp, tiled=True), _forward(inp))
+
+
+@pytest.mark.parametrize("wl,T", [("tiny", 16), ("qwen3_decode", 1), ("qwen3_decode", 64),
+                                  ("qwen3_decode", 256), ("qwen3_decode", 300), ("ep_shard_decode", 16),
+                                  ("ep_shard_decode", 256)])
+def test_forward_equals_the_entry_points_composed(wl, T):
+    # forward routes and permutes in one workgroup while the tokens are few
+    # and in two launches otherwise; either way it must give, bit for bit,
+    # what moe_route -> moe_permute -> two grouped GEMMs -> moe_finalize give
+    import torch
+    from w4a16_grouped_gemm_amd import ops
+    say(f"layer forward vs composed entry points {wl} T={T}")
+    inp = make_layer_inputs(wl, T)
+    w = inp.workload
+    x, logits = bf16_dev(inp.x), to_dev(inp.logits)
+    w13, s13, w2, s2 = to_dev(inp.w13_q), bf16_dev(inp.s13), to_dev(inp.w2_q), bf16_dev(inp.s2)
+    ids, wt = ops.route(logits, w.top_k)
+    _, offsets, perm, inv, _ = ops.permute(ids, w.num_local_experts, num_experts=w.num_experts,
+                                           expert_begin=w.expert_begin)
+    h = ops.grouped_gemm_w4a16(ops.W13_SWIGLU, x, offsets, w13, s13, num_tokens=T, top_k=w.top_k,
+                               a_row_index=perm, num_experts=w.num_experts)
+    y = ops.grouped_gemm_w4a16(ops.W2, h, offsets, w2, s2, num_tokens=T, top_k=w.top_k,
+                               num_experts=w.num_experts)
+    composed = ops.finalize(y, wt, inv)
+    torch.cuda.synchronize()
+    assert np.array_equal(_forward(inp), to_np_u16(composed))

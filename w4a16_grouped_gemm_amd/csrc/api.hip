@@ -302,9 +302,14 @@ moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const fl
     if (workspace_bytes < ws.bytes)
         return MOE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_route(sh, router_logits, ws.ids, ws.w, s);
-    if (e == hipSuccess)
-        e = launch_permute(sh, ws.ids, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s);
+    hipError_t e;
+    if (route_permute_fusable(sh)) {
+        e = launch_route_permute(sh, router_logits, ws.ids, ws.w, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s);
+    } else {
+        e = launch_route(sh, router_logits, ws.ids, ws.w, s);
+        if (e == hipSuccess)
+            e = launch_permute(sh, ws.ids, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s);
+    }
     if (e == hipSuccess) {
         GemmLaunch g = gemm_args(sh, MOE_GEMM_W13_SWIGLU);
         g.a = x;

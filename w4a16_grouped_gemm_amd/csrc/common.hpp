@@ -80,6 +80,10 @@ hipError_t launch_route(const moe_shape &sh, const float *logits, int32_t *ids, 
                         hipStream_t st);
 hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *perm, int32_t *inv_perm, hipStream_t st);
+bool route_permute_fusable(const moe_shape &sh);
+hipError_t launch_route_permute(const moe_shape &sh, const float *logits, int32_t *ids, float *w,
+                                int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
+                                hipStream_t st);
 hipError_t launch_gather(const moe_shape &sh, const uint16_t *x, const int32_t *perm,
                          const int32_t *offsets, uint16_t *x_perm, hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st);

@@ -749,14 +749,16 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     const int G = g.K / kGroup;
     const int ntiles = g.N / 16;
     // Measured on MI355X (Qwen3-30B-A3B and EP-shard decode shapes, 1..256
-    // tokens): two 16-row tiles per wave, 4-group K segments (8 for
+    // tokens): the streaming kernel once it has more than two waves per CU
+    // (active experts x 16-row tiles / 2 tiles per wave), split-K below
+    // that; two 16-row tiles per wave, 4-group K segments (8 for
     // K >= 4096); a 4-deep weight ring for long K or few rows per expert,
     // else 2; a second 16-token subtile once experts average more than 12
     // rows (each expert's weights are then streamed once instead of twice),
     // four (64 tokens, one group per segment) once they average more than 48.
-    int mode = m < 1.25 ? 0 : 1;
-    int nsub = m > 48.0 ? 4 : (m > 12.0 ? 2 : 1);
     int tpw = 2;
+    int mode = active * ntiles / tpw > 2.0 * device_cu_count() ? 1 : 0;
+    int nsub = m > 48.0 ? 4 : (m > 12.0 ? 2 : 1);
     int kseg = 4;
     int ring = (g.K >= 4096 || m < 3.0) ? 4 : 2;
     if (g.K >= 4096)

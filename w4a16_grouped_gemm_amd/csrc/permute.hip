@@ -13,7 +13,9 @@
 // copy only the valid rows, with wide vectors; rows are 16-byte aligned here
 // because H is a multiple of 128.
 #include "common.hpp"
+#include "route_core.hpp"
 
+#include <cstdlib>
 #include <mutex>
 
 namespace moe {
@@ -28,12 +30,18 @@ constexpr size_t kDynLdsMax = 144 * 1024; // dynamic LDS of one launch: bitmaps 
 // IDS_IN_LDS: the routing ids are read from global memory once, coalesced,
 // and every later pass reads LDS (each pass over global ids would cost a
 // memory round trip per slot of a thread).
-template <bool IDS_IN_LDS>
+// ROUTE: the workgroup routes the tokens itself first (logits in, ids and
+// weights written out as by moe_route, local ids kept in LDS), saving the
+// separate routing launch and its round trip through memory. TL and PL are
+// the routing shape (lanes per token, logits per lane).
+template <bool IDS_IN_LDS, bool ROUTE = false, int TL = 16, int PL = 8>
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int T, int k, int begin, int E, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm,
-    int chunk_tokens)
+    int chunk_tokens, const float *__restrict__ logits = nullptr, int E_g = 0,
+    int32_t *__restrict__ ids_out = nullptr, float *__restrict__ w_out = nullptr)
 {
+    static_assert(!ROUTE || IDS_IN_LDS, "routing in the kernel keeps the ids in LDS");
     __shared__ int s_count[kMaxExperts];
     __shared__ int s_cursor[kMaxExperts];
     __shared__ int s_wave_tot[kPermThreads / 64];
@@ -47,7 +55,25 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 
     for (int e = tid; e < E; e += kPermThreads)
         s_count[e] = 0;
-    if (IDS_IN_LDS) {
+    if (ROUTE) {
+        // 64 / TL tokens per wave and pass; a token's TL lanes form whole DPP rows
+        constexpr int TPWV = 64 / TL;
+        const int lane = tid & 63, q = lane % TL;
+        for (int t0 = (tid >> 6) * TPWV; t0 < T; t0 += (kPermThreads / 64) * TPWV) {
+            const int t = t0 + lane / TL;
+            if (t < T) {
+                int eg;
+                float wt;
+                route_token<TL, PL>(logits + (size_t)t * E_g, E_g, k, q, eg, wt);
+                if (q < k) {
+                    ids_out[(size_t)t * k + q] = eg;
+                    w_out[(size_t)t * k + q] = wt;
+                    const int e = eg - begin;
+                    s_ids[t * k + q] = (e >= 0 && e < E) ? e : -1;
+                }
+            }
+        }
+    } else if (IDS_IN_LDS) {
         // local expert index (or -1) of every slot
         for (int i = tid; i < (int)S; i += kPermThreads) {
             const int e = ids[i] - begin;
@@ -217,6 +243,49 @@ hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *coun
     } else
         hipLaunchKernelGGL(permute_kernel<false>, dim3(1), dim3(kPermThreads), lds, st, sh.num_tokens,
                            sh.top_k, sh.expert_begin, E, ids, counts, offsets, perm, inv_perm, chunk);
+    return hipGetLastError();
+}
+
+bool route_permute_fusable(const moe_shape &sh)
+{
+    const int E = sh.num_local_experts;
+    int chunk = chunk_tokens_for(E);
+    while (chunk > 32 && chunk / 2 >= sh.num_tokens)
+        chunk >>= 1;
+    const size_t lds = (size_t)E * (chunk / 32) * 8 + (size_t)sh.num_tokens * sh.top_k * 4;
+    // One workgroup routes every token: it pays while routing is one pass of
+    // its 16 waves (4 tokens each) and at most two waves share a SIMD; past that the separate routing launch,
+    // spread over many CUs, is faster. MOE_ROUTE_FUSE_MAX_T overrides.
+    static const int max_t = [] {
+        const char *env = getenv("MOE_ROUTE_FUSE_MAX_T");
+        return env ? atoi(env) : 32;
+    }();
+    return sh.num_experts <= 256 && sh.num_tokens <= max_t && lds <= kDynLdsMax;
+}
+
+hipError_t launch_route_permute(const moe_shape &sh, const float *logits, int32_t *ids, float *w,
+                                int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
+                                hipStream_t st)
+{
+    const int E = sh.num_local_experts;
+    int chunk = chunk_tokens_for(E);
+    while (chunk > 32 && chunk / 2 >= sh.num_tokens)
+        chunk >>= 1;
+    const size_t dyn = (size_t)E * (chunk / 32) * 8 + (size_t)sh.num_tokens * sh.top_k * 4;
+    auto launch = [&](auto kernel) {
+        if (dyn > 64 * 1024)
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDynLdsMax);
+        hipLaunchKernelGGL(kernel, dim3(1), dim3(kPermThreads), dyn, st, sh.num_tokens, sh.top_k,
+                           sh.expert_begin, E, nullptr, counts, offsets, perm, inv_perm, chunk, logits,
+                           sh.num_experts, ids, w);
+    };
+    if (sh.num_experts <= 64)
+        launch(permute_kernel<true, true, 16, 4>);
+    else if (sh.num_experts <= 128)
+        launch(permute_kernel<true, true, 16, 8>);
+    else
+        launch(permute_kernel<true, true, 16, 16>);
     return hipGetLastError();
 }
 
