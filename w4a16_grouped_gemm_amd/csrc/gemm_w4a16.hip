@@ -709,8 +709,7 @@ hipError_t launch_kind(const GemmArgs &a, int max_rows, int mode, int tpw, int n
     MOE_STREAM(2, 2, 2, 2) MOE_STREAM(2, 2, 4, 2) MOE_STREAM(2, 2, 4, 4) MOE_STREAM(2, 4, 2, 2)
     MOE_STREAM(4, 1, 2, 2) MOE_STREAM(4, 1, 4, 2) MOE_STREAM(4, 1, 4, 4) MOE_STREAM(4, 1, 8, 4)
     MOE_STREAM(4, 2, 2, 2) MOE_STREAM(4, 2, 4, 2) MOE_STREAM(4, 2, 4, 4) MOE_STREAM(4, 4, 2, 2)
-    MOE_STREAM(2, 8, 1, 2) MOE_STREAM(4, 8, 1, 2) MOE_STREAM(2, 4, 1, 2) MOE_STREAM(4, 4, 1, 2)
-    MOE_STREAM(2, 8, 2, 2) MOE_STREAM(4, 8, 2, 2)
+    MOE_STREAM(2, 4, 1, 2) MOE_STREAM(4, 4, 1, 2)
 #undef MOE_STREAM
     // no streaming instance for this combination: the split-K kernel takes any shape
     return launch_kind<KIND>(a, max_rows, 0, tpw, nsub, kseg, ring, st);
@@ -755,16 +754,19 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     // K >= 4096); a 4-deep weight ring for long K or few rows per expert,
     // else 2; a second 16-token subtile once experts average more than 12
     // rows (each expert's weights are then streamed once instead of twice),
-    // four (64 tokens, one group per segment) once they average more than 48.
+    // and with it four tiles per wave and a 2-deep ring (the correction
+    // MFMAs and the activation reads of a subtile serve twice the weights).
+    // Prefill (2048 tokens) is fastest with the same shape: four subtiles
+    // with one group per segment came out 8% slower.
     int tpw = 2;
     int mode = active * ntiles / tpw > 2.0 * device_cu_count() ? 1 : 0;
-    int nsub = m > 48.0 ? 4 : (m > 12.0 ? 2 : 1);
+    int nsub = m > 12.0 ? 2 : 1;
     int kseg = 4;
     int ring = (g.K >= 4096 || m < 3.0) ? 4 : 2;
     if (g.K >= 4096)
         kseg = 8;
-    if (nsub == 4) {                                     // prefill: 64-token chunks, one group per segment
-        kseg = 1;
+    if (nsub == 2) {
+        tpw = 4;
         ring = 2;
     }
     if (const char *env = getenv("MOE_GEMM_MODE"))
