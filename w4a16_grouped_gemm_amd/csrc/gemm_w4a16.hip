@@ -63,6 +63,7 @@ namespace {
 
 constexpr uint32_t kNeg136 = 0xC308C308u;  // bf16 pair (-136, -136)
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every descriptor
+constexpr int kXcds = 8;                         // MI355X: 8 XCDs of 32 CUs, one L2 each
 
 struct GemmArgs {
     const uint16_t *a;
@@ -330,7 +331,17 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
     const uint32_t gstride = group_stride(p);
 
-    for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+    // XCD-aware schedule: workgroups are dispatched round-robin over the
+    // XCDs (workgroup b runs on XCD b % kXcds), each with its own L2. XCD x
+    // takes the x-th contiguous share of the chunk-major item list, so the
+    // blocks of one chunk, which read the same activation rows, meet in one
+    // L2 instead of fetching them once per XCD. The host makes the grid a
+    // multiple of kXcds whenever it is at least kXcds.
+    const int nx = (int)gridDim.x >= kXcds ? kXcds : 1;
+    const int xcd = blockIdx.x % nx;
+    const int i_end = (int)((long long)total_items * (xcd + 1) / nx);
+    for (int item = (int)((long long)total_items * xcd / nx) + blockIdx.x / nx; item < i_end;
+         item += gridDim.x / nx) {
         const int chunk = item / nblocks;
         const int block = item - chunk * nblocks;
         const int e = uniform(chunk_expert(s_prefix, E, chunk));
@@ -672,7 +683,9 @@ hipError_t launch_stream(const GemmArgs &a, int max_rows, hipStream_t st)
     // persistent grid: at most the resident slots, at most the item bound
     const int nblocks = (a.N >> 4) / (4 * TPW);
     const long long chunks = (long long)min(a.num_experts, max_rows) + max_rows / CS;
-    const long long grid = grid_for(chunks * nblocks, per_cu);
+    long long grid = grid_for(chunks * nblocks, per_cu);
+    if (grid >= kXcds)
+        grid -= grid % kXcds;                          // whole XCD shares (see the kernel)
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
