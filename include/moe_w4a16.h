@@ -197,7 +197,9 @@ moe_status moe_grouped_gemm_w4a16(const moe_shape *shape, moe_gemm_kind kind, co
  * round to nearest even); each later present slot gives
  * acc = fma(y[r][c], w[t][j], acc) (IEEE binary32 FMA); no slot -> +0.0.
  * No flush-to-zero: subnormal inputs, products and sums are kept.
- *   y       [T*k][H]  bf16 or f32 (y_dtype)
+ *   y       [T*k][H]  bf16 or f32 (y_dtype); the whole array must be
+ *                     readable (the kernel may read row 0 for an absent slot
+ *                     and discard it)
  *   topk_w  f32 [T][k], inv_perm int32 [T][k]
  *   out     [T][H]    f32 (the accumulator) or bf16 (its RNE rounding)
  * Bit-exact against the IEEE definition.

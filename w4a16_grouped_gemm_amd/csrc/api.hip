@@ -322,6 +322,9 @@ moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const fl
         g.c_f32 = false;
         e = launch_grouped_gemm(g, s);
     }
+    // every slot local: the down GEMM writes y in slot order and the
+    // finalize reads it without the inv_perm indirection
+    const bool y_slot = sh.num_local_experts == sh.num_experts;
     if (e == hipSuccess) {
         GemmLaunch g = gemm_args(sh, MOE_GEMM_W2);
         g.a = ws.h;
@@ -330,11 +333,12 @@ moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const fl
         g.wq = w2_q;
         g.s = s2;
         g.c = ws.y;
+        g.c_row_index = y_slot ? ws.perm : nullptr;
         g.c_f32 = false;
         e = launch_grouped_gemm(g, s);
     }
     if (e == hipSuccess)
-        e = launch_finalize(sh, ws.y, false, ws.w, ws.inv_perm, out, false, s);
+        e = launch_finalize(sh, ws.y, false, ws.w, ws.inv_perm, out, false, s, y_slot);
     return from_hip(e);
 }
 

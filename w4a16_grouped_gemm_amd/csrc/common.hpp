@@ -67,6 +67,7 @@ struct GemmLaunch {
     const uint8_t *wq;
     const uint16_t *s;
     void *c;
+    const int32_t *c_row_index;  // NULL, or row r of the result is stored at row c_row_index[r]
     bool c_f32;
     int K;                    // reduction length
     int N;                    // weight rows per expert
@@ -90,7 +91,8 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st);
 hipError_t launch_pack_weights(int E, int N, int K, int half, bool pair_rows, const uint8_t *wq,
                                uint8_t *wq_tiled, hipStream_t st);
 hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const float *w,
-                           const int32_t *inv_perm, void *out, bool out_f32, hipStream_t st);
+                           const int32_t *inv_perm, void *out, bool out_f32, hipStream_t st,
+                           bool y_slot = false);
 
 int device_cu_count();
 

@@ -23,7 +23,11 @@ namespace {
 // KMAX >= k. All of a token's row indices and weights are read first, then
 // all of its expert rows, so a thread waits for two memory round trips
 // instead of two per slot; the combine then runs in slot order.
-template <bool Y_F32, bool OUT_F32, int KMAX>
+// Y_SLOT: y is in slot order (row t*k + j, as the layer's down GEMM writes
+// it when every slot is local), so the row loads need no index and go out
+// together with the index and weight loads: one round trip. inv_perm then
+// only says which slots are present.
+template <bool Y_F32, bool OUT_F32, int KMAX, bool Y_SLOT>
 __global__ __launch_bounds__(256) void finalize_kernel(int T, int k, int H,
                                                        const void *__restrict__ y,
                                                        const float *__restrict__ w,
@@ -36,26 +40,30 @@ __global__ __launch_bounds__(256) void finalize_kernel(int T, int k, int H,
          i += (long long)gridDim.x * blockDim.x) {
         const int t = (int)(i / vec_per_row);
         const int c0 = (int)(i - (long long)t * vec_per_row) * 8;
+        // No load below sits under a branch (a load under one makes the
+        // compiler wait for every earlier load first, serialising the round
+        // trips): slots past k re-read slot k - 1, absent slots read row 0,
+        // and both are masked in the combine.
         int32_t r[KMAX];
         float wt[KMAX];
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
-            r[j] = j < k ? inv[(size_t)t * k + j] : -1;
-            wt[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
+            const size_t sl = (size_t)t * k + (j < k ? j : k - 1);
+            r[j] = inv[sl];
+            wt[j] = w[sl];
         }
         float v[KMAX][8];
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
-            if (r[j] < 0)
-                continue;
+            const size_t yrow = Y_SLOT ? (size_t)t * k + (j < k ? j : k - 1) : (size_t)(r[j] >= 0 ? r[j] : 0);
             if (Y_F32) {
-                const float *src = static_cast<const float *>(y) + (size_t)r[j] * H + c0;
+                const float *src = static_cast<const float *>(y) + yrow * H + c0;
                 const floatx4 a = *reinterpret_cast<const floatx4 *>(src);
                 const floatx4 b = *reinterpret_cast<const floatx4 *>(src + 4);
                 v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
                 v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
             } else {
-                const uint16_t *src = static_cast<const uint16_t *>(y) + (size_t)r[j] * H + c0;
+                const uint16_t *src = static_cast<const uint16_t *>(y) + yrow * H + c0;
                 const u32x4 d = *reinterpret_cast<const u32x4 *>(src);
                 v[j][0] = bf16_to_f32(d.x & 0xFFFFu); v[j][1] = bf16_to_f32(d.x >> 16);
                 v[j][2] = bf16_to_f32(d.y & 0xFFFFu); v[j][3] = bf16_to_f32(d.y >> 16);
@@ -63,6 +71,10 @@ __global__ __launch_bounds__(256) void finalize_kernel(int T, int k, int H,
                 v[j][6] = bf16_to_f32(d.w & 0xFFFFu); v[j][7] = bf16_to_f32(d.w >> 16);
             }
         }
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j >= k)
+                r[j] = -1;
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q)
@@ -96,25 +108,28 @@ __global__ __launch_bounds__(256) void finalize_kernel(int T, int k, int H,
     }
 }
 
-template <bool Y_F32, bool OUT_F32>
+template <bool Y_F32, bool OUT_F32, bool Y_SLOT>
 void launch_fin(dim3 grid, dim3 block, hipStream_t st, int T, int k, int H, const void *y, const float *w,
                 const int32_t *inv, void *out)
 {
     if (k <= 2)
-        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 2>), grid, block, 0, st, T, k, H, y, w, inv, out);
-    else if (k <= 4)
-        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 4>), grid, block, 0, st, T, k, H, y, w, inv, out);
-    else if (k <= 8)
-        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 8>), grid, block, 0, st, T, k, H, y, w, inv, out);
-    else
-        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, kMaxTopK>), grid, block, 0, st, T, k, H, y, w, inv,
+        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 2, Y_SLOT>), grid, block, 0, st, T, k, H, y, w, inv,
                            out);
+    else if (k <= 4)
+        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 4, Y_SLOT>), grid, block, 0, st, T, k, H, y, w, inv,
+                           out);
+    else if (k <= 8)
+        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 8, Y_SLOT>), grid, block, 0, st, T, k, H, y, w, inv,
+                           out);
+    else
+        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, kMaxTopK, Y_SLOT>), grid, block, 0, st, T, k, H, y, w,
+                           inv, out);
 }
 
 }  // namespace
 
 hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const float *w,
-                           const int32_t *inv_perm, void *out, bool out_f32, hipStream_t st)
+                           const int32_t *inv_perm, void *out, bool out_f32, hipStream_t st, bool y_slot)
 {
     const long long total = (long long)sh.num_tokens * (sh.hidden / 8);
     long long blocks = (total + 255) / 256;
@@ -125,14 +140,16 @@ hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const
         blocks = 1;
     const dim3 grid((unsigned)blocks), block(256);
     const int T = sh.num_tokens, k = sh.top_k, H = sh.hidden;
-    if (y_f32 && out_f32)
-        launch_fin<true, true>(grid, block, st, T, k, H, y, w, inv_perm, out);
+    if (y_slot)                                   // the layer's path: bf16 y in slot order, bf16 out
+        launch_fin<false, false, true>(grid, block, st, T, k, H, y, w, inv_perm, out);
+    else if (y_f32 && out_f32)
+        launch_fin<true, true, false>(grid, block, st, T, k, H, y, w, inv_perm, out);
     else if (y_f32)
-        launch_fin<true, false>(grid, block, st, T, k, H, y, w, inv_perm, out);
+        launch_fin<true, false, false>(grid, block, st, T, k, H, y, w, inv_perm, out);
     else if (out_f32)
-        launch_fin<false, true>(grid, block, st, T, k, H, y, w, inv_perm, out);
+        launch_fin<false, true, false>(grid, block, st, T, k, H, y, w, inv_perm, out);
     else
-        launch_fin<false, false>(grid, block, st, T, k, H, y, w, inv_perm, out);
+        launch_fin<false, false, false>(grid, block, st, T, k, H, y, w, inv_perm, out);
     return hipGetLastError();
 }
 

@@ -72,6 +72,8 @@ struct GemmArgs {
     const uint8_t *wq;
     const uint16_t *s;
     void *c;
+    const int32_t *c_row_index;  // output row r goes to row c_row_index[r] (NULL: row r)
+    uint32_t c_row_bytes;        // bytes of c_row_index (0 when NULL)
     uint32_t a_bytes;  // bytes of `a` reachable through the buffer descriptor (< 2^31)
     int top_k;
     int num_experts;
@@ -229,9 +231,18 @@ __device__ __forceinline__ int tile_row(const GemmArgs &p, int tile, int n16)
 }
 
 // Store one lane's 4 results (tokens 4*kq+i of the subtile, row n16 of tile).
+// Output row of result row r: r itself, or c_row_index[r] (read here unless
+// the caller preloaded it into pre[i] for rows mbase + i).
+__device__ __forceinline__ int out_row(const GemmArgs &p, int r, const int *pre, int i)
+{
+    if (!p.c_row_index)
+        return r;
+    return pre ? pre[i] : p.c_row_index[r];
+}
+
 template <int KIND>
 __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx4 v, int tile, int row0, int mbase,
-                                           int nvalid, int n16)
+                                           int nvalid, int n16, const int *pre = nullptr)
 {
     float r[4] = {v.x, v.y, v.z, v.w};
     if (KIND == MOE_GEMM_W13_SWIGLU) {
@@ -245,7 +256,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx4 v, int til
             for (int i = 0; i < 4; ++i) {
                 const int m = mbase + i;
                 if (m < nvalid)
-                    c[(size_t)(row0 + m) * p.ldc + tile * 8 + n16] = (uint16_t)f32_to_bf16_rne(silu(r[i]) * u[i]);
+                    c[(size_t)out_row(p, row0 + m, pre, i) * p.ldc + tile * 8 + n16] =
+                        (uint16_t)f32_to_bf16_rne(silu(r[i]) * u[i]);
             }
         }
     } else {
@@ -253,7 +265,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx4 v, int til
         for (int i = 0; i < 4; ++i) {
             const int m = mbase + i;
             if (m < nvalid) {
-                const size_t off = (size_t)(row0 + m) * p.ldc + tile * 16 + n16;
+                const size_t off = (size_t)out_row(p, row0 + m, pre, i) * p.ldc + tile * 16 + n16;
                 if (p.c_f32)
                     static_cast<float *>(p.c)[off] = r[i];
                 else
@@ -337,6 +349,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
     // blocks of one chunk, which read the same activation rows, meet in one
     // L2 instead of fetching them once per XCD. The host makes the grid a
     // multiple of kXcds whenever it is at least kXcds.
+    // epilogue geometry (bf16 rows through LDS): lane -> (block, row, 16-byte part)
+    constexpr int EPI_COLS = KIND == MOE_GEMM_W13_SWIGLU ? 8 : 16;
+    constexpr int EPI_LPR = EPI_COLS * 2 / 16;          // lanes per output row
+    // with NSUB | (blocks per pass) a lane stores the same subtile row in every pass
+    constexpr bool EPI_ONE_ROW = (64 / (16 * EPI_LPR)) % NSUB == 0;
+    const int epi_m = ((lane / (16 * EPI_LPR)) % NSUB) * 16 + ((lane / EPI_LPR) & 15);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c_row_index, p.c_row_bytes);
     const int nx = (int)gridDim.x >= kXcds ? kXcds : 1;
     const int xcd = blockIdx.x % nx;
     const int i_end = (int)((long long)total_items * (xcd + 1) / nx);
@@ -359,6 +378,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
             voff_w[t] = code_offset(p, tile0 + t, row, G, row_bytes, lane);
             voff_s[t] = row * (uint32_t)G * 2;
         }
+        // output row of the one result row this lane stores in the LDS
+        // epilogue, read now (no load under a branch; zeros when unused)
+        const int32_t c_row = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+            rc, (uint32_t)(row0 + min(epi_m, nvalid - 1)) * 4u, 0, 0);
         uint32_t voff_x[NSUB];
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb) {
@@ -523,7 +546,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
                 const int m = sb * 16 + rr;
                 if (b < NBLK && sb < nsub && m < nvalid) {
                     const u32x4 d = *reinterpret_cast<const u32x4 *>(so + (b * 16 + rr) * COLS + part * 8);
-                    *reinterpret_cast<u32x4 *>(c + (size_t)(row0 + m) * p.ldc + (tile0 + t) * COLS + part * 8) = d;
+                    const int orow = !p.c_row_index ? row0 + m : (EPI_ONE_ROW ? c_row : p.c_row_index[row0 + m]);
+                    *reinterpret_cast<u32x4 *>(c + (size_t)orow * p.ldc + (tile0 + t) * COLS + part * 8) = d;
                 }
             }
         } else {
@@ -566,6 +590,7 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
     const uint32_t row_bytes = (uint32_t)(p.K >> 1);
     const bf16x8 neg136 = neg136_operand();
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c_row_index, p.c_row_bytes);
     const uint32_t gstride = group_stride(p);
 
     for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
@@ -579,6 +604,11 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
         const uint32_t row = (uint32_t)tile_row<KIND>(p, tile, n16);
         const uint32_t voff_w = code_offset(p, tile, row, G, row_bytes, lane);
         const uint32_t voff_s = row * (uint32_t)G * 2;
+        int c_rows[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            c_rows[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+                rc, (uint32_t)(row0 + min(kq * 4 + i, nvalid - 1)) * 4u, 0, 0);
         uint32_t voff_x = kOutOfRange;
         if (n16 < nvalid) {
             const int r = row0 + n16;
@@ -637,7 +667,7 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
                 sum.z += v.z;
                 sum.w += v.w;
             }
-            store_tile<KIND>(p, sum, tile, row0, kq * 4, nvalid, n16);
+            store_tile<KIND>(p, sum, tile, row0, kq * 4, nvalid, n16, c_rows);
         }
         __syncthreads();
     }
@@ -739,6 +769,8 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     a.wq = g.wq;
     a.s = g.s;
     a.c = g.c;
+    a.c_row_index = g.c_row_index;
+    a.c_row_bytes = g.c_row_index ? (uint32_t)g.max_rows * 4u : 0u;
     a.a_bytes = (uint32_t)g.a_bytes;
     a.top_k = g.top_k;
     a.num_experts = g.num_experts;

@@ -82,8 +82,9 @@ __device__ __forceinline__ void route_token(const float *__restrict__ row, int E
         const int e = q + TL * i;
         val[i] = e < E ? ordered_bits(row[e]) : 0u;
     }
-    float sel_v[kMaxTopK];
-    int sel_e[kMaxTopK];
+    float l0 = 0.0f;                                   // the largest logit (slot 0)
+    float my_v = 0.0f;                                 // lane q < k: logit of slot q
+    int my_e = -1;                                     // lane q < k: expert of slot q
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
         if (j >= k)
@@ -98,45 +99,43 @@ __device__ __forceinline__ void route_token(const float *__restrict__ row, int E
         for (int i = PL - 1; i >= 0; --i)               // lowest index of this lane holding m
             bi = val[i] == m ? (uint32_t)(q + TL * i) : bi;
         const int e = (int)token_reduce<TL, false>(bi);
-        sel_e[j] = e;
-        sel_v[j] = from_ordered_bits(m);
+        if (j == 0)
+            l0 = from_ordered_bits(m);
+        if (q == j) {
+            my_e = e;
+            my_v = from_ordered_bits(m);
+        }
         // the owner lane retires the winner
 #pragma unroll
         for (int i = 0; i < PL; ++i)
             if (q + TL * i == e)
                 val[i] = 0u;
     }
-    // renormalised softmax over the k selected logits (fp32). The difference
-    // l_j - l_0 is formed error-free (TwoSum: d + r == l_j - l_0 exactly) and
-    // exp(d + r) ~= exp(d) * (1 + r), so wide logit ranges lose no accuracy
-    // before the exponential.
-    const float l0 = sel_v[0];
-    float z = 0.0f;
-    float ex[kMaxTopK];
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-        if (j >= k)
-            break;
-        const float a = sel_v[j], b = -l0;
+    // renormalised softmax over the k selected logits (fp32), one slot per
+    // lane. The difference l_q - l_0 is formed error-free (TwoSum: d + r ==
+    // l_q - l_0 exactly) and exp(d + r) ~= exp(d) * (1 + r), so wide logit
+    // ranges lose no accuracy before the exponential. The normaliser is a
+    // DPP row sum over the 16 lanes holding the slots (k <= 16; lanes q >= k
+    // add 0); every lane of the row ends with the same sum.
+    float ex = 0.0f;
+    if (q < k) {
+        const float a = my_v, b = -l0;
         const float d = a + b;
         const float ap = d - b;
         const float bp = d - ap;
         const float r = (a - ap) + (b - bp);
-        const float e = expf(d);
-        ex[j] = __builtin_fmaf(e, r, e);
-        z += ex[j];
+        const float ed = expf(d);
+        ex = __builtin_fmaf(ed, r, ed);
     }
-    e_out = -1;
-    w_out = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-        if (j >= k)
-            break;
-        if (q == j) {
-            e_out = sel_e[j];
-            w_out = ex[j] / z;
-        }
-    }
+    float z = ex;
+#define MOE_DPP_ADD(ctrl) z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), ctrl, 0xF, 0xF, false));
+    MOE_DPP_ADD(0xB1)      // quad_perm [1,0,3,2]
+    MOE_DPP_ADD(0x4E)      // quad_perm [2,3,0,1]
+    MOE_DPP_ADD(0x141)     // row_half_mirror
+    MOE_DPP_ADD(0x140)     // row_mirror
+#undef MOE_DPP_ADD
+    e_out = q < k ? my_e : -1;
+    w_out = q < k ? ex / z : 0.0f;
 }
 
 }  // namespace moe
