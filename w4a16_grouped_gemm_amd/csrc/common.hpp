@@ -43,16 +43,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 // Wave-level (64-lane) exclusive prefix sum of an int; also returns the total.
 __device__ __forceinline__ int wave_exclusive_scan(int v, int &total)
 {
-    const int lane = threadIdx.x & 63;
-    int inc = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int o = __shfl_up(inc, d, 64);
-        if (lane >= d)
-            inc += o;
-    }
-    total = __shfl(inc, 63, 64);
-    return inc - v;
+    // inclusive scan in registers: row_shr 1, 2, 4, 8 within each 16-lane
+    // row (lanes shifted in from outside the row add 0), then row_bcast:15
+    // adds each row's last lane to the next row (rows 1 and 3) and
+    // row_bcast:31 adds lane 31 to rows 2 and 3
+    int x = v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+    total = __builtin_amdgcn_readlane(x, 63);
+    return x - v;
 }
 
 // ---- launchers (host side, one per kernel family) ------------------------

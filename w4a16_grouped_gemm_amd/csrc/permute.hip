@@ -74,10 +74,20 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
             }
         }
     } else if (IDS_IN_LDS) {
-        // local expert index (or -1) of every slot
-        for (int i = tid; i < (int)S; i += kPermThreads) {
-            const int e = ids[i] - begin;
-            s_ids[i] = (e >= 0 && e < E) ? e : -1;
+        // local expert index (or -1) of every slot; four loads per thread go
+        // out before the first is used (clamped indices, no branch)
+        for (int base = 0; base < (int)S; base += 4 * kPermThreads) {
+            int v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                v[u] = ids[min(base + u * kPermThreads + tid, (int)S - 1)];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = base + u * kPermThreads + tid;
+                const int e = v[u] - begin;
+                if (i < (int)S)
+                    s_ids[i] = (e >= 0 && e < E) ? e : -1;
+            }
         }
     }
     __syncthreads();
@@ -137,7 +147,10 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
             int le[kMaxTopK];                 // all of the token's ids first: one round trip
 #pragma unroll
             for (int j = 0; j < kMaxTopK; ++j)
-                le[j] = j < k ? local_expert((long long)t * k + j) : -1;
+                le[j] = local_expert((long long)t * k + min(j, k - 1));
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j)
+                le[j] = j < k ? le[j] : -1;
 #pragma unroll
             for (int j = 0; j < kMaxTopK; ++j)
                 if (le[j] >= 0)
@@ -158,7 +171,10 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
             int le[kMaxTopK];
 #pragma unroll
             for (int j = 0; j < kMaxTopK; ++j)
-                le[j] = j < k ? local_expert((long long)t * k + j) : -1;
+                le[j] = local_expert((long long)t * k + min(j, k - 1));
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j)
+                le[j] = j < k ? le[j] : -1;
 #pragma unroll
             for (int j = 0; j < kMaxTopK; ++j) {
                 if (j >= k)

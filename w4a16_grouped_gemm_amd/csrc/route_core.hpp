@@ -76,12 +76,18 @@ template <int TL, int PL>
 __device__ __forceinline__ void route_token(const float *__restrict__ row, int E, int k, int q, int &e_out,
                                             float &w_out)
 {
-    uint32_t val[PL];
+    // every load is issued (a clamped index, no branch), so the PL loads
+    // are one memory round trip; entries past E are masked afterwards
+    float lv[PL];
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
         const int e = q + TL * i;
-        val[i] = e < E ? ordered_bits(row[e]) : 0u;
+        lv[i] = row[e < E ? e : E - 1];
     }
+    uint32_t val[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+        val[i] = q + TL * i < E ? ordered_bits(lv[i]) : 0u;
     float l0 = 0.0f;                                   // the largest logit (slot 0)
     float my_v = 0.0f;                                 // lane q < k: logit of slot q
     int my_e = -1;                                     // lane q < k: expert of slot q
