@@ -74,6 +74,103 @@ def time_prefill(ops, reps, torch, layout, steps, warmup):
             "tflops": round(flops / (us * 1e-6) / 1e12, 1), "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
 
 
+def _graph_time(torch, fns, reps_n):
+    """Seconds per call of the launches `fns` (one each per replay), replayed
+    from a HIP graph, HIP events on the replaying stream."""
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for f in fns:
+                f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    graph.replay()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps_n):
+        graph.replay()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / 1000.0 / (reps_n * len(fns))
+
+
+def time_ep_shard(ops, torch, layout, steps, warmup, T=256, L=3):
+    """One GPU's shard of an expert-parallel layer (32 local of 256 experts,
+    hidden 7168, intermediate 2048) in decode: the layer on its local slots,
+    L replicas of 726 MB of weights."""
+    from w4a16_grouped_gemm_amd.inputs import WORKLOADS
+    wl = WORKLOADS["ep_shard_decode"]
+    _, reps = make_replicas(wl, T, L, torch, seed_base=11)
+    if layout == ops.WEIGHTS_TILED:
+        pack_replicas(reps, ops)
+    stats = routing_stats(ops, wl, reps, torch)
+    dt, _ = time_layer(ops, wl, reps, steps, warmup, torch, layout)
+    us = dt / steps * 1e6
+    w13b, w2b = weight_bytes_per_expert(wl.hidden, wl.inter)
+    act = sum(st["active"] for st in stats) / L
+    gbps = act * (w13b + w2b) / (us * 1e-6) / 1e9
+    del reps
+    torch.cuda.empty_cache()
+    return {"workload": "ep_shard_decode (32 of 256 experts, hidden 7168, inter 2048, top-8)", "tokens": T,
+            "us_per_layer": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1), "active_experts": act,
+            "local_rows": sum(st["rows"] for st in stats) / L, "weight_GBps": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def time_finalize_stream(ops, torch, T=4096, k=8, H=4096, E=128, reps_n=20):
+    """The finalize on its stress shape: fp32 y [T*k, H] (512 MiB, two buffers
+    alternate so the Infinity Cache cannot hold them), bf16 out [T, H]."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    logits = torch.randn((T, E), generator=g, device=dev)
+    ids, w = ops.route(logits, k)
+    _, _, _, inv, _ = ops.permute(ids, E)
+    ys = [torch.randn((T * k, H), generator=g, device=dev) for _ in range(2)]
+    outs = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    sec = _graph_time(torch, [lambda i=i: ops.finalize(ys[i], w, inv, out=outs[i]) for i in range(2)], reps_n)
+    nbytes = T * k * H * 4 + T * k * 8 + T * H * 2
+    del ys, outs
+    torch.cuda.empty_cache()
+    return {"shape": f"T={T} k={k} H={H}, fp32 y, bf16 out", "us": round(sec * 1e6, 2), "bytes": nbytes,
+            "GBps": round(nbytes / sec / 1e9, 1), "hbm_frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def time_dense(ops, torch, layout, Ms=(1, 16, 256), N=14336, K=4096, L=16, reps_n=20):
+    """Dense W4A16 GEMM c[M, N] = a[M, K] . W^T over L weight replicas
+    (L * 30 MB, more than the Infinity Cache holds)."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(99)
+    ws = []
+    for _ in range(L):
+        wq = torch.randint(0, 256, (N, K // 2), generator=g, device=dev, dtype=torch.uint8)
+        if layout == ops.WEIGHTS_TILED:
+            wq = ops.pack_dense_weights(wq)
+        sc = torch.empty((N, K // 128), device=dev).uniform_(0.005, 0.02, generator=g).to(torch.bfloat16)
+        ws.append((wq, sc))
+    wbytes = N * K // 2 + N * (K // 128) * 2
+    res = []
+    for M in Ms:
+        a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+        outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+        fns = [lambda i=i: ops.dense_gemm_w4a16(a, ws[i][0], ws[i][1], out=outs[i], weight_layout=layout)
+               for i in range(L)]
+        sec = _graph_time(torch, fns, reps_n)
+        res.append({"M": M, "N": N, "K": K, "us": round(sec * 1e6, 2),
+                    "weight_GBps": round(wbytes / sec / 1e9, 1), "hbm_frac": round(wbytes / sec / 1e9 / HBM_PEAK_GBPS, 4),
+                    "tflops": round(2.0 * M * N * K / sec / 1e12, 2)})
+    del ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def gemm1_algorithmic_bytes(wl, T, active, rows):
     """Bytes GEMM1 must move at least once: the weights and scales of every
     active expert, the T input rows, the rows x I SwiGLU outputs, the offsets
@@ -337,6 +434,17 @@ def main():
         log("prefill T=2048 (Zipf routing)")
         prefill = time_prefill(ops, reps, torch, layout, max(8, args.steps // 50), args.warmup // 10 + 1)
 
+    ep_shard = finalize_stream = dense = None
+    if not args.no_sweep:
+        del reps
+        torch.cuda.empty_cache()
+        log("EP shard decode T=256")
+        ep_shard = time_ep_shard(ops, torch, layout, max(60, args.steps // 4), max(6, args.warmup // 10))
+        log("finalize stream")
+        finalize_stream = time_finalize_stream(ops, torch)
+        log("dense W4A16 GEMM")
+        dense = time_dense(ops, torch, layout)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
@@ -361,6 +469,9 @@ def main():
         "cpu_baseline": cpu,
         "sweep": sweep,
         "prefill": prefill,
+        "ep_shard": ep_shard,
+        "finalize_stream": finalize_stream,
+        "dense_gemm": dense,
     }
     print(json.dumps(rec), flush=True)
 

@@ -191,6 +191,27 @@ moe_status moe_grouped_gemm_w4a16(const moe_shape *shape, moe_gemm_kind kind, co
                                   void *stream);
 
 /*
+ * Dense W4A16 GEMM: one weight matrix, every row of `a` through it, no
+ * routing ([FI] sections 2-3: the MoE GEMM and the dense GEMM share one
+ * W4A16 reference; here the dense case runs the grouped kernels with one
+ * expert holding all M rows).
+ *   c[m][n] = sum_k a[m][k] * W[n][k],  W[n][k] = q[n][k] * s[n][k/128]
+ *   M >= 0 (0: no-op); N, K multiples of 128, <= 65536; N*K/2 and M*K*2
+ *   below 2^31 bytes (MOE_ERR_UNSUPPORTED beyond)
+ *   a   bf16 [M][K]
+ *   wq  uint8 [N][K/2], the int4 format above (plain), or tiled by
+ *       moe_w4a16_pack_weights with kind MOE_GEMM_W2 and a shape with
+ *       E_loc = 1, hidden = N, inter = K (weight_layout says which)
+ *   s   bf16 [N][K/128]
+ *   c   [M][N], bf16 (RNE) or f32 (c_dtype)
+ * Accumulation as in moe_grouped_gemm_w4a16 (exact int4 codes, fp32 sums,
+ * the group scale applied in fp32).
+ */
+moe_status moe_w4a16_dense_gemm(int32_t M, int32_t N, int32_t K, const uint16_t *a, const uint8_t *wq,
+                                const uint16_t *s, void *c, moe_dtype c_dtype, int32_t weight_layout,
+                                void *stream);
+
+/*
  * Finalize: weighted unpermute / combine ([FI] section 1 `moe_finalize.py`).
  * For every token t and column c < H: the first slot j (slot order) with
  * inv_perm[t][j] >= 0 gives acc = y[r][c] * w[t][j] (IEEE binary32 multiply,

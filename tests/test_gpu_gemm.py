@@ -151,6 +151,8 @@ VARIANTS = [
     {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "2", "MOE_GEMM_NSUB": "4", "MOE_GEMM_KSEG": "1", "MOE_GEMM_RING": "2"},
     {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "4", "MOE_GEMM_NSUB": "1", "MOE_GEMM_KSEG": "8", "MOE_GEMM_RING": "4"},
     {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "4", "MOE_GEMM_NSUB": "2", "MOE_GEMM_KSEG": "4", "MOE_GEMM_RING": "2"},
+    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "1", "MOE_GEMM_NSUB": "1", "MOE_GEMM_KSEG": "8", "MOE_GEMM_RING": "4"},
+    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "1", "MOE_GEMM_NSUB": "2", "MOE_GEMM_KSEG": "4", "MOE_GEMM_RING": "4"},
 ]
 
 

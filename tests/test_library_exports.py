@@ -69,3 +69,20 @@ def test_layout_validation_without_gpu():
     assert lib.moe_w4a16_pack_weights(ctypes.byref(sh), 0, p, p, None) == 3
     assert lib.moe_w4a16_pack_weights(ctypes.byref(sh), 7, p, p, None) == 3
     assert lib.moe_w4a16_pack_weights(ctypes.byref(sh), 0, None, p, None) == 1
+
+
+def test_dense_validation_without_gpu():
+    # every case below is refused (or is the M = 0 no-op) on the host, before any launch
+    lib = ops.load_library()
+    p = ctypes.c_void_p(1 << 20)
+    f = lib.moe_w4a16_dense_gemm
+    assert f(4, 200, 256, p, p, p, p, 0, 0, None) == 2          # N % 128
+    assert f(4, 256, 64, p, p, p, p, 0, 0, None) == 2           # K < 128
+    assert f(-1, 256, 256, p, p, p, p, 0, 0, None) == 2         # M < 0
+    assert f(4, 131072, 256, p, p, p, p, 0, 0, None) == 2       # N > 65536
+    assert f(4, 65536, 65536, p, p, p, p, 0, 0, None) == 3      # weights beyond one descriptor
+    assert f(4, 256, 256, p, p, p, p, 7, 0, None) == 3          # output dtype
+    assert f(4, 256, 256, p, p, p, p, 0, 2, None) == 3          # weight layout
+    assert f(4, 256, 256, None, p, p, p, 0, 0, None) == 1       # NULL activations
+    assert f(4, 256, 256, ctypes.c_void_p((1 << 20) + 2), p, p, p, 0, 0, None) == 4   # misaligned
+    assert f(0, 256, 256, None, None, None, None, 0, 0, None) == 0    # M = 0: nothing to do

@@ -104,6 +104,8 @@ Workspace carve(const moe_shape &sh, void *base)
 
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+constexpr int32_t kMaxDenseDim = 65536;   // N and K of the dense GEMM
+
 GemmLaunch gemm_args(const moe_shape &sh, moe_gemm_kind kind)
 {
     GemmLaunch g{};
@@ -237,6 +239,47 @@ moe_status moe_grouped_gemm_w4a16(const moe_shape *shape, moe_gemm_kind kind, co
     g.s = s;
     g.c = c;
     g.c_f32 = c_dtype == MOE_F32;
+    return from_hip(launch_grouped_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_w4a16_dense_gemm(int32_t M, int32_t N, int32_t K, const uint16_t *a, const uint8_t *wq,
+                                const uint16_t *s, void *c, moe_dtype c_dtype, int32_t weight_layout,
+                                void *stream)
+{
+    if (M < 0 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0 || N > kMaxDenseDim || K > kMaxDenseDim)
+        return MOE_ERR_SHAPE;
+    if ((size_t)N * (K / 2) >= (size_t(1) << 31) || (size_t)M * K * 2 >= (size_t(1) << 31))
+        return MOE_ERR_UNSUPPORTED;                       // beyond one buffer descriptor's range
+    if (c_dtype != MOE_BF16 && c_dtype != MOE_F32)
+        return MOE_ERR_UNSUPPORTED;
+    if (weight_layout != MOE_WEIGHTS_PLAIN && weight_layout != MOE_WEIGHTS_TILED)
+        return MOE_ERR_UNSUPPORTED;
+    if (M == 0)
+        return MOE_OK;
+    if (!a || !wq || !s || !c)
+        return MOE_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(wq, 16) || !aligned(c, 16) || !aligned(s, 2))
+        return MOE_ERR_ALIGN;
+    // one expert holding every row: the grouped GEMM with offsets {0, M}
+    // passed by value (nothing to read from device memory)
+    GemmLaunch g{};
+    g.kind = MOE_GEMM_W2;
+    g.top_k = 1;
+    g.num_experts = 1;
+    g.max_rows = M;
+    g.expected_rows = M;
+    g.K = K;
+    g.N = N;
+    g.a = a;
+    g.a_row_index = nullptr;
+    g.a_bytes = (size_t)M * K * 2;
+    g.offsets = nullptr;
+    g.dense_rows = M;
+    g.wq = wq;
+    g.s = s;
+    g.c = c;
+    g.c_f32 = c_dtype == MOE_F32;
+    g.w_tiled = weight_layout == MOE_WEIGHTS_TILED;
     return from_hip(launch_grouped_gemm(g, static_cast<hipStream_t>(stream)));
 }
 

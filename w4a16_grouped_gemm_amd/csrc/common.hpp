@@ -65,7 +65,8 @@ struct GemmLaunch {
     const uint16_t *a;
     const int32_t *a_row_index;
     int top_k;
-    const int32_t *offsets;
+    const int32_t *offsets;   // NULL: one dense expert with dense_rows rows
+    int dense_rows;
     int num_experts;          // E_loc
     const uint8_t *wq;
     const uint16_t *s;

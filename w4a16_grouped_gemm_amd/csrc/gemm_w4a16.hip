@@ -68,7 +68,8 @@ constexpr int kXcds = 8;                         // MI355X: 8 XCDs of 32 CUs, on
 struct GemmArgs {
     const uint16_t *a;
     const int32_t *a_row_index;
-    const int32_t *offsets;
+    const int32_t *offsets;     // [E+1] on the device; NULL for one dense expert of dense_rows rows
+    int dense_rows;
     const uint8_t *wq;
     const uint16_t *s;
     void *c;
@@ -163,12 +164,19 @@ __device__ __forceinline__ bf16x8 neg136_operand()
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Row offset of expert e: offsets[e], or for a dense GEMM (offsets NULL,
+// one expert) 0 and dense_rows.
+__device__ __forceinline__ int expert_offset(const int32_t *offsets, int dense_rows, int e)
+{
+    return offsets ? offsets[e] : (e == 0 ? 0 : dense_rows);
+}
+
 // Chunk prefix over experts: s_prefix[e] = chunks of experts < e (chunk =
 // up to CS rows of one expert), s_prefix[E] = total. Block-wide.
 // When s_off is given it receives offsets[0..E] as well.
 template <int NT>
-__device__ void build_chunk_prefix(const int32_t *offsets, int E, int CS, int *s_prefix, int *s_wtot,
-                                   int *s_off = nullptr)
+__device__ void build_chunk_prefix(const int32_t *offsets, int dense_rows, int E, int CS, int *s_prefix,
+                                   int *s_wtot, int *s_off = nullptr)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int carry = 0;
@@ -176,7 +184,7 @@ __device__ void build_chunk_prefix(const int32_t *offsets, int E, int CS, int *s
         const int e = base + tid;
         int v = 0;
         if (e < E) {
-            const int o0 = offsets[e], o1 = offsets[e + 1];
+            const int o0 = expert_offset(offsets, dense_rows, e), o1 = expert_offset(offsets, dense_rows, e + 1);
             if (s_off) {
                 s_off[e] = o0;
                 if (e == E - 1)
@@ -322,7 +330,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
     const int wave = tid >> 6;
     const int n16 = lane & 15;
     const int kq = lane >> 4;
-    build_chunk_prefix<256>(p.offsets, E, CS, s_prefix, s_wtot, s_off);
+    build_chunk_prefix<256>(p.offsets, p.dense_rows, E, CS, s_prefix, s_wtot, s_off);
 
     const int ntiles = p.N >> 4;
     const int nblocks = ntiles / BT;
@@ -580,7 +588,7 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
     const int n16 = lane & 15;
     const int kq = lane >> 4;
     const int E = p.num_experts;
-    build_chunk_prefix<NWAVES * 64>(p.offsets, E, CS, s_prefix, s_wtot);
+    build_chunk_prefix<NWAVES * 64>(p.offsets, p.dense_rows, E, CS, s_prefix, s_wtot);
 
     const int ntiles = p.N >> 4;
     const int total_items = s_prefix[E] * ntiles;
@@ -597,8 +605,8 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
         const int chunk = item / ntiles;
         const int tile = item - chunk * ntiles;
         const int e = uniform(chunk_expert(s_prefix, E, chunk));
-        const int row0 = uniform(p.offsets[e] + (chunk - s_prefix[e]) * CS);
-        const int nvalid = uniform(min(CS, p.offsets[e + 1] - row0));
+        const int row0 = uniform(expert_offset(p.offsets, p.dense_rows, e) + (chunk - s_prefix[e]) * CS);
+        const int nvalid = uniform(min(CS, expert_offset(p.offsets, p.dense_rows, e + 1) - row0));
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (size_t)e * p.N * row_bytes, (uint32_t)p.N * row_bytes);
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s + (size_t)e * p.N * G, (uint32_t)p.N * G * 2);
         const uint32_t row = (uint32_t)tile_row<KIND>(p, tile, n16);
@@ -747,6 +755,7 @@ hipError_t launch_kind(const GemmArgs &a, int max_rows, int mode, int tpw, int n
     if (tpw == T && nsub == S && kseg == B && ring == R)      \
         return launch_stream<KIND, T, S, B, R>(a, max_rows, st);
     MOE_STREAM(1, 1, 2, 2) MOE_STREAM(1, 1, 4, 2) MOE_STREAM(1, 1, 4, 4) MOE_STREAM(1, 1, 8, 4) MOE_STREAM(1, 2, 2, 2)
+    MOE_STREAM(1, 2, 4, 2) MOE_STREAM(1, 2, 4, 4)
     MOE_STREAM(1, 4, 2, 2)
     MOE_STREAM(2, 1, 2, 2) MOE_STREAM(2, 1, 4, 2) MOE_STREAM(2, 1, 4, 4) MOE_STREAM(2, 1, 8, 4)
     MOE_STREAM(2, 2, 2, 2) MOE_STREAM(2, 2, 4, 2) MOE_STREAM(2, 2, 4, 4) MOE_STREAM(2, 4, 2, 2)
@@ -768,6 +777,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     a.offsets = g.offsets;
     a.wq = g.wq;
     a.s = g.s;
+    a.dense_rows = g.dense_rows;
     a.c = g.c;
     a.c_row_index = g.c_row_index;
     a.c_row_bytes = g.c_row_index ? (uint32_t)g.max_rows * 4u : 0u;
@@ -792,28 +802,36 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     const double m = R / (active > 1.0 ? active : 1.0);
     const int G = g.K / kGroup;
     const int ntiles = g.N / 16;
-    // Measured on MI355X (Qwen3-30B-A3B and EP-shard decode shapes, 1..256
-    // tokens): the streaming kernel once it has more than two waves per CU
-    // (active experts x 16-row tiles / 2 tiles per wave), split-K below
-    // that; two 16-row tiles per wave, 4-group K segments (8 for
-    // K >= 4096); a 4-deep weight ring for long K or few rows per expert,
-    // else 2; a second 16-token subtile once experts average more than 12
-    // rows (each expert's weights are then streamed once instead of twice),
-    // and with it four tiles per wave and a 2-deep ring (the correction
-    // MFMAs and the activation reads of a subtile serve twice the weights).
-    // Prefill (2048 tokens) is fastest with the same shape: four subtiles
-    // with one group per segment came out 8% slower.
-    int tpw = 2;
-    int mode = active * ntiles / tpw > 2.0 * device_cu_count() ? 1 : 0;
-    int nsub = m > 12.0 ? 2 : 1;
+    // Measured on MI355X (Qwen3-30B-A3B and EP-shard MoE shapes at 1..2048
+    // tokens, dense GEMMs of 1..1024 rows):
+    //  * a second 16-token subtile once experts average more than 12 rows
+    //    (each expert's weights are then streamed once instead of twice);
+    //  * tiles per wave: 4 with two subtiles (the correction MFMAs and the
+    //    LDS activation reads of a subtile serve four tiles), else 2, halved
+    //    while the streaming kernel would not have more than two waves per
+    //    CU (chunks x tiles / tiles-per-wave); split-K only when even one
+    //    tile per wave cannot fill the chip (one or two active experts);
+    //  * 4-group K segments (8 for K >= 4096); a 4-deep weight ring for long
+    //    K or few rows per expert, else 2, and 2 with four tiles per wave
+    //    (a deeper ring would not fit two waves per SIMD);
+    //  * prefill (2048 tokens) runs best with the two-subtile shape: four
+    //    subtiles with one group per segment came out 8% slower.
+    const double fill = 2.0 * device_cu_count();
+    // expert loads vary around m, so a second subtile pays from m > 12; one
+    // expert (a dense GEMM) has exactly m rows
+    const int nsub0 = (g.num_experts == 1 ? m > 16.0 : m > 12.0) ? 2 : 1;
+    const double chunks = fmax(active, R / (16.0 * nsub0));
+    int nsub = nsub0;
+    int tpw = nsub == 2 ? 4 : 2;
+    while (tpw > 1 && chunks * ntiles / tpw <= fill)
+        tpw >>= 1;
+    int mode = chunks * ntiles / tpw > fill ? 1 : 0;
     int kseg = 4;
     int ring = (g.K >= 4096 || m < 3.0) ? 4 : 2;
     if (g.K >= 4096)
         kseg = 8;
-    if (nsub == 2) {
-        tpw = 4;
+    if (tpw == 4 && nsub == 2)
         ring = 2;
-    }
     if (const char *env = getenv("MOE_GEMM_MODE"))
         mode = atoi(env);
     if (const char *env = getenv("MOE_GEMM_TPW"))

@@ -27,7 +27,8 @@ _STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUP
            4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP"}
 EXPORTED = ["moe_status_str", "moe_w4a16_check_shape", "moe_w4a16_is_supported",
             "moe_w4a16_workspace_size", "moe_w4a16_forward", "moe_route", "moe_permute_workspace_size",
-            "moe_permute", "moe_grouped_gemm_w4a16", "moe_finalize", "moe_w4a16_pack_weights"]
+            "moe_permute", "moe_grouped_gemm_w4a16", "moe_finalize", "moe_w4a16_pack_weights",
+            "moe_w4a16_dense_gemm"]
 
 
 class MoeShape(ctypes.Structure):
@@ -80,6 +81,9 @@ def load_library(path: str = LIB_PATH):
         lib.moe_finalize.restype = I
         lib.moe_w4a16_pack_weights.argtypes = [S, I, P, P, P]
         lib.moe_w4a16_pack_weights.restype = I
+        lib.moe_w4a16_dense_gemm.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P, I,
+                                             ctypes.c_int32, P]
+        lib.moe_w4a16_dense_gemm.restype = I
         _lib = lib
         return lib
 
@@ -225,6 +229,31 @@ def grouped_gemm_w4a16(kind: int, a: torch.Tensor, offsets: torch.Tensor, wq: to
     _check(load_library().moe_grouped_gemm_w4a16(ctypes.byref(sh), int(kind), _ptr(a), _ptr(a_row_index),
                                                  _ptr(offsets), _ptr(wq), _ptr(s), _ptr(out), dt,
                                                  _stream(stream)))
+    return out
+
+
+def pack_dense_weights(wq: torch.Tensor, *, stream=None) -> torch.Tensor:
+    """Plain -> tiled int4 codes of one dense weight matrix [N, K/2]."""
+    return pack_weights(W2, wq.unsqueeze(0), stream=stream)[0]
+
+
+def dense_gemm_w4a16(a: torch.Tensor, wq: torch.Tensor, s: torch.Tensor, *, out_dtype=torch.bfloat16,
+                     out: torch.Tensor | None = None, weight_layout: int = WEIGHTS_PLAIN, stream=None):
+    """Dense W4A16 GEMM: c [M, N] = a [M, K] . W^T, W[n, k] = q[n, k] * s[n, k // 128]."""
+    _need(a, torch.bfloat16, "a")
+    _need(wq, torch.uint8, "wq")
+    _need(s, torch.bfloat16, "s")
+    M, K = a.shape
+    N = wq.shape[0]
+    if wq.shape != (N, K // 2) or s.shape != (N, K // 128):
+        raise ValueError(f"weight shapes {tuple(wq.shape)}, {tuple(s.shape)} do not match K={K}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    dt = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}.get(out.dtype)
+    if dt is None:
+        raise ValueError("out dtype must be bfloat16 or float32")
+    _check(load_library().moe_w4a16_dense_gemm(M, N, K, _ptr(a), _ptr(wq), _ptr(s), _ptr(out), dt,
+                                               int(weight_layout), _stream(stream)))
     return out
 
 
