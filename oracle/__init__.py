@@ -53,9 +53,9 @@ def _load():
     lib.oracle_route.argtypes = [I, I, I, P, P, P]
     lib.oracle_permute.argtypes = [I, I, I, I, P, P, P, P, P]
     lib.oracle_grouped_gemm.argtypes = [I, I, I, I, I, P, P, I, P, P, P, P, P, I]
-    lib.oracle_finalize.argtypes = [I, I, I, P, I, P, P, P, P, I]
-    lib.oracle_layer.argtypes = [I] * 8 + [P] * 7 + [P] * 9
-    lib.oracle_layer_bruteforce.argtypes = [I] * 7 + [P] * 9
+    lib.oracle_finalize.argtypes = [I, I, I, P, I, P, P, I, P, P, P, I]
+    lib.oracle_layer.argtypes = [I] * 8 + [P] * 6 + [I] + [P] * 4 + [P] + [P] * 10
+    lib.oracle_layer_bruteforce.argtypes = [I] * 7 + [P] * 7 + [I] + [P] * 4 + [P] * 2
     _lib = lib
     return lib
 
@@ -129,8 +129,9 @@ def grouped_gemm(kind: int, a: np.ndarray, offsets: np.ndarray, wq: np.ndarray, 
 
 
 def finalize(y: np.ndarray, topk_w: np.ndarray, inv_perm: np.ndarray, *, out_f32: bool,
-             tok_sel: np.ndarray | None = None):
-    """Slot-ordered combine. y: float32 or uint16 (bf16) [R, H]."""
+             tok_sel: np.ndarray | None = None, ys: np.ndarray | None = None):
+    """Slot-ordered combine. y: float32 or uint16 (bf16) [R, H]; ys: the shared
+    experts' outputs [S, T, H] in y's dtype (added after the slots), or None."""
     topk_w = np.ascontiguousarray(topk_w, dtype=np.float32)
     inv_perm = np.ascontiguousarray(inv_perm, dtype=np.int32)
     T, k = topk_w.shape
@@ -139,14 +140,29 @@ def finalize(y: np.ndarray, topk_w: np.ndarray, inv_perm: np.ndarray, *, out_f32
     assert y_f32 or y.dtype == np.uint16
     out = np.zeros((T, H), np.float32 if out_f32 else np.uint16)
     sel = None if tok_sel is None else np.ascontiguousarray(tok_sel, dtype=np.uint8)
+    S = 0 if ys is None else ys.shape[0]
+    if ys is not None:
+        assert ys.dtype == y.dtype and ys.shape == (S, T, H)
     _load().oracle_finalize(T, k, H, _ptr(np.ascontiguousarray(y)), 1 if y_f32 else 0, _ptr(topk_w),
-                            _ptr(inv_perm), _ptr(sel), _ptr(out), 1 if out_f32 else 0)
+                            _ptr(inv_perm), S, _ptr(None if ys is None else np.ascontiguousarray(ys)), _ptr(sel),
+                            _ptr(out), 1 if out_f32 else 0)
     return out
 
 
+def _shared_args(shared):
+    """(S, w13_sh, s13_sh, w2_sh, s2_sh) pointers for an optional shared-expert tuple."""
+    if shared is None:
+        return 0, None, None, None, None
+    w13, s13, w2, s2 = (np.ascontiguousarray(a) for a in shared)
+    return w13.shape[0], w13, s13, w2, s2
+
+
 def layer(x, logits, w13_q, s13, w2_q, s2, *, top_k: int, expert_begin: int = 0,
-          tok_sel: np.ndarray | None = None, group: int = 128):
-    """The whole layer through the permutation; returns a dict of every stage."""
+          tok_sel: np.ndarray | None = None, group: int = 128, shared=None):
+    """The whole layer through the permutation; returns a dict of every stage.
+
+    shared: optional (w13_sh [S, 2I, H/2], s13_sh, w2_sh [S, H, I/2], s2_sh):
+    S always-on experts added after the routed slots (hs, ys in the result)."""
     T, H = x.shape
     E_g = logits.shape[1]
     E_loc, N13, _ = w13_q.shape
@@ -157,19 +173,24 @@ def layer(x, logits, w13_q, s13, w2_q, s2, *, top_k: int, expert_begin: int = 0,
         counts=np.empty(E_loc, np.int32), offsets=np.empty(E_loc + 1, np.int32),
         perm=np.empty(S, np.int32), inv_perm=np.empty((T, top_k), np.int32),
         h=np.zeros((S, I), np.uint16), y=np.zeros((S, H), np.uint16), out=np.zeros((T, H), np.uint16))
+    nsh, w13s, s13s, w2s, s2s = _shared_args(shared)
+    r["hs"] = np.zeros((nsh, T, I), np.uint16)
+    r["ys"] = np.zeros((nsh, T, H), np.uint16)
     sel = None if tok_sel is None else np.ascontiguousarray(tok_sel, dtype=np.uint8)
     _load().oracle_layer(T, E_g, top_k, expert_begin, E_loc, H, I, group,
                          _ptr(np.ascontiguousarray(x, dtype=np.uint16)),
                          _ptr(np.ascontiguousarray(logits, dtype=np.float32)),
                          _ptr(np.ascontiguousarray(w13_q)), _ptr(np.ascontiguousarray(s13)),
-                         _ptr(np.ascontiguousarray(w2_q)), _ptr(np.ascontiguousarray(s2)), _ptr(sel),
+                         _ptr(np.ascontiguousarray(w2_q)), _ptr(np.ascontiguousarray(s2)),
+                         nsh, _ptr(w13s), _ptr(s13s), _ptr(w2s), _ptr(s2s), _ptr(sel),
                          _ptr(r["topk_ids"]), _ptr(r["topk_w"]), _ptr(r["counts"]), _ptr(r["offsets"]),
-                         _ptr(r["perm"]), _ptr(r["inv_perm"]), _ptr(r["h"]), _ptr(r["y"]), _ptr(r["out"]))
+                         _ptr(r["perm"]), _ptr(r["inv_perm"]), _ptr(r["h"]), _ptr(r["y"]),
+                         _ptr(r["hs"] if nsh else None), _ptr(r["ys"] if nsh else None), _ptr(r["out"]))
     return r
 
 
 def layer_bruteforce(x, topk_ids, topk_w, w13_q, s13, w2_q, s2, *, expert_begin: int = 0,
-                     tok_sel: np.ndarray | None = None, group: int = 128):
+                     tok_sel: np.ndarray | None = None, group: int = 128, shared=None):
     """Naive per-(token, slot) expert MLPs + ordered combine; no permutation."""
     T, H = x.shape
     k = topk_ids.shape[1]
@@ -183,5 +204,10 @@ def layer_bruteforce(x, topk_ids, topk_w, w13_q, s13, w2_q, s2, *, expert_begin:
                                     _ptr(np.ascontiguousarray(topk_w, dtype=np.float32)),
                                     _ptr(np.ascontiguousarray(w13_q)), _ptr(np.ascontiguousarray(s13)),
                                     _ptr(np.ascontiguousarray(w2_q)), _ptr(np.ascontiguousarray(s2)),
-                                    _ptr(sel), _ptr(out))
+                                    *_shared_ptrs(shared), _ptr(sel), _ptr(out))
     return out
+
+
+def _shared_ptrs(shared):
+    nsh, w13s, s13s, w2s, s2s = _shared_args(shared)
+    return nsh, _ptr(w13s), _ptr(s13s), _ptr(w2s), _ptr(s2s)

@@ -23,7 +23,7 @@
  *         the rows and scatter them back to tokens).
  *   [GC]  "GC-MoE: Overlapping Expert-Parallel Token Dispatch with FP8/FP4
  *         Grouped GEMM via CUDA Green Contexts" (abstract): expert-parallel
- *         layers, fused SwiGLU.
+ *         layers, fused SwiGLU, optional (fused) shared experts.
  *
  * Readings of points the pages leave open (each also listed in the design
  * notes): int4 weights are two's-complement nibbles, element k of a row in
@@ -31,6 +31,11 @@
  * (row, 128-wide K group), no zero point; w13 rows [0, I) are gate and
  * [I, 2I) are up; silu(z) = z / (1 + exp(-z)); h, y and the layer output are
  * rounded to bf16 once each; the top-k order is (logit desc, index asc).
+ * Shared experts ([GC] names them without defining them): S always-on experts
+ * with the routed experts' shape, applied to every token; each one's bf16
+ * output is added to the binary32 combine with weight 1, after the routed
+ * slots, in shared-expert order (the first term of a token with no present
+ * routed slot initialises the accumulator).
  *
  * Arithmetic: every dot product is an fp64 sum in ascending k (products of a
  * bf16 activation and an exact dequantised weight are exact in fp64), then a
@@ -312,13 +317,17 @@ void oracle_grouped_gemm(int kind, int E_loc, int N, int K, int G,
  *       acc = y[r][c] * w[t][j]               (binary32 multiply, RNE)
  *   every later present slot gives
  *       acc = fmaf(y[r][c], w[t][j], acc)     (binary32 FMA, one rounding)
- *   no present slot: acc = +0.0.
+ *   then each shared expert s < S (ys[s][t][c], same dtype as y) gives
+ *       acc = acc + ys[s][t][c]               (binary32 add = fmaf(v, 1, acc)),
+ *       or acc = ys[s][t][c] when it is the first term
+ *   no term at all: acc = +0.0.
  * y is bf16 (y_f32 == 0) or binary32; out is binary32 (out_f32 != 0) or the
  * bf16 RNE rounding of acc. No flush-to-zero anywhere. Tokens whose tok_sel
  * entry is 0 are skipped (tok_sel may be NULL).
  */
 void oracle_finalize(int T, int k, int H, const void *y, int y_f32, const float *topk_w,
-                     const int32_t *inv_perm, const uint8_t *tok_sel, void *out, int out_f32)
+                     const int32_t *inv_perm, int S, const void *ys, const uint8_t *tok_sel, void *out,
+                     int out_f32)
 {
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
@@ -341,6 +350,12 @@ void oracle_finalize(int T, int k, int H, const void *y, int y_f32, const float 
                     acc = fmaf(v, w, acc);
                 }
             }
+            for (int sh = 0; sh < S; ++sh) {
+                int64_t i = ((int64_t)sh * T + t) * H + c;
+                float v = y_f32 ? ((const float *)ys)[i] : (float)bf16_to_double(((const uint16_t *)ys)[i]);
+                acc = first ? v : acc + v;
+                first = 0;
+            }
             if (out_f32)
                 ((float *)out)[(int64_t)t * H + c] = acc;
             else
@@ -358,15 +373,20 @@ void oracle_finalize(int T, int k, int H, const void *y, int y_f32, const float 
  * finalize. Caller-owned buffers receive every intermediate:
  *   topk_ids, topk_w, inv_perm [T*k]; perm [T*k]; counts [E_loc];
  *   offsets [E_loc+1]; h bf16 [T*k][I]; y bf16 [T*k][H]; out bf16 [T][H].
+ * S shared experts (S >= 0; weights w13_sh [S][2I][H/2], s13_sh, w2_sh,
+ * s2_sh in the routed layout) run on every token: hs bf16 [S][T][I] and
+ * ys bf16 [S][T][H] receive their intermediates (NULL when S == 0).
  * tok_sel (nullable) restricts the expert FFN and the combine to the selected
  * tokens; routing and the permutation always cover every token.
  */
 void oracle_layer(int T, int E_g, int k, int expert_begin, int E_loc, int H, int I, int G,
                   const uint16_t *x, const float *logits,
                   const uint8_t *w13_q, const uint16_t *s13, const uint8_t *w2_q, const uint16_t *s2,
-                  const uint8_t *tok_sel,
+                  int S_sh, const uint8_t *w13_sh, const uint16_t *s13_sh, const uint8_t *w2_sh,
+                  const uint16_t *s2_sh, const uint8_t *tok_sel,
                   int32_t *topk_ids, float *topk_w, int32_t *counts, int32_t *offsets,
-                  int32_t *perm, int32_t *inv_perm, uint16_t *h, uint16_t *y, uint16_t *out)
+                  int32_t *perm, int32_t *inv_perm, uint16_t *h, uint16_t *y, uint16_t *hs, uint16_t *ys,
+                  uint16_t *out)
 {
     oracle_route(T, E_g, k, logits, topk_ids, topk_w);
     oracle_permute(T, k, expert_begin, E_loc, topk_ids, counts, offsets, perm, inv_perm);
@@ -381,7 +401,17 @@ void oracle_layer(int T, int E_g, int k, int expert_begin, int E_loc, int H, int
     oracle_grouped_gemm(ORACLE_W13_SWIGLU, E_loc, 2 * I, H, G, x, perm, k, offsets, w13_q, s13,
                         row_sel, h, 0);
     oracle_grouped_gemm(ORACLE_W2, E_loc, H, I, G, h, NULL, k, offsets, w2_q, s2, row_sel, y, 0);
-    oracle_finalize(T, k, H, y, 0, topk_w, inv_perm, tok_sel, out, 0);
+    /* each shared expert: one expert holding all T token rows, in token order */
+    int32_t one[2] = {0, T};
+    for (int sh = 0; sh < S_sh; ++sh) {
+        oracle_grouped_gemm(ORACLE_W13_SWIGLU, 1, 2 * I, H, G, x, NULL, 1, one,
+                            w13_sh + (int64_t)sh * 2 * I * (H / 2), s13_sh + (int64_t)sh * 2 * I * (H / G),
+                            tok_sel, hs + (int64_t)sh * T * I, 0);
+        oracle_grouped_gemm(ORACLE_W2, 1, H, I, G, hs + (int64_t)sh * T * I, NULL, 1, one,
+                            w2_sh + (int64_t)sh * H * (I / 2), s2_sh + (int64_t)sh * H * (I / G),
+                            tok_sel, ys + (int64_t)sh * T * H, 0);
+    }
+    oracle_finalize(T, k, H, y, 0, topk_w, inv_perm, S_sh, ys, tok_sel, out, 0);
     free(row_sel);
 }
 
@@ -401,6 +431,8 @@ void oracle_layer_bruteforce(int T, int k, int expert_begin, int E_loc, int H, i
                              const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
                              const uint8_t *w13_q, const uint16_t *s13,
                              const uint8_t *w2_q, const uint16_t *s2,
+                             int S, const uint8_t *w13_sh, const uint16_t *s13_sh,
+                             const uint8_t *w2_sh, const uint16_t *s2_sh,
                              const uint8_t *tok_sel, uint16_t *out)
 {
 #pragma omp parallel for schedule(dynamic, 1)
@@ -432,6 +464,25 @@ void oracle_layer_bruteforce(int T, int k, int expert_begin, int E_loc, int H, i
                     d += hv[n] * weight(w2_q, s2, H, I, G, e, c, n);
                 float v = (float)bf16_to_double(oracle_bf16_from_double(d));
                 acc[c] = first ? v * w : fmaf(v, w, acc[c]);
+            }
+            first = 0;
+        }
+        /* shared experts: the same FFN on every token, weight 1, after the slots */
+        for (int sh = 0; sh < S; ++sh) {
+            for (int n = 0; n < I; ++n) {
+                double g = 0.0, u = 0.0;
+                for (int kk = 0; kk < H; ++kk)
+                    g += xv[kk] * weight(w13_sh, s13_sh, 2 * I, H, G, sh, n, kk);
+                for (int kk = 0; kk < H; ++kk)
+                    u += xv[kk] * weight(w13_sh, s13_sh, 2 * I, H, G, sh, I + n, kk);
+                hv[n] = bf16_to_double(oracle_bf16_from_double(silu(g) * u));
+            }
+            for (int c = 0; c < H; ++c) {
+                double d = 0.0;
+                for (int n = 0; n < I; ++n)
+                    d += hv[n] * weight(w2_sh, s2_sh, H, I, G, sh, c, n);
+                float v = (float)bf16_to_double(oracle_bf16_from_double(d));
+                acc[c] = first ? v : acc[c] + v;
             }
             first = 0;
         }

@@ -154,6 +154,18 @@ def make_layer_inputs(workload: str | Workload, tokens: int, seed: int | None = 
     return LayerInputs(wl, T, x, logits, w13_q, s13, w2_q, s2)
 
 
+def make_shared_weights(workload: str | Workload, num_shared: int, seed: int | None = None):
+    """Weights of `num_shared` always-on (shared) experts with the routed
+    experts' shape and distributions: (w13_sh, s13_sh, w2_sh, s2_sh), leading
+    axis num_shared. Seeded apart from the layer inputs (seed default:
+    the workload's seed + 500000 + num_shared)."""
+    wl = WORKLOADS[workload] if isinstance(workload, str) else workload
+    H, I, S = wl.hidden, wl.inter, num_shared
+    rng = np.random.Generator(np.random.PCG64(seed_for(wl.index, 0) + 500000 + S if seed is None else seed))
+    return (random_int4_packed(rng, (S, 2 * I, H // 2)), random_scales(rng, (S, 2 * I, H // GROUP)),
+            random_int4_packed(rng, (S, H, I // 2)), random_scales(rng, (S, H, I // GROUP)))
+
+
 @dataclass
 class FinalizeStressInputs:
     logits: np.ndarray      # float32 [T, E]: route these with top_k to get ids / weights
