@@ -123,6 +123,33 @@ def time_ep_shard(ops, torch, layout, steps, warmup, T=256, L=3):
             "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
+def time_shared(ops, wl, reps, torch, layout, steps, warmup, S=1):
+    """The decode layer with S shared experts of the routed shape (every token
+    through each; DeepSeek-style), on the same replicas."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    H, I = wl.hidden, wl.inter
+    reps_s = []
+    for i, r in enumerate(reps):
+        g.manual_seed(31000 + i)
+        w13 = torch.randint(0, 256, (S, 2 * I, H // 2), generator=g, device=dev, dtype=torch.uint8)
+        w2 = torch.randint(0, 256, (S, H, I // 2), generator=g, device=dev, dtype=torch.uint8)
+        if layout == ops.WEIGHTS_TILED:
+            w13, w2 = ops.pack_weights(ops.W13_SWIGLU, w13), ops.pack_weights(ops.W2, w2)
+        s13 = torch.empty((S, 2 * I, H // 128), device=dev).uniform_(0.005, 0.02, generator=g).to(torch.bfloat16)
+        s2 = torch.empty((S, H, I // 128), device=dev).uniform_(0.005, 0.02, generator=g).to(torch.bfloat16)
+        reps_s.append(dict(r, shared=(w13, s13, w2, s2)))
+    T = reps[0]["x"].shape[0]
+    dt, _ = time_layer(ops, wl, reps_s, steps, warmup, torch, layout)
+    us = dt / steps * 1e6
+    w13b, w2b = weight_bytes_per_expert(H, I)
+    stats = routing_stats(ops, wl, reps, torch)
+    act = sum(st["active"] for st in stats) / len(reps) + S
+    gbps = act * (w13b + w2b) / (us * 1e-6) / 1e9
+    return {"shared_experts": S, "tokens": T, "us_per_layer": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1),
+            "experts_streamed": act, "weight_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def time_finalize_stream(ops, torch, T=4096, k=8, H=4096, E=128, reps_n=20):
     """The finalize on its stress shape: fp32 y [T*k, H] (512 MiB, two buffers
     alternate so the Infinity Cache cannot hold them), bf16 out [T, H]."""
@@ -230,14 +257,18 @@ def time_layer(ops, wl, reps, steps, warmup, torch, layout=0):
     L = len(reps)
     T = reps[0]["x"].shape[0]
     outs = [torch.empty((T, wl.hidden), dtype=torch.bfloat16, device="cuda") for _ in reps]
-    wsz = ops.workspace_size(ops.make_shape(T, wl.hidden, wl.inter, wl.num_experts, wl.num_local_experts,
-                                            wl.top_k, wl.expert_begin, weight_layout=layout))
+    shape = ops.make_shape(T, wl.hidden, wl.inter, wl.num_experts, wl.num_local_experts, wl.top_k,
+                           wl.expert_begin, weight_layout=layout)
+    nsh = reps[0]["shared"][0].shape[0] if reps[0].get("shared") is not None else 0
+    wsz = ops.workspace_size(shape) if nsh == 0 else \
+        int(ops.load_library().moe_w4a16_workspace_size_shared(__import__("ctypes").byref(shape), nsh))
     ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device="cuda")
 
     def fwd(i):
         r = reps[i]
         ops.moe_w4a16_forward(r["x"], r["logits"], r["w13"], r["s13"], r["w2"], r["s2"], wl.top_k,
-                              out=outs[i], expert_begin=wl.expert_begin, workspace=ws, weight_layout=layout)
+                              out=outs[i], expert_begin=wl.expert_begin, workspace=ws, weight_layout=layout,
+                              shared=r.get("shared"))
 
     for i in range(L):          # eager pass (also loads kernels)
         fwd(i)
@@ -434,8 +465,10 @@ def main():
         log("prefill T=2048 (Zipf routing)")
         prefill = time_prefill(ops, reps, torch, layout, max(8, args.steps // 50), args.warmup // 10 + 1)
 
-    ep_shard = finalize_stream = dense = None
+    ep_shard = finalize_stream = dense = shared = None
     if not args.no_sweep:
+        log("layer with one shared expert T=256")
+        shared = time_shared(ops, wl, reps, torch, layout, max(100, args.steps // 2), args.warmup)
         del reps
         torch.cuda.empty_cache()
         log("EP shard decode T=256")
@@ -469,6 +502,7 @@ def main():
         "cpu_baseline": cpu,
         "sweep": sweep,
         "prefill": prefill,
+        "shared_expert": shared,
         "ep_shard": ep_shard,
         "finalize_stream": finalize_stream,
         "dense_gemm": dense,

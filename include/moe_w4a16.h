@@ -138,6 +138,27 @@ moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const fl
                              size_t workspace_bytes, void *stream);
 
 /*
+ * The layer with shared experts ([GC] abstract: optional, fused shared
+ * experts; the reading taken): num_shared (1..4) always-on experts with the
+ * routed experts' shape and formats run on every token, and each one's bf16
+ * output is added to the binary32 combine with weight 1 after the routed
+ * slots (acc = acc + v, or v for a token's first term). They run inside the
+ * same launches as the routed experts (extra experts of the grouped GEMMs).
+ *   w13_sh [num_shared][2*I][H/2], s13_sh [num_shared][2*I][H/128],
+ *   w2_sh  [num_shared][H][I/2],   s2_sh  [num_shared][H][I/128]
+ *   (codes plain or tiled per weight_layout, like the routed weights)
+ *   workspace >= moe_w4a16_workspace_size_shared(shape, num_shared) bytes
+ * Everything else as moe_w4a16_forward. Under expert parallelism pass the
+ * shared experts only on the rank that owns the tokens.
+ */
+size_t moe_w4a16_workspace_size_shared(const moe_shape *shape, int32_t num_shared);
+moe_status moe_w4a16_forward_shared(const moe_shape *shape, int32_t num_shared, const uint16_t *x,
+                                    const float *router_logits, const uint8_t *w13_q, const uint16_t *s13,
+                                    const uint8_t *w2_q, const uint16_t *s2, const uint8_t *w13_sh,
+                                    const uint16_t *s13_sh, const uint8_t *w2_sh, const uint16_t *s2_sh,
+                                    uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Top-k routing ([FI] section 2; the layer definition: softmax over all E_g
  * experts, keep the top-k, renormalise). Selection order: larger logit first,
  * lower expert index first among equal logits (-0 == +0); the i-th selected

@@ -86,3 +86,17 @@ def test_dense_validation_without_gpu():
     assert f(4, 256, 256, None, p, p, p, 0, 0, None) == 1       # NULL activations
     assert f(4, 256, 256, ctypes.c_void_p((1 << 20) + 2), p, p, p, 0, 0, None) == 4   # misaligned
     assert f(0, 256, 256, None, None, None, None, 0, 0, None) == 0    # M = 0: nothing to do
+
+
+def test_shared_validation_without_gpu():
+    # refused on the host before any launch
+    lib = ops.load_library()
+    sh = ops.make_shape(4, 256, 512, 8, 8, 2)
+    p = ctypes.c_void_p(1 << 20)
+    f = lib.moe_w4a16_forward_shared
+    assert f(ctypes.byref(sh), 0, p, p, p, p, p, p, p, p, p, p, p, p, 1 << 30, None) == 3    # no shared expert
+    assert f(ctypes.byref(sh), 5, p, p, p, p, p, p, p, p, p, p, p, p, 1 << 30, None) == 3    # more than 4
+    assert f(ctypes.byref(sh), 1, p, p, p, p, p, p, None, p, p, p, p, p, 1 << 30, None) == 1  # NULL shared w13
+    assert f(ctypes.byref(sh), 1, p, p, p, p, p, p, p, p, p, p, p, p, 16, None) == 5        # workspace too small
+    assert lib.moe_w4a16_workspace_size_shared(ctypes.byref(sh), 2) > lib.moe_w4a16_workspace_size_shared(
+        ctypes.byref(sh), 1)

@@ -78,10 +78,13 @@ struct Workspace {
     size_t bytes;
 };
 
-Workspace carve(const moe_shape &sh, void *base)
+// nsh shared experts add nsh*T rows after the T*k routed rows and nsh
+// experts after the E_loc routed ones.
+Workspace carve(const moe_shape &sh, void *base, int nsh = 0)
 {
-    const size_t S = (size_t)sh.num_tokens * sh.top_k;
-    const size_t E = (size_t)sh.num_local_experts;
+    const size_t Sr = (size_t)sh.num_tokens * sh.top_k;
+    const size_t S = Sr + (size_t)nsh * sh.num_tokens;
+    const size_t E = (size_t)sh.num_local_experts + nsh;
     char *p = static_cast<char *>(base);
     size_t off = 0;
     Workspace ws{};
@@ -90,12 +93,12 @@ Workspace carve(const moe_shape &sh, void *base)
         off += align_up(bytes);
         return r;
     };
-    ws.ids = reinterpret_cast<int32_t *>(take(S * 4));
-    ws.w = reinterpret_cast<float *>(take(S * 4));
+    ws.ids = reinterpret_cast<int32_t *>(take(Sr * 4));
+    ws.w = reinterpret_cast<float *>(take(Sr * 4));
     ws.counts = reinterpret_cast<int32_t *>(take(E * 4));
     ws.offsets = reinterpret_cast<int32_t *>(take((E + 1) * 4));
     ws.perm = reinterpret_cast<int32_t *>(take(S * 4));
-    ws.inv_perm = reinterpret_cast<int32_t *>(take(S * 4));
+    ws.inv_perm = reinterpret_cast<int32_t *>(take(Sr * 4));
     ws.h = reinterpret_cast<uint16_t *>(take(S * (size_t)sh.inter * 2));
     ws.y = reinterpret_cast<uint16_t *>(take(S * (size_t)sh.hidden * 2));
     ws.bytes = off;
@@ -105,6 +108,7 @@ Workspace carve(const moe_shape &sh, void *base)
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 constexpr int32_t kMaxDenseDim = 65536;   // N and K of the dense GEMM
+constexpr int32_t kMaxSharedExperts = 4;  // shared experts of one layer call (finalize unrolls them)
 
 GemmLaunch gemm_args(const moe_shape &sh, moe_gemm_kind kind)
 {
@@ -157,6 +161,13 @@ size_t moe_w4a16_workspace_size(const moe_shape *shape)
     if (check_shape(shape) != MOE_OK)
         return 0;
     return carve(*shape, nullptr).bytes;
+}
+
+size_t moe_w4a16_workspace_size_shared(const moe_shape *shape, int32_t num_shared)
+{
+    if (check_shape(shape) != MOE_OK || num_shared < 1 || num_shared > kMaxSharedExperts)
+        return 0;
+    return carve(*shape, nullptr, num_shared).bytes;
 }
 
 size_t moe_permute_workspace_size(const moe_shape *shape)
@@ -325,36 +336,62 @@ moe_status moe_w4a16_pack_weights(const moe_shape *shape, moe_gemm_kind kind, co
                                         static_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const float *router_logits,
-                             const uint8_t *w13_q, const uint16_t *s13, const uint8_t *w2_q,
-                             const uint16_t *s2, uint16_t *out, void *workspace,
-                             size_t workspace_bytes, void *stream)
+// The layer, with nsh >= 0 shared experts folded into the same launches:
+// the permutation appends one T-row segment per shared expert, the grouped
+// GEMMs see E_loc + nsh experts (the last nsh read the shared weights) and
+// the finalize adds the shared rows after the routed slots.
+static moe_status forward_impl(const moe_shape *shape, int nsh, const uint16_t *x, const float *router_logits,
+                               const uint8_t *w13_q, const uint16_t *s13, const uint8_t *w2_q, const uint16_t *s2,
+                               const uint8_t *w13_sh, const uint16_t *s13_sh, const uint8_t *w2_sh,
+                               const uint16_t *s2_sh, uint16_t *out, void *workspace, size_t workspace_bytes,
+                               void *stream)
 {
     moe_status st = check_shape(shape);
     if (st != MOE_OK)
         return st;
     const moe_shape &sh = *shape;
+    if (nsh < 0 || nsh > kMaxSharedExperts)
+        return MOE_ERR_UNSUPPORTED;
+    const long long rows = (long long)sh.num_tokens * (sh.top_k + nsh);
+    if (rows * (sh.hidden > sh.inter ? sh.hidden : sh.inter) * 2 >= (1LL << 31))
+        return MOE_ERR_UNSUPPORTED;
     if (sh.num_tokens == 0)
         return MOE_OK;
     if (!x || !router_logits || !w13_q || !s13 || !w2_q || !s2 || !out || !workspace)
         return MOE_ERR_NULL;
+    if (nsh > 0 && (!w13_sh || !s13_sh || !w2_sh || !s2_sh))
+        return MOE_ERR_NULL;
     if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w13_q, 16) || !aligned(w2_q, 16) ||
         !aligned(s13, 2) || !aligned(s2, 2) || !aligned(router_logits, 4) || !aligned(workspace, kAlign))
         return MOE_ERR_ALIGN;
-    Workspace ws = carve(sh, workspace);
+    if (nsh > 0 && (!aligned(w13_sh, 16) || !aligned(w2_sh, 16) || !aligned(s13_sh, 2) || !aligned(s2_sh, 2)))
+        return MOE_ERR_ALIGN;
+    Workspace ws = carve(sh, workspace, nsh);
     if (workspace_bytes < ws.bytes)
         return MOE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (route_permute_fusable(sh)) {
-        e = launch_route_permute(sh, router_logits, ws.ids, ws.w, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s);
+        e = launch_route_permute(sh, router_logits, ws.ids, ws.w, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s,
+                                 nsh);
     } else {
         e = launch_route(sh, router_logits, ws.ids, ws.w, s);
         if (e == hipSuccess)
-            e = launch_permute(sh, ws.ids, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s);
+            e = launch_permute(sh, ws.ids, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s, nsh);
     }
+    auto with_shared = [&](GemmLaunch &g, const uint8_t *wq_sh, const uint16_t *s_sh) {
+        if (nsh == 0)
+            return;
+        g.e_routed = g.num_experts;
+        g.num_experts += nsh;
+        g.max_rows += nsh * sh.num_tokens;
+        g.expected_rows += nsh * sh.num_tokens;
+        g.wq_sh = wq_sh;
+        g.s_sh = s_sh;
+    };
     if (e == hipSuccess) {
         GemmLaunch g = gemm_args(sh, MOE_GEMM_W13_SWIGLU);
+        with_shared(g, w13_sh, s13_sh);
         g.a = x;
         g.a_row_index = ws.perm;
         g.a_bytes = (size_t)sh.num_tokens * sh.hidden * 2;
@@ -365,13 +402,15 @@ moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const fl
         g.c_f32 = false;
         e = launch_grouped_gemm(g, s);
     }
-    // every slot local: the down GEMM writes y in slot order and the
-    // finalize reads it without the inv_perm indirection
-    const bool y_slot = sh.num_local_experts == sh.num_experts;
+    // every slot local (and no shared rows): the down GEMM writes y in slot
+    // order and the finalize reads it without the inv_perm indirection
+    const bool y_slot = sh.num_local_experts == sh.num_experts && nsh == 0;
     if (e == hipSuccess) {
         GemmLaunch g = gemm_args(sh, MOE_GEMM_W2);
+        with_shared(g, w2_sh, s2_sh);
         g.a = ws.h;
         g.a_row_index = nullptr;
+        g.a_bytes = (size_t)g.max_rows * sh.inter * 2;
         g.offsets = ws.offsets;
         g.wq = w2_q;
         g.s = s2;
@@ -381,8 +420,30 @@ moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const fl
         e = launch_grouped_gemm(g, s);
     }
     if (e == hipSuccess)
-        e = launch_finalize(sh, ws.y, false, ws.w, ws.inv_perm, out, false, s, y_slot);
+        e = launch_finalize(sh, ws.y, false, ws.w, ws.inv_perm, out, false, s, y_slot, nsh,
+                            ws.offsets + sh.num_local_experts);
     return from_hip(e);
+}
+
+moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const float *router_logits,
+                             const uint8_t *w13_q, const uint16_t *s13, const uint8_t *w2_q,
+                             const uint16_t *s2, uint16_t *out, void *workspace,
+                             size_t workspace_bytes, void *stream)
+{
+    return forward_impl(shape, 0, x, router_logits, w13_q, s13, w2_q, s2, nullptr, nullptr, nullptr, nullptr, out,
+                        workspace, workspace_bytes, stream);
+}
+
+moe_status moe_w4a16_forward_shared(const moe_shape *shape, int32_t num_shared, const uint16_t *x,
+                                    const float *router_logits, const uint8_t *w13_q, const uint16_t *s13,
+                                    const uint8_t *w2_q, const uint16_t *s2, const uint8_t *w13_sh,
+                                    const uint16_t *s13_sh, const uint8_t *w2_sh, const uint16_t *s2_sh,
+                                    uint16_t *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (num_shared < 1)
+        return MOE_ERR_UNSUPPORTED;
+    return forward_impl(shape, num_shared, x, router_logits, w13_q, s13, w2_q, s2, w13_sh, s13_sh, w2_sh, s2_sh, out,
+                        workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

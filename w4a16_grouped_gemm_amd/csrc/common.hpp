@@ -70,6 +70,9 @@ struct GemmLaunch {
     int num_experts;          // E_loc
     const uint8_t *wq;
     const uint16_t *s;
+    const uint8_t *wq_sh;     // NULL, or the shared experts (experts e_routed.. of the launch)
+    const uint16_t *s_sh;
+    int e_routed;
     void *c;
     const int32_t *c_row_index;  // NULL, or row r of the result is stored at row c_row_index[r]
     bool c_f32;
@@ -84,11 +87,13 @@ struct GemmLaunch {
 hipError_t launch_route(const moe_shape &sh, const float *logits, int32_t *ids, float *w,
                         hipStream_t st);
 hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *counts,
-                          int32_t *offsets, int32_t *perm, int32_t *inv_perm, hipStream_t st);
+                          int32_t *offsets, int32_t *perm, int32_t *inv_perm, hipStream_t st,
+                          int num_shared = 0);
 bool route_permute_fusable(const moe_shape &sh);
 hipError_t launch_route_permute(const moe_shape &sh, const float *logits, int32_t *ids, float *w,
                                 int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
-                                hipStream_t st);
+                                hipStream_t st,
+                                int num_shared = 0);
 hipError_t launch_gather(const moe_shape &sh, const uint16_t *x, const int32_t *perm,
                          const int32_t *offsets, uint16_t *x_perm, hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st);
@@ -96,7 +101,8 @@ hipError_t launch_pack_weights(int E, int N, int K, int half, bool pair_rows, co
                                uint8_t *wq_tiled, hipStream_t st);
 hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const float *w,
                            const int32_t *inv_perm, void *out, bool out_f32, hipStream_t st,
-                           bool y_slot = false);
+                           bool y_slot = false, int num_shared = 0,
+                           const int32_t *shared_row0 = nullptr);
 
 int device_cu_count();
 

@@ -27,13 +27,21 @@ namespace {
 // it when every slot is local), so the row loads need no index and go out
 // together with the index and weight loads: one round trip. inv_perm then
 // only says which slots are present.
-template <bool Y_F32, bool OUT_F32, int KMAX, bool Y_SLOT>
+// SHARED: the layer's shared experts (GC-MoE abstract: optional shared
+// experts): nsh <= kMaxShared rows per token at y row R + s*T + t, R =
+// *shared_row0 (the routed row count), each added with weight 1 after the
+// routed slots: acc = acc + v, or v as the token's first term.
+constexpr int kMaxShared = 4;
+
+template <bool Y_F32, bool OUT_F32, int KMAX, bool Y_SLOT, bool SHARED>
 __global__ __launch_bounds__(256) void finalize_kernel(int T, int k, int H,
                                                        const void *__restrict__ y,
                                                        const float *__restrict__ w,
                                                        const int32_t *__restrict__ inv,
-                                                       void *__restrict__ out)
+                                                       void *__restrict__ out, int nsh,
+                                                       const int32_t *__restrict__ shared_row0)
 {
+    const int R0 = SHARED ? shared_row0[0] : 0;
     const int vec_per_row = H >> 3;
     const long long total = (long long)T * vec_per_row;
     for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -75,6 +83,20 @@ __global__ __launch_bounds__(256) void finalize_kernel(int T, int k, int H,
         for (int j = 0; j < KMAX; ++j)
             if (j >= k)
                 r[j] = -1;
+        float vs[SHARED ? kMaxShared : 1][8];
+        if (SHARED) {
+#pragma unroll
+            for (int sh = 0; sh < kMaxShared; ++sh) {
+                // every row is loaded (clamped to the last shared expert), no branch
+                const size_t row = (size_t)R0 + (size_t)(sh < nsh ? sh : nsh - 1) * T + t;
+                const uint16_t *src = static_cast<const uint16_t *>(y) + row * H + c0;
+                const u32x4 d = *reinterpret_cast<const u32x4 *>(src);
+                vs[sh][0] = bf16_to_f32(d.x & 0xFFFFu); vs[sh][1] = bf16_to_f32(d.x >> 16);
+                vs[sh][2] = bf16_to_f32(d.y & 0xFFFFu); vs[sh][3] = bf16_to_f32(d.y >> 16);
+                vs[sh][4] = bf16_to_f32(d.z & 0xFFFFu); vs[sh][5] = bf16_to_f32(d.z >> 16);
+                vs[sh][6] = bf16_to_f32(d.w & 0xFFFFu); vs[sh][7] = bf16_to_f32(d.w >> 16);
+            }
+        }
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q)
@@ -95,6 +117,17 @@ __global__ __launch_bounds__(256) void finalize_kernel(int T, int k, int H,
                     acc[q] = __fmaf_rn(v[j][q], wt[j], acc[q]);
             }
         }
+        if (SHARED) {
+#pragma unroll
+            for (int sh = 0; sh < kMaxShared; ++sh) {
+                if (sh >= nsh)
+                    break;
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    acc[q] = first ? vs[sh][q] : __fadd_rn(acc[q], vs[sh][q]);
+                first = false;
+            }
+        }
         if (OUT_F32) {
             float *dst = static_cast<float *>(out) + (size_t)t * H + c0;
             *reinterpret_cast<floatx4 *>(dst) = floatx4{acc[0], acc[1], acc[2], acc[3]};
@@ -108,28 +141,29 @@ __global__ __launch_bounds__(256) void finalize_kernel(int T, int k, int H,
     }
 }
 
-template <bool Y_F32, bool OUT_F32, bool Y_SLOT>
+template <bool Y_F32, bool OUT_F32, bool Y_SLOT, bool SHARED = false>
 void launch_fin(dim3 grid, dim3 block, hipStream_t st, int T, int k, int H, const void *y, const float *w,
-                const int32_t *inv, void *out)
+                const int32_t *inv, void *out, int nsh = 0, const int32_t *r0 = nullptr)
 {
     if (k <= 2)
-        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 2, Y_SLOT>), grid, block, 0, st, T, k, H, y, w, inv,
-                           out);
+        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 2, Y_SLOT, SHARED>), grid, block, 0, st, T, k, H, y, w,
+                           inv, out, nsh, r0);
     else if (k <= 4)
-        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 4, Y_SLOT>), grid, block, 0, st, T, k, H, y, w, inv,
-                           out);
+        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 4, Y_SLOT, SHARED>), grid, block, 0, st, T, k, H, y, w,
+                           inv, out, nsh, r0);
     else if (k <= 8)
-        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 8, Y_SLOT>), grid, block, 0, st, T, k, H, y, w, inv,
-                           out);
+        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, 8, Y_SLOT, SHARED>), grid, block, 0, st, T, k, H, y, w,
+                           inv, out, nsh, r0);
     else
-        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, kMaxTopK, Y_SLOT>), grid, block, 0, st, T, k, H, y, w,
-                           inv, out);
+        hipLaunchKernelGGL((finalize_kernel<Y_F32, OUT_F32, kMaxTopK, Y_SLOT, SHARED>), grid, block, 0, st, T, k, H,
+                           y, w, inv, out, nsh, r0);
 }
 
 }  // namespace
 
 hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const float *w,
-                           const int32_t *inv_perm, void *out, bool out_f32, hipStream_t st, bool y_slot)
+                           const int32_t *inv_perm, void *out, bool out_f32, hipStream_t st, bool y_slot,
+                           int num_shared, const int32_t *shared_row0)
 {
     const long long total = (long long)sh.num_tokens * (sh.hidden / 8);
     long long blocks = (total + 255) / 256;
@@ -140,7 +174,10 @@ hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const
         blocks = 1;
     const dim3 grid((unsigned)blocks), block(256);
     const int T = sh.num_tokens, k = sh.top_k, H = sh.hidden;
-    if (y_slot)                                   // the layer's path: bf16 y in slot order, bf16 out
+    if (num_shared > 0)                           // the layer with shared experts: bf16 y and out
+        launch_fin<false, false, false, true>(grid, block, st, T, k, H, y, w, inv_perm, out, num_shared,
+                                              shared_row0);
+    else if (y_slot)                              // the layer's path: bf16 y in slot order, bf16 out
         launch_fin<false, false, true>(grid, block, st, T, k, H, y, w, inv_perm, out);
     else if (y_f32 && out_f32)
         launch_fin<true, true, false>(grid, block, st, T, k, H, y, w, inv_perm, out);

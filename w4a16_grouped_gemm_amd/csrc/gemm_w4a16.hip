@@ -72,6 +72,9 @@ struct GemmArgs {
     int dense_rows;
     const uint8_t *wq;
     const uint16_t *s;
+    const uint8_t *wq_sh;        // experts e >= e_routed: shared experts, weights at index e - e_routed
+    const uint16_t *s_sh;
+    int e_routed;
     void *c;
     const int32_t *c_row_index;  // output row r goes to row c_row_index[r] (NULL: row r)
     uint32_t c_row_bytes;        // bytes of c_row_index (0 when NULL)
@@ -163,6 +166,18 @@ __device__ __forceinline__ bf16x8 neg136_operand()
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Codes and scales of expert e: the routed arrays, or past e_routed the
+// shared experts' arrays (e is uniform: a scalar select, no branch).
+__device__ __forceinline__ const uint8_t *expert_codes(const GemmArgs &p, int e, uint32_t bytes)
+{
+    return e < p.e_routed ? p.wq + (size_t)e * bytes : p.wq_sh + (size_t)(e - p.e_routed) * bytes;
+}
+
+__device__ __forceinline__ const uint16_t *expert_scales(const GemmArgs &p, int e, uint32_t n)
+{
+    return e < p.e_routed ? p.s + (size_t)e * n : p.s_sh + (size_t)(e - p.e_routed) * n;
+}
 
 // Row offset of expert e: offsets[e], or for a dense GEMM (offsets NULL,
 // one expert) 0 and dense_rows.
@@ -376,8 +391,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         const int nvalid = uniform(min(CS, s_off[e + 1] - row0));
         const int nsub = (nvalid + 15) >> 4;
         const int tile0 = block * BT + wave * TPW;
-        const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (size_t)e * p.N * row_bytes, (uint32_t)p.N * row_bytes);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s + (size_t)e * p.N * G, (uint32_t)p.N * G * 2);
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(expert_codes(p, e, (uint32_t)p.N * row_bytes), (uint32_t)p.N * row_bytes);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(expert_scales(p, e, (uint32_t)p.N * G), (uint32_t)p.N * G * 2);
 
         uint32_t voff_w[TPW], voff_s[TPW];
 #pragma unroll
@@ -607,8 +622,8 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
         const int e = uniform(chunk_expert(s_prefix, E, chunk));
         const int row0 = uniform(expert_offset(p.offsets, p.dense_rows, e) + (chunk - s_prefix[e]) * CS);
         const int nvalid = uniform(min(CS, expert_offset(p.offsets, p.dense_rows, e + 1) - row0));
-        const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (size_t)e * p.N * row_bytes, (uint32_t)p.N * row_bytes);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s + (size_t)e * p.N * G, (uint32_t)p.N * G * 2);
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(expert_codes(p, e, (uint32_t)p.N * row_bytes), (uint32_t)p.N * row_bytes);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(expert_scales(p, e, (uint32_t)p.N * G), (uint32_t)p.N * G * 2);
         const uint32_t row = (uint32_t)tile_row<KIND>(p, tile, n16);
         const uint32_t voff_w = code_offset(p, tile, row, G, row_bytes, lane);
         const uint32_t voff_s = row * (uint32_t)G * 2;
@@ -776,6 +791,9 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     a.a_row_index = g.a_row_index;
     a.offsets = g.offsets;
     a.wq = g.wq;
+    a.wq_sh = g.wq_sh;
+    a.s_sh = g.s_sh;
+    a.e_routed = g.wq_sh ? g.e_routed : g.num_experts;
     a.s = g.s;
     a.dense_rows = g.dense_rows;
     a.c = g.c;

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int T, int k, int begin, int E, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm,
     int chunk_tokens, const float *__restrict__ logits = nullptr, int E_g = 0,
-    int32_t *__restrict__ ids_out = nullptr, float *__restrict__ w_out = nullptr)
+    int32_t *__restrict__ ids_out = nullptr, float *__restrict__ w_out = nullptr, int num_shared = 0)
 {
     static_assert(!ROUTE || IDS_IN_LDS, "routing in the kernel keeps the ids in LDS");
     __shared__ int s_count[kMaxExperts];
@@ -135,6 +135,14 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     if (tid == 0)
         offsets[E] = carry;
     const int R = carry;
+    // shared experts (layer path only): expert E + s holds every token, row
+    // R + s*T + t, whose perm entry t*k makes the GEMM read token t
+    for (int sh = tid; sh < num_shared; sh += kPermThreads) {
+        counts[E + sh] = T;
+        offsets[E + 1 + sh] = R + (sh + 1) * T;
+    }
+    for (long long r = tid; r < (long long)num_shared * T; r += kPermThreads)
+        perm[R + r] = (int32_t)((r % T) * k);
 
     // 3. stable scatter, chunk by chunk of tokens
     for (int t0 = 0; t0 < T; t0 += chunk_tokens) {
@@ -197,8 +205,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
             s_cursor[e] += s_wprefix[e * words + words - 1] + __popc(s_mask[e * words + words - 1]);
         __syncthreads();
     }
-    // rows past R hold no slot
-    for (long long r = R + tid; r < S; r += kPermThreads)
+    // rows past the routed and shared rows hold no slot
+    for (long long r = R + (long long)num_shared * T + tid; r < S + (long long)num_shared * T; r += kPermThreads)
         perm[r] = -1;
 }
 
@@ -236,7 +244,7 @@ static int chunk_tokens_for(int E)
 }
 
 hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *counts,
-                          int32_t *offsets, int32_t *perm, int32_t *inv_perm, hipStream_t st)
+                          int32_t *offsets, int32_t *perm, int32_t *inv_perm, hipStream_t st, int num_shared)
 {
     const int E = sh.num_local_experts;
     int chunk = chunk_tokens_for(E);
@@ -255,10 +263,11 @@ hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *coun
         }
         hipLaunchKernelGGL(permute_kernel<true>, dim3(1), dim3(kPermThreads), dyn, st,
                            sh.num_tokens, sh.top_k, sh.expert_begin, E, ids, counts, offsets, perm, inv_perm,
-                           chunk);
+                           chunk, nullptr, 0, nullptr, nullptr, num_shared);
     } else
         hipLaunchKernelGGL(permute_kernel<false>, dim3(1), dim3(kPermThreads), lds, st, sh.num_tokens,
-                           sh.top_k, sh.expert_begin, E, ids, counts, offsets, perm, inv_perm, chunk);
+                           sh.top_k, sh.expert_begin, E, ids, counts, offsets, perm, inv_perm, chunk, nullptr, 0,
+                           nullptr, nullptr, num_shared);
     return hipGetLastError();
 }
 
@@ -281,7 +290,7 @@ bool route_permute_fusable(const moe_shape &sh)
 
 hipError_t launch_route_permute(const moe_shape &sh, const float *logits, int32_t *ids, float *w,
                                 int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
-                                hipStream_t st)
+                                hipStream_t st, int num_shared)
 {
     const int E = sh.num_local_experts;
     int chunk = chunk_tokens_for(E);
@@ -294,7 +303,7 @@ hipError_t launch_route_permute(const moe_shape &sh, const float *logits, int32_
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDynLdsMax);
         hipLaunchKernelGGL(kernel, dim3(1), dim3(kPermThreads), dyn, st, sh.num_tokens, sh.top_k,
                            sh.expert_begin, E, nullptr, counts, offsets, perm, inv_perm, chunk, logits,
-                           sh.num_experts, ids, w);
+                           sh.num_experts, ids, w, num_shared);
     };
     if (sh.num_experts <= 64)
         launch(permute_kernel<true, true, 16, 4>);

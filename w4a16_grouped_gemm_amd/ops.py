@@ -28,7 +28,7 @@ _STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUP
 EXPORTED = ["moe_status_str", "moe_w4a16_check_shape", "moe_w4a16_is_supported",
             "moe_w4a16_workspace_size", "moe_w4a16_forward", "moe_route", "moe_permute_workspace_size",
             "moe_permute", "moe_grouped_gemm_w4a16", "moe_finalize", "moe_w4a16_pack_weights",
-            "moe_w4a16_dense_gemm"]
+            "moe_w4a16_dense_gemm", "moe_w4a16_workspace_size_shared", "moe_w4a16_forward_shared"]
 
 
 class MoeShape(ctypes.Structure):
@@ -84,6 +84,10 @@ def load_library(path: str = LIB_PATH):
         lib.moe_w4a16_dense_gemm.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P, I,
                                              ctypes.c_int32, P]
         lib.moe_w4a16_dense_gemm.restype = I
+        lib.moe_w4a16_workspace_size_shared.argtypes = [S, ctypes.c_int32]
+        lib.moe_w4a16_workspace_size_shared.restype = Z
+        lib.moe_w4a16_forward_shared.argtypes = [S, ctypes.c_int32] + [P] * 12 + [Z, P]
+        lib.moe_w4a16_forward_shared.restype = I
         _lib = lib
         return lib
 
@@ -293,11 +297,13 @@ def moe_w4a16_forward(x: torch.Tensor, router_logits: torch.Tensor, w13_q: torch
                       s13: torch.Tensor, w2_q: torch.Tensor, s2: torch.Tensor, top_k: int,
                       out: torch.Tensor | None = None, stream=None, *, expert_begin: int = 0,
                       workspace: torch.Tensor | None = None,
-                      weight_layout: int = WEIGHTS_PLAIN) -> torch.Tensor:
+                      weight_layout: int = WEIGHTS_PLAIN, shared=None) -> torch.Tensor:
     """The whole quantized MoE expert layer (route, permute, GEMM1+SwiGLU, GEMM2, finalize).
 
     weight_layout=WEIGHTS_TILED takes codes from pack_weights (w13 packed
-    with W13_SWIGLU, w2 with W2)."""
+    with W13_SWIGLU, w2 with W2). shared: optional (w13_sh [S, 2I, H/2],
+    s13_sh, w2_sh [S, H, I/2], s2_sh) always-on experts, added after the
+    routed slots."""
     _need(x, torch.bfloat16, "x")
     _need(router_logits, torch.float32, "router_logits")
     _need(w13_q, torch.uint8, "w13_q")
@@ -318,6 +324,25 @@ def moe_w4a16_forward(x: torch.Tensor, router_logits: torch.Tensor, w13_q: torch
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     lib = load_library()
+    if shared is not None:
+        w13s, s13s, w2s, s2s = shared
+        for t, d, n in ((w13s, torch.uint8, "w13_sh"), (s13s, torch.bfloat16, "s13_sh"),
+                        (w2s, torch.uint8, "w2_sh"), (s2s, torch.bfloat16, "s2_sh")):
+            _need(t, d, n)
+        nsh = w13s.shape[0]
+        if (w13s.shape != (nsh, 2 * I, H // 2) or w2s.shape != (nsh, H, I // 2)
+                or s13s.shape != (nsh, 2 * I, H // 128) or s2s.shape != (nsh, H, I // 128)):
+            raise ValueError("shared expert shapes do not match the routed experts")
+        nbytes = int(lib.moe_w4a16_workspace_size_shared(ctypes.byref(sh), nsh))
+        if nbytes == 0:
+            _check(int(lib.moe_w4a16_check_shape(ctypes.byref(sh))) or 3)
+        if workspace is None:
+            workspace = _workspace(nbytes, x.device)
+        _check(lib.moe_w4a16_forward_shared(ctypes.byref(sh), nsh, _ptr(x), _ptr(router_logits), _ptr(w13_q),
+                                            _ptr(s13), _ptr(w2_q), _ptr(s2), _ptr(w13s), _ptr(s13s), _ptr(w2s),
+                                            _ptr(s2s), _ptr(out), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _stream(stream)))
+        return out
     nbytes = int(lib.moe_w4a16_workspace_size(ctypes.byref(sh)))
     if nbytes == 0:
         _check(int(lib.moe_w4a16_check_shape(ctypes.byref(sh))) or 2)
