@@ -50,16 +50,22 @@
  *   Weight arrays start at local expert 0 (global id expert_begin).
  *
  * Tiled code layout (moe_shape.weight_layout == MOE_WEIGHTS_TILED; scales
- * keep the plain layout above). The same bytes as the plain codes of a
- * weight matrix with N rows and K columns, reordered so that one 64-lane
- * load of 16 bytes per lane reads 1 KiB contiguously:
- *   tiled[e][b][g][i][l][0..16) = plain[e][row(16*(8*b+i), l%16)][64*g + 16*(l/16) .. +16)
+ * keep the plain layout above). The codes of a weight matrix with N rows and
+ * K columns, reordered so that one 64-lane load of 16 bytes per lane reads
+ * 1 KiB contiguously, and so that each 32-bit word holds its 8 codes in the
+ * order the matrix unit consumes them:
+ *   run(e, b, g, i, l) = plain[e][row(16*(8*b+i), l%16)][64*g + 16*(l/16) .. +16)
+ *   tiled[e][b][g][i][l][4*w .. 4*w+4) = shuffle(word w of run(e, b, g, i, l)), w < 4
  *   b < N/128 (blocks of 8 sixteen-row tiles), g < K/128, i < 8, l < 64,
  *   row(t0, n) = t0 + n                           for MOE_GEMM_W2 / W13_RAW,
  *   row(16*t, n) = 8*t + n (n < 8), I + 8*t + n - 8 (n >= 8)
  *                                                 for MOE_GEMM_W13_SWIGLU
- *   (a gate row and its up row share a tile). moe_w4a16_pack_weights writes
- *   it; it is an offline, once-per-model step.
+ *   (a gate row and its up row share a tile). A plain little-endian word
+ *   holds codes c0..c7 of 8 consecutive columns, c_j in bits [4j, 4j+4);
+ *   shuffle() puts the even codes c0, c2, c4, c6 in nibbles 0..3 and the odd
+ *   codes c1, c3, c5, c7 in nibbles 4..7, so that nibble pairs (j, j+4) are
+ *   column pairs (2j, 2j+1). moe_w4a16_pack_weights writes it; it is an
+ *   offline, once-per-model step.
  */
 #ifndef MOE_W4A16_H
 #define MOE_W4A16_H

@@ -55,10 +55,25 @@ def assert_layer_close(got_u16, ref_u16, what=""):
     assert mean_rel <= MEAN_REL, (what, mean_rel)
 
 
+def shuffle_words(b):
+    """The tiled layout's word shuffle, from its definition in the C header:
+    code c_j of a little-endian word (bits 4j..4j+3) moves to nibble j/2 for
+    even j and to nibble 4 + (j-1)/2 for odd j. b: uint8 array, last axis a
+    multiple of 4."""
+    w = np.ascontiguousarray(b).view("<u4")
+    out = np.zeros_like(w)
+    for j in range(8):
+        code = (w >> np.uint32(4 * j)) & np.uint32(0xF)
+        dst = j // 2 if j % 2 == 0 else 4 + (j - 1) // 2
+        out |= code << np.uint32(4 * dst)
+    return out.view(np.uint8).reshape(b.shape)
+
+
 def tiled_codes(wq, kind, inter):
     """The tiled code layout written out from its definition in the C header:
-    tiled[e][b][g][i][l] = plain[e][row(16*(8b+i), l%16)][64g + 16(l//16) : +16].
-    kind 0 (W13_SWIGLU) pairs gate row 8t+n with up row I+8t+n in tile t."""
+    tiled[e][b][g][i][l] = shuffle(plain[e][row(16*(8b+i), l%16)][64g + 16(l//16) : +16]),
+    each 4-byte word shuffled. kind 0 (W13_SWIGLU) pairs gate row 8t+n with
+    up row I+8t+n in tile t."""
     wq = np.asarray(wq, np.uint8)
     E, N, K2 = wq.shape
     G = (2 * K2) // 128
@@ -74,4 +89,4 @@ def tiled_codes(wq, kind, inter):
                 for g in range(G):
                     for kq in range(4):
                         out[:, b, g, i, 16 * kq + n, :] = wq[:, row, 64 * g + 16 * kq: 64 * g + 16 * kq + 16]
-    return out.reshape(E, N, K2)
+    return shuffle_words(out).reshape(E, N, K2)

@@ -127,6 +127,38 @@ def test_swiglu_and_down_vs_oracle(wl, T, tiled):
     _close_bf16(y[:R], y_ref[:R], "y")
 
 
+@pytest.mark.parametrize("wl,T,n", [("qwen3_prefill", 256, None), ("qwen3_prefill", 2048, 96), ("tiny", 40, None)])
+def test_tile_kernel_vs_oracle(wl, T, n, monkeypatch):
+    # the prefill tile kernel forced (many rows per expert: chunks of 64 rows,
+    # ragged last chunks, the per-item -136 correction); sampled rows at 2048
+    from w4a16_grouped_gemm_amd import ops
+    monkeypatch.setenv("MOE_GEMM_MODE", "2")
+    say(f"gemm tile kernel {wl} T={T}")
+    inp = make_layer_inputs(wl, T)
+    k = inp.workload.top_k
+    ids, _ = oracle.route(inp.logits, k)
+    _, offsets, perm, _ = oracle.permute(ids, inp.workload.num_local_experts, 0)
+    R = int(offsets[-1])
+    sel = None
+    rows = np.arange(R)
+    if n is not None:
+        rows = np.unique(np.linspace(0, R - 1, n).astype(int))
+        sel = np.zeros(T * k, np.uint8)
+        sel[rows] = 1
+    h_ref = oracle.grouped_gemm(oracle.W13_SWIGLU, inp.x, offsets, inp.w13_q, inp.s13, rows=T * k,
+                                a_row_index=perm, top_k=k, row_sel=sel)
+    h = _gpu_gemm(ops.W13_SWIGLU, inp.x, offsets, inp.w13_q, inp.s13, T=T, k=k, a_row_index=perm,
+                  out_f32=False, tiled=True)
+    _close_bf16(h[rows], h_ref[rows], "h")
+    # down projection on bf16 activations drawn like h (the oracle's full h is not
+    # computed when rows are sampled)
+    rng = np.random.default_rng(T)
+    a2 = bf16_bits((rng.standard_normal((T * k, inp.workload.inter)) * 0.05).astype(np.float32))
+    y_ref = oracle.grouped_gemm(oracle.W2, a2, offsets, inp.w2_q, inp.s2, rows=T * k, row_sel=sel)
+    y = _gpu_gemm(ops.W2, a2, offsets, inp.w2_q, inp.s2, T=T, k=k, out_f32=False, tiled=True)
+    _close_bf16(y[rows], y_ref[rows], "y")
+
+
 @pytest.mark.parametrize("kind", [0, 1, 2])
 @pytest.mark.parametrize("wl", ["tiny", "qwen3_decode"])
 def test_pack_matches_layout_definition(kind, wl):
@@ -153,6 +185,7 @@ VARIANTS = [
     {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "4", "MOE_GEMM_NSUB": "2", "MOE_GEMM_KSEG": "4", "MOE_GEMM_RING": "2"},
     {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "1", "MOE_GEMM_NSUB": "1", "MOE_GEMM_KSEG": "8", "MOE_GEMM_RING": "4"},
     {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "1", "MOE_GEMM_NSUB": "2", "MOE_GEMM_KSEG": "4", "MOE_GEMM_RING": "4"},
+    {"MOE_GEMM_MODE": "2"},            # tile kernel (tiled codes, K <= 2048; plain codes fall back)
 ]
 
 

@@ -21,12 +21,15 @@
 //    expert, 32-bit lane offsets, group offsets folded into the instruction),
 //    16 bytes per lane per group and 16-row tile (= 32 int4 codes of one row).
 //    A lane's 32 codes feed 4 MFMAs.
-//  * Unpack: ((w >> 4j) & 0x000F000F) ^ 0x43084308 turns two nibbles into the
-//    bf16 values 128 + (q + 8) -- exact -- in one v_bitop3_b32 (plus a shift
-//    shared by the 8 codes of the dword). The K order inside each dword comes
-//    out as (0,4,1,5,2,6,3,7); activation fragments are permuted the same way
-//    when they are staged (a common K permutation leaves the dot product
-//    unchanged).
+//  * Unpack: ((w >> 4j) & 0x000F000F) ^ 0x43084308 turns nibbles j and j+4
+//    into the bf16 values 128 + (q + 8) -- exact -- in one v_bitop3_b32 (plus
+//    a shift shared by the 8 codes of the dword). With plain codes the K
+//    order inside each dword comes out as (0,4,1,5,2,6,3,7) and activation
+//    fragments are permuted the same way when they are staged (a common K
+//    permutation leaves the dot product unchanged; the matrix unit's result
+//    does not depend on the order of a lane's 8 K values). The tiled layout
+//    stores each word's codes pre-shuffled so they unpack in column order,
+//    and activations are then used as they lie in memory.
 //  * The +136 offset is removed inside the matrix unit: per 16-token subtile
 //    and group a chain of MFMAs against a constant -136 operand gives
 //    -136 * sum(x); every weight tile's chain starts from it, so the chain
@@ -117,7 +120,8 @@ __device__ __forceinline__ uint32_t bload_scale(__amdgpu_buffer_rsrc_t r, uint32
     return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
 
-// Two nibbles per 16-bit half -> bf16 pair (128 + (q+8)); K order (0,4,1,5,..).
+// Nibbles j and j+4 -> bf16 pair j (128 + (q+8)): K order (0,4,1,5,..) for
+// plain codes, column order for tiled ones.
 __device__ __forceinline__ bf16x8 unpack8(uint32_t w)
 {
     u32x4 o;
@@ -128,7 +132,8 @@ __device__ __forceinline__ bf16x8 unpack8(uint32_t w)
     return __builtin_bit_cast(bf16x8, o);
 }
 
-// Eight consecutive bf16 activations -> the same (0,4,1,5,2,6,3,7) order.
+// Eight consecutive bf16 activations -> the (0,4,1,5,2,6,3,7) order of
+// plain codes.
 __device__ __forceinline__ u32x4 permute_act(u32x4 d)
 {
     u32x4 o;
@@ -451,7 +456,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
             for (int j = 0; j < KSEG; ++j)
 #pragma unroll
                 for (int sb = 0; sb < NSUB; ++sb)
-                    dst[(j * NSUB + sb) * 256 + st_idx] = permute_act(xr[j][sb]);
+                    dst[(j * NSUB + sb) * 256 + st_idx] = p.w_tiled ? xr[j][sb] : permute_act(xr[j][sb]);
         };
         auto load_w = [&](int g, int b) {
             const uint32_t oor = g < G ? 0u : kOutOfRange;
@@ -662,7 +667,7 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
                 u32x4 a[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    a[i] = permute_act(xa[j][i]);
+                    a[i] = p.w_tiled ? xa[j][i] : permute_act(xa[j][i]);
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -693,6 +698,392 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
             store_tile<KIND>(p, sum, tile, row0, kq * 4, nvalid, n16, c_rows);
         }
         __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gemm_tile_kernel: many rows per expert (prefill). One workgroup of 8 waves
+// per CU owns an item = (chunk of up to 64 rows of one expert, block of 8 x 4
+// sixteen-row tiles); wave w computes all four 16-token subtiles of its 4
+// tiles, so each unpacked code fragment feeds up to 4 MFMAs.
+//  * Both operands reach LDS through the buffer unit's LDS-DMA (no
+//    registers, no staging instructions), three 128-wide groups deep: the
+//    activations of a group (64 rows x 256 bytes, shared by the 8 waves) and
+//    each wave's own codes (4 tiles x 1 KiB). With two groups in flight the
+//    latency of a code fetch that misses L2 stays hidden. A group's copies
+//    are waited for with an explicit vmcnt (every group issues the same 6
+//    copies, so the count is a constant) and a bare s_barrier (a
+//    __syncthreads fence would wait for every copy in flight).
+//  * Rows past the chunk are read out of range (zeros).
+//  * Scales: each lane loads the scales of groups 4kq .. 4kq+3 of its row
+//    once per item; a group's scale is fetched from the owning lane with
+//    ds_bpermute.
+//  * The +136 offset is removed once per item instead of once per group and
+//    tile: per group, waves w and w+4 add 136 * sum(x) of subtile w's two
+//    halves of K to column g of one MFMA tile (operand B one-hot on column
+//    g), and after the last group one MFMA per (subtile, tile) adds
+//    sum_g s[n][g] * (-136 * sum_g x), each sum split into two bf16 terms
+//    (hi + lo, 16 significant bits). Needs G <= 16 (one column per group).
+//  * Tiled codes only: they unpack in column order, matching the
+//    activations as they lie in memory.
+// ---------------------------------------------------------------------------
+constexpr int kTileWaves = 8;
+constexpr int kTileStages = 3;
+constexpr int kTileActBytes = 16 * 64 * 16;           // one group: 16 copies x 64 lanes x 16 bytes
+constexpr int kTileCodeBytes = kTileWaves * 4 * 1024; // one group: 8 waves x 4 tiles x 1 KiB
+constexpr int kTileSxBytes = kTileWaves * 16 * 16 * 4;
+
+// fp32 pair -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32; fp32
+// denormals are kept, so this is the IEEE rounding for every finite value)
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), b2));
+}
+
+constexpr uint32_t vmcnt_imm(int n)                   // s_waitcnt vmcnt(n), other counters untouched
+{
+    return (uint32_t)((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_tile_kernel(GemmArgs p)
+{
+    constexpr int TPW = 4;                              // tiles per wave
+    constexpr int NS = 4;                               // 16-token subtiles per item
+    constexpr int CS = 16 * NS;
+    constexpr int BT = kTileWaves * TPW;                // tiles per block
+    constexpr int NCOPY = 2 + TPW;                      // copies a wave issues per group
+    extern __shared__ __align__(16) unsigned char s_dyn[];
+    u32x4 *s_a = reinterpret_cast<u32x4 *>(s_dyn);                                  // [stage][copy][lane]
+    u32x4 *s_w = reinterpret_cast<u32x4 *>(s_dyn + kTileStages * kTileActBytes);   // [stage][wave][tile][lane]
+    float *s_sx = reinterpret_cast<float *>(s_dyn + kTileStages * (kTileActBytes + kTileCodeBytes));
+    const int E = p.num_experts;
+    int *s_prefix = reinterpret_cast<int *>(s_dyn + kTileStages * (kTileActBytes + kTileCodeBytes) + kTileSxBytes);
+    int *s_off = s_prefix + (E + 1);
+    int *s_wtot = s_off + (E + 1);
+    int *s_crow = s_wtot + kTileWaves;                 // output row of each of the item's 64 rows
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);                // scalar: wave-dependent choices are branches
+    const int n16 = lane & 15;
+    const int kq = lane >> 4;
+    build_chunk_prefix<kTileWaves * 64>(p.offsets, p.dense_rows, E, CS, s_prefix, s_wtot, s_off);
+
+    const int ntiles = p.N >> 4;
+    const int nblocks = ntiles / BT;
+    const int total_items = s_prefix[E] * nblocks;
+    const int G = p.K / kGroup;
+    const uint32_t row_bytes = (uint32_t)(p.K >> 1);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c_row_index, p.c_row_bytes);
+    typedef __attribute__((address_space(3))) unsigned char lds_byte;
+
+    // epilogue geometry: a wave's bf16 results (64 rows x OCOLS columns)
+    // pass through its part of the stage buffers; each store instruction
+    // then writes whole row runs of OCOLS * 2 bytes (LPR lanes of 16 bytes
+    // per row, RPP rows per pass)
+    constexpr bool SWI = KIND == MOE_GEMM_W13_SWIGLU;
+    constexpr int COLS = SWI ? 8 : 16;                  // output columns per tile
+    constexpr int OCOLS = TPW * COLS;
+    constexpr int LPR = OCOLS * 2 / 16;
+    constexpr int RPP = 64 / LPR;
+    static_assert(kTileWaves * CS * OCOLS * 2 <= kTileStages * (kTileActBytes + kTileCodeBytes),
+                  "epilogue fits the stage buffers");
+
+    const int nx = (int)gridDim.x >= kXcds ? kXcds : 1;
+    const int xcd = blockIdx.x % nx;
+    const int i_end = (int)((long long)total_items * (xcd + 1) / nx);
+    for (int item = (int)((long long)total_items * xcd / nx) + blockIdx.x / nx; item < i_end;
+         item += gridDim.x / nx) {
+        const int chunk = item / nblocks;
+        const int block = item - chunk * nblocks;
+        const int e = uniform(chunk_expert(s_prefix, E, chunk));
+        const int row0 = uniform(s_off[e] + (chunk - s_prefix[e]) * CS);
+        const int nvalid = uniform(min(CS, s_off[e + 1] - row0));
+        const int nsub = (nvalid + 15) >> 4;
+        const int tile0 = block * BT + wave * TPW;
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(expert_codes(p, e, (uint32_t)p.N * row_bytes), (uint32_t)p.N * row_bytes);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(expert_scales(p, e, (uint32_t)p.N * G), (uint32_t)p.N * G * 2);
+
+        // per item, before any copy (so no copy wait counts them): this
+        // lane's scales of groups 4kq .. 4kq+3, the item's output rows and
+        // this lane's activation row
+        uint32_t voff_w[TPW];
+        u32x2 csc[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const uint32_t row = (uint32_t)tile_row<KIND>(p, tile0 + t, n16);
+            voff_w[t] = code_offset(p, tile0 + t, row, G, row_bytes, lane);
+            const uint32_t vs = row * (uint32_t)G * 2 + kq * 8;
+            csc[t].x = __builtin_amdgcn_raw_buffer_load_b32(rs, vs, 0, 0);
+            csc[t].y = __builtin_amdgcn_raw_buffer_load_b32(rs, vs + 4, 0, 0);
+        }
+        if (wave == 0)                                   // read by the epilogue, after the group barriers
+            s_crow[lane] = p.c_row_index ? (int)__builtin_amdgcn_raw_buffer_load_b32(
+                                               rc, (uint32_t)(row0 + min(lane, nvalid - 1)) * 4u, 0, 0)
+                                         : row0 + lane;
+        // Activation copy q = 2 wave + j (j < 2) is MFMA fragment (subtile
+        // q / 4, step q % 4) of the group: lane (n16, kq) brings the 16 bytes
+        // it will read, chunk 4 kq + q % 4 of token 16 (q / 4) + n16 (MFMA
+        // step i of lane (n16, kq) multiplies K = 32 kq + 8 i .. +8 of the
+        // group: a lane's 16 code bytes hold K = 32 kq .. +32, one word per
+        // step). Both copies of a wave read rows of the same 16 tokens.
+        uint32_t voff_a;
+        {
+            const int m = 16 * (wave >> 1) + n16;
+            const int r = row0 + min(m, nvalid - 1);          // always a valid row: no branch around the load
+            const uint32_t src = p.a_row_index ? (uint32_t)(p.a_row_index[r] / p.top_k) : (uint32_t)r;
+            voff_a = (m < nvalid) ? src * (uint32_t)p.K * 2 + (uint32_t)kq * 64 : kOutOfRange;
+        }
+
+        floatx4 tot[TPW][NS];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int sb = 0; sb < NS; ++sb)
+                tot[t][sb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        floatx4 sxacc = {0.f, 0.f, 0.f, 0.f};
+
+        // group g -> stage st: 2 activation copies, and this wave's 4 code
+        // copies (issued separately: the codes sit in the wave's own part of
+        // the stage, which it refills as soon as it has read it). Lane l's 16
+        // bytes land at the LDS pointer + 16 l (the instruction's immediate
+        // offset would move the LDS side too; it stays 0, and the step's
+        // 16-byte column offset is a scalar offset).
+        auto copy_act = [&](int g, int st) {
+            const uint32_t soff = (uint32_t)g * (kGroup * 2) + (uint32_t)(wave & 1) * 32;
+            lds_byte *da = (lds_byte *)(s_a + (st * 16 + 2 * wave) * 64);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, da + j * 1024, 16, voff_a, soff + j * 16, 0, 0);
+        };
+        auto copy_codes = [&](int g, int st) {
+            lds_byte *dw = (lds_byte *)(s_w + ((st * kTileWaves + wave) * TPW) * 64);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dw + t * 1024, 16, voff_w[t], (uint32_t)g * 8192u, 0, 0);
+        };
+        // The group pipeline, NSV valid subtiles (a compile-time count: the
+        // MFMA chains of a group are one branch-free block). Iteration g:
+        //   wait for this wave's activation reads of group g and its copies
+        //   of group g + 1 (only group g + 2's copies, if any, were issued
+        //   after them); barrier (every wave has group g's activations in
+        //   registers, so their part of stage g % 3 is free, and every copy
+        //   of group g + 1 has landed); start group g + 3's activation
+        //   copies; compute group g, reading this wave's codes of stage g % 3;
+        //   refill that part with group g + 3's codes; read group g + 1's
+        //   activations.
+        // Waves read right after their own compute, not all at once after a
+        // barrier, so the LDS reads of the 8 waves spread out.
+        auto groups = [&](auto nsc) {
+            constexpr int NSV = decltype(nsc)::value;
+            u32x4 a[NSV][4];
+            auto read = [&](int st) {
+                const u32x4 *src = s_a + st * 16 * 64 + lane;
+#pragma unroll
+                for (int sb = 0; sb < NSV; ++sb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        a[sb][i] = src[(4 * sb + i) * 64];
+            };
+            auto compute = [&](int g, int st) {
+                // 136 * sum(x) of subtile wave % 4, steps 2 (wave / 4) .. +1, into column g
+                const uint32_t oh = n16 == g ? 0x43084308u : 0u;
+                const bf16x8 ohv = __builtin_bit_cast(bf16x8, u32x4{oh, oh, oh, oh});
+#pragma unroll
+                for (int w = 0; w < NSV; ++w) {
+                    if ((wave & 3) == w) {
+                        if (wave < 4) {
+                            sxacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[w][0]), ohv, sxacc, 0, 0, 0);
+                            sxacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[w][1]), ohv, sxacc, 0, 0, 0);
+                        } else {
+                            sxacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[w][2]), ohv, sxacc, 0, 0, 0);
+                            sxacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[w][3]), ohv, sxacc, 0, 0, 0);
+                        }
+                    }
+                }
+                const u32x4 *wsrc = s_w + ((st * kTileWaves + wave) * TPW) * 64 + lane;
+                const int src_lane = 4 * (n16 + 16 * (g >> 2));  // lane holding this row's scale of group g
+                // tile t + 1's codes and scale are read while tile t computes
+                u32x4 w_next = wsrc[0];
+                uint32_t sd_next = __builtin_amdgcn_ds_bpermute(src_lane, (int)((g & 2) ? csc[0].y : csc[0].x));
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    const u32x4 w4 = w_next;
+                    const uint32_t sd = sd_next;
+                    if (t + 1 < TPW) {
+                        w_next = wsrc[(t + 1) * 64];
+                        sd_next = __builtin_amdgcn_ds_bpermute(src_lane, (int)((g & 2) ? csc[t + 1].y : csc[t + 1].x));
+                    }
+                    const float sc = __uint_as_float((g & 1) ? (sd & 0xFFFF0000u) : (sd << 16));
+                    const bf16x8 q[4] = {unpack8(w4.x), unpack8(w4.y), unpack8(w4.z), unpack8(w4.w)};
+                    // steps outer, subtiles inner: the NSV chains interleave, so
+                    // dependent MFMAs are NSV issues apart
+                    floatx4 acc[NSV];
+#pragma unroll
+                    for (int sb = 0; sb < NSV; ++sb)
+                        acc[sb] = mfma(a[sb][0], q[0], floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 1; i < 4; ++i)
+#pragma unroll
+                        for (int sb = 0; sb < NSV; ++sb)
+                            acc[sb] = mfma(a[sb][i], q[i], acc[sb]);
+#pragma unroll
+                    for (int sb = 0; sb < NSV; ++sb) {
+                        tot[t][sb].x = __builtin_fmaf(sc, acc[sb].x, tot[t][sb].x);
+                        tot[t][sb].y = __builtin_fmaf(sc, acc[sb].y, tot[t][sb].y);
+                        tot[t][sb].z = __builtin_fmaf(sc, acc[sb].z, tot[t][sb].z);
+                        tot[t][sb].w = __builtin_fmaf(sc, acc[sb].w, tot[t][sb].w);
+                    }
+                }
+            };
+            // barrier with every LDS read of this wave complete and only
+            // `after` groups' copies of this wave still in flight (compile-
+            // time counts; sched_barrier(0) keeps every load on its side)
+            auto meet = [&](int after) {
+                constexpr uint32_t W12 = vmcnt_imm(2 * NCOPY) & 0xF0FFu, W6 = vmcnt_imm(NCOPY) & 0xF0FFu,
+                                   W0 = vmcnt_imm(0) & 0xF0FFu;   // lgkmcnt(0) as well
+                __builtin_amdgcn_sched_barrier(0);
+                if (after >= 2)
+                    __builtin_amdgcn_s_waitcnt(W12);
+                else if (after == 1)
+                    __builtin_amdgcn_s_waitcnt(W6);
+                else
+                    __builtin_amdgcn_s_waitcnt(W0);
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                __builtin_amdgcn_s_barrier();
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                __builtin_amdgcn_sched_barrier(0);
+            };
+
+            // prologue: groups 0, 1, 2 are being copied (activations, then codes)
+            meet(min(G - 1, 2));                     // group 0 landed
+            read(0);
+            int st = 0;
+            for (int g = 0; g < G; ++g) {
+                meet(g + 2 < G ? 1 : 0);             // activation reads of g done, group g + 1 landed
+                if (g + 3 < G)
+                    copy_act(g + 3, st);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(g, st);
+                __builtin_amdgcn_sched_barrier(0);  // this wave's codes of stage st have been read
+                if (g + 3 < G)
+                    copy_codes(g + 3, st);
+                __builtin_amdgcn_sched_barrier(0);
+                st = st == 2 ? 0 : st + 1;
+                if (g + 1 < G)
+                    read(st);
+            }
+        };
+
+        __builtin_amdgcn_sched_barrier(0);
+        copy_act(0, 0);
+        copy_codes(0, 0);
+        copy_act(1, 1);                            // G >= 2
+        copy_codes(1, 1);
+        if (G > 2) {
+            copy_act(2, 2);
+            copy_codes(2, 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (nsub >= 4)
+            groups(std::integral_constant<int, 4>());
+        else if (nsub == 3)
+            groups(std::integral_constant<int, 3>());
+        else if (nsub == 2)
+            groups(std::integral_constant<int, 2>());
+        else
+            groups(std::integral_constant<int, 1>());
+
+        // ---- per-item correction: every copy has landed (the last group
+        // waited for all of them) and every wave is done with the stage
+        // buffers after this barrier ----
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s_sx[wave * 256 + (kq * 4 + i) * 16 + n16] = sxacc[i];
+        __syncthreads();
+        u32x4 bcorr[TPW];                                // B: s[n][4kq + j] twice, j = 0..3
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            uint32_t h[4] = {csc[t].x & 0xFFFFu, csc[t].x >> 16, csc[t].y & 0xFFFFu, csc[t].y >> 16};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                h[j] = (kq * 4 + j < G) ? h[j] * 0x10001u : 0u;
+            bcorr[t] = u32x4{h[0], h[1], h[2], h[3]};
+        }
+#pragma unroll
+        for (int sb = 0; sb < NS; ++sb) {
+            if (sb < nsub) {
+                const floatx4 v0 = *reinterpret_cast<const floatx4 *>(s_sx + sb * 256 + n16 * 16 + kq * 4);
+                const floatx4 v1 = *reinterpret_cast<const floatx4 *>(s_sx + (sb + 4) * 256 + n16 * 16 + kq * 4);
+                const float vv[4] = {v0.x + v1.x, v0.y + v1.y, v0.z + v1.z, v0.w + v1.w};
+                uint32_t d[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float nv = -vv[j];
+                    const float hi = __uint_as_float(bf16_pair(nv, 0.f) << 16);
+                    d[j] = bf16_pair(hi, nv - hi);
+                }
+                const u32x4 acorr = {d[0], d[1], d[2], d[3]};
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+                    tot[t][sb] = mfma(acorr, __builtin_bit_cast(bf16x8, bcorr[t]), tot[t][sb]);
+            }
+        }
+
+        // ---- epilogue: bf16 results pass through this wave's part of the
+        // stage buffers, then every store writes whole row runs ----
+        if (SWI || !p.c_f32) {
+            uint16_t *so = reinterpret_cast<uint16_t *>(s_dyn) + wave * (CS * OCOLS);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int sb = 0; sb < NS; ++sb) {
+                    const floatx4 v = tot[t][sb];
+                    const float r4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = sb * 16 + kq * 4 + i;
+                        if (SWI) {
+                            // lanes n16 and n16 + 8 hold the gate and the up row of
+                            // one feature: both form silu(gate) * up, bit for bit
+                            // the same value, and write it to the same place
+                            const float other = row_swap8(r4[i]);
+                            const float gate = n16 < 8 ? r4[i] : other, up = n16 < 8 ? other : r4[i];
+                            so[rr * OCOLS + t * COLS + (n16 & 7)] = (uint16_t)bf16_pair(silu_fast(gate) * up, 0.f);
+                        } else {
+                            so[rr * OCOLS + t * COLS + n16] = (uint16_t)bf16_pair(r4[i], 0.f);
+                        }
+                    }
+                }
+            __builtin_amdgcn_wave_barrier();
+            uint16_t *c = static_cast<uint16_t *>(p.c) + (size_t)tile0 * COLS;
+            const int part = lane % LPR;
+#pragma unroll
+            for (int pass = 0; pass < CS / RPP; ++pass) {
+                const int m = pass * RPP + lane / LPR;
+                if (m < nvalid) {
+                    const u32x4 d = *reinterpret_cast<const u32x4 *>(so + m * OCOLS + part * 8);
+                    *reinterpret_cast<u32x4 *>(c + (size_t)s_crow[m] * p.ldc + part * 8) = d;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int sb = 0; sb < NS; ++sb)
+                    if (sb < nsub)
+                        store_tile<KIND>(p, tot[t][sb], tile0 + t, row0, sb * 16 + kq * 4, nvalid, n16);
+        }
+        // stage buffers and sums free for the next item's copies: every LDS
+        // read above has completed (its data fed a store). A bare barrier:
+        // the stores themselves need not have landed.
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
 }
 
@@ -743,6 +1134,21 @@ hipError_t launch_stream(const GemmArgs &a, int max_rows, hipStream_t st)
     return hipGetLastError();
 }
 
+template <int KIND>
+hipError_t launch_tile(const GemmArgs &a, int max_rows, hipStream_t st)
+{
+    auto kernel = gemm_tile_kernel<KIND>;
+    const size_t lds = (size_t)kTileStages * (kTileActBytes + kTileCodeBytes) + kTileSxBytes +
+                       sizeof(int) * (2 * (a.num_experts + 1) + kTileWaves + 64);
+    const int nblocks = (a.N >> 4) / (4 * kTileWaves);
+    const long long chunks = (long long)min(a.num_experts, max_rows) + max_rows / 64;
+    long long grid = grid_for(chunks * nblocks, 1);    // one workgroup per CU (its LDS)
+    if (grid >= kXcds)
+        grid -= grid % kXcds;                          // whole XCD shares (see the streaming kernel)
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kTileWaves * 64), lds, st, a);
+    return hipGetLastError();
+}
+
 template <int KIND, int NWAVES>
 hipError_t launch_splitk(const GemmArgs &a, int max_rows, hipStream_t st)
 {
@@ -756,6 +1162,8 @@ template <int KIND>
 hipError_t launch_kind(const GemmArgs &a, int max_rows, int mode, int tpw, int nsub, int kseg, int ring,
                        hipStream_t st)
 {
+    if (mode == 2)
+        return launch_tile<KIND>(a, max_rows, st);
     if (mode == 0) {
         const int G = a.K / kGroup;
         if (G >= 24)
@@ -783,6 +1191,15 @@ hipError_t launch_kind(const GemmArgs &a, int max_rows, int mode, int tpw, int n
 }
 
 }  // namespace
+
+// Shapes the tile kernel takes: tiled codes, K/128 even (groups run in pairs)
+// and at most 16 (one correction column per group), 512-row blocks, expert
+// tables in the LDS left over.
+static bool tile_fits(const GemmLaunch &g)
+{
+    const int G = g.K / kGroup;
+    return g.w_tiled && G % 2 == 0 && G <= 16 && (g.N / 16) % (4 * kTileWaves) == 0 && g.num_experts <= 256;
+}
 
 hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
 {
@@ -850,6 +1267,12 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
         kseg = 8;
     if (tpw == 4 && nsub == 2)
         ring = 2;
+    // the tile kernel (64-row chunks, 512-row blocks, both operands through
+    // LDS-DMA) for the gate/up GEMM once experts average about 96 rows or
+    // more: 10% faster there at 128 rows per expert, slower at 64 and for the
+    // down projection (measured on MI355X, Qwen3-30B-A3B prefill shapes)
+    if (g.kind == MOE_GEMM_W13_SWIGLU && m >= 96.0 && tile_fits(g))
+        mode = 2;
     if (const char *env = getenv("MOE_GEMM_MODE"))
         mode = atoi(env);
     if (const char *env = getenv("MOE_GEMM_TPW"))
@@ -867,7 +1290,9 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
         kseg >>= 1;
     if (kseg % ring != 0 && !(kseg == 1 && ring == 2))   // instantiated ring depths
         ring = 2;
-    if (mode != 0 && (ntiles % (4 * tpw) != 0 || G % kseg != 0))
+    if (mode == 2 && !tile_fits(g))
+        mode = 1;
+    if (mode == 1 && (ntiles % (4 * tpw) != 0 || G % kseg != 0))
         mode = 0;                                         // shapes the streaming tiles do not divide
     if (g.kind == MOE_GEMM_W13_SWIGLU)
         return launch_kind<MOE_GEMM_W13_SWIGLU>(a, g.max_rows, mode, tpw, nsub, kseg, ring, st);

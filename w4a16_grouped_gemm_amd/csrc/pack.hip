@@ -5,7 +5,8 @@
 // plain row-major layout those 64 lanes touch 16 rows x 64 bytes; the tiled
 // layout stores exactly those 1 KiB contiguously, and the 8 tiles of a block
 // next to each other for each group, so a workgroup streams its weights as
-// one sequential run. FlashInfer PR #7196 analysis, section 3, likewise keeps
+// one sequential run. Inside each word the codes are reordered so that they
+// unpack in column order (activations are then used as they lie in memory). FlashInfer PR #7196 analysis, section 3, likewise keeps
 // a kernel-internal weight layout that its tests invert back to a plain one.
 #include "common.hpp"
 
@@ -13,9 +14,21 @@ namespace moe {
 
 namespace {
 
+// Nibbles of one little-endian word: even codes (columns 0,2,4,6) to nibbles
+// 0..3, odd codes (1,3,5,7) to nibbles 4..7. The GEMM's unpack pairs nibble j
+// with nibble j + 4, which are then the adjacent columns 2j and 2j + 1.
+__device__ __forceinline__ uint32_t shuffle_word(uint32_t d)
+{
+    auto squeeze = [](uint32_t x) {                   // low nibble of each byte -> 16 bits
+        x = (x | (x >> 4)) & 0x00FF00FFu;
+        return (x | (x >> 8)) & 0x0000FFFFu;
+    };
+    return squeeze(d & 0x0F0F0F0Fu) | (squeeze((d >> 4) & 0x0F0F0F0Fu) << 16);
+}
+
 // One thread per 16-byte unit of the output: unit u of expert e is
 // (((b * G + g) * 8 + i) * 64 + l), read from plain row row(16*(8b+i), l%16),
-// bytes [64g + 16(l/16), +16).
+// bytes [64g + 16(l/16), +16), each word shuffled.
 __global__ __launch_bounds__(256) void pack_kernel(int E, int N, int K, int half, int pair_rows,
                                                    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst)
 {
@@ -37,7 +50,9 @@ __global__ __launch_bounds__(256) void pack_kernel(int E, int N, int K, int half
         const int n = l & 15;
         const int row = pair_rows ? (n < 8 ? 8 * tile + n : half + 8 * tile + n - 8) : 16 * tile + n;
         const uint8_t *s = src + ((long long)e * N + row) * row_bytes + 64 * g + 16 * (l >> 4);
-        *reinterpret_cast<u32x4 *>(dst + u * 16) = *reinterpret_cast<const u32x4 *>(s);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(s);
+        *reinterpret_cast<u32x4 *>(dst + u * 16) =
+            u32x4{shuffle_word(v.x), shuffle_word(v.y), shuffle_word(v.z), shuffle_word(v.w)};
     }
 }
 
