@@ -53,8 +53,16 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int *s_wprefix = reinterpret_cast<int *>(s_mask + (size_t)E * words);   // [E][words]
     int *s_ids = s_wprefix + (size_t)E * words;                         // [S] local expert or -1
 
+    // All tokens in one bitmap chunk (the usual decode case): the per-expert
+    // counts come from the bitmaps' popcounts, so the kernel needs four
+    // barriers (ids, bitmaps, per-expert scan, wave totals) instead of a
+    // histogram pass and a chunk loop.
+    const bool one_chunk = T <= chunk_tokens && E <= kPermThreads;
     for (int e = tid; e < E; e += kPermThreads)
         s_count[e] = 0;
+    if (one_chunk)
+        for (int i = tid; i < E * words; i += kPermThreads)
+            s_mask[i] = 0u;
     if (ROUTE) {
         // 64 / TL tokens per wave and pass; a token's TL lanes form whole DPP rows
         constexpr int TPWV = 64 / TL;
@@ -97,6 +105,78 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
         const int e = ids[slot] - begin;
         return (e >= 0 && e < E) ? e : -1;
     };
+
+    if (one_chunk) {
+        // bitmaps: bit t of expert e's words <=> token t routed to local e
+        for (int t = tid; t < T; t += kPermThreads) {
+            int le[kMaxTopK];                 // all of the token's ids first
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j)
+                le[j] = local_expert((long long)t * k + min(j, k - 1));
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j)
+                if (j < k && le[j] >= 0)
+                    atomicOr(&s_mask[le[j] * words + (t >> 5)], 1u << (t & 31));
+        }
+        __syncthreads();
+        // per expert (thread e): prefix popcounts over its words, its count,
+        // and the exclusive scan of the counts across the workgroup
+        const int e = tid;
+        int cnt = 0;
+        if (e < E)
+            for (int wd = 0; wd < words; ++wd) {
+                s_wprefix[e * words + wd] = cnt;
+                cnt += __popc(s_mask[e * words + wd]);
+            }
+        int wtot;
+        const int ex = wave_exclusive_scan(cnt, wtot);
+        if ((tid & 63) == 0)
+            s_wave_tot[tid >> 6] = wtot;
+        __syncthreads();
+        int wbase = 0, R = 0;
+        for (int w = 0; w < kPermThreads / 64; ++w) {
+            const int t = s_wave_tot[w];
+            wbase += (w < (tid >> 6)) ? t : 0;
+            R += t;
+        }
+        if (e < E) {
+            offsets[e] = wbase + ex;
+            counts[e] = cnt;
+            s_cursor[e] = wbase + ex;
+        }
+        if (tid == 0)
+            offsets[E] = R;
+        for (int sh = tid; sh < num_shared; sh += kPermThreads) {
+            counts[E + sh] = T;
+            offsets[E + 1 + sh] = R + (sh + 1) * T;
+        }
+        for (long long r = tid; r < (long long)num_shared * T; r += kPermThreads)
+            perm[R + r] = (int32_t)((r % T) * k);
+        __syncthreads();
+        for (int t = tid; t < T; t += kPermThreads) {
+            int le[kMaxTopK];
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j)
+                le[j] = local_expert((long long)t * k + min(j, k - 1));
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j) {
+                if (j >= k)
+                    break;
+                const long long slot = (long long)t * k + j;
+                const int le_j = le[j];
+                int32_t row = -1;
+                if (le_j >= 0) {
+                    const uint32_t m = s_mask[le_j * words + (t >> 5)];
+                    row = s_cursor[le_j] + s_wprefix[le_j * words + (t >> 5)] + __popc(m & ((1u << (t & 31)) - 1u));
+                    perm[row] = (int32_t)slot;
+                }
+                inv_perm[slot] = row;
+            }
+        }
+        for (long long r = R + (long long)num_shared * T + tid; r < S + (long long)num_shared * T; r += kPermThreads)
+            perm[r] = -1;
+        return;
+    }
 
     // 1. histogram of local slots
     for (long long i = tid; i < S; i += kPermThreads) {
