@@ -175,7 +175,13 @@ moe_status moe_w4a16_forward_shared(const moe_shape *shape, int32_t num_shared, 
 moe_status moe_route(const moe_shape *shape, const float *logits, int32_t *topk_ids,
                      float *topk_w, void *stream);
 
-/* Workspace bytes moe_permute needs (0 if the shape is invalid). */
+/*
+ * Workspace bytes moe_permute needs: 0 for a shape it permutes in one
+ * workgroup, else int32 counts per (token range, local expert) for the
+ * parallel path over many tokens (at most 64 ranges, so at most
+ * 256 * E_loc bytes). 0 if the shape is invalid. The workspace holds no state
+ * between calls; calls that share one on a stream run in order.
+ */
 size_t moe_permute_workspace_size(const moe_shape *shape);
 
 /*
@@ -191,6 +197,8 @@ size_t moe_permute_workspace_size(const moe_shape *shape);
  *                x_perm bf16 [T*k][H], row r = x[perm[r] / k] (rows >= R
  *                untouched)
  * Bit-exact and deterministic (no atomics decide a position).
+ * workspace: device memory of moe_permute_workspace_size(shape) bytes,
+ * 4-byte aligned (NULL if that is 0); smaller -> MOE_ERR_WORKSPACE.
  */
 moe_status moe_permute(const moe_shape *shape, const int32_t *topk_ids, const uint16_t *x,
                        int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,

@@ -101,3 +101,27 @@ def test_permute_local_window_and_chunks(begin, E_loc, E_g):
     torch.cuda.synchronize()
     assert np.array_equal(gc.cpu().numpy(), c) and np.array_equal(go.cpu().numpy(), o)
     assert np.array_equal(gp.cpu().numpy(), p) and np.array_equal(ginv.cpu().numpy(), inv)
+
+
+# (T, E_g, E_loc, expert_begin, k): one workgroup over two bitmap chunks
+# (1024 experts leave 128-token chunks); just past the token count where the
+# permutation splits into ranges; ranges over a window of 1024 experts; and
+# the 64-range cap with ranges too long to stage their ids in LDS.
+RANGES = [(200, 1024, 1024, 0, 16), (513, 128, 128, 0, 8), (5000, 1024, 512, 256, 16),
+          (160000, 64, 32, 16, 16)]
+
+
+@pytest.mark.parametrize("T,E_g,E_loc,begin,k", RANGES)
+def test_permute_token_ranges(T, E_g, E_loc, begin, k):
+    import torch
+    from w4a16_grouped_gemm_amd import ops
+    say(f"permute ranges T={T} E_g={E_g} E_loc={E_loc} begin={begin} k={k}")
+    rng = np.random.default_rng(T + E_g)
+    # k distinct experts per token, skewed so some experts get far more slots
+    keys = rng.random((T, E_g)) * np.linspace(1.0, 3.0, E_g)
+    ids = np.argsort(keys, axis=1)[:, :k].astype(np.int32)
+    c, o, p, inv = oracle.permute(ids, E_loc, begin)
+    gc, go, gp, ginv, _ = ops.permute(to_dev(ids), E_loc, num_experts=E_g, expert_begin=begin)
+    torch.cuda.synchronize()
+    assert np.array_equal(gc.cpu().numpy(), c) and np.array_equal(go.cpu().numpy(), o)
+    assert np.array_equal(gp.cpu().numpy(), p) and np.array_equal(ginv.cpu().numpy(), inv)

@@ -75,6 +75,7 @@ struct Workspace {
     int32_t *inv_perm;
     uint16_t *h;
     uint16_t *y;
+    int32_t *part;    // per-range expert counts of the parallel permutation (many tokens)
     size_t bytes;
 };
 
@@ -101,6 +102,7 @@ Workspace carve(const moe_shape &sh, void *base, int nsh = 0)
     ws.inv_perm = reinterpret_cast<int32_t *>(take(Sr * 4));
     ws.h = reinterpret_cast<uint16_t *>(take(S * (size_t)sh.inter * 2));
     ws.y = reinterpret_cast<uint16_t *>(take(S * (size_t)sh.hidden * 2));
+    ws.part = reinterpret_cast<int32_t *>(take(permute_workspace_bytes(sh)));
     ws.bytes = off;
     return ws;
 }
@@ -174,7 +176,7 @@ size_t moe_permute_workspace_size(const moe_shape *shape)
 {
     if (check_shape(shape) != MOE_OK)
         return 0;
-    return 0;
+    return permute_workspace_bytes(*shape);
 }
 
 moe_status moe_route(const moe_shape *shape, const float *logits, int32_t *topk_ids, float *topk_w,
@@ -196,13 +198,18 @@ moe_status moe_permute(const moe_shape *shape, const int32_t *topk_ids, const ui
                        int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
                        uint16_t *x_perm, void *workspace, size_t workspace_bytes, void *stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
     moe_status st = check_shape(shape);
     if (st != MOE_OK)
         return st;
     if (!counts || !offsets)
         return MOE_ERR_NULL;
+    const size_t need = permute_workspace_bytes(*shape);
+    if (need && !workspace)
+        return MOE_ERR_NULL;
+    if (workspace_bytes < need)
+        return MOE_ERR_WORKSPACE;
+    if (need && !aligned(workspace, 4))
+        return MOE_ERR_ALIGN;
     if ((x == nullptr) != (x_perm == nullptr))
         return MOE_ERR_NULL;
     if (shape->num_tokens > 0 && (!topk_ids || !perm || !inv_perm))
@@ -213,7 +220,8 @@ moe_status moe_permute(const moe_shape *shape, const int32_t *topk_ids, const ui
         !aligned(inv_perm, 4))
         return MOE_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_permute(*shape, topk_ids, counts, offsets, perm, inv_perm, s);
+    hipError_t e = launch_permute(*shape, topk_ids, counts, offsets, perm, inv_perm, s, 0,
+                                  static_cast<int32_t *>(workspace));
     if (e == hipSuccess && x && shape->num_tokens > 0)
         e = launch_gather(*shape, x, perm, offsets, x_perm, s);
     return from_hip(e);
@@ -377,7 +385,7 @@ static moe_status forward_impl(const moe_shape *shape, int nsh, const uint16_t *
     } else {
         e = launch_route(sh, router_logits, ws.ids, ws.w, s);
         if (e == hipSuccess)
-            e = launch_permute(sh, ws.ids, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s, nsh);
+            e = launch_permute(sh, ws.ids, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s, nsh, ws.part);
     }
     auto with_shared = [&](GemmLaunch &g, const uint8_t *wq_sh, const uint16_t *s_sh) {
         if (nsh == 0)

@@ -86,9 +86,12 @@ struct GemmLaunch {
 
 hipError_t launch_route(const moe_shape &sh, const float *logits, int32_t *ids, float *w,
                         hipStream_t st);
+// part: workspace of permute_workspace_bytes(sh) (the per-range counts of
+// the parallel path for many tokens; NULL when that size is 0)
 hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *perm, int32_t *inv_perm, hipStream_t st,
-                          int num_shared = 0);
+                          int num_shared = 0, int32_t *part = nullptr);
+size_t permute_workspace_bytes(const moe_shape &sh);
 bool route_permute_fusable(const moe_shape &sh);
 hipError_t launch_route_permute(const moe_shape &sh, const float *logits, int32_t *ids, float *w,
                                 int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,

@@ -34,12 +34,17 @@ constexpr size_t kDynLdsMax = 144 * 1024; // dynamic LDS of one launch: bitmaps 
 // weights written out as by moe_route, local ids kept in LDS), saving the
 // separate routing launch and its round trip through memory. TL and PL are
 // the routing shape (lanes per token, logits per lane).
+// bases != NULL: the workgroup only scatters tokens [b*tpb, (b+1)*tpb) of the
+// permutation (b = blockIdx.x), its experts' first rows given by
+// bases[b*E + e] (the parallel path for many tokens; counts and offsets are
+// written by permute_scan_kernel).
 template <bool IDS_IN_LDS, bool ROUTE = false, int TL = 16, int PL = 8>
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int T, int k, int begin, int E, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm,
     int chunk_tokens, const float *__restrict__ logits = nullptr, int E_g = 0,
-    int32_t *__restrict__ ids_out = nullptr, float *__restrict__ w_out = nullptr, int num_shared = 0)
+    int32_t *__restrict__ ids_out = nullptr, float *__restrict__ w_out = nullptr, int num_shared = 0,
+    const int32_t *__restrict__ bases = nullptr, int tpb = 0)
 {
     static_assert(!ROUTE || IDS_IN_LDS, "routing in the kernel keeps the ids in LDS");
     __shared__ int s_count[kMaxExperts];
@@ -48,7 +53,11 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     extern __shared__ uint32_t s_dyn[];
     const int tid = threadIdx.x;
     const int words = chunk_tokens >> 5;
-    const long long S = (long long)T * k;
+    // token range of this workgroup: all tokens, or one range of the parallel path
+    const int t_beg = bases ? (int)blockIdx.x * tpb : 0;
+    const int t_end = bases ? min(T, t_beg + tpb) : T;
+    const long long slot0 = (long long)t_beg * k;
+    const long long S = (long long)(t_end - t_beg) * k;                 // slots of the range
     uint32_t *s_mask = s_dyn;                                           // [E][words]
     int *s_wprefix = reinterpret_cast<int *>(s_mask + (size_t)E * words);   // [E][words]
     int *s_ids = s_wprefix + (size_t)E * words;                         // [S] local expert or -1
@@ -57,7 +66,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     // counts come from the bitmaps' popcounts, so the kernel needs four
     // barriers (ids, bitmaps, per-expert scan, wave totals) instead of a
     // histogram pass and a chunk loop.
-    const bool one_chunk = T <= chunk_tokens && E <= kPermThreads;
+    const bool one_chunk = !bases && T <= chunk_tokens && E <= kPermThreads;
     for (int e = tid; e < E; e += kPermThreads)
         s_count[e] = 0;
     if (one_chunk)
@@ -88,7 +97,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
             int v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                v[u] = ids[min(base + u * kPermThreads + tid, (int)S - 1)];
+                v[u] = ids[slot0 + min(base + u * kPermThreads + tid, (int)S - 1)];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int i = base + u * kPermThreads + tid;
@@ -99,9 +108,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
         }
     }
     __syncthreads();
-    auto local_expert = [&](long long slot) -> int {
+    auto local_expert = [&](long long slot) -> int {      // slot: global index t*k + j
         if (IDS_IN_LDS)
-            return s_ids[slot];
+            return s_ids[slot - slot0];
         const int e = ids[slot] - begin;
         return (e >= 0 && e < E) ? e : -1;
     };
@@ -178,6 +187,12 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
         return;
     }
 
+    int R = 0;
+    if (bases) {
+        for (int e = tid; e < E; e += kPermThreads)
+            s_cursor[e] = bases[(size_t)blockIdx.x * E + e];
+        __syncthreads();
+    } else {
     // 1. histogram of local slots
     for (long long i = tid; i < S; i += kPermThreads) {
         const int e = local_expert(i);
@@ -214,7 +229,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     }
     if (tid == 0)
         offsets[E] = carry;
-    const int R = carry;
+    R = carry;
     // shared experts (layer path only): expert E + s holds every token, row
     // R + s*T + t, whose perm entry t*k makes the GEMM read token t
     for (int sh = tid; sh < num_shared; sh += kPermThreads) {
@@ -223,13 +238,14 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     }
     for (long long r = tid; r < (long long)num_shared * T; r += kPermThreads)
         perm[R + r] = (int32_t)((r % T) * k);
+    }
 
     // 3. stable scatter, chunk by chunk of tokens
-    for (int t0 = 0; t0 < T; t0 += chunk_tokens) {
+    for (int t0 = t_beg; t0 < t_end; t0 += chunk_tokens) {
         for (int i = tid; i < E * words; i += kPermThreads)
             s_mask[i] = 0u;
         __syncthreads();
-        const int nt = min(chunk_tokens, T - t0);
+        const int nt = min(chunk_tokens, t_end - t0);
         for (int tl = tid; tl < nt; tl += kPermThreads) {
             const int t = t0 + tl;
             int le[kMaxTopK];                 // all of the token's ids first: one round trip
@@ -286,6 +302,98 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
         __syncthreads();
     }
     // rows past the routed and shared rows hold no slot
+    if (!bases)
+        for (long long r = R + (long long)num_shared * T + tid; r < S + (long long)num_shared * T; r += kPermThreads)
+            perm[r] = -1;
+}
+
+// Parallel path, step 1: expert histogram of each workgroup's token range
+// (tpb tokens) -> part[b][e].
+__global__ __launch_bounds__(256) void permute_hist_kernel(int T, int k, int begin, int E, int tpb,
+                                                           const int32_t *__restrict__ ids,
+                                                           int32_t *__restrict__ part)
+{
+    __shared__ int s_cnt[kMaxExperts];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 256)
+        s_cnt[e] = 0;
+    __syncthreads();
+    const long long s0 = (long long)blockIdx.x * tpb * k;
+    const long long s1 = min((long long)T, (long long)(blockIdx.x + 1) * tpb) * k;
+    for (long long i = s0 + tid; i < s1; i += 256) {
+        const int e = ids[i] - begin;
+        if (e >= 0 && e < E)
+            atomicAdd(&s_cnt[e], 1);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += 256)
+        part[(size_t)blockIdx.x * E + e] = s_cnt[e];
+}
+
+// Parallel path, step 2 (one workgroup, thread e per expert): counts,
+// offsets (exclusive scan over experts), and part[b][e] replaced by the first
+// row of expert e's slots in range b (offsets[e] + the slots of earlier
+// ranges); the shared segments and the -1 rows as in permute_kernel.
+__global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(int T, int k, int E, int B,
+                                                                    int32_t *__restrict__ part,
+                                                                    int32_t *__restrict__ counts,
+                                                                    int32_t *__restrict__ offsets,
+                                                                    int32_t *__restrict__ perm, int num_shared)
+{
+    __shared__ int s_wave_tot[kPermThreads / 64];
+    const int tid = threadIdx.x;
+    const int e = tid;
+    const int ec = min(e, E - 1);                      // clamped: loads never sit under a branch
+    int cnt = 0;
+    for (int b0 = 0; b0 < B; b0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            v[j] = part[(size_t)min(b0 + j, B - 1) * E + ec];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            cnt += (b0 + j < B) ? v[j] : 0;
+    }
+    if (e >= E)
+        cnt = 0;
+    int wtot;
+    const int ex = wave_exclusive_scan(cnt, wtot);
+    if ((tid & 63) == 0)
+        s_wave_tot[tid >> 6] = wtot;
+    __syncthreads();
+    int wbase = 0, R = 0;
+    for (int w = 0; w < kPermThreads / 64; ++w) {
+        const int t = s_wave_tot[w];
+        wbase += (w < (tid >> 6)) ? t : 0;
+        R += t;
+    }
+    const int off = wbase + ex;
+    if (e < E) {
+        counts[e] = cnt;
+        offsets[e] = off;
+        int run = off;
+        for (int b0 = 0; b0 < B; b0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v[j] = part[(size_t)min(b0 + j, B - 1) * E + e];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (b0 + j < B) {
+                    part[(size_t)(b0 + j) * E + e] = run;
+                    run += v[j];
+                }
+        }
+    }
+    if (tid == 0)
+        offsets[E] = R;
+    for (int sh = tid; sh < num_shared; sh += kPermThreads) {
+        counts[E + sh] = T;
+        offsets[E + 1 + sh] = R + (sh + 1) * T;
+    }
+    const long long S = (long long)T * k;
+    for (long long r = tid; r < (long long)num_shared * T; r += kPermThreads)
+        perm[R + r] = (int32_t)((r % T) * k);
     for (long long r = R + (long long)num_shared * T + tid; r < S + (long long)num_shared * T; r += kPermThreads)
         perm[r] = -1;
 }
@@ -323,31 +431,71 @@ static int chunk_tokens_for(int E)
     return c;
 }
 
-hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *counts,
-                          int32_t *offsets, int32_t *perm, int32_t *inv_perm, hipStream_t st, int num_shared)
+// Past this many tokens (MOE_PERMUTE_PARALLEL_MIN_T overrides) the
+// permutation runs over nb token ranges in three launches (histogram, scan,
+// scatter) instead of one workgroup; at most 64 ranges, so the scan reads
+// few partial counts per expert.
+static int parallel_ranges(const moe_shape &sh)
 {
+    static const int min_t = [] {
+        const char *env = getenv("MOE_PERMUTE_PARALLEL_MIN_T");
+        return env ? atoi(env) : 512;
+    }();
+    const int T = sh.num_tokens;
+    if (T <= min_t || T < 2)
+        return 0;
+    return min(64, (T + 127) / 128);
+}
+
+size_t permute_workspace_bytes(const moe_shape &sh)
+{
+    return (size_t)parallel_ranges(sh) * sh.num_local_experts * sizeof(int32_t);
+}
+
+template <typename K>
+static void allow_dyn_lds(K kernel)
+{
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kDynLdsMax);
+}
+
+hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *counts,
+                          int32_t *offsets, int32_t *perm, int32_t *inv_perm, hipStream_t st, int num_shared,
+                          int32_t *part)
+{
+    static std::once_flag once;
+    std::call_once(once, [] {
+        allow_dyn_lds(permute_kernel<true>);
+        allow_dyn_lds(permute_kernel<false>);
+    });
     const int E = sh.num_local_experts;
+    const int T = sh.num_tokens;
+    const int nb = parallel_ranges(sh);
+    const int tpb = nb ? (T + nb - 1) / nb : T;        // tokens per workgroup
     int chunk = chunk_tokens_for(E);
-    while (chunk > 32 && chunk / 2 >= sh.num_tokens)      // no wider than the token count needs
+    while (chunk > 32 && chunk / 2 >= tpb)              // no wider than the token count needs
         chunk >>= 1;
     const size_t lds = (size_t)E * (chunk / 32) * 8;
-    const long long S = (long long)sh.num_tokens * sh.top_k;
-    if (lds + (size_t)S * 4 <= kDynLdsMax) {
-        const size_t dyn = lds + (size_t)S * 4;
-        if (dyn > 64 * 1024) {
-            static std::once_flag once;
-            std::call_once(once, [] {
-                (void)hipFuncSetAttribute(reinterpret_cast<const void *>(permute_kernel<true>),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDynLdsMax);
-            });
-        }
-        hipLaunchKernelGGL(permute_kernel<true>, dim3(1), dim3(kPermThreads), dyn, st,
-                           sh.num_tokens, sh.top_k, sh.expert_begin, E, ids, counts, offsets, perm, inv_perm,
-                           chunk, nullptr, 0, nullptr, nullptr, num_shared);
-    } else
-        hipLaunchKernelGGL(permute_kernel<false>, dim3(1), dim3(kPermThreads), lds, st, sh.num_tokens,
-                           sh.top_k, sh.expert_begin, E, ids, counts, offsets, perm, inv_perm, chunk, nullptr, 0,
-                           nullptr, nullptr, num_shared);
+    const long long S = (long long)tpb * sh.top_k;
+    const bool ids_in_lds = lds + (size_t)S * 4 <= kDynLdsMax;
+    const size_t dyn = ids_in_lds ? lds + (size_t)S * 4 : lds;
+    if (nb) {
+        if (!part)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(256), 0, st, T, sh.top_k, sh.expert_begin, E, tpb,
+                           ids, part);
+        hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kPermThreads), 0, st, T, sh.top_k, E, nb, part, counts,
+                           offsets, perm, num_shared);
+    }
+    const dim3 grid(nb ? nb : 1);
+    if (ids_in_lds)
+        hipLaunchKernelGGL(permute_kernel<true>, grid, dim3(kPermThreads), dyn, st, T, sh.top_k, sh.expert_begin, E,
+                           ids, counts, offsets, perm, inv_perm, chunk, nullptr, 0, nullptr, nullptr, num_shared,
+                           nb ? part : nullptr, tpb);
+    else
+        hipLaunchKernelGGL(permute_kernel<false>, grid, dim3(kPermThreads), dyn, st, T, sh.top_k, sh.expert_begin,
+                           E, ids, counts, offsets, perm, inv_perm, chunk, nullptr, 0, nullptr, nullptr, num_shared,
+                           nb ? part : nullptr, tpb);
     return hipGetLastError();
 }
 
@@ -383,7 +531,7 @@ hipError_t launch_route_permute(const moe_shape &sh, const float *logits, int32_
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDynLdsMax);
         hipLaunchKernelGGL(kernel, dim3(1), dim3(kPermThreads), dyn, st, sh.num_tokens, sh.top_k,
                            sh.expert_begin, E, nullptr, counts, offsets, perm, inv_perm, chunk, logits,
-                           sh.num_experts, ids, w, num_shared);
+                           sh.num_experts, ids, w, num_shared, nullptr, 0);
     };
     if (sh.num_experts <= 64)
         launch(permute_kernel<true, true, 16, 4>);

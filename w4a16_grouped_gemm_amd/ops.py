@@ -177,8 +177,11 @@ def permute(topk_ids: torch.Tensor, num_local_experts: int, *, num_experts: int 
     offsets = torch.empty(num_local_experts + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv_perm = torch.empty((T, k), dtype=torch.int32, device=dev)
-    _check(load_library().moe_permute(ctypes.byref(sh), _ptr(topk_ids), _ptr(x), _ptr(counts), _ptr(offsets),
-                                      _ptr(perm), _ptr(inv_perm), _ptr(x_perm), None, 0, _stream(stream)))
+    lib = load_library()
+    nws = lib.moe_permute_workspace_size(ctypes.byref(sh))
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    _check(lib.moe_permute(ctypes.byref(sh), _ptr(topk_ids), _ptr(x), _ptr(counts), _ptr(offsets),
+                           _ptr(perm), _ptr(inv_perm), _ptr(x_perm), _ptr(ws), nws, _stream(stream)))
     return counts, offsets, perm, inv_perm, x_perm
 
 
