@@ -9,7 +9,9 @@ matmul on the dequantised weights).
 - Random bf16 activations: within an error bound derived from the kernel's
   arithmetic (below), fp32 and bf16 outputs.
 - The dense entry point equals the grouped GEMM with offsets {0, M} bit for
-  bit, and the tiled code layout equals the plain one bit for bit.
+  bit, and the tiled code layout equals the plain one bit for bit through
+  the same kernel (the prefill tile kernel, with its own summation order,
+  is held to the bound instead).
 """
 import numpy as np
 import pytest
@@ -103,7 +105,7 @@ def test_dense_vs_oracle_within_bound(M, N, K):
     assert np.all(np.abs(got16 - ref) <= bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref))
 
 
-def test_dense_equals_one_expert_grouped_gemm():
+def test_dense_equals_one_expert_grouped_gemm(monkeypatch):
     import torch
     from w4a16_grouped_gemm_amd import ops
     say("dense == grouped GEMM with one expert")
@@ -115,6 +117,14 @@ def test_dense_equals_one_expert_grouped_gemm():
                                      bf16_dev(s[None]), num_tokens=M, top_k=1)
     torch.cuda.synchronize()
     assert np.array_equal(got, to_np_u16(grouped))
+    # at 300 rows tiled codes with bf16 output take the tile kernel (its own
+    # summation order): within the bound of the oracle
+    ref = _oracle(q, a, s, out_f32=True).astype(np.float64)
+    bound = _error_bound(q, a, s) + np.abs(ref) * U
+    tile = bf16_to_f64(_dense(a, wq, s, out_f32=False, tiled=True))
+    assert np.all(np.abs(tile - ref) <= bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref))
+    # through the streaming kernel the tiled layout equals the plain one bit for bit
+    monkeypatch.setenv("MOE_GEMM_MODE", "1")
     assert np.array_equal(got, _dense(a, wq, s, out_f32=False, tiled=True))
 
 

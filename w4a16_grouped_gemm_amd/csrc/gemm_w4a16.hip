@@ -796,8 +796,30 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
     const int nx = (int)gridDim.x >= kXcds ? kXcds : 1;
     const int xcd = blockIdx.x % nx;
     const int i_end = (int)((long long)total_items * (xcd + 1) / nx);
-    for (int item = (int)((long long)total_items * xcd / nx) + blockIdx.x / nx; item < i_end;
-         item += gridDim.x / nx) {
+    const int i_beg = (int)((long long)total_items * xcd / nx) + blockIdx.x / nx;
+    const int i_step = gridDim.x / nx;
+    // This lane's activation row of item `it` (the gather index, or the row
+    // itself) is loaded one item ahead: an item's first copies then wait for
+    // no load of their own, and its start costs one memory round trip, not
+    // two. The item's last group waits for every load, this one included.
+    const int m_act = 16 * (wave >> 1) + n16;
+    auto act_src = [&](int it) -> int {
+        const int ch = it / nblocks;
+        const int ee = uniform(chunk_expert(s_prefix, E, ch));
+        const int r0 = uniform(s_off[ee] + (ch - s_prefix[ee]) * CS);
+        const int r = r0 + min(m_act, uniform(min(CS, s_off[ee + 1] - r0)) - 1);   // a valid row
+        return p.a_row_index ? p.a_row_index[r] : r;
+    };
+    int src_next = 0;
+    if (i_beg < i_end)
+        src_next = act_src(i_beg);
+    {
+        constexpr uint32_t W0 = vmcnt_imm(0);
+        __builtin_amdgcn_s_waitcnt(W0);   // as at the end of every item: no load in flight at the loop head
+    }
+    for (int item = i_beg; item < i_end; item += i_step) {
+        const int src_act = src_next;
+        src_next = act_src(min(item + i_step, i_end - 1));
         const int chunk = item / nblocks;
         const int block = item - chunk * nblocks;
         const int e = uniform(chunk_expert(s_prefix, E, chunk));
@@ -821,23 +843,20 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
             csc[t].x = __builtin_amdgcn_raw_buffer_load_b32(rs, vs, 0, 0);
             csc[t].y = __builtin_amdgcn_raw_buffer_load_b32(rs, vs + 4, 0, 0);
         }
-        if (wave == 0)                                   // read by the epilogue, after the group barriers
-            s_crow[lane] = p.c_row_index ? (int)__builtin_amdgcn_raw_buffer_load_b32(
-                                               rc, (uint32_t)(row0 + min(lane, nvalid - 1)) * 4u, 0, 0)
-                                         : row0 + lane;
+        // output row of the item's row `lane` (kept in a register: it goes
+        // to LDS at the epilogue, so no wave waits for this load here). The
+        // load is always issued: with no row index its buffer holds 0 bytes
+        // and it returns 0 without touching memory.
+        const int crow = (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(row0 + min(lane, nvalid - 1)) * 4u, 0, 0) +
+                         (p.c_row_index ? 0 : row0 + lane);
         // Activation copy q = 2 wave + j (j < 2) is MFMA fragment (subtile
         // q / 4, step q % 4) of the group: lane (n16, kq) brings the 16 bytes
         // it will read, chunk 4 kq + q % 4 of token 16 (q / 4) + n16 (MFMA
         // step i of lane (n16, kq) multiplies K = 32 kq + 8 i .. +8 of the
         // group: a lane's 16 code bytes hold K = 32 kq .. +32, one word per
         // step). Both copies of a wave read rows of the same 16 tokens.
-        uint32_t voff_a;
-        {
-            const int m = 16 * (wave >> 1) + n16;
-            const int r = row0 + min(m, nvalid - 1);          // always a valid row: no branch around the load
-            const uint32_t src = p.a_row_index ? (uint32_t)(p.a_row_index[r] / p.top_k) : (uint32_t)r;
-            voff_a = (m < nvalid) ? src * (uint32_t)p.K * 2 + (uint32_t)kq * 64 : kOutOfRange;
-        }
+        const uint32_t src = p.a_row_index ? (uint32_t)(src_act / p.top_k) : (uint32_t)src_act;
+        const uint32_t voff_a = (m_act < nvalid) ? src * (uint32_t)p.K * 2 + (uint32_t)kq * 64 : kOutOfRange;
 
         floatx4 tot[TPW][NS];
 #pragma unroll
@@ -1004,6 +1023,8 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             s_sx[wave * 256 + (kq * 4 + i) * 16 + n16] = sxacc[i];
+        if (wave == 0)
+            s_crow[lane] = crow;
         __syncthreads();
         u32x4 bcorr[TPW];                                // B: s[n][4kq + j] twice, j = 0..3
 #pragma unroll
@@ -1036,7 +1057,7 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
 
         // ---- epilogue: bf16 results pass through this wave's part of the
         // stage buffers, then every store writes whole row runs ----
-        if (SWI || !p.c_f32) {
+        {
             uint16_t *so = reinterpret_cast<uint16_t *>(s_dyn) + wave * (CS * OCOLS);
 #pragma unroll
             for (int t = 0; t < TPW; ++t)
@@ -1044,39 +1065,43 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
                 for (int sb = 0; sb < NS; ++sb) {
                     const floatx4 v = tot[t][sb];
                     const float r4[4] = {v.x, v.y, v.z, v.w};
+                    if (SWI) {
+                        // lane n16 < 8 holds the gate row of feature n16 for
+                        // token rows 4 kq + 0..3, lane n16 + 8 the up row: the
+                        // gate lane forms rows 0 and 1 (it receives two up
+                        // values), the up lane rows 2 and 3 (two gate values)
+                        const bool gl = n16 < 8;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int rr = sb * 16 + kq * 4 + i;
-                        if (SWI) {
-                            // lanes n16 and n16 + 8 hold the gate and the up row of
-                            // one feature: both form silu(gate) * up, bit for bit
-                            // the same value, and write it to the same place
-                            const float other = row_swap8(r4[i]);
-                            const float gate = n16 < 8 ? r4[i] : other, up = n16 < 8 ? other : r4[i];
+                        for (int j = 0; j < 2; ++j) {
+                            const float recv = row_swap8(gl ? r4[j + 2] : r4[j]);
+                            const float gate = gl ? r4[j] : recv, up = gl ? recv : r4[j + 2];
+                            const int rr = sb * 16 + kq * 4 + (gl ? j : j + 2);
                             so[rr * OCOLS + t * COLS + (n16 & 7)] = (uint16_t)bf16_pair(silu_fast(gate) * up, 0.f);
-                        } else {
-                            so[rr * OCOLS + t * COLS + n16] = (uint16_t)bf16_pair(r4[i], 0.f);
                         }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            so[(sb * 16 + kq * 4 + i) * OCOLS + t * COLS + n16] = (uint16_t)bf16_pair(r4[i], 0.f);
                     }
                 }
             __builtin_amdgcn_wave_barrier();
             uint16_t *c = static_cast<uint16_t *>(p.c) + (size_t)tile0 * COLS;
-            const int part = lane % LPR;
+            // the lane index passes through an empty asm statement: the
+            // per-pass LDS addresses are then formed here, per item, instead
+            // of being hoisted out of the item loop (where they would hold
+            // registers for the whole loop, or spill)
+            int le = lane;
+            asm volatile("" : "+v"(le));
+            const int part = le % LPR;
+            const u32x4 *src_row = reinterpret_cast<const u32x4 *>(so + (le / LPR) * OCOLS + part * 8);
 #pragma unroll
             for (int pass = 0; pass < CS / RPP; ++pass) {
-                const int m = pass * RPP + lane / LPR;
+                const int m = pass * RPP + le / LPR;
                 if (m < nvalid) {
-                    const u32x4 d = *reinterpret_cast<const u32x4 *>(so + m * OCOLS + part * 8);
+                    const u32x4 d = src_row[pass * RPP * OCOLS / 8];
                     *reinterpret_cast<u32x4 *>(c + (size_t)s_crow[m] * p.ldc + part * 8) = d;
                 }
             }
-        } else {
-#pragma unroll
-            for (int t = 0; t < TPW; ++t)
-#pragma unroll
-                for (int sb = 0; sb < NS; ++sb)
-                    if (sb < nsub)
-                        store_tile<KIND>(p, tot[t][sb], tile0 + t, row0, sb * 16 + kq * 4, nvalid, n16);
         }
         // stage buffers and sums free for the next item's copies: every LDS
         // read above has completed (its data fed a store). A bare barrier:
@@ -1194,11 +1219,12 @@ hipError_t launch_kind(const GemmArgs &a, int max_rows, int mode, int tpw, int n
 
 // Shapes the tile kernel takes: tiled codes, K/128 even (groups run in pairs)
 // and at most 16 (one correction column per group), 512-row blocks, expert
-// tables in the LDS left over.
+// tables in the LDS left over, bf16 output.
 static bool tile_fits(const GemmLaunch &g)
 {
     const int G = g.K / kGroup;
-    return g.w_tiled && G % 2 == 0 && G <= 16 && (g.N / 16) % (4 * kTileWaves) == 0 && g.num_experts <= 256;
+    return g.w_tiled && G % 2 == 0 && G <= 16 && (g.N / 16) % (4 * kTileWaves) == 0 && g.num_experts <= 256 &&
+           (g.kind == MOE_GEMM_W13_SWIGLU || !g.c_f32);
 }
 
 hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
@@ -1268,10 +1294,10 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     if (tpw == 4 && nsub == 2)
         ring = 2;
     // the tile kernel (64-row chunks, 512-row blocks, both operands through
-    // LDS-DMA) for the gate/up GEMM once experts average about 96 rows or
-    // more: 10% faster there at 128 rows per expert, slower at 64 and for the
-    // down projection (measured on MI355X, Qwen3-30B-A3B prefill shapes)
-    if (g.kind == MOE_GEMM_W13_SWIGLU && m >= 96.0 && tile_fits(g))
+    // LDS-DMA) once experts average about 96 rows or more: faster there for
+    // both GEMMs at 128 rows per expert, slower at 64 (measured on MI355X,
+    // Qwen3-30B-A3B prefill shapes)
+    if (m >= 96.0 && tile_fits(g))
         mode = 2;
     if (const char *env = getenv("MOE_GEMM_MODE"))
         mode = atoi(env);
