@@ -81,6 +81,8 @@ struct GemmArgs {
     void *c;
     const int32_t *c_row_index;  // output row r goes to row c_row_index[r] (NULL: row r)
     uint32_t c_row_bytes;        // bytes of c_row_index (0 when NULL)
+    uint32_t a_row_bytes;        // bytes of a_row_index (0 when NULL)
+    uint32_t c_bytes;            // bytes of c the tile kernel's buffer stores reach (< 2^31)
     uint32_t a_bytes;  // bytes of `a` reachable through the buffer descriptor (< 2^31)
     int top_k;
     int num_experts;
@@ -766,10 +768,20 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
     int *s_crow = s_wtot + kTileWaves;                 // output row of each of the item's 64 rows
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
     const int wave = uniform(tid >> 6);                // scalar: wave-dependent choices are branches
-    const int n16 = lane & 15;
-    const int kq = lane >> 4;
+    // The lane index and what derives from it are re-formed at the start of
+    // every item, behind an empty asm statement: the compiler then forms the
+    // lane-dependent addresses where they are used instead of hoisting them
+    // out of the item loop, where they would hold registers throughout (and
+    // spill, each reload waiting for every load in flight).
+    int lane = tid & 63, n16 = lane & 15, kq = lane >> 4;
+    int m_act = 16 * (wave >> 1) + n16;                // this lane's activation row in an item
+    auto refresh_lane = [&]() {
+        asm volatile("" : "+v"(lane));
+        n16 = lane & 15;
+        kq = lane >> 4;
+        m_act = 16 * (wave >> 1) + n16;
+    };
     build_chunk_prefix<kTileWaves * 64>(p.offsets, p.dense_rows, E, CS, s_prefix, s_wtot, s_off);
 
     const int ntiles = p.N >> 4;
@@ -778,85 +790,175 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
     const int G = p.K / kGroup;
     const uint32_t row_bytes = (uint32_t)(p.K >> 1);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+    const __amdgpu_buffer_rsrc_t ri = make_rsrc(p.a_row_index, p.a_row_bytes);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c_row_index, p.c_row_bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.c, p.c_bytes);
     typedef __attribute__((address_space(3))) unsigned char lds_byte;
 
-    // epilogue geometry: a wave's bf16 results (64 rows x OCOLS columns)
-    // pass through its part of the stage buffers; each store instruction
-    // then writes whole row runs of OCOLS * 2 bytes (LPR lanes of 16 bytes
-    // per row, RPP rows per pass)
+    // Epilogue: a wave's bf16 results pass through its own 4 KiB of the
+    // codes of the item's last stage (64 rows x OCOLS columns, in HALVES
+    // passes), then each store writes whole row runs of OCOLS * 2 bytes (LPR
+    // lanes of 16 bytes per row, RPP rows per store).
     constexpr bool SWI = KIND == MOE_GEMM_W13_SWIGLU;
     constexpr int COLS = SWI ? 8 : 16;                  // output columns per tile
-    constexpr int OCOLS = TPW * COLS;
+    constexpr int HALVES = SWI ? 1 : 2;
+    constexpr int TH = TPW / HALVES;                    // tiles per pass
+    constexpr int OCOLS = TH * COLS;
     constexpr int LPR = OCOLS * 2 / 16;
     constexpr int RPP = 64 / LPR;
-    static_assert(kTileWaves * CS * OCOLS * 2 <= kTileStages * (kTileActBytes + kTileCodeBytes),
-                  "epilogue fits the stage buffers");
+    constexpr int NST = HALVES * (CS / RPP);            // stores per wave and item, always issued
+    static_assert(kTileWaves * CS * OCOLS * 2 == kTileCodeBytes, "a pass fills one stage's codes");
 
     const int nx = (int)gridDim.x >= kXcds ? kXcds : 1;
     const int xcd = blockIdx.x % nx;
     const int i_end = (int)((long long)total_items * (xcd + 1) / nx);
     const int i_beg = (int)((long long)total_items * xcd / nx) + blockIdx.x / nx;
     const int i_step = gridDim.x / nx;
-    // This lane's activation row of item `it` (the gather index, or the row
-    // itself) is loaded one item ahead: an item's first copies then wait for
-    // no load of their own, and its start costs one memory round trip, not
-    // two. The item's last group waits for every load, this one included.
-    const int m_act = 16 * (wave >> 1) + n16;
-    auto act_src = [&](int it) -> int {
-        const int ch = it / nblocks;
-        const int ee = uniform(chunk_expert(s_prefix, E, ch));
-        const int r0 = uniform(s_off[ee] + (ch - s_prefix[ee]) * CS);
-        const int r = r0 + min(m_act, uniform(min(CS, s_off[ee + 1] - r0)) - 1);   // a valid row
-        return p.a_row_index ? p.a_row_index[r] : r;
-    };
-    int src_next = 0;
-    if (i_beg < i_end)
-        src_next = act_src(i_beg);
-    {
-        constexpr uint32_t W0 = vmcnt_imm(0);
-        __builtin_amdgcn_s_waitcnt(W0);   // as at the end of every item: no load in flight at the loop head
-    }
-    for (int item = i_beg; item < i_end; item += i_step) {
-        const int src_act = src_next;
-        src_next = act_src(min(item + i_step, i_end - 1));
-        const int chunk = item / nblocks;
-        const int block = item - chunk * nblocks;
-        const int e = uniform(chunk_expert(s_prefix, E, chunk));
-        const int row0 = uniform(s_off[e] + (chunk - s_prefix[e]) * CS);
-        const int nvalid = uniform(min(CS, s_off[e + 1] - row0));
-        const int nsub = (nvalid + 15) >> 4;
-        const int tile0 = block * BT + wave * TPW;
-        const __amdgpu_buffer_rsrc_t rw = make_rsrc(expert_codes(p, e, (uint32_t)p.N * row_bytes), (uint32_t)p.N * row_bytes);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(expert_scales(p, e, (uint32_t)p.N * G), (uint32_t)p.N * G * 2);
 
-        // per item, before any copy (so no copy wait counts them): this
-        // lane's scales of groups 4kq .. 4kq+3, the item's output rows and
-        // this lane's activation row
-        uint32_t voff_w[TPW];
-        u32x2 csc[TPW];
+    // ---- item geometry (all uniform) ----
+    struct Geo {
+        int e, row0, nvalid, tile0;
+    };
+    auto geo = [&](int it) {
+        Geo q;
+        const int ch = it / nblocks;
+        const int block = it - ch * nblocks;
+        q.e = uniform(chunk_expert(s_prefix, E, ch));
+        q.row0 = uniform(s_off[q.e] + (ch - s_prefix[q.e]) * CS);
+        q.nvalid = uniform(min(CS, s_off[q.e + 1] - q.row0));
+        q.tile0 = block * BT + wave * TPW;
+        return q;
+    };
+    // gather index of that row (the row itself without one): one load, always
+    // issued (with no index its buffer holds 0 bytes and the load returns 0)
+    auto load_src = [&](const Geo &q) -> int {
+        const int r = q.row0 + min(m_act, q.nvalid - 1);
+        return (int)__builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)r * 4u, 0, 0) + (p.a_row_index ? 0 : r);
+    };
+    auto act_offset = [&](const Geo &q, int src, bool valid) -> uint32_t {
+        const uint32_t s = p.a_row_index ? (uint32_t)(src / p.top_k) : (uint32_t)src;
+        return (valid && m_act < q.nvalid) ? s * (uint32_t)p.K * 2 + (uint32_t)kq * 64 : kOutOfRange;
+    };
+    auto codes_rsrc = [&](const Geo &q) {
+        return make_rsrc(expert_codes(p, q.e, (uint32_t)p.N * row_bytes), (uint32_t)p.N * row_bytes);
+    };
+    // this lane's scales of groups 4kq .. 4kq+3 for each tile, and the row
+    // index entry of the item's row `lane` (0 without an index; the output
+    // row is this plus row0 + lane then): TPW + 1 loads
+    auto load_item_rows = [&](const Geo &q, bool valid, u32x2 (&sc)[TPW], int &crow) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(expert_scales(p, q.e, (uint32_t)p.N * G), (uint32_t)p.N * G * 2);
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            const uint32_t row = (uint32_t)tile_row<KIND>(p, tile0 + t, n16);
-            voff_w[t] = code_offset(p, tile0 + t, row, G, row_bytes, lane);
-            const uint32_t vs = row * (uint32_t)G * 2 + kq * 8;
-            csc[t].x = __builtin_amdgcn_raw_buffer_load_b32(rs, vs, 0, 0);
-            csc[t].y = __builtin_amdgcn_raw_buffer_load_b32(rs, vs + 4, 0, 0);
+            const uint32_t row = (uint32_t)tile_row<KIND>(p, q.tile0 + t, n16);
+            const uint32_t vs = valid ? row * (uint32_t)G * 2 + kq * 8 : kOutOfRange;
+            sc[t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, vs, 0, 0));
         }
-        // output row of the item's row `lane` (kept in a register: it goes
-        // to LDS at the epilogue, so no wave waits for this load here). The
-        // load is always issued: with no row index its buffer holds 0 bytes
-        // and it returns 0 without touching memory.
-        const int crow = (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(row0 + min(lane, nvalid - 1)) * 4u, 0, 0) +
-                         (p.c_row_index ? 0 : row0 + lane);
-        // Activation copy q = 2 wave + j (j < 2) is MFMA fragment (subtile
-        // q / 4, step q % 4) of the group: lane (n16, kq) brings the 16 bytes
-        // it will read, chunk 4 kq + q % 4 of token 16 (q / 4) + n16 (MFMA
-        // step i of lane (n16, kq) multiplies K = 32 kq + 8 i .. +8 of the
-        // group: a lane's 16 code bytes hold K = 32 kq .. +32, one word per
-        // step). Both copies of a wave read rows of the same 16 tokens.
-        const uint32_t src = p.a_row_index ? (uint32_t)(src_act / p.top_k) : (uint32_t)src_act;
-        const uint32_t voff_a = (m_act < nvalid) ? src * (uint32_t)p.K * 2 + (uint32_t)kq * 64 : kOutOfRange;
+        crow = (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(q.row0 + min(lane, q.nvalid - 1)) * 4u, 0, 0);
+    };
+
+    // Group g of an item -> stage st: 2 activation copies, and this wave's 4
+    // code copies (issued separately: the codes sit in the wave's own part of
+    // the stage, which it refills as soon as it has read it). Lane l's 16
+    // bytes land at the LDS pointer + 16 l (the instruction's immediate
+    // offset would move the LDS side too; it stays 0, and the step's 16-byte
+    // column offset is a scalar offset).
+    // Activation copy q = 2 wave + j (j < 2) is MFMA fragment (subtile q / 4,
+    // step q % 4) of the group: lane (n16, kq) brings the 16 bytes it will
+    // read, chunk 4 kq + q % 4 of token 16 (q / 4) + n16 (MFMA step i of lane
+    // (n16, kq) multiplies K = 32 kq + 8 i .. +8 of the group: a lane's 16
+    // code bytes hold K = 32 kq .. +32, one word per step).
+    auto copy_act = [&](uint32_t voff_a, int g, int st) {
+        const uint32_t soff = (uint32_t)g * (kGroup * 2) + (uint32_t)(wave & 1) * 32;
+        lds_byte *da = (lds_byte *)(s_a + (st * 16 + 2 * wave) * 64);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, da + j * 1024, 16, voff_a, soff + j * 16, 0, 0);
+    };
+    // (the tile's place in the tiled layout is a scalar offset: one lane
+    // offset register serves every copy)
+    auto copy_codes = [&](__amdgpu_buffer_rsrc_t rw, int tile0, bool valid, int g, int st) {
+        lds_byte *dw = (lds_byte *)(s_w + ((st * kTileWaves + wave) * TPW) * 64);
+        const uint32_t vo = valid ? (uint32_t)lane * 16u : kOutOfRange;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int tl = tile0 + t;
+            const uint32_t so = (uint32_t)((tl >> 3) * G * 8 + (tl & 7)) * 1024u + (uint32_t)g * 8192u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dw + t * 1024, 16, vo, so, 0, 0);
+        }
+    };
+    auto wait_barrier = [&](auto vm) {                  // s_waitcnt vmcnt(vm) lgkmcnt(0); s_barrier
+        constexpr uint32_t W = vmcnt_imm(decltype(vm)::value) & 0xF0FFu;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(W);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using I0 = std::integral_constant<int, 0>;
+
+    // Pipeline across items. The copies of groups 0 and 1 of the next item
+    // go out during this item's groups G-3 and G-2 (into the stages those
+    // free), its scales and output rows at this item's start, its group 2
+    // after this item's epilogue (whose staging used that stage). Every item
+    // issues the same loads and stores, in the same order, per wave:
+    //   [gather index two items on] [next: TPW scale loads, 1 row load]
+    //   [its group 2] [its groups 3 .. G-1] [next: group 0] [next: group 1]
+    //   [NST stores] | wait for all but the stores, barrier | ...
+    // (an item with no next item issues those copies and loads out of
+    // range), so each wait below is an exact compile-time count: before
+    // group 0, NCOPY + NST + TPW + 2 + NCOPY later loads and stores; before
+    // group 1, NST + TPW + 2 + NCOPY; later, one group's NCOPY. Each item's
+    // loads of scales, rows and gather indices are complete before the item
+    // starts, as the compiler can see.
+    u32x2 csc[TPW], csc_n[TPW];                         // scales of this item and the next
+    int crow = 0, crow_n = 0;                           // output-row entries of this item and the next
+    int src_cur = 0, src_n1 = 0;                        // gather indices of this item and the next
+    Geo q_cur{0, 0, 1, 0}, q_nxt{0, 0, 1, 0};
+    if (i_beg < i_end) {
+        q_cur = geo(i_beg);
+        q_nxt = geo(min(i_beg + i_step, i_end - 1));
+        src_cur = load_src(q_cur);
+        src_n1 = load_src(q_nxt);
+        load_item_rows(q_cur, true, csc, crow);
+        {
+            constexpr uint32_t W0 = vmcnt_imm(0);
+            __builtin_amdgcn_s_waitcnt(W0);
+        }
+        const uint32_t va = act_offset(q_cur, src_cur, true);
+        const __amdgpu_buffer_rsrc_t rw = codes_rsrc(q_cur);
+        __builtin_amdgcn_sched_barrier(0);
+        copy_act(va, 0, 0);
+        copy_codes(rw, q_cur.tile0, true, 0, 0);
+        copy_act(va, 1, 1);
+        copy_codes(rw, q_cur.tile0, true, 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NST; ++j)                   // in place of a previous item's stores
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, ro, kOutOfRange, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    int st0 = 0;                                        // stage of the item's group 0
+    for (int item = i_beg; item < i_end; item += i_step) {
+        refresh_lane();
+        const Geo q = q_cur, qn = q_nxt;                 // qn: this item again when it is the last
+        const Geo qnn = geo(min(item + 2 * i_step, i_end - 1));
+        const int nsub = (q.nvalid + 15) >> 4;
+        const __amdgpu_buffer_rsrc_t rw = codes_rsrc(q);
+        const uint32_t voff_a = act_offset(q, src_cur, true);
+        const bool has_next = item + i_step < i_end;
+        const __amdgpu_buffer_rsrc_t rwn = codes_rsrc(qn);
+        const uint32_t voff_an = act_offset(qn, src_n1, has_next);
+        const int st2 = st0 == 0 ? 2 : st0 - 1;        // stage of group 2
+        const int st_last = (st0 + G - 1) % 3;
+
+        __builtin_amdgcn_sched_barrier(0);
+        const int src_n2 = load_src(qnn);               // used two items on
+        load_item_rows(qn, has_next, csc_n, crow_n);    // used by the next item
+        __builtin_amdgcn_sched_barrier(0);
+        copy_act(voff_a, 2, st2);
+        copy_codes(rw, q.tile0, true, 2, st2);
+        __builtin_amdgcn_sched_barrier(0);
 
         floatx4 tot[TPW][NS];
 #pragma unroll
@@ -866,35 +968,15 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
                 tot[t][sb] = floatx4{0.f, 0.f, 0.f, 0.f};
         floatx4 sxacc = {0.f, 0.f, 0.f, 0.f};
 
-        // group g -> stage st: 2 activation copies, and this wave's 4 code
-        // copies (issued separately: the codes sit in the wave's own part of
-        // the stage, which it refills as soon as it has read it). Lane l's 16
-        // bytes land at the LDS pointer + 16 l (the instruction's immediate
-        // offset would move the LDS side too; it stays 0, and the step's
-        // 16-byte column offset is a scalar offset).
-        auto copy_act = [&](int g, int st) {
-            const uint32_t soff = (uint32_t)g * (kGroup * 2) + (uint32_t)(wave & 1) * 32;
-            lds_byte *da = (lds_byte *)(s_a + (st * 16 + 2 * wave) * 64);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, da + j * 1024, 16, voff_a, soff + j * 16, 0, 0);
-        };
-        auto copy_codes = [&](int g, int st) {
-            lds_byte *dw = (lds_byte *)(s_w + ((st * kTileWaves + wave) * TPW) * 64);
-#pragma unroll
-            for (int t = 0; t < TPW; ++t)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dw + t * 1024, 16, voff_w[t], (uint32_t)g * 8192u, 0, 0);
-        };
         // The group pipeline, NSV valid subtiles (a compile-time count: the
         // MFMA chains of a group are one branch-free block). Iteration g:
         //   wait for this wave's activation reads of group g and its copies
-        //   of group g + 1 (only group g + 2's copies, if any, were issued
-        //   after them); barrier (every wave has group g's activations in
-        //   registers, so their part of stage g % 3 is free, and every copy
-        //   of group g + 1 has landed); start group g + 3's activation
-        //   copies; compute group g, reading this wave's codes of stage g % 3;
-        //   refill that part with group g + 3's codes; read group g + 1's
-        //   activations.
+        //   of group g + 1; barrier (every wave has group g's activations in
+        //   registers, so their part of stage st is free, and every copy of
+        //   group g + 1 has landed); start the activation copies of group
+        //   g + 3 (or of the next item's group g + 3 - G); compute group g,
+        //   reading this wave's codes of stage st; refill that part with the
+        //   matching codes; read group g + 1's activations.
         // Waves read right after their own compute, not all at once after a
         // barrier, so the LDS reads of the 8 waves spread out.
         auto groups = [&](auto nsc) {
@@ -938,18 +1020,18 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
                         sd_next = __builtin_amdgcn_ds_bpermute(src_lane, (int)((g & 2) ? csc[t + 1].y : csc[t + 1].x));
                     }
                     const float sc = __uint_as_float((g & 1) ? (sd & 0xFFFF0000u) : (sd << 16));
-                    const bf16x8 q[4] = {unpack8(w4.x), unpack8(w4.y), unpack8(w4.z), unpack8(w4.w)};
+                    const bf16x8 qv[4] = {unpack8(w4.x), unpack8(w4.y), unpack8(w4.z), unpack8(w4.w)};
                     // steps outer, subtiles inner: the NSV chains interleave, so
                     // dependent MFMAs are NSV issues apart
                     floatx4 acc[NSV];
 #pragma unroll
                     for (int sb = 0; sb < NSV; ++sb)
-                        acc[sb] = mfma(a[sb][0], q[0], floatx4{0.f, 0.f, 0.f, 0.f});
+                        acc[sb] = mfma(a[sb][0], qv[0], floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                     for (int i = 1; i < 4; ++i)
 #pragma unroll
                         for (int sb = 0; sb < NSV; ++sb)
-                            acc[sb] = mfma(a[sb][i], q[i], acc[sb]);
+                            acc[sb] = mfma(a[sb][i], qv[i], acc[sb]);
 #pragma unroll
                     for (int sb = 0; sb < NSV; ++sb) {
                         tot[t][sb].x = __builtin_fmaf(sc, acc[sb].x, tot[t][sb].x);
@@ -959,55 +1041,35 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
                     }
                 }
             };
-            // barrier with every LDS read of this wave complete and only
-            // `after` groups' copies of this wave still in flight (compile-
-            // time counts; sched_barrier(0) keeps every load on its side)
-            auto meet = [&](int after) {
-                constexpr uint32_t W12 = vmcnt_imm(2 * NCOPY) & 0xF0FFu, W6 = vmcnt_imm(NCOPY) & 0xF0FFu,
-                                   W0 = vmcnt_imm(0) & 0xF0FFu;   // lgkmcnt(0) as well
-                __builtin_amdgcn_sched_barrier(0);
-                if (after >= 2)
-                    __builtin_amdgcn_s_waitcnt(W12);
-                else if (after == 1)
-                    __builtin_amdgcn_s_waitcnt(W6);
-                else
-                    __builtin_amdgcn_s_waitcnt(W0);
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                __builtin_amdgcn_s_barrier();
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                __builtin_amdgcn_sched_barrier(0);
-            };
 
-            // prologue: groups 0, 1, 2 are being copied (activations, then codes)
-            meet(min(G - 1, 2));                     // group 0 landed
-            read(0);
-            int st = 0;
+            wait_barrier(std::integral_constant<int, 2 * NCOPY + TPW + 2 + NST>());   // group 0 landed
+            read(st0);
+            int st = st0;
             for (int g = 0; g < G; ++g) {
-                meet(g + 2 < G ? 1 : 0);             // activation reads of g done, group g + 1 landed
-                if (g + 3 < G)
-                    copy_act(g + 3, st);
+                if (g == 0)
+                    wait_barrier(std::integral_constant<int, NCOPY + TPW + 2 + NST>());   // group 1
+                else if (g + 1 < G)
+                    wait_barrier(std::integral_constant<int, NCOPY>());             // group g + 1
+                else
+                    wait_barrier(std::integral_constant<int, 2 * NCOPY>());         // nothing new to land
+                const bool own = g + 3 < G, nxt = !own && g + 3 - G < 2;
+                if (own)
+                    copy_act(voff_a, g + 3, st);
+                else if (nxt)
+                    copy_act(voff_an, g + 3 - G, st);
                 __builtin_amdgcn_sched_barrier(0);
                 compute(g, st);
                 __builtin_amdgcn_sched_barrier(0);  // this wave's codes of stage st have been read
-                if (g + 3 < G)
-                    copy_codes(g + 3, st);
+                if (own)
+                    copy_codes(rw, q.tile0, true, g + 3, st);
+                else if (nxt)
+                    copy_codes(rwn, qn.tile0, has_next, g + 3 - G, st);
                 __builtin_amdgcn_sched_barrier(0);
                 st = st == 2 ? 0 : st + 1;
                 if (g + 1 < G)
                     read(st);
             }
         };
-
-        __builtin_amdgcn_sched_barrier(0);
-        copy_act(0, 0);
-        copy_codes(0, 0);
-        copy_act(1, 1);                            // G >= 2
-        copy_codes(1, 1);
-        if (G > 2) {
-            copy_act(2, 2);
-            copy_codes(2, 2);
-        }
-        __builtin_amdgcn_sched_barrier(0);
         if (nsub >= 4)
             groups(std::integral_constant<int, 4>());
         else if (nsub == 3)
@@ -1017,15 +1079,14 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
         else
             groups(std::integral_constant<int, 1>());
 
-        // ---- per-item correction: every copy has landed (the last group
-        // waited for all of them) and every wave is done with the stage
-        // buffers after this barrier ----
+        // ---- per-item correction: the s_sx sums of every wave (and the
+        // output rows) after a barrier that waits for no copy ----
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             s_sx[wave * 256 + (kq * 4 + i) * 16 + n16] = sxacc[i];
         if (wave == 0)
-            s_crow[lane] = crow;
-        __syncthreads();
+            s_crow[lane] = crow + (p.c_row_index ? 0 : q.row0 + lane);
+        wait_barrier(std::integral_constant<int, 63>());
         u32x4 bcorr[TPW];                                // B: s[n][4kq + j] twice, j = 0..3
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
@@ -1055,60 +1116,72 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
             }
         }
 
-        // ---- epilogue: bf16 results pass through this wave's part of the
-        // stage buffers, then every store writes whole row runs ----
+        // ---- epilogue: bf16 results pass through this wave's own codes of
+        // the last stage, then every store writes whole row runs; a row past
+        // the chunk stores out of range (the store count stays fixed) ----
         {
-            uint16_t *so = reinterpret_cast<uint16_t *>(s_dyn) + wave * (CS * OCOLS);
+            uint16_t *so = reinterpret_cast<uint16_t *>(s_w + ((st_last * kTileWaves + wave) * TPW) * 64);
 #pragma unroll
-            for (int t = 0; t < TPW; ++t)
+            for (int hf = 0; hf < HALVES; ++hf) {
 #pragma unroll
-                for (int sb = 0; sb < NS; ++sb) {
-                    const floatx4 v = tot[t][sb];
-                    const float r4[4] = {v.x, v.y, v.z, v.w};
-                    if (SWI) {
-                        // lane n16 < 8 holds the gate row of feature n16 for
-                        // token rows 4 kq + 0..3, lane n16 + 8 the up row: the
-                        // gate lane forms rows 0 and 1 (it receives two up
-                        // values), the up lane rows 2 and 3 (two gate values)
-                        const bool gl = n16 < 8;
+                for (int tt = 0; tt < TH; ++tt)
 #pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const float recv = row_swap8(gl ? r4[j + 2] : r4[j]);
-                            const float gate = gl ? r4[j] : recv, up = gl ? recv : r4[j + 2];
-                            const int rr = sb * 16 + kq * 4 + (gl ? j : j + 2);
-                            so[rr * OCOLS + t * COLS + (n16 & 7)] = (uint16_t)bf16_pair(silu_fast(gate) * up, 0.f);
+                    for (int sb = 0; sb < NS; ++sb) {
+                        const floatx4 v = tot[hf * TH + tt][sb];
+                        const float r4[4] = {v.x, v.y, v.z, v.w};
+                        if (SWI) {
+                            // lane n16 < 8 holds the gate row of feature n16 for
+                            // token rows 4 kq + 0..3, lane n16 + 8 the up row: the
+                            // gate lane forms rows 0 and 1 (it receives two up
+                            // values), the up lane rows 2 and 3 (two gate values)
+                            const bool gl = n16 < 8;
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
+                                const float recv = row_swap8(gl ? r4[j + 2] : r4[j]);
+                                const float gate = gl ? r4[j] : recv, up = gl ? recv : r4[j + 2];
+                                const int rr = sb * 16 + kq * 4 + (gl ? j : j + 2);
+                                so[rr * OCOLS + tt * COLS + (n16 & 7)] = (uint16_t)bf16_pair(silu_fast(gate) * up, 0.f);
+                            }
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                so[(sb * 16 + kq * 4 + i) * OCOLS + tt * COLS + n16] = (uint16_t)bf16_pair(r4[i], 0.f);
                         }
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            so[(sb * 16 + kq * 4 + i) * OCOLS + t * COLS + n16] = (uint16_t)bf16_pair(r4[i], 0.f);
                     }
-                }
-            __builtin_amdgcn_wave_barrier();
-            uint16_t *c = static_cast<uint16_t *>(p.c) + (size_t)tile0 * COLS;
-            // the lane index passes through an empty asm statement: the
-            // per-pass LDS addresses are then formed here, per item, instead
-            // of being hoisted out of the item loop (where they would hold
-            // registers for the whole loop, or spill)
-            int le = lane;
-            asm volatile("" : "+v"(le));
-            const int part = le % LPR;
-            const u32x4 *src_row = reinterpret_cast<const u32x4 *>(so + (le / LPR) * OCOLS + part * 8);
+                __builtin_amdgcn_wave_barrier();
+                const int le = lane;
+                const int part = le % LPR;
+                const u32x4 *src_row = reinterpret_cast<const u32x4 *>(so + (le / LPR) * OCOLS + part * 8);
+                const uint32_t col = (uint32_t)((q.tile0 + hf * TH) * COLS + part * 8);
 #pragma unroll
-            for (int pass = 0; pass < CS / RPP; ++pass) {
-                const int m = pass * RPP + le / LPR;
-                if (m < nvalid) {
+                for (int pass = 0; pass < CS / RPP; ++pass) {
+                    const int m = pass * RPP + le / LPR;
                     const u32x4 d = src_row[pass * RPP * OCOLS / 8];
-                    *reinterpret_cast<u32x4 *>(c + (size_t)s_crow[m] * p.ldc + part * 8) = d;
+                    const uint32_t vo = m < q.nvalid ? ((uint32_t)s_crow[m] * (uint32_t)p.ldc + col) * 2u : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b128(d, ro, vo, 0, 0);
                 }
+                __builtin_amdgcn_wave_barrier();
             }
         }
-        // stage buffers and sums free for the next item's copies: every LDS
-        // read above has completed (its data fed a store). A bare barrier:
-        // the stores themselves need not have landed.
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        // every wave's staging reads are done (their data fed the stores):
+        // the last stage is free for the next item's group 2. The wait leaves
+        // only this epilogue's stores in flight (the next item's groups 0 and
+        // 1 are due at its start anyway), so every load the next item's first
+        // instructions use is known complete.
+        wait_barrier(std::integral_constant<int, NST>());
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+            csc[t] = csc_n[t];
+        crow = crow_n;
+        src_cur = src_n1;
+        src_n1 = src_n2;
+        q_cur = q_nxt;
+        q_nxt = qnn;
+        st0 = (st0 + G) % 3;
+    }
+    {
+        constexpr uint32_t W0 = vmcnt_imm(0);            // no copy lands after the workgroup ends
+        __builtin_amdgcn_s_waitcnt(W0);
     }
 }
 
@@ -1217,14 +1290,17 @@ hipError_t launch_kind(const GemmArgs &a, int max_rows, int mode, int tpw, int n
 
 }  // namespace
 
-// Shapes the tile kernel takes: tiled codes, K/128 even (groups run in pairs)
-// and at most 16 (one correction column per group), 512-row blocks, expert
-// tables in the LDS left over, bf16 output.
+// Shapes the tile kernel takes: tiled codes, K/128 even, at least 4 (the
+// next item's first groups are copied during groups G-3 and G-2) and at most
+// 16 (one correction column per group), 512-row blocks, expert tables in the
+// LDS left over, bf16 output that 32-bit buffer offsets reach.
 static bool tile_fits(const GemmLaunch &g)
 {
     const int G = g.K / kGroup;
-    return g.w_tiled && G % 2 == 0 && G <= 16 && (g.N / 16) % (4 * kTileWaves) == 0 && g.num_experts <= 256 &&
-           (g.kind == MOE_GEMM_W13_SWIGLU || !g.c_f32);
+    const int ldc = g.kind == MOE_GEMM_W13_SWIGLU ? g.N / 2 : g.N;
+    return g.w_tiled && G % 2 == 0 && G >= 4 && G <= 16 && (g.N / 16) % (4 * kTileWaves) == 0 &&
+           g.num_experts <= 256 && (g.kind == MOE_GEMM_W13_SWIGLU || !g.c_f32) &&
+           (size_t)g.max_rows * (size_t)ldc * 2 < 0x80000000u;
 }
 
 hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
@@ -1242,6 +1318,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     a.c = g.c;
     a.c_row_index = g.c_row_index;
     a.c_row_bytes = g.c_row_index ? (uint32_t)g.max_rows * 4u : 0u;
+    a.a_row_bytes = g.a_row_index ? (uint32_t)g.max_rows * 4u : 0u;
     a.a_bytes = (uint32_t)g.a_bytes;
     a.top_k = g.top_k;
     a.num_experts = g.num_experts;
@@ -1251,6 +1328,10 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     a.w_tiled = g.w_tiled ? 1 : 0;
     a.half = g.N / 2;
     a.ldc = (g.kind == MOE_GEMM_W13_SWIGLU) ? g.N / 2 : g.N;
+    {
+        const size_t cb = (size_t)g.max_rows * (size_t)a.ldc * 2;
+        a.c_bytes = cb < 0x80000000u ? (uint32_t)cb : 0u;   // 0: too large for the tile kernel
+    }
 
     // Expected rows per active expert (uniform routing estimate) picks the
     // kernel and the tile shape. Only the launch shape depends on it, never
