@@ -217,3 +217,35 @@ def test_integer_exact_every_launch_shape(variant, kind, H, I, tiled, monkeypatc
         r0, r1 = offsets[e], offsets[e + 1]
         want = (xi[idx[r0:r1] // k].astype(np.int64) @ q[e].T.astype(np.int64)).astype(np.float64) * 2.0 ** -6
         assert np.array_equal(got[r0:r1].astype(np.float64), want), e
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("gather", [False, True])
+def test_tile_kernel_many_items_smallest_k(kind, gather, monkeypatch):
+    # the prefill tile kernel forced at K = 512 (four groups, the fewest it
+    # takes: the next item's first two groups are copied during groups 0 and
+    # 1) over ragged experts (empty, single-row, 63/64/65-row and long ones):
+    # 350-700 items, so workgroups run several items back to back and the
+    # last item of each copies out of range; sampled rows against the oracle
+    from w4a16_grouped_gemm_amd import ops
+    monkeypatch.setenv("MOE_GEMM_MODE", "2")
+    say(f"gemm tile kernel K=512 many items kind={kind} gather={gather}")
+    rng = np.random.default_rng(41 + kind + 2 * gather)
+    H = I = 512
+    N, K = (2 * I, H) if kind == ops.W13_SWIGLU else (H, I)
+    counts = np.concatenate([[0, 1, 63, 64, 65, 0, 129], rng.integers(0, 5000, size=9)]).astype(np.int64)
+    E = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    q = rng.integers(-8, 8, size=(E, N, K), dtype=np.int8)
+    wq = pack_int4(q)
+    s = bf16_bits(rng.uniform(0.005, 0.02, size=(E, N, K // 128)).astype(np.float32))
+    a = bf16_bits((rng.standard_normal((R, K)) * (1.0 if kind == ops.W13_SWIGLU else 0.05)).astype(np.float32))
+    idx = rng.permutation(R).astype(np.int32) if gather else None
+    rows = np.unique(np.concatenate([offsets[:-1][counts > 0], offsets[1:][counts > 0] - 1,
+                                     rng.integers(0, R, size=48)]))
+    sel = np.zeros(R, np.uint8)
+    sel[rows] = 1
+    ref = oracle.grouped_gemm(kind, a, offsets, wq, s, rows=R, a_row_index=idx, top_k=1, row_sel=sel)
+    got = _gpu_gemm(kind, a, offsets, wq, s, T=R, k=1, a_row_index=idx, out_f32=False, tiled=True)
+    _close_bf16(got[rows], ref[rows], "tile K=512")
