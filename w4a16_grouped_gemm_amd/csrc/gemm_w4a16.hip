@@ -734,6 +734,7 @@ constexpr int kTileStages = 3;
 constexpr int kTileActBytes = 16 * 64 * 16;           // one group: 16 copies x 64 lanes x 16 bytes
 constexpr int kTileCodeBytes = kTileWaves * 4 * 1024; // one group: 8 waves x 4 tiles x 1 KiB
 constexpr int kTileSxBytes = kTileWaves * 16 * 16 * 4;
+constexpr int kTileChunkTable = 1024;                 // chunk -> expert entries kept in LDS
 
 // fp32 pair -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32; fp32
 // denormals are kept, so this is the IEEE rounding for every finite value)
@@ -766,6 +767,7 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
     int *s_off = s_prefix + (E + 1);
     int *s_wtot = s_off + (E + 1);
     int *s_crow = s_wtot + kTileWaves;                 // output row of each of the item's 64 rows
+    int *s_chunk_e = s_crow + 64;                      // expert of each chunk (when they fit)
 
     const int tid = threadIdx.x;
     const int wave = uniform(tid >> 6);                // scalar: wave-dependent choices are branches
@@ -819,11 +821,19 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
     struct Geo {
         int e, row0, nvalid, tile0;
     };
+    // the expert of every chunk, looked up once here instead of a binary
+    // search at every item (the search stays for more chunks than the table)
+    const bool chunk_table = s_prefix[E] <= kTileChunkTable;
+    if (chunk_table) {
+        for (int c = tid; c < s_prefix[E]; c += kTileWaves * 64)
+            s_chunk_e[c] = chunk_expert(s_prefix, E, c);
+        __syncthreads();
+    }
     auto geo = [&](int it) {
         Geo q;
         const int ch = it / nblocks;
         const int block = it - ch * nblocks;
-        q.e = uniform(chunk_expert(s_prefix, E, ch));
+        q.e = uniform(chunk_table ? s_chunk_e[ch] : chunk_expert(s_prefix, E, ch));
         q.row0 = uniform(s_off[q.e] + (ch - s_prefix[q.e]) * CS);
         q.nvalid = uniform(min(CS, s_off[q.e + 1] - q.row0));
         q.tile0 = block * BT + wave * TPW;
@@ -1237,7 +1247,7 @@ hipError_t launch_tile(const GemmArgs &a, int max_rows, hipStream_t st)
 {
     auto kernel = gemm_tile_kernel<KIND>;
     const size_t lds = (size_t)kTileStages * (kTileActBytes + kTileCodeBytes) + kTileSxBytes +
-                       sizeof(int) * (2 * (a.num_experts + 1) + kTileWaves + 64);
+                       sizeof(int) * (2 * (a.num_experts + 1) + kTileWaves + 64 + kTileChunkTable);
     const int nblocks = (a.N >> 4) / (4 * kTileWaves);
     const long long chunks = (long long)min(a.num_experts, max_rows) + max_rows / 64;
     long long grid = grid_for(chunks * nblocks, 1);    // one workgroup per CU (its LDS)
