@@ -96,3 +96,20 @@ def test_shared_argument_errors():
     assert lib.moe_w4a16_workspace_size_shared(ctypes.byref(sh), 5) == 0
     assert lib.moe_w4a16_workspace_size_shared(ctypes.byref(sh), 1) > lib.moe_w4a16_workspace_size(ctypes.byref(sh))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("wl,T,S", [("qwen3_decode", 1024, 2), ("qwen3_prefill", 2048, 1)])
+def test_shared_many_tokens_sampled(wl, T, S):
+    # past 512 tokens the permutation runs over token ranges (its scan writes
+    # the shared segments); at 2048 tokens both GEMMs take the tile kernel,
+    # shared experts included. 64 sampled tokens against the oracle
+    say(f"shared layer {wl} T={T} S={S} (sampled)")
+    inp = make_layer_inputs(wl, T)
+    sh = make_shared_weights(wl, S)
+    got = _forward(inp, sh, tiled=True)
+    sel = np.zeros(T, np.uint8)
+    rows = np.unique(np.linspace(0, T - 1, 64).astype(int))
+    sel[rows] = 1
+    ref = oracle.layer(inp.x, inp.logits, inp.w13_q, inp.s13, inp.w2_q, inp.s2, top_k=inp.workload.top_k,
+                       expert_begin=inp.workload.expert_begin, tok_sel=sel, shared=sh)
+    assert_layer_close(got[rows], ref["out"][rows], f"shared {wl} T={T}")
