@@ -1128,7 +1128,10 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
 
         // ---- epilogue: bf16 results pass through this wave's own codes of
         // the last stage, then every store writes whole row runs; a row past
-        // the chunk stores out of range (the store count stays fixed) ----
+        // the chunk stores out of range (the store count stays fixed). The
+        // 16-byte column chunks of row rr sit at chunk position c ^ ((rr / 4)
+        // % 4), so the four row quads a write instruction covers fall on
+        // different LDS banks ----
         {
             uint16_t *so = reinterpret_cast<uint16_t *>(s_w + ((st_last * kTileWaves + wave) * TPW) * 64);
 #pragma unroll
@@ -1150,18 +1153,23 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
                                 const float recv = row_swap8(gl ? r4[j + 2] : r4[j]);
                                 const float gate = gl ? r4[j] : recv, up = gl ? recv : r4[j + 2];
                                 const int rr = sb * 16 + kq * 4 + (gl ? j : j + 2);
-                                so[rr * OCOLS + tt * COLS + (n16 & 7)] = (uint16_t)bf16_pair(silu_fast(gate) * up, 0.f);
+                                so[rr * OCOLS + ((tt ^ kq) << 3) + (n16 & 7)] =
+                                    (uint16_t)bf16_pair(silu_fast(gate) * up, 0.f);
                             }
                         } else {
+                            const int cs = (((tt * COLS + n16) >> 3) ^ kq) << 3 | (n16 & 7);
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                so[(sb * 16 + kq * 4 + i) * OCOLS + tt * COLS + n16] = (uint16_t)bf16_pair(r4[i], 0.f);
+                                so[(sb * 16 + kq * 4 + i) * OCOLS + cs] = (uint16_t)bf16_pair(r4[i], 0.f);
                         }
                     }
                 __builtin_amdgcn_wave_barrier();
                 const int le = lane;
                 const int part = le % LPR;
-                const u32x4 *src_row = reinterpret_cast<const u32x4 *>(so + (le / LPR) * OCOLS + part * 8);
+                // row le / LPR + pass * RPP has (row / 4) % 4 = (le / 16) % 4 in every pass
+                static_assert(LPR == 4 && RPP % 16 == 0, "chunk swizzle per lane");
+                const u32x4 *src_row =
+                    reinterpret_cast<const u32x4 *>(so + (le / LPR) * OCOLS + ((part ^ ((le >> 4) & 3)) << 3));
                 const uint32_t col = (uint32_t)((q.tile0 + hf * TH) * COLS + part * 8);
 #pragma unroll
                 for (int pass = 0; pass < CS / RPP; ++pass) {
