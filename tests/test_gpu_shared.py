@@ -100,8 +100,8 @@ def test_shared_argument_errors():
 
 @pytest.mark.parametrize("wl,T,S", [("qwen3_decode", 1024, 2), ("qwen3_prefill", 2048, 1)])
 def test_shared_many_tokens_sampled(wl, T, S):
-    # past 512 tokens the permutation runs over token ranges (its scan writes
-    # the shared segments); at 2048 tokens both GEMMs take the tile kernel,
+    # past 384 tokens the permutation runs over token ranges (the first
+    # range writes the shared segments); at 2048 tokens both GEMMs take the tile kernel,
     # shared experts included. 64 sampled tokens against the oracle
     say(f"shared layer {wl} T={T} S={S} (sampled)")
     inp = make_layer_inputs(wl, T)

@@ -35,9 +35,9 @@ constexpr size_t kDynLdsMax = 144 * 1024; // dynamic LDS of one launch: bitmaps 
 // separate routing launch and its round trip through memory. TL and PL are
 // the routing shape (lanes per token, logits per lane).
 // bases != NULL: the workgroup only scatters tokens [b*tpb, (b+1)*tpb) of the
-// permutation (b = blockIdx.x), its experts' first rows given by
-// bases[b*E + e] (the parallel path for many tokens; counts and offsets are
-// written by permute_scan_kernel).
+// permutation (b = blockIdx.x); bases[b'*E + e] holds the slots of expert e
+// in each range b' (permute_hist_kernel), from which every workgroup forms
+// its own first rows (the parallel path for many tokens).
 template <bool IDS_IN_LDS, bool ROUTE = false, int TL = 16, int PL = 8>
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int T, int k, int begin, int E, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
@@ -189,8 +189,60 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 
     int R = 0;
     if (bases) {
-        for (int e = tid; e < E; e += kPermThreads)
-            s_cursor[e] = bases[(size_t)blockIdx.x * E + e];
+        // bases[b][e]: expert e's slots in token range b. Thread e sums its
+        // column (its total, and the ranges before this one), the block scans
+        // the totals into offsets; range b's slots of expert e start at
+        // offsets[e] + (slots of e in ranges < b). Range 0 also writes the
+        // counts, offsets, shared segments and the -1 rows.
+        const int B = gridDim.x, b = blockIdx.x;
+        const int e = tid;                                // E <= kPermThreads
+        const int ec = min(e, E - 1);                     // clamped: loads never sit under a branch
+        int total = 0, before = 0;
+        for (int b0 = 0; b0 < B; b0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v[j] = bases[(size_t)min(b0 + j, B - 1) * E + ec];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int vj = (b0 + j < B) ? v[j] : 0;
+                total += vj;
+                before += (b0 + j < b) ? vj : 0;
+            }
+        }
+        if (e >= E)
+            total = before = 0;
+        int wtot;
+        const int ex = wave_exclusive_scan(total, wtot);
+        if ((tid & 63) == 0)
+            s_wave_tot[tid >> 6] = wtot;
+        __syncthreads();
+        int wbase = 0;
+        for (int w = 0; w < kPermThreads / 64; ++w) {
+            const int t = s_wave_tot[w];
+            wbase += (w < (tid >> 6)) ? t : 0;
+            R += t;
+        }
+        if (e < E)
+            s_cursor[e] = wbase + ex + before;
+        if (b == 0) {
+            if (e < E) {
+                counts[e] = total;
+                offsets[e] = wbase + ex;
+            }
+            if (tid == 0)
+                offsets[E] = R;
+            for (int sh = tid; sh < num_shared; sh += kPermThreads) {
+                counts[E + sh] = T;
+                offsets[E + 1 + sh] = R + (sh + 1) * T;
+            }
+            const long long S_all = (long long)T * k;
+            for (long long r = tid; r < (long long)num_shared * T; r += kPermThreads)
+                perm[R + r] = (int32_t)((r % T) * k);
+            for (long long r = R + (long long)num_shared * T + tid; r < S_all + (long long)num_shared * T;
+                 r += kPermThreads)
+                perm[r] = -1;
+        }
         __syncthreads();
     } else {
     // 1. histogram of local slots
@@ -330,74 +382,6 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(int T, int k, int beg
         part[(size_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
-// Parallel path, step 2 (one workgroup, thread e per expert): counts,
-// offsets (exclusive scan over experts), and part[b][e] replaced by the first
-// row of expert e's slots in range b (offsets[e] + the slots of earlier
-// ranges); the shared segments and the -1 rows as in permute_kernel.
-__global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(int T, int k, int E, int B,
-                                                                    int32_t *__restrict__ part,
-                                                                    int32_t *__restrict__ counts,
-                                                                    int32_t *__restrict__ offsets,
-                                                                    int32_t *__restrict__ perm, int num_shared)
-{
-    __shared__ int s_wave_tot[kPermThreads / 64];
-    const int tid = threadIdx.x;
-    const int e = tid;
-    const int ec = min(e, E - 1);                      // clamped: loads never sit under a branch
-    int cnt = 0;
-    for (int b0 = 0; b0 < B; b0 += 8) {
-        int v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            v[j] = part[(size_t)min(b0 + j, B - 1) * E + ec];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            cnt += (b0 + j < B) ? v[j] : 0;
-    }
-    if (e >= E)
-        cnt = 0;
-    int wtot;
-    const int ex = wave_exclusive_scan(cnt, wtot);
-    if ((tid & 63) == 0)
-        s_wave_tot[tid >> 6] = wtot;
-    __syncthreads();
-    int wbase = 0, R = 0;
-    for (int w = 0; w < kPermThreads / 64; ++w) {
-        const int t = s_wave_tot[w];
-        wbase += (w < (tid >> 6)) ? t : 0;
-        R += t;
-    }
-    const int off = wbase + ex;
-    if (e < E) {
-        counts[e] = cnt;
-        offsets[e] = off;
-        int run = off;
-        for (int b0 = 0; b0 < B; b0 += 8) {
-            int v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                v[j] = part[(size_t)min(b0 + j, B - 1) * E + e];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (b0 + j < B) {
-                    part[(size_t)(b0 + j) * E + e] = run;
-                    run += v[j];
-                }
-        }
-    }
-    if (tid == 0)
-        offsets[E] = R;
-    for (int sh = tid; sh < num_shared; sh += kPermThreads) {
-        counts[E + sh] = T;
-        offsets[E + 1 + sh] = R + (sh + 1) * T;
-    }
-    const long long S = (long long)T * k;
-    for (long long r = tid; r < (long long)num_shared * T; r += kPermThreads)
-        perm[R + r] = (int32_t)((r % T) * k);
-    for (long long r = R + (long long)num_shared * T + tid; r < S + (long long)num_shared * T; r += kPermThreads)
-        perm[r] = -1;
-}
-
 // x_perm[r] = x[perm[r] / k] for r < R; 16 bytes per thread.
 __global__ __launch_bounds__(256) void gather_kernel(int H, int k, int E,
                                                      const uint16_t *__restrict__ x,
@@ -432,14 +416,15 @@ static int chunk_tokens_for(int E)
 }
 
 // Past this many tokens (MOE_PERMUTE_PARALLEL_MIN_T overrides) the
-// permutation runs over nb token ranges in three launches (histogram, scan,
-// scatter) instead of one workgroup; at most 64 ranges, so the scan reads
-// few partial counts per expert.
+// permutation runs over nb token ranges in two launches (per-range
+// histograms, then a scatter whose workgroups each scan the histograms for
+// their own first rows) instead of one workgroup; at most 64 ranges, so that
+// scan reads few partial counts per expert.
 static int parallel_ranges(const moe_shape &sh)
 {
     static const int min_t = [] {
         const char *env = getenv("MOE_PERMUTE_PARALLEL_MIN_T");
-        return env ? atoi(env) : 512;
+        return env ? atoi(env) : 384;
     }();
     const int T = sh.num_tokens;
     if (T <= min_t || T < 2)
@@ -484,8 +469,6 @@ hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *coun
             return hipErrorInvalidValue;
         hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(256), 0, st, T, sh.top_k, sh.expert_begin, E, tpb,
                            ids, part);
-        hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kPermThreads), 0, st, T, sh.top_k, E, nb, part, counts,
-                           offsets, perm, num_shared);
     }
     const dim3 grid(nb ? nb : 1);
     if (ids_in_lds)
