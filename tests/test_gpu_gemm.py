@@ -127,12 +127,14 @@ def test_swiglu_and_down_vs_oracle(wl, T, tiled):
     _close_bf16(y[:R], y_ref[:R], "y")
 
 
+@pytest.mark.parametrize("mode", ["2", "3"])
 @pytest.mark.parametrize("wl,T,n", [("qwen3_prefill", 256, None), ("qwen3_prefill", 2048, 96), ("tiny", 40, None)])
-def test_tile_kernel_vs_oracle(wl, T, n, monkeypatch):
-    # the prefill tile kernel forced (many rows per expert: chunks of 64 rows,
-    # ragged last chunks, the per-item -136 correction); sampled rows at 2048
+def test_tile_kernel_vs_oracle(wl, T, n, mode, monkeypatch):
+    # the tile kernel forced, both shapes (mode 2: 8 waves, 64-row chunks;
+    # mode 3: 4 waves, 32-row chunks, two workgroups per CU): ragged last
+    # chunks, the per-item -136 correction; sampled rows at 2048
     from w4a16_grouped_gemm_amd import ops
-    monkeypatch.setenv("MOE_GEMM_MODE", "2")
+    monkeypatch.setenv("MOE_GEMM_MODE", mode)
     say(f"gemm tile kernel {wl} T={T}")
     inp = make_layer_inputs(wl, T)
     k = inp.workload.top_k
@@ -219,17 +221,18 @@ def test_integer_exact_every_launch_shape(variant, kind, H, I, tiled, monkeypatc
         assert np.array_equal(got[r0:r1].astype(np.float64), want), e
 
 
+@pytest.mark.parametrize("mode", ["2", "3"])
 @pytest.mark.parametrize("kind", [0, 1])
 @pytest.mark.parametrize("gather", [False, True])
-def test_tile_kernel_many_items_smallest_k(kind, gather, monkeypatch):
+def test_tile_kernel_many_items_smallest_k(kind, gather, mode, monkeypatch):
     # the prefill tile kernel forced at K = 512 (four groups, the fewest it
     # takes: the next item's first two groups are copied during groups 0 and
     # 1) over ragged experts (empty, single-row, 63/64/65-row and long ones):
     # 350-700 items, so workgroups run several items back to back and the
     # last item of each copies out of range; sampled rows against the oracle
     from w4a16_grouped_gemm_amd import ops
-    monkeypatch.setenv("MOE_GEMM_MODE", "2")
-    say(f"gemm tile kernel K=512 many items kind={kind} gather={gather}")
+    monkeypatch.setenv("MOE_GEMM_MODE", mode)
+    say(f"gemm tile kernel (mode {mode}) K=512 many items kind={kind} gather={gather}")
     rng = np.random.default_rng(41 + kind + 2 * gather)
     H = I = 512
     N, K = (2 * I, H) if kind == ops.W13_SWIGLU else (H, I)

@@ -729,12 +729,19 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
 //  * Tiled codes only: they unpack in column order, matching the
 //    activations as they lie in memory.
 // ---------------------------------------------------------------------------
-constexpr int kTileWaves = 8;
+// Tile kernel shapes: WAVES waves, NS 16-row subtiles per item (4 * NS
+// activation copies per group, two per wave). 8 x 4: one workgroup per CU
+// (prefill); 4 x 2: two per CU (32-row chunks).
 constexpr int kTileStages = 3;
-constexpr int kTileActBytes = 16 * 64 * 16;           // one group: 16 copies x 64 lanes x 16 bytes
-constexpr int kTileCodeBytes = kTileWaves * 4 * 1024; // one group: 8 waves x 4 tiles x 1 KiB
-constexpr int kTileSxBytes = kTileWaves * 16 * 16 * 4;
-constexpr int kTileChunkTable = 1024;                 // chunk -> expert entries kept in LDS
+constexpr int tile_act_bytes(int NS) { return NS * 4 * 64 * 16; }         // one group's activation fragments
+constexpr int tile_code_bytes(int WAVES) { return WAVES * 4 * 1024; }    // one group: 4 tiles x 1 KiB per wave
+constexpr int tile_sx_bytes(int WAVES) { return WAVES * 16 * 16 * 4; }
+constexpr int tile_chunk_table(int WAVES) { return WAVES == 8 ? 1024 : 256; }   // chunk -> expert entries in LDS
+constexpr size_t tile_lds_bytes(int WAVES, int NS, int E)
+{
+    return (size_t)kTileStages * (tile_act_bytes(NS) + tile_code_bytes(WAVES)) + tile_sx_bytes(WAVES) +
+           sizeof(int) * (2 * (E + 1) + WAVES + 64 + tile_chunk_table(WAVES));
+}
 
 // fp32 pair -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32; fp32
 // denormals are kept, so this is the IEEE rounding for every finite value)
@@ -750,12 +757,16 @@ constexpr uint32_t vmcnt_imm(int n)                   // s_waitcnt vmcnt(n), oth
     return (uint32_t)((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int KIND>
+template <int KIND, int kTileWaves, int NS>
 __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_tile_kernel(GemmArgs p)
 {
     constexpr int TPW = 4;                              // tiles per wave
-    constexpr int NS = 4;                               // 16-token subtiles per item
-    constexpr int CS = 16 * NS;
+    static_assert(4 * NS == 2 * kTileWaves, "two activation copies per wave and group");
+    constexpr int CS = 16 * NS;                         // rows per item
+    constexpr int kTileActBytes = tile_act_bytes(NS);
+    constexpr int kTileCodeBytes = tile_code_bytes(kTileWaves);
+    constexpr int kTileSxBytes = tile_sx_bytes(kTileWaves);
+    constexpr int kTileChunkTable = tile_chunk_table(kTileWaves);
     constexpr int BT = kTileWaves * TPW;                // tiles per block
     constexpr int NCOPY = 2 + TPW;                      // copies a wave issues per group
     extern __shared__ __align__(16) unsigned char s_dyn[];
@@ -809,7 +820,7 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
     constexpr int LPR = OCOLS * 2 / 16;
     constexpr int RPP = 64 / LPR;
     constexpr int NST = HALVES * (CS / RPP);            // stores per wave and item, always issued
-    static_assert(kTileWaves * CS * OCOLS * 2 == kTileCodeBytes, "a pass fills one stage's codes");
+    static_assert(CS * OCOLS * 2 <= TPW * 1024, "a pass fits the wave's codes of one stage");
 
     const int nx = (int)gridDim.x >= kXcds ? kXcds : 1;
     const int xcd = blockIdx.x % nx;
@@ -879,7 +890,7 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
     // code bytes hold K = 32 kq .. +32, one word per step).
     auto copy_act = [&](uint32_t voff_a, int g, int st) {
         const uint32_t soff = (uint32_t)g * (kGroup * 2) + (uint32_t)(wave & 1) * 32;
-        lds_byte *da = (lds_byte *)(s_a + (st * 16 + 2 * wave) * 64);
+        lds_byte *da = (lds_byte *)(s_a + (st * 4 * NS + 2 * wave) * 64);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, da + j * 1024, 16, voff_a, soff + j * 16, 0, 0);
@@ -993,7 +1004,7 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
             constexpr int NSV = decltype(nsc)::value;
             u32x4 a[NSV][4];
             auto read = [&](int st) {
-                const u32x4 *src = s_a + st * 16 * 64 + lane;
+                const u32x4 *src = s_a + st * 4 * NS * 64 + lane;
 #pragma unroll
                 for (int sb = 0; sb < NSV; ++sb)
 #pragma unroll
@@ -1001,13 +1012,13 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
                         a[sb][i] = src[(4 * sb + i) * 64];
             };
             auto compute = [&](int g, int st) {
-                // 136 * sum(x) of subtile wave % 4, steps 2 (wave / 4) .. +1, into column g
+                // 136 * sum(x) of subtile wave % NS, steps 2 (wave / NS) .. +1, into column g
                 const uint32_t oh = n16 == g ? 0x43084308u : 0u;
                 const bf16x8 ohv = __builtin_bit_cast(bf16x8, u32x4{oh, oh, oh, oh});
 #pragma unroll
                 for (int w = 0; w < NSV; ++w) {
-                    if ((wave & 3) == w) {
-                        if (wave < 4) {
+                    if (wave % NS == w) {
+                        if (wave < NS) {
                             sxacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[w][0]), ohv, sxacc, 0, 0, 0);
                             sxacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[w][1]), ohv, sxacc, 0, 0, 0);
                         } else {
@@ -1080,14 +1091,18 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
                     read(st);
             }
         };
-        if (nsub >= 4)
-            groups(std::integral_constant<int, 4>());
-        else if (nsub == 3)
-            groups(std::integral_constant<int, 3>());
-        else if (nsub == 2)
-            groups(std::integral_constant<int, 2>());
-        else
+        if (nsub >= NS)
+            groups(std::integral_constant<int, NS>());
+        else if constexpr (NS == 4) {
+            if (nsub == 3)
+                groups(std::integral_constant<int, 3>());
+            else if (nsub == 2)
+                groups(std::integral_constant<int, 2>());
+            else
+                groups(std::integral_constant<int, 1>());
+        } else {
             groups(std::integral_constant<int, 1>());
+        }
 
         // ---- per-item correction: the s_sx sums of every wave (and the
         // output rows) after a barrier that waits for no copy ----
@@ -1110,7 +1125,7 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
         for (int sb = 0; sb < NS; ++sb) {
             if (sb < nsub) {
                 const floatx4 v0 = *reinterpret_cast<const floatx4 *>(s_sx + sb * 256 + n16 * 16 + kq * 4);
-                const floatx4 v1 = *reinterpret_cast<const floatx4 *>(s_sx + (sb + 4) * 256 + n16 * 16 + kq * 4);
+                const floatx4 v1 = *reinterpret_cast<const floatx4 *>(s_sx + (sb + NS) * 256 + n16 * 16 + kq * 4);
                 const float vv[4] = {v0.x + v1.x, v0.y + v1.y, v0.z + v1.z, v0.w + v1.w};
                 uint32_t d[4];
 #pragma unroll
@@ -1250,18 +1265,18 @@ hipError_t launch_stream(const GemmArgs &a, int max_rows, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int KIND>
+template <int KIND, int WAVES, int NS>
 hipError_t launch_tile(const GemmArgs &a, int max_rows, hipStream_t st)
 {
-    auto kernel = gemm_tile_kernel<KIND>;
-    const size_t lds = (size_t)kTileStages * (kTileActBytes + kTileCodeBytes) + kTileSxBytes +
-                       sizeof(int) * (2 * (a.num_experts + 1) + kTileWaves + 64 + kTileChunkTable);
-    const int nblocks = (a.N >> 4) / (4 * kTileWaves);
-    const long long chunks = (long long)min(a.num_experts, max_rows) + max_rows / 64;
-    long long grid = grid_for(chunks * nblocks, 1);    // one workgroup per CU (its LDS)
+    auto kernel = gemm_tile_kernel<KIND, WAVES, NS>;
+    const size_t lds = tile_lds_bytes(WAVES, NS, a.num_experts);
+    const int nblocks = (a.N >> 4) / (4 * WAVES);
+    const long long chunks = (long long)min(a.num_experts, max_rows) + max_rows / (16 * NS);
+    // one workgroup per CU for 8 waves, two for 4 (their LDS)
+    long long grid = grid_for(chunks * nblocks, WAVES == 8 ? 1 : 2);
     if (grid >= kXcds)
         grid -= grid % kXcds;                          // whole XCD shares (see the streaming kernel)
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kTileWaves * 64), lds, st, a);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(WAVES * 64), lds, st, a);
     return hipGetLastError();
 }
 
@@ -1279,7 +1294,9 @@ hipError_t launch_kind(const GemmArgs &a, int max_rows, int mode, int tpw, int n
                        hipStream_t st)
 {
     if (mode == 2)
-        return launch_tile<KIND>(a, max_rows, st);
+        return launch_tile<KIND, 8, 4>(a, max_rows, st);
+    if (mode == 3)
+        return launch_tile<KIND, 4, 2>(a, max_rows, st);
     if (mode == 0) {
         const int G = a.K / kGroup;
         if (G >= 24)
@@ -1312,11 +1329,11 @@ hipError_t launch_kind(const GemmArgs &a, int max_rows, int mode, int tpw, int n
 // next item's first groups are copied during groups G-3 and G-2) and at most
 // 16 (one correction column per group), 512-row blocks, expert tables in the
 // LDS left over, bf16 output that 32-bit buffer offsets reach.
-static bool tile_fits(const GemmLaunch &g)
+static bool tile_fits(const GemmLaunch &g, int waves)
 {
     const int G = g.K / kGroup;
     const int ldc = g.kind == MOE_GEMM_W13_SWIGLU ? g.N / 2 : g.N;
-    return g.w_tiled && G % 2 == 0 && G >= 4 && G <= 16 && (g.N / 16) % (4 * kTileWaves) == 0 &&
+    return g.w_tiled && G % 2 == 0 && G >= 4 && G <= 16 && (g.N / 16) % (4 * waves) == 0 &&
            g.num_experts <= 256 && (g.kind == MOE_GEMM_W13_SWIGLU || !g.c_f32) &&
            (size_t)g.max_rows * (size_t)ldc * 2 < 0x80000000u;
 }
@@ -1393,10 +1410,13 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     if (tpw == 4 && nsub == 2)
         ring = 2;
     // the tile kernel (64-row chunks, 512-row blocks, both operands through
-    // LDS-DMA) once experts average about 96 rows or more: faster there for
-    // both GEMMs at 128 rows per expert, slower at 64 (measured on MI355X,
-    // Qwen3-30B-A3B prefill shapes)
-    if (m >= 96.0 && tile_fits(g))
+    // LDS-DMA) once experts average about 96 rows or more, 64 for the down
+    // GEMM (measured on MI355X, Qwen3-30B-A3B shapes: at 64 rows per expert
+    // 7% faster for the down GEMM, 5% slower for the gate/up GEMM; at 16 rows
+    // slower for both). The 4-wave variant (32-row chunks, two workgroups per
+    // CU, MOE_GEMM_MODE=3) came out within run-to-run spread of the
+    // streaming kernel from 16 to 64 rows per expert and is not chosen.
+    if (m >= (g.kind == MOE_GEMM_W2 ? 64.0 : 96.0) && tile_fits(g, 8))
         mode = 2;
     if (const char *env = getenv("MOE_GEMM_MODE"))
         mode = atoi(env);
@@ -1415,7 +1435,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
         kseg >>= 1;
     if (kseg % ring != 0 && !(kseg == 1 && ring == 2))   // instantiated ring depths
         ring = 2;
-    if (mode == 2 && !tile_fits(g))
+    if ((mode == 2 && !tile_fits(g, 8)) || (mode == 3 && !tile_fits(g, 4)))
         mode = 1;
     if (mode == 1 && (ntiles % (4 * tpw) != 0 || G % kseg != 0))
         mode = 0;                                         // shapes the streaming tiles do not divide
