@@ -105,9 +105,11 @@ def test_permute_local_window_and_chunks(begin, E_loc, E_g):
 
 # (T, E_g, E_loc, expert_begin, k): one workgroup over two bitmap chunks
 # (1024 experts leave 128-token chunks); just past the token count where the
-# permutation splits into ranges; ranges over a window of 1024 experts; and
-# the 64-range cap with ranges too long to stage their ids in LDS.
-RANGES = [(200, 1024, 1024, 0, 16), (385, 128, 128, 0, 8), (513, 128, 128, 0, 8), (5000, 1024, 512, 256, 16),
+# permutation splits into ranges; one local expert; ranges over a window of
+# 1024 experts; and the 64-range cap with ranges too long to stage their ids
+# in LDS.
+RANGES = [(200, 1024, 1024, 0, 16), (385, 128, 128, 0, 8), (513, 128, 128, 0, 8), (1000, 16, 1, 5, 2),
+          (5000, 1024, 512, 256, 16),
           (160000, 64, 32, 16, 16)]
 
 

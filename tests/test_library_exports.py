@@ -100,3 +100,26 @@ def test_shared_validation_without_gpu():
     assert f(ctypes.byref(sh), 1, p, p, p, p, p, p, p, p, p, p, p, p, 16, None) == 5        # workspace too small
     assert lib.moe_w4a16_workspace_size_shared(ctypes.byref(sh), 2) > lib.moe_w4a16_workspace_size_shared(
         ctypes.byref(sh), 1)
+
+
+def test_permute_workspace_without_gpu(lib):
+    # 0 bytes while one workgroup permutes (up to 384 tokens), else int32
+    # counts per (token range, local expert); a short or missing workspace is
+    # refused before anything reaches the device
+    S = ops.MoeShape
+    lib.moe_permute_workspace_size.argtypes = [ctypes.POINTER(S)]
+    lib.moe_permute_workspace_size.restype = ctypes.c_size_t
+    small = ops.make_shape(384, 256, 512, 128, 128, 8)
+    assert lib.moe_permute_workspace_size(ctypes.byref(small)) == 0
+    for T, E in [(385, 128), (2048, 128), (100000, 32)]:
+        sh = ops.make_shape(T, 256, 512, E, E, 8)
+        ranges = min(64, (T + 127) // 128)
+        assert lib.moe_permute_workspace_size(ctypes.byref(sh)) == ranges * E * 4
+    sh = ops.make_shape(2048, 256, 512, 128, 128, 8)
+    need = lib.moe_permute_workspace_size(ctypes.byref(sh))
+    fake = ctypes.c_void_p(1 << 20)                       # never dereferenced: validation fails first
+    args = [ctypes.byref(sh), fake, None, fake, fake, fake, fake, None]
+    lib.moe_permute.restype = ctypes.c_int
+    MOE_ERR_NULL, MOE_ERR_WORKSPACE = 1, 5
+    assert lib.moe_permute(*args, fake, ctypes.c_size_t(need - 4), None) == MOE_ERR_WORKSPACE
+    assert lib.moe_permute(*args, None, ctypes.c_size_t(need), None) == MOE_ERR_NULL
