@@ -188,6 +188,12 @@ VARIANTS = [
     {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "1", "MOE_GEMM_NSUB": "1", "MOE_GEMM_KSEG": "8", "MOE_GEMM_RING": "4"},
     {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "1", "MOE_GEMM_NSUB": "2", "MOE_GEMM_KSEG": "4", "MOE_GEMM_RING": "4"},
     {"MOE_GEMM_MODE": "2"},            # tile kernel (tiled codes, K <= 2048; plain codes fall back)
+    {"MOE_GEMM_MODE": "3"},            # its 4-wave, 32-row shape
+    # streaming kernel with either code-load cache policy (non-temporal or default)
+    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "4", "MOE_GEMM_NSUB": "2", "MOE_GEMM_KSEG": "4", "MOE_GEMM_RING": "2",
+     "MOE_GEMM_NT": "1"},
+    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "4", "MOE_GEMM_NSUB": "2", "MOE_GEMM_KSEG": "4", "MOE_GEMM_RING": "2",
+     "MOE_GEMM_NT": "0"},
 ]
 
 
