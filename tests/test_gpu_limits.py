@@ -8,6 +8,8 @@
 - H = 16384 (GEMM1 reduces over 128 groups; GEMM2 has 16384 weight rows) and
   I = 16384 (the reverse), with two experts.
 - Many rows on few experts (5000 tokens on 2 experts, k = 2).
+- A long prefill (8192 tokens, Zipf routing): 64 token ranges in the permutation and
+  several thousand tile-kernel items.
 - The dense GEMM at N = 65536 and at K = 65536.
 All within the layer tolerance (or the dense GEMM's derived bound).
 """
@@ -16,7 +18,7 @@ import pytest
 
 import oracle
 from helpers import assert_layer_close, bf16_dev, bf16_to_f64, say, to_dev, to_np_u16
-from w4a16_grouped_gemm_amd.inputs import Workload, bf16_bits, make_layer_inputs, make_shared_weights, pack_int4
+from w4a16_grouped_gemm_amd.inputs import WORKLOADS, Workload, bf16_bits, make_layer_inputs, make_shared_weights, pack_int4
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +30,7 @@ LIMITS = [
     (Workload("hidden_16384", 14, 2, 2, 0, 1, 16384, 128, (3,)), 3, None),
     (Workload("inter_16384", 15, 2, 2, 0, 1, 128, 16384, (3,)), 3, None),
     (Workload("rows_5000", 16, 2, 2, 0, 2, 256, 256, (5000,)), 5000, 24),
+    (WORKLOADS["qwen3_prefill"], 8192, 48),           # tiled codes (the tile kernel)
 ]
 
 
@@ -37,8 +40,13 @@ def test_layer_at_limits(wl, T, n):
     from w4a16_grouped_gemm_amd import ops
     say(f"limits {wl.name} T={T}")
     inp = make_layer_inputs(wl, T)
-    o = ops.moe_w4a16_forward(bf16_dev(inp.x), to_dev(inp.logits), to_dev(inp.w13_q), bf16_dev(inp.s13),
-                              to_dev(inp.w2_q), bf16_dev(inp.s2), wl.top_k, expert_begin=wl.expert_begin)
+    w13, w2 = to_dev(inp.w13_q), to_dev(inp.w2_q)
+    tiled = wl.name == "qwen3_prefill"
+    if tiled:
+        w13, w2 = ops.pack_weights(ops.W13_SWIGLU, w13), ops.pack_weights(ops.W2, w2)
+    o = ops.moe_w4a16_forward(bf16_dev(inp.x), to_dev(inp.logits), w13, bf16_dev(inp.s13), w2, bf16_dev(inp.s2),
+                              wl.top_k, expert_begin=wl.expert_begin,
+                              weight_layout=ops.WEIGHTS_TILED if tiled else ops.WEIGHTS_PLAIN)
     torch.cuda.synchronize()
     got = to_np_u16(o)
     sel = None
