@@ -1,19 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the W4A16 MoE expert layer on one MI355X.
 
-Workload: the Qwen3-30B-A3B MoE layer (128 experts, top-8, hidden 2048,
-expert intermediate 768, int4 group-128 weights, bf16 activations) in
+Headline workload: the Qwen3-30B-A3B MoE layer (128 experts, top-8, hidden
+2048, expert intermediate 768, int4 group-128 weights, bf16 activations) in
 decode at 256 tokens. One step = one full layer forward (route, permute,
-GEMM1 + SwiGLU, GEMM2, finalize) on one batch. Steps rotate over L layer
-replicas with distinct weights and logits (L * 311 MB of weights), so the
-256 MB Infinity Cache cannot serve the weights from one step to the next.
-Replica 0 is the seeded workload of the parity tests; replicas 1..L-1 are
-drawn on the GPU. All inputs are resident in HBM before timing starts; the
-steps are replayed from HIP graphs (one graph per L steps).
+GEMM1 + SwiGLU, GEMM2, finalize) on one batch. Steps rotate over layer
+replicas with distinct weights and logits, so the 256 MB Infinity Cache
+cannot serve the weights from one step to the next. Replica 0 is the seeded
+workload of the parity tests; the others are drawn on the GPU. All inputs are
+resident in HBM before timing starts; the steps are replayed from HIP graphs.
 
-Prints ONE JSON line (rank 0) with the layer throughput, the roofline of the
-dominant kernel (GEMM1, bound by HBM weight bytes), a decode-size sweep and
-the CPU oracle timed on the host as a reported baseline.
+`value` times exactly --steps steps (after --warmup untimed ones). Every
+workload is also measured the way the measurement plan asks: one HIP graph of
+several layer calls with distinct weights and batches, 10 warm-up replays,
+then 50 replays each timed with HIP events on the replaying stream; the
+median per call is reported:
+  - the decode sweep at 1 / 16 / 64 / 256 tokens (weight HBM GB/s, % of peak),
+  - the 2048-token Zipf prefill (TFLOP/s, % of the bf16 MFMA peak),
+  - the expert-parallel shard (32 of 256 experts, H 7168, I 2048) at
+    1 / 16 / 64 / 256 tokens,
+  - the layer with one shared expert, the finalize stream, the dense GEMM.
+Prints ONE JSON line with the headline, the roofline of the dominant kernel
+(GEMM1, HBM-bound on weight bytes) and of GEMM2, and the CPU oracle timed on
+the host (per workload) as a reported baseline.
 """
 from __future__ import annotations
 
@@ -21,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -29,8 +39,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s; weight HBM GB/s % peak (decode), MFMA % (prefill)"
 HBM_PEAK_GBPS = 8000.0
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "gemm1_swiglu_qwen3_decode_t256_counters.json")
+MFMA_PEAK_TFLOPS = 2500.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["w4a16_grouped_gemm_amd/csrc/gemm_w4a16.hip", "w4a16_grouped_gemm_amd/csrc/common.hpp"]
+WARM_REPLAYS = 10
+TIMED_REPLAYS = 50
+CACHE_BYTES = 256e6          # Infinity Cache (MALL); the L2s (8 x 4 MB) are smaller
 
 
 def log(*a):
@@ -52,32 +66,13 @@ def weight_bytes_per_expert(H: int, I: int):
     return w13, w2
 
 
-MFMA_PEAK_TFLOPS = 2500.0
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
 
-
-def time_prefill(ops, reps, torch, layout, steps, warmup):
-    """The same layer shape in prefill: 2048 tokens whose routing follows Zipf(1.1)
-    expert popularity, weights of the decode replicas. Reported against the
-    dense bf16 MFMA peak (algorithmic flops 6 * I * H per routed row)."""
-    from w4a16_grouped_gemm_amd.inputs import WORKLOADS, make_layer_inputs
-    wl = WORKLOADS["qwen3_prefill"]
-    T = 2048
-    inp = make_layer_inputs(wl, T, weights=False)
-    dev = torch.device("cuda")
-    x = torch.from_numpy(inp.x).to(dev).view(torch.bfloat16)
-    lg = torch.from_numpy(inp.logits).to(dev)
-    reps_p = [dict(r, x=x, logits=lg) for r in reps]
-    dt, _ = time_layer(ops, wl, reps_p, steps, warmup, torch, layout)
-    us = dt / steps * 1e6
-    flops = 6.0 * wl.inter * wl.hidden * T * wl.top_k
-    return {"tokens": T, "routing": "zipf(1.1)", "us_per_layer": round(us, 1), "tokens_per_s": round(T / (us * 1e-6), 1),
-            "tflops": round(flops / (us * 1e-6) / 1e12, 1), "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4)}
-
-
-def _graph_time(torch, fns, reps_n):
-    """Seconds per call of the launches `fns` (one each per replay), replayed
-    from a HIP graph, HIP events on the replaying stream."""
-    for f in fns:
+def capture(torch, fns):
+    """One HIP graph holding one call of each function in `fns`."""
+    for f in fns:                   # eager pass (loads kernels, checks arguments)
         f()
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
@@ -89,87 +84,189 @@ def _graph_time(torch, fns, reps_n):
                 f()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
+    return graph
+
+
+def replay_stats(torch, graph, calls, warm=WARM_REPLAYS, reps=TIMED_REPLAYS):
+    """`warm` untimed replays, then `reps` replays each bracketed by HIP events
+    on the replaying stream; microseconds per call (graph time / calls)."""
     stream = torch.cuda.current_stream()
-    graph.replay()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(reps_n):
+    for _ in range(warm):
         graph.replay()
-    end.record(stream)
-    end.synchronize()
-    return start.elapsed_time(end) / 1000.0 / (reps_n * len(fns))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        graph.replay()
+        ev[i + 1].record(stream)
+    ev[-1].synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 / calls for i in range(reps)]
+    return {"median_us": round(statistics.median(per), 3), "mean_us": round(sum(per) / reps, 3),
+            "min_us": round(min(per), 3), "max_us": round(max(per), 3), "replays": reps,
+            "warmup_replays": warm, "calls_per_replay": calls}
 
 
-def time_ep_shard(ops, torch, layout, steps, warmup, T=256, L=3):
-    """One GPU's shard of an expert-parallel layer (32 local of 256 experts,
-    hidden 7168, intermediate 2048) in decode: the layer on its local slots,
-    L replicas of 726 MB of weights."""
-    from w4a16_grouped_gemm_amd.inputs import WORKLOADS
-    wl = WORKLOADS["ep_shard_decode"]
-    _, reps = make_replicas(wl, T, L, torch, seed_base=11)
-    if layout == ops.WEIGHTS_TILED:
-        pack_replicas(reps, ops)
-    stats = routing_stats(ops, wl, reps, torch)
-    dt, _ = time_layer(ops, wl, reps, steps, warmup, torch, layout)
-    us = dt / steps * 1e6
-    w13b, w2b = weight_bytes_per_expert(wl.hidden, wl.inter)
-    act = sum(st["active"] for st in stats) / L
-    gbps = act * (w13b + w2b) / (us * 1e-6) / 1e9
-    del reps
-    torch.cuda.empty_cache()
-    return {"workload": "ep_shard_decode (32 of 256 experts, hidden 7168, inter 2048, top-8)", "tokens": T,
-            "us_per_layer": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1), "active_experts": act,
-            "local_rows": sum(st["rows"] for st in stats) / L, "weight_GBps": round(gbps, 1),
-            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+# ---------------------------------------------------------------------------
+# inputs
+# ---------------------------------------------------------------------------
 
-
-def time_shared(ops, wl, reps, torch, layout, steps, warmup, S=1):
-    """The decode layer with S shared experts of the routed shape (every token
-    through each; DeepSeek-style), on the same replicas."""
+def make_weights(wl, L, torch, ops, layout, seed_base):
+    """L weight replicas: replica 0 the seeded numpy workload, the rest drawn
+    on the GPU with the same distributions. Codes packed when tiled."""
+    from w4a16_grouped_gemm_amd.inputs import make_layer_inputs
     dev = torch.device("cuda")
+    H, I, El = wl.hidden, wl.inter, wl.num_local_experts
+    inp = make_layer_inputs(wl, 1)
+
+    def d(a, dtype=None):
+        t = torch.from_numpy(a).to(dev)
+        return t.view(dtype) if dtype is not None else t
+
+    reps = [dict(w13=d(inp.w13_q), s13=d(inp.s13, torch.bfloat16), w2=d(inp.w2_q), s2=d(inp.s2, torch.bfloat16))]
     g = torch.Generator(device=dev)
-    H, I = wl.hidden, wl.inter
-    reps_s = []
-    for i, r in enumerate(reps):
-        g.manual_seed(31000 + i)
-        w13 = torch.randint(0, 256, (S, 2 * I, H // 2), generator=g, device=dev, dtype=torch.uint8)
-        w2 = torch.randint(0, 256, (S, H, I // 2), generator=g, device=dev, dtype=torch.uint8)
-        if layout == ops.WEIGHTS_TILED:
-            w13, w2 = ops.pack_weights(ops.W13_SWIGLU, w13), ops.pack_weights(ops.W2, w2)
-        s13 = torch.empty((S, 2 * I, H // 128), device=dev).uniform_(0.005, 0.02, generator=g).to(torch.bfloat16)
-        s2 = torch.empty((S, H, I // 128), device=dev).uniform_(0.005, 0.02, generator=g).to(torch.bfloat16)
-        reps_s.append(dict(r, shared=(w13, s13, w2, s2)))
-    T = reps[0]["x"].shape[0]
-    dt, _ = time_layer(ops, wl, reps_s, steps, warmup, torch, layout)
-    us = dt / steps * 1e6
-    w13b, w2b = weight_bytes_per_expert(H, I)
-    stats = routing_stats(ops, wl, reps, torch)
-    act = sum(st["active"] for st in stats) / len(reps) + S
-    gbps = act * (w13b + w2b) / (us * 1e-6) / 1e9
-    return {"shared_experts": S, "tokens": T, "us_per_layer": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 1),
-            "experts_streamed": act, "weight_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    for i in range(1, L):
+        g.manual_seed(seed_base * 1000 + i)
+        reps.append(dict(
+            w13=torch.randint(0, 256, (El, 2 * I, H // 2), generator=g, device=dev, dtype=torch.uint8),
+            s13=torch.empty((El, 2 * I, H // 128), device=dev).uniform_(0.005, 0.02, generator=g).to(torch.bfloat16),
+            w2=torch.randint(0, 256, (El, H, I // 2), generator=g, device=dev, dtype=torch.uint8),
+            s2=torch.empty((El, H, I // 128), device=dev).uniform_(0.005, 0.02, generator=g).to(torch.bfloat16)))
+    if layout == ops.WEIGHTS_TILED:
+        for r in reps:
+            r["w13"] = ops.pack_weights(ops.W13_SWIGLU, r["w13"])
+            r["w2"] = ops.pack_weights(ops.W2, r["w2"])
+    return reps
 
 
-def time_finalize_stream(ops, torch, T=4096, k=8, H=4096, E=128, reps_n=20):
-    """The finalize on its stress shape: fp32 y [T*k, H] (512 MiB, two buffers
-    alternate so the Infinity Cache cannot hold them), bf16 out [T, H]."""
+def make_batches(wl, T, n, torch, seed):
+    """n batches (x, logits): batch 0 the seeded numpy workload of T tokens,
+    the rest drawn on the GPU (Zipf routing redrawn on the host per batch)."""
+    import numpy as np
+    from w4a16_grouped_gemm_amd.inputs import make_layer_inputs, zipf_logits
+    dev = torch.device("cuda")
+    inp = make_layer_inputs(wl, T, weights=False)
+    out = [dict(x=torch.from_numpy(inp.x).to(dev).view(torch.bfloat16), logits=torch.from_numpy(inp.logits).to(dev))]
+    g = torch.Generator(device=dev)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for i in range(1, n):
+        g.manual_seed(seed * 1000 + i)
+        x = torch.randn((T, wl.hidden), generator=g, device=dev).to(torch.bfloat16)
+        if wl.routing == "zipf":
+            lg = torch.from_numpy(zipf_logits(rng, T, wl.num_experts)).to(dev)
+        else:
+            lg = torch.randn((T, wl.num_experts), generator=g, device=dev)
+        out.append(dict(x=x, logits=lg))
+    return out
+
+
+def n_calls_for(active_bytes, minimum=8):
+    """Layer calls per graph: at least `minimum`, and enough that the weights
+    one replay streams are several times the Infinity Cache."""
+    n = minimum
+    while n < 64 and n * active_bytes < 3 * CACHE_BYTES:
+        n *= 2
+    return n
+
+
+def routing_stats(ops, wl, batches, torch):
+    """Per batch: active local experts and local rows (from the GPU routing)."""
+    res = []
+    for b in batches:
+        ids, _ = ops.route(b["logits"], wl.top_k)
+        counts, offsets, *_ = ops.permute(ids, wl.num_local_experts, num_experts=wl.num_experts,
+                                          expert_begin=wl.expert_begin)
+        res.append((counts, offsets))
+    torch.cuda.synchronize()
+    return [dict(active=int((c > 0).sum().item()), rows=int(o[-1].item())) for c, o in res]
+
+
+def layer_fns(ops, wl, weights, batches, calls, torch, layout, shared=None):
+    """`calls` forward calls: call i uses weight replica i % L and batch i % B."""
+    T = batches[0]["x"].shape[0]
+    shape = ops.make_shape(T, wl.hidden, wl.inter, wl.num_experts, wl.num_local_experts, wl.top_k,
+                           wl.expert_begin, weight_layout=layout)
+    if shared is None:
+        wsz = ops.workspace_size(shape)
+    else:
+        import ctypes
+        wsz = int(ops.load_library().moe_w4a16_workspace_size_shared(ctypes.byref(shape), shared[0][0].shape[0]))
+    ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((T, wl.hidden), dtype=torch.bfloat16, device="cuda") for _ in range(calls)]
+
+    def fwd(i):
+        w, b = weights[i % len(weights)], batches[i % len(batches)]
+        ops.moe_w4a16_forward(b["x"], b["logits"], w["w13"], w["s13"], w["w2"], w["s2"], wl.top_k, out=outs[i],
+                              expert_begin=wl.expert_begin, workspace=ws, weight_layout=layout,
+                              shared=None if shared is None else shared[i % len(shared)])
+    return [lambda i=i: fwd(i) for i in range(calls)]
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def decode_point(ops, wl, weights, T, torch, layout, seed, shared=None):
+    """One decode point: median per layer call, weight bytes of the active
+    experts (int4 + bf16 scales) per call, and the fraction of HBM peak."""
+    w13b, w2b = weight_bytes_per_expert(wl.hidden, wl.inter)
+    probe = make_batches(wl, T, 4, torch, seed)
+    act0 = sum(s["active"] for s in routing_stats(ops, wl, probe, torch)) / len(probe)
+    calls = n_calls_for(act0 * (w13b + w2b))
+    batches = make_batches(wl, T, calls, torch, seed)
+    st = routing_stats(ops, wl, batches, torch)
+    act = sum(s["active"] for s in st) / calls
+    rows = sum(s["rows"] for s in st) / calls
+    nsh = 0 if shared is None else shared[0][0].shape[0]
+    g = capture(torch, layer_fns(ops, wl, weights, batches, calls, torch, layout, shared))
+    r = replay_stats(torch, g, calls)
+    del g
+    us = r["median_us"]
+    streamed = (act + nsh) * (w13b + w2b)
+    gbps = streamed / (us * 1e-6) / 1e9
+    rec = {"tokens": T, "us_per_layer": us, "tokens_per_s": round(T / (us * 1e-6), 1),
+           "active_experts": act, "local_rows": rows, "weight_bytes": round(streamed),
+           "weight_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+           "layer_calls_per_graph": calls, "weight_replicas": len(weights), "timing": r}
+    if nsh:
+        rec["shared_experts"] = nsh
+    return rec
+
+
+def prefill_point(ops, wl, weights, torch, layout, T=2048):
+    """2048 tokens with Zipf(1.1) expert popularity: algorithmic flops
+    6 * I * H per routed row against the dense bf16 MFMA peak."""
+    batches = make_batches(wl, T, 8, torch, seed=2048)
+    g = capture(torch, layer_fns(ops, wl, weights, batches, 8, torch, layout))
+    r = replay_stats(torch, g, 8)
+    del g
+    us = r["median_us"]
+    flops = 6.0 * wl.inter * wl.hidden * T * wl.top_k
+    tf = flops / (us * 1e-6) / 1e12
+    return {"tokens": T, "routing": "zipf(1.1)", "us_per_layer": us, "tokens_per_s": round(T / (us * 1e-6), 1),
+            "tflops": round(tf, 1), "mfma_frac": round(tf / MFMA_PEAK_TFLOPS, 4), "flops": flops, "timing": r}
+
+
+def finalize_point(ops, torch, T=4096, k=8, H=4096, E=128):
+    """The finalize on its stress shape: fp32 y [T*k, H] (512 MiB; four
+    buffers rotate so the Infinity Cache cannot hold them), bf16 out [T, H]."""
     dev = torch.device("cuda")
     g = torch.Generator(device=dev)
     g.manual_seed(4242)
     logits = torch.randn((T, E), generator=g, device=dev)
     ids, w = ops.route(logits, k)
     _, _, _, inv, _ = ops.permute(ids, E)
-    ys = [torch.randn((T * k, H), generator=g, device=dev) for _ in range(2)]
-    outs = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
-    sec = _graph_time(torch, [lambda i=i: ops.finalize(ys[i], w, inv, out=outs[i]) for i in range(2)], reps_n)
-    nbytes = T * k * H * 4 + T * k * 8 + T * H * 2
-    del ys, outs
+    ys = [torch.randn((T * k, H), generator=g, device=dev) for _ in range(4)]
+    outs = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    gr = capture(torch, [lambda i=i: ops.finalize(ys[i], w, inv, out=outs[i]) for i in range(4)])
+    r = replay_stats(torch, gr, 4)
+    del gr, ys, outs
     torch.cuda.empty_cache()
-    return {"shape": f"T={T} k={k} H={H}, fp32 y, bf16 out", "us": round(sec * 1e6, 2), "bytes": nbytes,
-            "GBps": round(nbytes / sec / 1e9, 1), "hbm_frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBPS, 4)}
+    nbytes = T * k * H * 4 + T * k * 8 + T * H * 2
+    gbps = nbytes / (r["median_us"] * 1e-6) / 1e9
+    return {"shape": f"T={T} k={k} H={H}, fp32 y, bf16 out", "us": r["median_us"], "bytes": nbytes,
+            "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "timing": r}
 
 
-def time_dense(ops, torch, layout, Ms=(1, 16, 256), N=14336, K=4096, L=16, reps_n=20):
+def dense_points(ops, torch, layout, Ms=(1, 16, 256), N=14336, K=4096, L=16):
     """Dense W4A16 GEMM c[M, N] = a[M, K] . W^T over L weight replicas
     (L * 30 MB, more than the Infinity Cache holds)."""
     dev = torch.device("cuda")
@@ -187,10 +284,12 @@ def time_dense(ops, torch, layout, Ms=(1, 16, 256), N=14336, K=4096, L=16, reps_
     for M in Ms:
         a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
         outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(L)]
-        fns = [lambda i=i: ops.dense_gemm_w4a16(a, ws[i][0], ws[i][1], out=outs[i], weight_layout=layout)
-               for i in range(L)]
-        sec = _graph_time(torch, fns, reps_n)
-        res.append({"M": M, "N": N, "K": K, "us": round(sec * 1e6, 2),
+        gr = capture(torch, [lambda i=i: ops.dense_gemm_w4a16(a, ws[i][0], ws[i][1], out=outs[i],
+                                                             weight_layout=layout) for i in range(L)])
+        r = replay_stats(torch, gr, L)
+        del gr
+        sec = r["median_us"] * 1e-6
+        res.append({"M": M, "N": N, "K": K, "us": r["median_us"],
                     "weight_GBps": round(wbytes / sec / 1e9, 1), "hbm_frac": round(wbytes / sec / 1e9 / HBM_PEAK_GBPS, 4),
                     "tflops": round(2.0 * M * N * K / sec / 1e12, 2)})
     del ws
@@ -198,194 +297,183 @@ def time_dense(ops, torch, layout, Ms=(1, 16, 256), N=14336, K=4096, L=16, reps_
     return res
 
 
-def gemm1_algorithmic_bytes(wl, T, active, rows):
-    """Bytes GEMM1 must move at least once: the weights and scales of every
-    active expert, the T input rows, the rows x I SwiGLU outputs, the offsets
-    and the row index."""
-    w13b, _ = weight_bytes_per_expert(wl.hidden, wl.inter)
-    return (active * w13b + T * wl.hidden * 2 + rows * wl.inter * 2 + (wl.num_local_experts + 1) * 4
-            + rows * 4)
-
-
-def make_replicas(wl, T, L, torch, seed_base=7):
-    """Replica 0 from the seeded numpy generator, the rest drawn on the GPU."""
-    from w4a16_grouped_gemm_amd.inputs import make_layer_inputs
-    dev = torch.device("cuda")
-    H, I, E, El = wl.hidden, wl.inter, wl.num_experts, wl.num_local_experts
-    inp = make_layer_inputs(wl, T)
-
-    def d(a, dtype=None):
-        t = torch.from_numpy(a).to(dev)
-        return t.view(dtype) if dtype is not None else t
-
-    reps = [dict(x=d(inp.x, torch.bfloat16), logits=d(inp.logits), w13=d(inp.w13_q), s13=d(inp.s13, torch.bfloat16),
-                 w2=d(inp.w2_q), s2=d(inp.s2, torch.bfloat16))]
-    g = torch.Generator(device=dev)
-    for i in range(1, L):
-        g.manual_seed(seed_base * 1000 + i)
-        reps.append(dict(
-            x=torch.randn((T, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16),
-            logits=torch.randn((T, E), generator=g, device=dev, dtype=torch.float32),
-            w13=torch.randint(0, 256, (El, 2 * I, H // 2), generator=g, device=dev, dtype=torch.uint8),
-            s13=torch.empty((El, 2 * I, H // 128), device=dev).uniform_(0.005, 0.02, generator=g).to(torch.bfloat16),
-            w2=torch.randint(0, 256, (El, H, I // 2), generator=g, device=dev, dtype=torch.uint8),
-            s2=torch.empty((El, H, I // 128), device=dev).uniform_(0.005, 0.02, generator=g).to(torch.bfloat16)))
-    return inp, reps
-
-
-def pack_replicas(reps, ops):
-    """Reorder every replica's codes into the tiled layout (a once-per-model step, untimed)."""
-    for r in reps:
-        r["w13"] = ops.pack_weights(ops.W13_SWIGLU, r["w13"])
-        r["w2"] = ops.pack_weights(ops.W2, r["w2"])
-
-
-def new_batch(wl, T, reps, torch, seed):
-    """Fresh activations / logits of T tokens for every replica (weights kept)."""
+def shared_weights(ops, wl, L, torch, layout, S=1):
     dev = torch.device("cuda")
     g = torch.Generator(device=dev)
+    H, I = wl.hidden, wl.inter
     out = []
-    for i, r in enumerate(reps):
-        g.manual_seed(seed * 1000 + i)
-        out.append(dict(r, x=torch.randn((T, wl.hidden), generator=g, device=dev).to(torch.bfloat16),
-                        logits=torch.randn((T, wl.num_experts), generator=g, device=dev)))
+    for i in range(L):
+        g.manual_seed(31000 + i)
+        w13 = torch.randint(0, 256, (S, 2 * I, H // 2), generator=g, device=dev, dtype=torch.uint8)
+        w2 = torch.randint(0, 256, (S, H, I // 2), generator=g, device=dev, dtype=torch.uint8)
+        if layout == ops.WEIGHTS_TILED:
+            w13, w2 = ops.pack_weights(ops.W13_SWIGLU, w13), ops.pack_weights(ops.W2, w2)
+        s13 = torch.empty((S, 2 * I, H // 128), device=dev).uniform_(0.005, 0.02, generator=g).to(torch.bfloat16)
+        s2 = torch.empty((S, H, I // 128), device=dev).uniform_(0.005, 0.02, generator=g).to(torch.bfloat16)
+        out.append((w13, s13, w2, s2))
     return out
 
 
-def time_layer(ops, wl, reps, steps, warmup, torch, layout=0):
-    """Capture L forwards in one graph; replay; return (seconds for `steps` steps, outs)."""
-    L = len(reps)
-    T = reps[0]["x"].shape[0]
-    outs = [torch.empty((T, wl.hidden), dtype=torch.bfloat16, device="cuda") for _ in reps]
-    shape = ops.make_shape(T, wl.hidden, wl.inter, wl.num_experts, wl.num_local_experts, wl.top_k,
-                           wl.expert_begin, weight_layout=layout)
-    nsh = reps[0]["shared"][0].shape[0] if reps[0].get("shared") is not None else 0
-    wsz = ops.workspace_size(shape) if nsh == 0 else \
-        int(ops.load_library().moe_w4a16_workspace_size_shared(__import__("ctypes").byref(shape), nsh))
-    ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device="cuda")
+# ---------------------------------------------------------------------------
+# the GEMMs alone (roofline of the dominant kernel)
+# ---------------------------------------------------------------------------
 
-    def fwd(i):
-        r = reps[i]
-        ops.moe_w4a16_forward(r["x"], r["logits"], r["w13"], r["s13"], r["w2"], r["s2"], wl.top_k,
-                              out=outs[i], expert_begin=wl.expert_begin, workspace=ws, weight_layout=layout,
-                              shared=r.get("shared"))
+def gemm_alone(ops, wl, weights, batches, torch, layout, kind):
+    """Average duration of one grouped-GEMM launch (GEMM1 with SwiGLU, or
+    GEMM2), HIP events on the replaying stream over the timed replays, and
+    its algorithmic bytes: active experts' weights and scales, the activation
+    rows read, the output rows written, offsets and row index."""
+    T = batches[0]["x"].shape[0]
+    k, H, I = wl.top_k, wl.hidden, wl.inter
+    calls = len(batches)
+    pre = []
+    for i, b in enumerate(batches):
+        ids, _ = ops.route(b["logits"], k)
+        counts, offsets, perm, _, _ = ops.permute(ids, wl.num_local_experts, num_experts=wl.num_experts,
+                                                  expert_begin=wl.expert_begin)
+        pre.append((counts, offsets, perm))
+    hs = [torch.randn((T * k, I), device="cuda").to(torch.bfloat16) * 0.05 for _ in range(calls)]
+    outs = [torch.empty((T * k, I if kind == ops.W13_SWIGLU else H), dtype=torch.bfloat16, device="cuda")
+            for _ in range(calls)]
 
-    for i in range(L):          # eager pass (also loads kernels)
-        fwd(i)
+    def call(i):
+        w, b = weights[i % len(weights)], batches[i]
+        _, offsets, perm = pre[i]
+        if kind == ops.W13_SWIGLU:
+            ops.grouped_gemm_w4a16(ops.W13_SWIGLU, b["x"], offsets, w["w13"], w["s13"], num_tokens=T, top_k=k,
+                                   a_row_index=perm, num_experts=wl.num_experts, out=outs[i], weight_layout=layout)
+        else:
+            ops.grouped_gemm_w4a16(ops.W2, hs[i], offsets, w["w2"], w["s2"], num_tokens=T, top_k=k,
+                                   num_experts=wl.num_experts, out=outs[i], weight_layout=layout)
+
+    g = capture(torch, [lambda i=i: call(i) for i in range(calls)])
+    r = replay_stats(torch, g, calls)
+    del g
     torch.cuda.synchronize()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    graphs_all = torch.cuda.CUDAGraph()
-    singles = [torch.cuda.CUDAGraph() for _ in range(L)]
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(graphs_all, stream=s):
-            for i in range(L):
-                fwd(i)
-        for i in range(L):
-            with torch.cuda.graph(singles[i], stream=s):
-                fwd(i)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-
-    def run(n):
-        full, rem = divmod(n, L)
-        for _ in range(full):
-            graphs_all.replay()
-        for i in range(rem):
-            singles[i].replay()
-
-    run(warmup)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run(steps)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    return dt, outs
+    w13b, w2b = weight_bytes_per_expert(H, I)
+    nb = 0.0
+    for counts, offsets, _ in pre:
+        act = int((counts > 0).sum().item())
+        rows = int(offsets[-1].item())
+        if kind == ops.W13_SWIGLU:
+            nb += act * w13b + T * H * 2 + rows * I * 2 + (wl.num_local_experts + 1) * 4 + rows * 4
+        else:
+            nb += act * w2b + rows * I * 2 + rows * H * 2 + (wl.num_local_experts + 1) * 4
+    nb /= calls
+    return r["mean_us"], nb, r
 
 
-def routing_stats(ops, wl, reps, torch):
-    """Per replica: perm / offsets (for the kernel timing) and active experts."""
-    res = []
-    for r in reps:
-        ids, w = ops.route(r["logits"], wl.top_k)
-        counts, offsets, perm, inv, _ = ops.permute(ids, wl.num_local_experts, num_experts=wl.num_experts,
-                                                    expert_begin=wl.expert_begin)
-        res.append(dict(offsets=offsets, perm=perm, counts=counts))
-    torch.cuda.synchronize()
-    for d in res:
-        d["active"] = int((d["counts"] > 0).sum().item())
-        d["rows"] = int(d["offsets"][-1].item())
-    return res
-
-
-def time_gemm1(ops, wl, reps, stats, reps_n, torch, layout=0):
-    """Average duration of one GEMM1 (w13 + SwiGLU) launch, HIP events on its stream."""
-    L = len(reps)
-    T = reps[0]["x"].shape[0]
-    hs = [torch.empty((T * wl.top_k, wl.inter), dtype=torch.bfloat16, device="cuda") for _ in reps]
-
-    def g1(i):
-        ops.grouped_gemm_w4a16(ops.W13_SWIGLU, reps[i]["x"], stats[i]["offsets"], reps[i]["w13"],
-                               reps[i]["s13"], num_tokens=T, top_k=wl.top_k, a_row_index=stats[i]["perm"],
-                               num_experts=wl.num_experts, out=hs[i], weight_layout=layout)
-
-    for i in range(L):
-        g1(i)
-    torch.cuda.synchronize()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(graph, stream=s):
-            for i in range(L):
-                g1(i)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    graph.replay()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(reps_n):
-        graph.replay()
-    end.record(stream)
-    end.synchronize()
-    return start.elapsed_time(end) / 1000.0 / (reps_n * L)
-
-
-def load_traffic(expected_hash):
-    if not os.path.exists(PROFILE_COUNTERS):
-        return None, "no counter profile"
-    with open(PROFILE_COUNTERS) as f:
+def load_traffic(name, expected_hash):
+    """HBM bytes per dispatch from a committed counter summary, scaled by the
+    same counters read on a device copy of known size; None once the kernel
+    source has changed since the counters were taken."""
+    path = os.path.join(PROFILE_DIR, name)
+    if not os.path.exists(path):
+        return None, f"no counter summary {name}"
+    with open(path) as f:
         c = json.load(f)
     if c.get("kernel_source_sha256") != expected_hash:
         return None, "kernel changed since the counters were taken"
     ff = c["copy_bytes"] / (c["copy_fetch_kib"] * 1024.0)
     fw = c["copy_bytes"] / (c["copy_write_kib"] * 1024.0)
     return (c["fetch_kib_per_dispatch"] * ff + c["write_kib_per_dispatch"] * fw) * 1024.0, \
-        f"FETCH_SIZE x {ff:.4f} + WRITE_SIZE x {fw:.4f} (copy-kernel scale)"
+        f"FETCH_SIZE x {ff:.4f} + WRITE_SIZE x {fw:.4f} (copy-kernel scale), {name}"
 
 
-def cpu_baseline(inp, wl, budget_s=10.0, max_runs=64):
-    """The oracle's full layer on the seeded batch, repeated until about
-    `budget_s` seconds of host time are spent; tokens per second overall."""
+# ---------------------------------------------------------------------------
+# the CPU oracle on the host (reported baseline)
+# ---------------------------------------------------------------------------
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _time_runs(fn, max_runs=3, long_s=0.5):
+    """Median wall time of up to `max_runs` runs; a single run once one takes
+    longer than long_s (keeps the leg near 30 s of host time)."""
+    ts = []
+    for _ in range(max_runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+        if ts[-1] > long_s:
+            break
+    return statistics.median(ts), len(ts)
+
+
+def cpu_baseline():
+    """The oracle (fp64 C, OpenMP) on every workload, on the host cores.
+    Each workload's weights are drawn once (its largest token count) and
+    reused with the seeded activations and logits of the other token counts;
+    long layers run on a seeded sample of tokens (tokens are independent, so
+    a sample's tokens/s is the layer's); the finalize stress on 512 of its
+    4096 tokens. Headline: the 256-token decode layer."""
+    import dataclasses
+    import numpy as np
     import oracle
+    from w4a16_grouped_gemm_amd.inputs import make_finalize_stress, make_layer_inputs
     oracle.build(force=False)
     cores = len(os.sched_getaffinity(0))
     env_threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
     threads = min(cores, env_threads) if env_threads > 0 else cores
-    oracle.set_threads(threads)
-    runs, total = 0, 0.0
-    while runs < max_runs and total < budget_s:
-        t0 = time.perf_counter()
-        oracle.layer(inp.x, inp.logits, inp.w13_q, inp.s13, inp.w2_q, inp.s2, top_k=wl.top_k,
-                     expert_begin=wl.expert_begin)
-        total += time.perf_counter() - t0
-        runs += 1
-    return {"value": inp.tokens * runs / total, "unit": "tokens/s", "cores": oracle.get_threads(),
-            "kind": "oracle",
-            "sample": f"{runs} run(s) of the full layer (fp64) over the seeded {inp.tokens}-token batch of "
-                      f"replica 0, {total:.1f} s in all"}
+    per = []
 
+    def layer_case(inp, n_sample=None):
+        w, T = inp.workload, inp.tokens
+        sel, n = None, T
+        if n_sample is not None and n_sample < T:
+            sel = np.zeros(T, np.uint8)
+            sel[np.unique(np.linspace(0, T - 1, n_sample).astype(int))] = 1
+            n = int(sel.sum())
+        sec, runs = _time_runs(lambda: oracle.layer(inp.x, inp.logits, inp.w13_q, inp.s13, inp.w2_q, inp.s2,
+                                                    top_k=w.top_k, expert_begin=w.expert_begin, tok_sel=sel))
+        per.append({"workload": w.name, "tokens": T, "tokens_computed": n, "seconds": round(sec, 4), "runs": runs,
+                    "tokens_per_s": round(n / sec, 2), "threads": oracle.get_threads()})
+        return per[-1]
+
+    def with_batch(base, wl, T):
+        b = make_layer_inputs(wl, T, weights=False)
+        return dataclasses.replace(base, workload=b.workload, tokens=T, x=b.x, logits=b.logits)
+
+    tiny = make_layer_inputs("tiny", 16)
+    oracle.set_threads(1)
+    c0_single = layer_case(tiny)
+    oracle.set_threads(threads)
+    layer_case(tiny)
+    q = make_layer_inputs("qwen3_decode", 256)
+    for T in (1, 16, 64):
+        layer_case(with_batch(q, "qwen3_decode", T))
+    head = layer_case(q)
+    layer_case(with_batch(q, "qwen3_prefill", 2048), n_sample=128)
+    ep = make_layer_inputs("ep_shard_decode", 16)
+    for T in (1, 16, 64, 256):
+        layer_case(ep if T == 16 else with_batch(ep, "ep_shard_decode", T), n_sample=16)
+    del q, ep
+    fs = make_finalize_stress(tokens=512)
+    ids, w = oracle.route(fs.logits, 8)
+    w = np.where(fs.zero_mask, np.float32(0.0), w).astype(np.float32)
+    _, _, _, inv = oracle.permute(ids, 128, 0)
+    sec, runs = _time_runs(lambda: oracle.finalize(fs.y, w, inv, out_f32=True))
+    nbytes = fs.y.nbytes + 512 * 8 * 8 + 512 * 4096 * 4
+    per.append({"workload": "finalize_stress", "tokens": 512, "seconds": round(sec, 4), "runs": runs,
+                "tokens_per_s": round(512 / sec, 1), "GBps": round(nbytes / sec / 1e9, 3),
+                "threads": oracle.get_threads()})
+    return {"value": head["tokens_per_s"], "unit": "tokens/s", "cores": oracle.get_threads(), "kind": "oracle",
+            "sample": "the oracle's full 256-token decode layer (fp64 C, OpenMP) on the seeded batch, "
+                      f"{head['runs']} run(s), median",
+            "cpu_model": cpu_model(), "host_cpus": cores,
+            "c0_single_thread": {"seconds": c0_single["seconds"], "tokens_per_s": c0_single["tokens_per_s"]},
+            "per_workload": per}
+
+
+# ---------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
@@ -396,6 +484,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of extra workloads to time "
+                    "(decode,prefill,ep,shared,finalize,dense); default all")
     ap.add_argument("--weights", choices=["tiled", "plain"], default="tiled",
                     help="int4 code layout the layer reads (tiled: packed once before timing)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -414,74 +504,92 @@ def main():
     from w4a16_grouped_gemm_amd.inputs import WORKLOADS
 
     ops.load_library()
+    only = set(filter(None, args.only.split(","))) or {"decode", "prefill", "ep", "shared", "finalize", "dense"}
+    if args.no_sweep:
+        only = set()
+    layout = ops.WEIGHTS_TILED if args.weights == "tiled" else ops.WEIGHTS_PLAIN
     wl = WORKLOADS["qwen3_decode"]
     T, L = args.tokens, args.replicas
-    log(f"generating {L} replicas of {wl.name} (T={T})")
-    inp, reps = make_replicas(wl, T, L, torch)
-    layout = ops.WEIGHTS_TILED if args.weights == "tiled" else ops.WEIGHTS_PLAIN
-    if layout == ops.WEIGHTS_TILED:
-        pack_replicas(reps, ops)
-    stats = routing_stats(ops, wl, reps, torch)
+    log(f"generating {L} weight replicas of {wl.name}")
+    weights = make_weights(wl, L, torch, ops, layout, seed_base=7)
+    batches = make_batches(wl, T, L, torch, seed=T)
     w13b, w2b = weight_bytes_per_expert(wl.hidden, wl.inter)
-    log("timing the layer")
-    dt, _ = time_layer(ops, wl, reps, args.steps, args.warmup, torch, layout)
+
+    # ---- the headline: exactly --steps steps after --warmup, one step = one layer call
+    log(f"timing {args.steps} steps at T={T}")
+    fns = layer_fns(ops, wl, weights, batches, L, torch, layout)
+    graph_all = capture(torch, fns)
+    singles = [capture(torch, [f]) for f in fns]
+
+    def run(n):
+        full, rem = divmod(n, L)
+        for _ in range(full):
+            graph_all.replay()
+        for i in range(rem):
+            singles[i].replay()
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(args.steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    del graph_all, singles
     ms = dt / args.steps * 1e3
     tok_s = T * args.steps / dt
-    mean_active = sum(s["active"] for s in stats) / L
-    layer_bytes = mean_active * (w13b + w2b)
-    layer_gbps = layer_bytes / (ms * 1e-3) / 1e9
+    st = routing_stats(ops, wl, batches, torch)
+    mean_active = sum(s["active"] for s in st) / L
+    layer_gbps = mean_active * (w13b + w2b) / (ms * 1e-3) / 1e9
 
-    log("timing GEMM1 alone")
-    g1 = time_gemm1(ops, wl, reps, stats, max(4, args.steps // L), torch, layout)
-    g1_bytes = sum(gemm1_algorithmic_bytes(wl, T, s["active"], s["rows"]) for s in stats) / L
-    achieved = g1_bytes / g1 / 1e9
-    traffic, traffic_note = load_traffic(kernel_source_hash())
+    log("timing GEMM1 and GEMM2 alone")
+    g1_us, g1_bytes, g1_r = gemm_alone(ops, wl, weights, batches, torch, layout, ops.W13_SWIGLU)
+    g2_us, g2_bytes, g2_r = gemm_alone(ops, wl, weights, batches, torch, layout, ops.W2)
+    src = kernel_source_hash()
+    traffic, traffic_note = load_traffic("gemm1_swiglu_qwen3_decode_t256_counters.json", src)
+    traffic2, traffic2_note = load_traffic("gemm2_down_qwen3_decode_t256_counters.json", src)
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
 
-    sweep = []
-    if not args.no_sweep:
-        for ts in (1, 16, 64):
-            log(f"sweep T={ts}")
-            reps_t = new_batch(wl, ts, reps, torch, seed=ts)
-            st = routing_stats(ops, wl, reps_t, torch)
-            n = max(args.steps, 200)
-            dts, _ = time_layer(ops, wl, reps_t, n, args.warmup, torch, layout)
-            act = sum(s["active"] for s in st) / L
-            us = dts / n * 1e6
-            sweep.append({"tokens": ts, "us_per_layer": round(us, 2), "tokens_per_s": round(ts * n / dts, 1),
-                          "active_experts": act, "weight_GBps": round(act * (w13b + w2b) / (us * 1e-6) / 1e9, 1),
-                          "hbm_frac": round(act * (w13b + w2b) / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
-        sweep.append({"tokens": T, "us_per_layer": round(ms * 1e3, 2), "tokens_per_s": round(tok_s, 1),
-                      "active_experts": mean_active, "weight_GBps": round(layer_gbps, 1),
-                      "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4)})
-
-    prefill = None
-    if not args.no_sweep:
+    sweep, prefill, ep, shared, fin, dense = [], None, [], None, None, None
+    if "decode" in only:
+        for ts in (1, 16, 64, 256):
+            log(f"decode T={ts}")
+            sweep.append(decode_point(ops, wl, weights, ts, torch, layout, seed=ts))
+    if "prefill" in only:
         log("prefill T=2048 (Zipf routing)")
-        prefill = time_prefill(ops, reps, torch, layout, max(8, args.steps // 50), args.warmup // 10 + 1)
-
-    ep_shard = finalize_stream = dense = shared = None
-    if not args.no_sweep:
-        log("layer with one shared expert T=256")
-        shared = time_shared(ops, wl, reps, torch, layout, max(100, args.steps // 2), args.warmup)
-        del reps
+        prefill = prefill_point(ops, WORKLOADS["qwen3_prefill"], weights, torch, layout)
+    if "shared" in only:
+        log("decode T=256 with one shared expert")
+        sh = shared_weights(ops, wl, L, torch, layout)
+        shared = decode_point(ops, wl, weights, 256, torch, layout, seed=256, shared=sh)
+        del sh
+    del weights
+    torch.cuda.empty_cache()
+    if "ep" in only:
+        wle = WORKLOADS["ep_shard_decode"]
+        log("EP shard: generating 8 weight replicas (726 MB each)")
+        we = make_weights(wle, 8, torch, ops, layout, seed_base=11)
+        for ts in (1, 16, 64, 256):
+            log(f"EP shard T={ts}")
+            ep.append(decode_point(ops, wle, we, ts, torch, layout, seed=ts + 7))
+        del we
         torch.cuda.empty_cache()
-        log("EP shard decode T=256")
-        ep_shard = time_ep_shard(ops, torch, layout, max(60, args.steps // 4), max(6, args.warmup // 10))
+    if "finalize" in only:
         log("finalize stream")
-        finalize_stream = time_finalize_stream(ops, torch)
+        fin = finalize_point(ops, torch)
+    if "dense" in only:
         log("dense W4A16 GEMM")
-        dense = time_dense(ops, torch, layout)
+        dense = dense_points(ops, torch, layout)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        cpu = cpu_baseline(inp, wl)
+        cpu = cpu_baseline()
 
     rec = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -490,21 +598,26 @@ def main():
         "config": {"workload": f"{wl.name} (Qwen3-30B-A3B MoE layer, decode)", "tokens": T,
                    "experts": wl.num_experts, "top_k": wl.top_k, "hidden": wl.hidden, "inter": wl.inter,
                    "weights": f"int4 group-128 ({args.weights} code layout), bf16 scales",
-                   "activations": "bf16", "replicas": L,
-                   "parallelism": "single GPU"},
+                   "activations": "bf16", "replicas": L, "parallelism": "single GPU"},
         "layer_weight_GBps": round(layer_gbps, 1), "layer_hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4),
-        "roofline": {"kernel": "gemm_stream_kernel<W13_SWIGLU> (GEMM1 + SwiGLU)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "roofline": {"kernel": "grouped GEMM1 (w13 + SwiGLU)", "bound": "hbm",
+                     "achieved": round(g1_bytes / (g1_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(g1_bytes / (g1_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "algorithmic_bytes": round(g1_bytes), "avg_launch_us": round(g1 * 1e6, 3),
-                     "traffic_note": traffic_note},
+                     "algorithmic_bytes": round(g1_bytes), "avg_launch_us": round(g1_us, 3),
+                     "median_launch_us": g1_r["median_us"], "traffic_note": traffic_note},
+        "roofline_gemm2": {"kernel": "grouped GEMM2 (w2)", "bound": "hbm",
+                           "achieved": round(g2_bytes / (g2_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                           "unit": "GB/s", "frac": round(g2_bytes / (g2_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                           "traffic": None if traffic2 is None else round(traffic2),
+                           "algorithmic_bytes": round(g2_bytes), "avg_launch_us": round(g2_us, 3),
+                           "median_launch_us": g2_r["median_us"], "traffic_note": traffic2_note},
         "cpu_baseline": cpu,
-        "sweep": sweep,
+        "decode_sweep": sweep,
         "prefill": prefill,
         "shared_expert": shared,
-        "ep_shard": ep_shard,
-        "finalize_stream": finalize_stream,
+        "ep_shard": ep,
+        "finalize_stream": fin,
         "dense_gemm": dense,
     }
     print(json.dumps(rec), flush=True)

@@ -112,7 +112,10 @@ typedef struct {
     int32_t weight_layout;     /* moe_weight_layout of w13_q / w2_q / wq         */
 } moe_shape;
 
-/* Human-readable name of a status code (static string, never NULL). */
+/* Human-readable name of a status code (static string, never NULL). The
+ * status split follows [FI2] section 1: a run entry point reports a failure
+ * (here as a code, which the Python binding raises), while is_supported
+ * answers without failing. Unknown codes give "unknown moe_status". */
 const char *moe_status_str(moe_status s);
 
 /* Validate a shape without raising: MOE_OK if every entry point supports it,
@@ -123,12 +126,20 @@ moe_status moe_w4a16_check_shape(const moe_shape *shape);
 int moe_w4a16_is_supported(const moe_shape *shape);
 
 /* Bytes of workspace moe_w4a16_forward needs for this shape (0 if the shape
- * is invalid). Layout is private to the library. */
+ * is invalid). It holds the layer's intermediates that [IL] section 2.2
+ * names between its steps: the routing ids and weights, the per-expert counts
+ * and offsets, the permutation and its inverse, the SwiGLU output h [T*k][I]
+ * and the expert outputs y [T*k][H] (bf16), plus the permutation's per-range
+ * counts for many tokens. Layout is private to the library; the caller owns
+ * the memory, and the workspace holds no state from one call to the next. */
 size_t moe_w4a16_workspace_size(const moe_shape *shape);
 
 /*
- * The whole layer: route -> permute -> GEMM1 (w13, SwiGLU) -> GEMM2 (w2) ->
- * finalize, all on `stream`, no host synchronisation.
+ * The whole layer ([IL] section 2.2: route, bucket by expert, gate/up grouped
+ * GEMM with SwiGLU, down grouped GEMM, weighted combine back to tokens; [FI]
+ * section 1: the combine's slot order; [GC] abstract: the 1-256 token decode
+ * regime it is tuned for): route -> permute -> GEMM1 (w13, SwiGLU) -> GEMM2
+ * (w2) -> finalize, all on `stream`, no host synchronisation.
  *   x             bf16  [T][H]        activations
  *   router_logits f32   [T][E_g]
  *   w13_q, s13, w2_q, s2              local experts' weights (formats above;
@@ -218,7 +229,9 @@ moe_status moe_permute(const moe_shape *shape, const int32_t *topk_ids, const ui
  *   W2:         K = I, c [T*k][H]  = A.w2^T,  bf16 or f32 (c_dtype).
  * Accumulation is fp32 over exact int4 codes; the scale of each 128-wide
  * group is applied in fp32. Rows >= R of c are untouched. `offsets` stays on
- * the device: the grid never depends on the counts.
+ * the device: the grid never depends on the counts. The call takes no
+ * workspace: every kernel keeps its work list and partial sums in LDS and
+ * registers (each workgroup derives its items from `offsets`).
  */
 moe_status moe_grouped_gemm_w4a16(const moe_shape *shape, moe_gemm_kind kind, const uint16_t *a,
                                   const int32_t *a_row_index, const int32_t *offsets,
@@ -279,6 +292,34 @@ moe_status moe_finalize(const moe_shape *shape, const void *y, moe_dtype y_dtype
  */
 moe_status moe_w4a16_pack_weights(const moe_shape *shape, moe_gemm_kind kind, const uint8_t *wq,
                                   uint8_t *wq_tiled, void *stream);
+
+/*
+ * Launch-shape override, for tests and tuning (not a passage of the pages: a
+ * switch over this library's own kernel variants). Every field -1 keeps the
+ * automatic choice. A field changes which kernel variant runs and how it
+ * tiles the work, never a result: the variants compute the same bits, which
+ * the tests check by forcing each one. Process-wide; set it from one thread
+ * while no other call is being issued. NULL resets every field to -1. Values
+ * a kernel does not support fall back to a supported variant. Returns MOE_OK.
+ */
+typedef struct {
+    int32_t gemm_mode;                   /* grouped GEMM kernel: 0 split-K, 1 streaming,
+                                            2 tile kernel (8 waves, 64-row chunks),
+                                            3 tile kernel (4 waves, 32-row chunks)      */
+    int32_t gemm_tiles_per_wave;         /* streaming: 16-row weight tiles per wave     */
+    int32_t gemm_subtiles;               /* streaming: 16-token subtiles per chunk      */
+    int32_t gemm_kseg;                   /* streaming: 128-wide groups per K segment    */
+    int32_t gemm_ring;                   /* streaming: weight register ring depth       */
+    int32_t gemm_nontemporal;            /* streaming: 1 non-temporal code loads, 0 not */
+    int32_t permute_parallel_min_tokens; /* permute over token ranges past this T       */
+    int32_t route_fuse_max_tokens;       /* layer routes inside the permute up to this T */
+    int32_t decode_max_tokens;           /* layer takes the small-batch path up to this T
+                                            (routing inside the gate/up GEMM; 0: never) */
+    int32_t decode_combine_max_tokens;   /* small-batch path: down GEMM and combine in one
+                                            launch up to this T (0: never)              */
+} moe_launch_override;
+
+moe_status moe_w4a16_set_launch_override(const moe_launch_override *ov);
 
 #ifdef __cplusplus
 }

@@ -105,7 +105,7 @@ def test_dense_vs_oracle_within_bound(M, N, K):
     assert np.all(np.abs(got16 - ref) <= bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref))
 
 
-def test_dense_equals_one_expert_grouped_gemm(monkeypatch):
+def test_dense_equals_one_expert_grouped_gemm():
     import torch
     from w4a16_grouped_gemm_amd import ops
     say("dense == grouped GEMM with one expert")
@@ -124,8 +124,8 @@ def test_dense_equals_one_expert_grouped_gemm(monkeypatch):
     tile = bf16_to_f64(_dense(a, wq, s, out_f32=False, tiled=True))
     assert np.all(np.abs(tile - ref) <= bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref))
     # through the streaming kernel the tiled layout equals the plain one bit for bit
-    monkeypatch.setenv("MOE_GEMM_MODE", "1")
-    assert np.array_equal(got, _dense(a, wq, s, out_f32=False, tiled=True))
+    with ops.launch_override(gemm_mode=1):
+        assert np.array_equal(got, _dense(a, wq, s, out_f32=False, tiled=True))
 
 
 def test_dense_zero_rows_and_errors():

@@ -127,15 +127,20 @@ def test_swiglu_and_down_vs_oracle(wl, T, tiled):
     _close_bf16(y[:R], y_ref[:R], "y")
 
 
-@pytest.mark.parametrize("mode", ["2", "3"])
+@pytest.mark.parametrize("mode", [2, 3])
 @pytest.mark.parametrize("wl,T,n", [("qwen3_prefill", 256, None), ("qwen3_prefill", 2048, 96), ("tiny", 40, None)])
-def test_tile_kernel_vs_oracle(wl, T, n, mode, monkeypatch):
+def test_tile_kernel_vs_oracle(wl, T, n, mode):
     # the tile kernel forced, both shapes (mode 2: 8 waves, 64-row chunks;
     # mode 3: 4 waves, 32-row chunks, two workgroups per CU): ragged last
     # chunks, the per-item -136 correction; sampled rows at 2048
     from w4a16_grouped_gemm_amd import ops
-    monkeypatch.setenv("MOE_GEMM_MODE", mode)
-    say(f"gemm tile kernel {wl} T={T}")
+    say(f"gemm tile kernel {wl} T={T} mode={mode}")
+    with ops.launch_override(gemm_mode=mode):
+        _tile_kernel_vs_oracle(wl, T, n)
+
+
+def _tile_kernel_vs_oracle(wl, T, n):
+    from w4a16_grouped_gemm_amd import ops
     inp = make_layer_inputs(wl, T)
     k = inp.workload.top_k
     ids, _ = oracle.route(inp.logits, k)
@@ -177,34 +182,35 @@ def test_pack_matches_layout_definition(kind, wl):
 
 # Launch shapes chosen by the host heuristic depend on the expected load; the
 # integer-exact pin must hold for every kernel variant, so each is forced here
-# (MOE_GEMM_* environment overrides are read at every launch).
+# through the library's launch override.
+def _v(mode, tpw=-1, nsub=-1, kseg=-1, ring=-1, nt=-1):
+    return dict(gemm_mode=mode, gemm_tiles_per_wave=tpw, gemm_subtiles=nsub, gemm_kseg=kseg, gemm_ring=ring,
+                gemm_nontemporal=nt)
+
+
 VARIANTS = [
-    {"MOE_GEMM_MODE": "0"},
-    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "2", "MOE_GEMM_NSUB": "1", "MOE_GEMM_KSEG": "4", "MOE_GEMM_RING": "4"},
-    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "2", "MOE_GEMM_NSUB": "2", "MOE_GEMM_KSEG": "2", "MOE_GEMM_RING": "2"},
-    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "2", "MOE_GEMM_NSUB": "4", "MOE_GEMM_KSEG": "1", "MOE_GEMM_RING": "2"},
-    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "4", "MOE_GEMM_NSUB": "1", "MOE_GEMM_KSEG": "8", "MOE_GEMM_RING": "4"},
-    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "4", "MOE_GEMM_NSUB": "2", "MOE_GEMM_KSEG": "4", "MOE_GEMM_RING": "2"},
-    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "1", "MOE_GEMM_NSUB": "1", "MOE_GEMM_KSEG": "8", "MOE_GEMM_RING": "4"},
-    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "1", "MOE_GEMM_NSUB": "2", "MOE_GEMM_KSEG": "4", "MOE_GEMM_RING": "4"},
-    {"MOE_GEMM_MODE": "2"},            # tile kernel (tiled codes, K <= 2048; plain codes fall back)
-    {"MOE_GEMM_MODE": "3"},            # its 4-wave, 32-row shape
+    _v(0),
+    _v(1, 2, 1, 4, 4), _v(1, 2, 2, 2, 2), _v(1, 2, 4, 1, 2), _v(1, 4, 1, 8, 4), _v(1, 4, 2, 4, 2),
+    _v(1, 1, 1, 8, 4), _v(1, 1, 2, 4, 4),
+    _v(2),            # tile kernel (tiled codes, K <= 2048; plain codes fall back)
+    _v(3),            # its 4-wave, 32-row shape
     # streaming kernel with either code-load cache policy (non-temporal or default)
-    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "4", "MOE_GEMM_NSUB": "2", "MOE_GEMM_KSEG": "4", "MOE_GEMM_RING": "2",
-     "MOE_GEMM_NT": "1"},
-    {"MOE_GEMM_MODE": "1", "MOE_GEMM_TPW": "4", "MOE_GEMM_NSUB": "2", "MOE_GEMM_KSEG": "4", "MOE_GEMM_RING": "2",
-     "MOE_GEMM_NT": "0"},
+    _v(1, 4, 2, 4, 2, nt=1), _v(1, 4, 2, 4, 2, nt=0),
 ]
 
 
 @pytest.mark.parametrize("variant", range(len(VARIANTS)))
 @pytest.mark.parametrize("kind,H,I", [(2, 2048, 768), (1, 1024, 1024)])
 @pytest.mark.parametrize("tiled", [False, True])
-def test_integer_exact_every_launch_shape(variant, kind, H, I, tiled, monkeypatch):
+def test_integer_exact_every_launch_shape(variant, kind, H, I, tiled):
     from w4a16_grouped_gemm_amd import ops
-    for k_, v_ in VARIANTS[variant].items():
-        monkeypatch.setenv(k_, v_)
     say(f"gemm integer-exact variant={VARIANTS[variant]} kind={kind} H={H} I={I} tiled={tiled}")
+    with ops.launch_override(**VARIANTS[variant]):
+        _integer_exact_variant(variant, kind, H, I, tiled)
+
+
+def _integer_exact_variant(variant, kind, H, I, tiled):
+    from w4a16_grouped_gemm_amd import ops
     rng = np.random.default_rng(variant * 7 + kind)
     counts = np.array([0, 1, 17, 40, 3, 0, 70, 16, 33, 128, 65, 200])
     E = len(counts)
@@ -227,18 +233,23 @@ def test_integer_exact_every_launch_shape(variant, kind, H, I, tiled, monkeypatc
         assert np.array_equal(got[r0:r1].astype(np.float64), want), e
 
 
-@pytest.mark.parametrize("mode", ["2", "3"])
+@pytest.mark.parametrize("mode", [2, 3])
 @pytest.mark.parametrize("kind", [0, 1])
 @pytest.mark.parametrize("gather", [False, True])
-def test_tile_kernel_many_items_smallest_k(kind, gather, mode, monkeypatch):
+def test_tile_kernel_many_items_smallest_k(kind, gather, mode):
     # the prefill tile kernel forced at K = 512 (four groups, the fewest it
     # takes: the next item's first two groups are copied during groups 0 and
     # 1) over ragged experts (empty, single-row, 63/64/65-row and long ones):
     # 350-700 items, so workgroups run several items back to back and the
     # last item of each copies out of range; sampled rows against the oracle
     from w4a16_grouped_gemm_amd import ops
-    monkeypatch.setenv("MOE_GEMM_MODE", mode)
     say(f"gemm tile kernel (mode {mode}) K=512 many items kind={kind} gather={gather}")
+    with ops.launch_override(gemm_mode=mode):
+        _tile_many_items(kind, gather)
+
+
+def _tile_many_items(kind, gather):
+    from w4a16_grouped_gemm_amd import ops
     rng = np.random.default_rng(41 + kind + 2 * gather)
     H = I = 512
     N, K = (2 * I, H) if kind == ops.W13_SWIGLU else (H, I)
@@ -258,3 +269,38 @@ def test_tile_kernel_many_items_smallest_k(kind, gather, mode, monkeypatch):
     ref = oracle.grouped_gemm(kind, a, offsets, wq, s, rows=R, a_row_index=idx, top_k=1, row_sel=sel)
     got = _gpu_gemm(kind, a, offsets, wq, s, T=R, k=1, a_row_index=idx, out_f32=False, tiled=True)
     _close_bf16(got[rows], ref[rows], "tile K=512")
+
+
+@pytest.mark.parametrize("mode", [2, 3])
+@pytest.mark.parametrize("gather", [False, True])
+def test_tile_kernel_integer_exact_large_sums(mode, gather):
+    # The tile kernel removes the +136 code offset once per item with
+    # -136 * sum(x) per 128-wide group. With activations in [0, 8] that sum
+    # reaches 136 * 1024 (18 significant bits), so the correction must carry
+    # every bit of it: codes in [-8, 7], scales 2^-6 and integer activations
+    # keep every partial sum exact in fp32, and the bf16 output must equal the
+    # oracle's correctly rounded exact value bit for bit.
+    from w4a16_grouped_gemm_amd import ops
+    say(f"gemm tile kernel integer-exact, large sums, mode {mode} gather={gather}")
+    rng = np.random.default_rng(5 + mode + 2 * gather)
+    H, I = 1024, 2048                                   # W2: N = 1024 rows, K = 2048 (16 groups)
+    counts = np.array([0, 1, 63, 64, 65, 0, 200, 7, 130])
+    E = len(counts)
+    q = rng.integers(-8, 8, size=(E, H, I), dtype=np.int8)
+    s = np.full((E, H, I // 128), bf16_bits(np.float32(2.0 ** -6)), np.uint16)
+    offsets = _offsets(counts)
+    R = int(offsets[-1])
+    xi = rng.integers(0, 9, size=(R, I))
+    a = bf16_bits(xi.astype(np.float32))
+    idx = rng.permutation(R).astype(np.int32) if gather else None
+    wq = pack_int4(q)
+    with ops.launch_override(gemm_mode=mode):
+        got = _gpu_gemm(ops.W2, a, offsets, wq, s, T=R, k=1, a_row_index=idx, out_f32=False, tiled=True)
+    ref = oracle.grouped_gemm(oracle.W2, a, offsets, wq, s, rows=R, a_row_index=idx, top_k=1)
+    assert np.array_equal(got[:R], ref[:R])
+    # the oracle's value is the exact integer product, rounded once
+    e = 6
+    r0, r1 = offsets[e], offsets[e + 1]
+    rows = xi[idx[r0:r1]] if gather else xi[r0:r1]
+    exact = (rows.astype(np.int64) @ q[e].T.astype(np.int64)).astype(np.float64) * 2.0 ** -6
+    assert np.all(np.abs(bf16_to_f64(ref[r0:r1]) - exact) <= 2.0 ** -8 * np.abs(exact))

@@ -100,6 +100,28 @@ def test_shared_at_limits():
     assert_layer_close(to_np_u16(o), ref["out"], "shared S=4")
 
 
+@pytest.mark.parametrize("mode", [0, -1])
+def test_shared_at_expert_limit_split_k(mode):
+    # 1024 routed experts plus four shared ones: the grouped GEMMs see 1028
+    # experts, so every kernel's chunk table must hold 1029 entries. One token
+    # with the split-K kernel forced (and the automatic choice)
+    import torch
+    from w4a16_grouped_gemm_amd import ops
+    wl = LIMITS[0][0]
+    T = 1
+    say(f"limits shared S=4 {wl.name} T={T} gemm_mode={mode}")
+    inp = make_layer_inputs(wl, T)
+    w13s, s13s, w2s, s2s = make_shared_weights(wl, 4)
+    with ops.launch_override(gemm_mode=mode):
+        o = ops.moe_w4a16_forward(bf16_dev(inp.x), to_dev(inp.logits), to_dev(inp.w13_q), bf16_dev(inp.s13),
+                                  to_dev(inp.w2_q), bf16_dev(inp.s2), wl.top_k,
+                                  shared=(to_dev(w13s), bf16_dev(s13s), to_dev(w2s), bf16_dev(s2s)))
+        torch.cuda.synchronize()
+    ref = oracle.layer(inp.x, inp.logits, inp.w13_q, inp.s13, inp.w2_q, inp.s2, top_k=wl.top_k,
+                       shared=(w13s, s13s, w2s, s2s))
+    assert_layer_close(to_np_u16(o), ref["out"], "shared S=4, 1028 experts")
+
+
 def test_shared_zero_tokens():
     import torch
     from w4a16_grouped_gemm_amd import ops

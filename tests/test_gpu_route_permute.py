@@ -59,10 +59,24 @@ def test_route_ties_and_signed_zeros():
         logits[3] = np.round(logits[3])                  # many exact duplicates
         logits[4] = -np.inf
         logits[4, E - 1] = 1.0
-        ref_ids, _ = oracle.route(logits, k)
-        ids, _ = ops.route(to_dev(logits), k)
+        # fewer finite logits than slots: the rest are masked experts (-inf)
+        logits[5] = -np.inf
+        logits[5, rng.permutation(E)[: max(1, k // 2)]] = rng.standard_normal(max(1, k // 2))
+        # l_q - l_0 overflows binary32 (to -inf) for the negative slots
+        logits[6] = rng.choice(np.float32([-3e38, 3e38, -2.5e38]), size=E)
+        ref_ids, ref_w = oracle.route(logits, k)
+        ids, wt = ops.route(to_dev(logits), k)
         torch.cuda.synchronize()
         assert np.array_equal(ids.cpu().numpy(), ref_ids), (E, k)
+        # weights: finite everywhere, exactly 0 where the exact weight is 0
+        # (exp of a -inf difference), else within the k+7 ulp bound below
+        got_w = wt.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got_w)), (E, k)
+        zero = ref_w == 0
+        assert np.all(got_w[zero] == 0.0), (E, k)
+        ulps = np.abs(got_w[~zero] - ref_w[~zero]) / np.spacing(ref_w[~zero]).astype(np.float64)
+        assert ulps.max() <= k + 7, (E, k, ulps.max())
+        assert np.all(np.abs(got_w[4] - np.eye(k)[0]) == 0.0), (E, k)
 
 
 @pytest.mark.parametrize("wl,T", CASES)

@@ -123,3 +123,14 @@ def test_permute_workspace_without_gpu(lib):
     MOE_ERR_NULL, MOE_ERR_WORKSPACE = 1, 5
     assert lib.moe_permute(*args, fake, ctypes.c_size_t(need - 4), None) == MOE_ERR_WORKSPACE
     assert lib.moe_permute(*args, None, ctypes.c_size_t(need), None) == MOE_ERR_NULL
+
+
+def test_launch_override_without_gpu():
+    # the override is host state only: setting, resetting and rejecting an
+    # unknown field need no device
+    ops.set_launch_override(gemm_mode=1, gemm_tiles_per_wave=2)
+    ops.set_launch_override()
+    with ops.launch_override(route_fuse_max_tokens=0):
+        pass
+    with pytest.raises(ValueError):
+        ops.set_launch_override(no_such_field=1)

@@ -29,6 +29,19 @@ int device_cu_count()
 
 namespace {
 
+std::mutex g_override_mu;
+moe_launch_override g_override = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+
+}  // namespace
+
+moe_launch_override launch_override()
+{
+    std::lock_guard<std::mutex> lock(g_override_mu);
+    return g_override;
+}
+
+namespace {
+
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -76,6 +89,7 @@ struct Workspace {
     uint16_t *h;
     uint16_t *y;
     int32_t *part;    // per-range expert counts of the parallel permutation (many tokens)
+    int32_t *pres;    // small-batch path: slot index if the slot's expert is local, else -1
     size_t bytes;
 };
 
@@ -103,6 +117,7 @@ Workspace carve(const moe_shape &sh, void *base, int nsh = 0)
     ws.h = reinterpret_cast<uint16_t *>(take(S * (size_t)sh.inter * 2));
     ws.y = reinterpret_cast<uint16_t *>(take(S * (size_t)sh.hidden * 2));
     ws.part = reinterpret_cast<int32_t *>(take(permute_workspace_bytes(sh)));
+    ws.pres = reinterpret_cast<int32_t *>(take(Sr * 4));
     ws.bytes = off;
     return ws;
 }
@@ -110,7 +125,6 @@ Workspace carve(const moe_shape &sh, void *base, int nsh = 0)
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 constexpr int32_t kMaxDenseDim = 65536;   // N and K of the dense GEMM
-constexpr int32_t kMaxSharedExperts = 4;  // shared experts of one layer call (finalize unrolls them)
 
 GemmLaunch gemm_args(const moe_shape &sh, moe_gemm_kind kind)
 {
@@ -155,6 +169,16 @@ const char *moe_status_str(moe_status s)
 }
 
 moe_status moe_w4a16_check_shape(const moe_shape *shape) { return check_shape(shape); }
+
+moe_status moe_w4a16_set_launch_override(const moe_launch_override *ov)
+{
+    std::lock_guard<std::mutex> lock(g_override_mu);
+    if (ov)
+        g_override = *ov;
+    else
+        g_override = moe_launch_override{-1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+    return MOE_OK;
+}
 
 int moe_w4a16_is_supported(const moe_shape *shape) { return check_shape(shape) == MOE_OK ? 1 : 0; }
 
@@ -379,6 +403,21 @@ static moe_status forward_impl(const moe_shape *shape, int nsh, const uint16_t *
         return MOE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
+    if (decode_path_fits(sh, nsh)) {
+        // small batch: routing inside the gate/up GEMM, h and y in slot order,
+        // no permutation; the combine inside the down GEMM for the fewest tokens
+        e = launch_decode_gate_up(sh, router_logits, x, w13_q, s13, ws.ids, ws.w, ws.pres, ws.h, s);
+        if (e == hipSuccess) {
+            if (decode_combine_fits(sh)) {
+                e = launch_decode_down_combine(sh, ws.ids, ws.w, ws.pres, ws.h, w2_q, s2, out, s);
+            } else {
+                e = launch_decode_down(sh, ws.ids, ws.pres, ws.h, w2_q, s2, ws.y, s);
+                if (e == hipSuccess)
+                    e = launch_finalize(sh, ws.y, false, ws.w, ws.pres, out, false, s, true);
+            }
+        }
+        return from_hip(e);
+    }
     if (route_permute_fusable(sh)) {
         e = launch_route_permute(sh, router_logits, ws.ids, ws.w, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s,
                                  nsh);

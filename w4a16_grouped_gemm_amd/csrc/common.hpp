@@ -12,6 +12,8 @@ namespace moe {
 
 constexpr int kGroup = 128;          // quantisation group along K
 constexpr int kMaxExperts = 1024;    // E_g and E_loc limit (LDS tables)
+constexpr int kMaxSharedExperts = 4; // shared experts of one layer call; the grouped GEMMs then
+                                     // see up to kMaxExperts + kMaxSharedExperts experts
 constexpr int kMaxTopK = 16;
 constexpr int kMaxDim = 16384;       // H and I limit
 constexpr int kMaxTokens = 1 << 18;
@@ -107,6 +109,24 @@ hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const
                            bool y_slot = false, int num_shared = 0,
                            const int32_t *shared_row0 = nullptr);
 
+// The layer's small-batch path (decode.hip): up to 16 tokens, no shared
+// experts, E_g <= 256. h and y are in slot order; pres[t*k + j] is the slot
+// index when the slot's expert is local, else -1.
+bool decode_path_fits(const moe_shape &sh, int num_shared);
+bool decode_combine_fits(const moe_shape &sh);
+hipError_t launch_decode_gate_up(const moe_shape &sh, const float *logits, const uint16_t *x, const uint8_t *w13,
+                                 const uint16_t *s13, int32_t *ids, float *w, int32_t *pres, uint16_t *h,
+                                 hipStream_t st);
+hipError_t launch_decode_down(const moe_shape &sh, const int32_t *ids, const int32_t *pres, const uint16_t *h,
+                              const uint8_t *w2, const uint16_t *s2, uint16_t *y, hipStream_t st);
+hipError_t launch_decode_down_combine(const moe_shape &sh, const int32_t *ids, const float *w, const int32_t *pres,
+                                      const uint16_t *h, const uint8_t *w2, const uint16_t *s2, uint16_t *out,
+                                      hipStream_t st);
+
 int device_cu_count();
+
+// Process-wide launch-shape override (moe_w4a16_set_launch_override); every
+// field -1 = automatic. Only which kernel runs and its tiling depend on it.
+moe_launch_override launch_override();
 
 }  // namespace moe

@@ -1,0 +1,524 @@
+// decode.hip -- the layer's small-batch path (1 to 16 tokens): two or three
+// launches instead of five, and no permutation.
+//
+// Pages: GC-MoE abstract (decode holds 1-256 tokens per rank and is dominated
+// by dispatch latency and weight traffic); FlashInfer PR #7196 analysis,
+// section 2 (only routed rows are computed; the MMA's token extent follows
+// the routed-token count) and section 1 (the combine: fp32 multiply for the
+// first slot, fp32 FMA for later slots in slot order); InfiniLM PR #500
+// report, section 2.2 (the layer's steps).
+//
+// With at most 16 tokens every expert holds at most 16 routed rows, one
+// MFMA subtile, so no permutation is needed: a workgroup that knows the
+// routing can list an expert's rows itself.
+//  * decode_gate_up_kernel: every workgroup routes all T tokens itself (the
+//    logits are a few KiB), so routing costs no launch and no memory round
+//    trip of its own. The "leader" of an expert is its first slot in slot
+//    order; items are (leader, 16-row weight tile). An item's rows are the
+//    slots routed to that expert, in token order; their SwiGLU outputs go
+//    to h in slot order (row t*k + j). Workgroup 0 also writes each slot's
+//    expert id, routing weight and presence (slot index, or -1 when the
+//    expert is not local).
+//  * decode_down_kernel (4 < T <= 16): the same items from the stored slot
+//    table; y in slot order, then the finalize kernel reads y[t*k + j].
+//  * decode_down_combine_kernel (T <= 4): items are (token, 16-column tile);
+//    the workgroup computes the tile for each of the token's present slots
+//    and combines them in slot order (multiply, then FMA), so the finalize
+//    needs no launch of its own. An expert used by several of the tokens is
+//    then streamed once per token (at 4 tokens of top-8 over 128 experts,
+//    about 12% more down-projection bytes than once per expert).
+// Every tile is computed with the split-K body of gemm_core.hpp and the same
+// wave count per K-group count as the standalone grouped GEMM's split-K
+// kernel (which takes 16 tokens and fewer), and the combine repeats the
+// finalize kernel's operations, so the path is bit-identical to the
+// standalone entry points composed.
+#include "gemm_core.hpp"
+#include "route_core.hpp"
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+namespace moe {
+
+namespace {
+
+constexpr int kDecMaxSlots = 128;       // T * k of the small-batch path
+
+struct DecodeArgs {
+    int T, k, E_g, begin, E_loc;
+    const float *logits;                // [T][E_g] (gate/up kernel)
+    int32_t *ids;                       // [T*k] global expert id of each slot
+    float *w;                           // [T*k] routing weight
+    int32_t *pres;                      // [T*k] slot index if its expert is local, else -1
+    const uint16_t *a;                  // gate/up: x [T][K]; down: h [T*k][K]
+    uint32_t a_bytes;
+    const uint8_t *wq;                  // codes of the local experts
+    const uint16_t *s;                  // scales
+    int K, N, w_tiled;
+    uint16_t *c;                        // gate/up: h [T*k][N/2]; down: y [T*k][N]; combine: out [T][N]
+};
+
+// Weight row of lane n16 in tile `tile` (gate/up: gate rows 8t.., then the
+// matching up rows; down: 16t + n16) and the lane offset of its codes.
+template <int KIND>
+__device__ __forceinline__ uint32_t dec_row(const DecodeArgs &p, int tile, int n16)
+{
+    if (KIND == MOE_GEMM_W13_SWIGLU)
+        return (uint32_t)(n16 < 8 ? tile * 8 + n16 : p.N / 2 + tile * 8 + (n16 - 8));
+    return (uint32_t)(tile * 16 + n16);
+}
+
+__device__ __forceinline__ uint32_t dec_code_offset(const DecodeArgs &p, int tile, uint32_t row, int G, int lane)
+{
+    if (p.w_tiled)
+        return (uint32_t)((tile >> 3) * G * 8 + (tile & 7)) * 1024u + (uint32_t)lane * 16u;
+    return row * (uint32_t)(p.K >> 1) + (uint32_t)(lane >> 4) * 16u;
+}
+
+// Slot of row r of an expert whose slots are the set bits of (m0, m1): the
+// r-th set bit, or -1 past the last.
+__device__ __forceinline__ int nth_slot(uint64_t m0, uint64_t m1, int r)
+{
+    const int c0 = __popcll(m0);
+    uint64_t m = r < c0 ? m0 : m1;
+    int rr = r < c0 ? r : r - c0;
+    if (rr >= __popcll(m))
+        return -1;
+    for (int i = 0; i < rr; ++i)
+        m &= m - 1;
+    return (r < c0 ? 0 : 64) + __builtin_ctzll(m);
+}
+
+// Shared slot bookkeeping of the two expert-major kernels, after s_loc[s]
+// (local expert of slot s, or -1) is in LDS: s_first[e] = first slot of
+// expert e, then the leaders in slot order in s_lead. Block-wide.
+template <int NT>
+__device__ void build_leaders(int S, int E_loc, const int *s_loc, int *s_first, int *s_lead, int *s_nlead)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    for (int s = tid; s < S; s += NT)
+        if (s_loc[s] >= 0)
+            atomicMin(&s_first[s_loc[s]], s);
+    __syncthreads();
+    if (tid < 64) {
+        int base = 0;
+        for (int s0 = 0; s0 < S; s0 += 64) {
+            const int s = s0 + lane;
+            const bool lead = s < S && s_loc[s] >= 0 && s_first[s_loc[s]] == s;
+            const uint64_t m = __ballot(lead);
+            if (lead)
+                s_lead[base + __popcll(m & ((1ull << lane) - 1ull))] = s;
+            base += __popcll(m);
+        }
+        if (lane == 0)
+            *s_nlead = base;
+    }
+    __syncthreads();
+}
+
+// One expert-major item: expert e (leader slot `lead`), 16-row tile `tile`.
+// Rows are the slots of expert e in slot order; row r reads activation row
+// a_row(slot) and its result goes to output row `slot`.
+template <int KIND, int NW, bool A_BY_TOKEN>
+__device__ __forceinline__ void expert_item(const DecodeArgs &p, const int *s_loc, floatx4 (*s_red)[64], int e,
+                                            int tile, int S)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n16 = lane & 15, kq = lane >> 4;
+    const int G = p.K / kGroup;
+    int g0, g1;
+    splitk_groups(wave, G, NW, g0, g1);
+    // the expert's slots: bits of (m0, m1) over slots 0..127
+    const uint64_t m0 = __ballot(lane < S && s_loc[lane] == e);
+    const uint64_t m1 = __ballot(64 + lane < S && s_loc[64 + lane] == e);
+    const int nrows = __popcll(m0) + __popcll(m1);
+    const int my_slot = nth_slot(m0, m1, n16);         // activation row of lane n16
+    const uint32_t wbytes = (uint32_t)p.N * (uint32_t)(p.K >> 1);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (size_t)e * wbytes, wbytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.s + (size_t)e * p.N * G, (uint32_t)p.N * G * 2);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+    const uint32_t row = dec_row<KIND>(p, tile, n16);
+    const uint32_t voff_w = dec_code_offset(p, tile, row, G, lane);
+    const uint32_t voff_s = row * (uint32_t)G * 2;
+    uint32_t voff_x = kOutOfRange;
+    if (my_slot >= 0) {
+        const uint32_t src = A_BY_TOKEN ? (uint32_t)(my_slot / p.k) : (uint32_t)my_slot;
+        voff_x = src * (uint32_t)p.K * 2 + kq * 64;
+    }
+    const floatx4 tot = splitk_wave_sum<4>(rw, voff_w, p.w_tiled ? 8192u : 64u, rs, voff_s, ra, voff_x, g0, g1,
+                                           p.w_tiled != 0);
+    const floatx4 sum = splitk_reduce<NW>(tot, s_red, wave, lane);
+    if (wave != 0)
+        return;
+    const float r[4] = {sum.x, sum.y, sum.z, sum.w};
+    int orow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        orow[i] = __shfl(my_slot, kq * 4 + i, 64);       // output row of result row 4kq + i
+    if (KIND == MOE_GEMM_W13_SWIGLU) {
+        float u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            u[i] = __shfl_xor(r[i], 8, 64);               // partner lane holds the up row
+        if (n16 < 8) {
+            const int ldc = p.N / 2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (kq * 4 + i < nrows)
+                    p.c[(size_t)orow[i] * ldc + tile * 8 + n16] = (uint16_t)f32_to_bf16_rne(silu(r[i]) * u[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (kq * 4 + i < nrows)
+                p.c[(size_t)orow[i] * p.N + tile * 16 + n16] = (uint16_t)f32_to_bf16_rne(r[i]);
+    }
+}
+
+// Gate/up with routing inside: every workgroup routes all tokens (PL logits
+// per lane, 16 lanes per token, E_g <= 256), builds the slot table and the
+// leaders, then runs its share of the (leader, tile) items.
+template <int NW, int PL>
+__global__ __launch_bounds__(NW * 64) void decode_gate_up_kernel(DecodeArgs p)
+{
+    __shared__ int s_loc[kDecMaxSlots];
+    __shared__ int s_first[kMaxExperts];
+    __shared__ int s_lead[kDecMaxSlots];
+    __shared__ int s_nlead;
+    __shared__ floatx4 s_red[NW][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n16 = lane & 15;
+    const int S = p.T * p.k;
+    for (int e = tid; e < p.E_loc; e += NW * 64)
+        s_first[e] = kDecMaxSlots;
+    // four tokens per wave and pass, one DPP row (16 lanes) each
+    for (int t0 = wave * 4; t0 < p.T; t0 += NW * 4) {
+        const int t = t0 + (lane >> 4);
+        if (t < p.T) {
+            int eg;
+            float wt;
+            route_token<16, PL>(p.logits + (size_t)t * p.E_g, p.E_g, p.k, n16, eg, wt);
+            if (n16 < p.k) {
+                const int s = t * p.k + n16;
+                const int le = eg - p.begin;
+                const int loc = (le >= 0 && le < p.E_loc) ? le : -1;
+                s_loc[s] = loc;
+                if (blockIdx.x == 0) {
+                    p.ids[s] = eg;
+                    p.w[s] = wt;
+                    p.pres[s] = loc >= 0 ? s : -1;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    build_leaders<NW * 64>(S, p.E_loc, s_loc, s_first, s_lead, &s_nlead);
+    const int ntiles = p.N >> 4;
+    const int items = s_nlead * ntiles;
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int lead = s_lead[item / ntiles];
+        expert_item<MOE_GEMM_W13_SWIGLU, NW, true>(p, s_loc, s_red, uniform(s_loc[lead]), item % ntiles, S);
+    }
+}
+
+// Down projection, expert-major, from the stored slot table; y in slot order.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void decode_down_kernel(DecodeArgs p)
+{
+    __shared__ int s_loc[kDecMaxSlots];
+    __shared__ int s_first[kMaxExperts];
+    __shared__ int s_lead[kDecMaxSlots];
+    __shared__ int s_nlead;
+    __shared__ floatx4 s_red[NW][64];
+    const int tid = threadIdx.x;
+    const int S = p.T * p.k;
+    for (int e = tid; e < p.E_loc; e += NW * 64)
+        s_first[e] = kDecMaxSlots;
+    for (int s = tid; s < S; s += NW * 64)
+        s_loc[s] = p.pres[s] >= 0 ? p.ids[s] - p.begin : -1;
+    __syncthreads();
+    build_leaders<NW * 64>(S, p.E_loc, s_loc, s_first, s_lead, &s_nlead);
+    const int ntiles = p.N >> 4;
+    const int items = s_nlead * ntiles;
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int lead = s_lead[item / ntiles];
+        expert_item<MOE_GEMM_W2, NW, false>(p, s_loc, s_red, uniform(s_loc[lead]), item % ntiles, S);
+    }
+}
+
+// Down projection and combine, token-major. Item = (token t, 16-column tile).
+// KS waves split K exactly as the split-K kernel does; SP such wave groups
+// take the token's slots j = sp, sp + SP (at most two each, so k <= 2 SP).
+// The token's h rows are staged in LDS (k * K bf16); each wave prefetches the
+// codes and scales of both its slots before computing either. Partial sums of
+// result row 0 go to LDS; wave 0 reduces them in wave order, rounds y to
+// bf16 and combines the present slots in slot order.
+constexpr int kCombineMaxHBytes = 64 * 1024;            // k * K * 2 bytes of staged h rows
+constexpr int kCombineMaxGroups = 4;                    // groups per wave (G / KS)
+
+template <int KS, int SP>
+__global__ __launch_bounds__(KS * SP * 64) void decode_down_combine_kernel(DecodeArgs p)
+{
+    constexpr int NW = KS * SP;
+    extern __shared__ __align__(16) unsigned char s_dyn[];
+    uint16_t *s_h = reinterpret_cast<uint16_t *>(s_dyn);                     // [k][K]
+    __shared__ float s_part[kMaxTopK][KS][16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n16 = lane & 15, kq = lane >> 4;
+    const int sp = wave / KS, ks = wave % KS;
+    const int k = p.k, K = p.K, G = K / kGroup;
+    int g0, g1;
+    splitk_groups(ks, G, KS, g0, g1);
+    const int ntiles = p.N >> 4;
+    const uint32_t wbytes = (uint32_t)p.N * (uint32_t)(K >> 1);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+    const int chunks = k * K / 8;                         // 16-byte pieces of the token's h rows
+    for (int item = blockIdx.x; item < p.T * ntiles; item += gridDim.x) {
+        const int t = item / ntiles, tile = item % ntiles;
+        // slot table of token t: lane j < k holds slot j
+        const int js = min(lane, k - 1);
+        const int pres_l = p.pres[t * k + js];
+        const int id_l = p.ids[t * k + js];
+        const float w_l = p.w[t * k + js];
+        // stage the present slots' h rows (absent rows read as zeros)
+        for (int c = tid; c < chunks; c += NW * 64) {
+            const int j = c / (K / 8);
+            const int pj = __shfl(pres_l, j, 64);
+            const uint32_t vo = pj >= 0 ? ((uint32_t)(t * k + j) * (uint32_t)K + (uint32_t)(c % (K / 8)) * 8u) * 2u
+                                        : kOutOfRange;
+            *reinterpret_cast<u32x4 *>(s_h + (size_t)c * 8) = bload16(ra, vo, 0);
+        }
+        // this wave's slots: codes and scales of groups g0..g1 (absent: zeros, no traffic)
+        u32x4 wv[2][kCombineMaxGroups];
+        uint32_t sc[2][kCombineMaxGroups];
+        int jj[2];
+        bool present[2];
+        const uint32_t row = (uint32_t)(tile * 16 + n16);
+        const uint32_t voff_w = p.w_tiled ? (uint32_t)((tile >> 3) * G * 8 + (tile & 7)) * 1024u + (uint32_t)lane * 16u
+                                          : row * (uint32_t)(K >> 1) + (uint32_t)(lane >> 4) * 16u;
+        const uint32_t voff_s = row * (uint32_t)G * 2;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int j = sp + u * SP;
+            jj[u] = j;
+            const int pj = __shfl(pres_l, min(j, k - 1), 64);
+            present[u] = j < k && pj >= 0;
+            const int e = present[u] ? __shfl(id_l, j, 64) - p.begin : 0;
+            const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (size_t)uniform(e) * wbytes, present[u] ? wbytes : 0u);
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(p.s + (size_t)uniform(e) * p.N * G, present[u] ? (uint32_t)p.N * G * 2 : 0u);
+#pragma unroll
+            for (int q = 0; q < kCombineMaxGroups; ++q) {
+                const int g = g0 + q;
+                const uint32_t oor = g < g1 ? 0u : kOutOfRange;
+                wv[u][q] = bload16_codes<true>(rw, voff_w | oor, (uint32_t)(g < g1 ? g : 0) * (p.w_tiled ? 8192u : 64u));
+                sc[u][q] = bload_scale(rs, voff_s | oor, (uint32_t)(g < g1 ? g : 0) * 2u);
+            }
+        }
+        __syncthreads();                                  // h rows staged
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (!uniform(present[u]))
+                continue;
+            floatx4 tot = {0.f, 0.f, 0.f, 0.f};
+            const uint16_t *hrow = s_h + (size_t)jj[u] * K;
+#pragma unroll
+            for (int q = 0; q < kCombineMaxGroups; ++q) {
+                const int g = g0 + q;
+                if (g >= g1)
+                    break;
+                u32x4 a[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(hrow + g * kGroup + kq * 32 + i * 8);
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    const u32x4 va = n16 == 0 ? v : z;        // row 0 only: the token's h row
+                    a[i] = p.w_tiled ? va : permute_act(va);
+                }
+                splitk_group(a, wv[u][q], sc[u][q], tot);
+            }
+            if (kq == 0)
+                s_part[jj[u]][ks][n16] = tot.x;
+        }
+        __syncthreads();
+        if (wave == 0 && lane < 16) {
+            float acc = 0.0f;
+            bool first = true;
+            for (int j = 0; j < k; ++j) {
+                const int pj = __shfl(pres_l, j, 16);
+                const float wj = __shfl(w_l, j, 16);
+                if (pj < 0)
+                    continue;
+                float y = s_part[j][0][n16];
+#pragma unroll
+                for (int q = 1; q < KS; ++q)
+                    y += s_part[j][q][n16];
+                const float v = bf16_to_f32(f32_to_bf16_rne(y));
+                acc = first ? __fmul_rn(v, wj) : __fmaf_rn(v, wj, acc);
+                first = false;
+            }
+            p.c[(size_t)t * p.N + tile * 16 + n16] = (uint16_t)f32_to_bf16_rne(acc);
+        }
+        __syncthreads();                                  // LDS free for the next item
+    }
+}
+
+// Persistent grid: the workgroups one launch keeps resident (occupancy of
+// the kernel at this LDS size, cached), capped by the item bound.
+long long resident_grid(const void *kernel, int threads, size_t lds, long long items)
+{
+    static std::mutex mu;
+    static std::map<std::pair<const void *, size_t>, int> cache;
+    int per_cu = 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        const auto key = std::make_pair(kernel, lds);
+        auto it = cache.find(key);
+        if (it != cache.end()) {
+            per_cu = it->second;
+        } else {
+            if (lds > 48 * 1024)
+                (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
+                per_cu < 1)
+                per_cu = 1;
+            cache[key] = per_cu;
+        }
+    }
+    long long cap = (long long)device_cu_count() * per_cu;
+    long long g = items < cap ? items : cap;
+    return g < 1 ? 1 : g;
+}
+
+}  // namespace
+
+bool decode_path_fits(const moe_shape &sh, int nsh)
+{
+    const moe_launch_override ov = launch_override();
+    const int max_t = ov.decode_max_tokens >= 0 ? ov.decode_max_tokens : 16;
+    return nsh == 0 && sh.num_tokens <= max_t && sh.num_tokens * sh.top_k <= kDecMaxSlots &&
+           sh.num_experts <= 256;
+}
+
+bool decode_combine_fits(const moe_shape &sh)
+{
+    const moe_launch_override ov = launch_override();
+    const int max_t = ov.decode_combine_max_tokens >= 0 ? ov.decode_combine_max_tokens : 4;
+    const int G = sh.inter / kGroup, KS = splitk_waves(G);
+    const int SP = (sh.top_k + 1) / 2;
+    const int sp2 = SP <= 1 ? 1 : SP <= 2 ? 2 : SP <= 4 ? 4 : 8;
+    return sh.num_tokens <= max_t && (G + KS - 1) / KS <= kCombineMaxGroups && KS * sp2 <= 16 &&
+           (size_t)sh.top_k * sh.inter * 2 <= (size_t)kCombineMaxHBytes;
+}
+
+hipError_t launch_decode_gate_up(const moe_shape &sh, const float *logits, const uint16_t *x, const uint8_t *w13,
+                                 const uint16_t *s13, int32_t *ids, float *w, int32_t *pres, uint16_t *h,
+                                 hipStream_t st)
+{
+    DecodeArgs p{};
+    p.T = sh.num_tokens;
+    p.k = sh.top_k;
+    p.E_g = sh.num_experts;
+    p.begin = sh.expert_begin;
+    p.E_loc = sh.num_local_experts;
+    p.logits = logits;
+    p.ids = ids;
+    p.w = w;
+    p.pres = pres;
+    p.a = x;
+    p.a_bytes = (uint32_t)((size_t)sh.num_tokens * sh.hidden * 2);
+    p.wq = w13;
+    p.s = s13;
+    p.K = sh.hidden;
+    p.N = 2 * sh.inter;
+    p.w_tiled = sh.weight_layout == MOE_WEIGHTS_TILED;
+    p.c = h;
+    const int G = p.K / kGroup;
+    const long long items = (long long)sh.num_tokens * sh.top_k * (p.N / 16);
+    auto go = [&](auto kernel, int nw) {
+        const long long grid = resident_grid(reinterpret_cast<const void *>(kernel), nw * 64, 0, items);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(nw * 64), 0, st, p);
+    };
+    const int E = sh.num_experts;
+#define MOE_DEC_GU(NW)                                                                     \
+    if (E <= 64)                                                                           \
+        go(decode_gate_up_kernel<NW, 4>, NW);                                              \
+    else if (E <= 128)                                                                     \
+        go(decode_gate_up_kernel<NW, 8>, NW);                                              \
+    else                                                                                   \
+        go(decode_gate_up_kernel<NW, 16>, NW);
+    switch (splitk_waves(G)) {
+    case 8: MOE_DEC_GU(8) break;
+    case 4: MOE_DEC_GU(4) break;
+    case 2: MOE_DEC_GU(2) break;
+    default: MOE_DEC_GU(1) break;
+    }
+#undef MOE_DEC_GU
+    return hipGetLastError();
+}
+
+static DecodeArgs down_args(const moe_shape &sh, const int32_t *ids, const float *w, const int32_t *pres,
+                            const uint16_t *h, const uint8_t *w2, const uint16_t *s2, uint16_t *c)
+{
+    DecodeArgs p{};
+    p.T = sh.num_tokens;
+    p.k = sh.top_k;
+    p.E_g = sh.num_experts;
+    p.begin = sh.expert_begin;
+    p.E_loc = sh.num_local_experts;
+    p.ids = const_cast<int32_t *>(ids);
+    p.w = const_cast<float *>(w);
+    p.pres = const_cast<int32_t *>(pres);
+    p.a = h;
+    p.a_bytes = (uint32_t)((size_t)sh.num_tokens * sh.top_k * sh.inter * 2);
+    p.wq = w2;
+    p.s = s2;
+    p.K = sh.inter;
+    p.N = sh.hidden;
+    p.w_tiled = sh.weight_layout == MOE_WEIGHTS_TILED;
+    p.c = c;
+    return p;
+}
+
+hipError_t launch_decode_down(const moe_shape &sh, const int32_t *ids, const int32_t *pres, const uint16_t *h,
+                              const uint8_t *w2, const uint16_t *s2, uint16_t *y, hipStream_t st)
+{
+    const DecodeArgs p = down_args(sh, ids, nullptr, pres, h, w2, s2, y);
+    const long long items = (long long)sh.num_tokens * sh.top_k * (p.N / 16);
+    auto go = [&](auto kernel, int nw) {
+        const long long grid = resident_grid(reinterpret_cast<const void *>(kernel), nw * 64, 0, items);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(nw * 64), 0, st, p);
+    };
+    switch (splitk_waves(p.K / kGroup)) {
+    case 8: go(decode_down_kernel<8>, 8); break;
+    case 4: go(decode_down_kernel<4>, 4); break;
+    case 2: go(decode_down_kernel<2>, 2); break;
+    default: go(decode_down_kernel<1>, 1); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_down_combine(const moe_shape &sh, const int32_t *ids, const float *w, const int32_t *pres,
+                                      const uint16_t *h, const uint8_t *w2, const uint16_t *s2, uint16_t *out,
+                                      hipStream_t st)
+{
+    const DecodeArgs p = down_args(sh, ids, w, pres, h, w2, s2, out);
+    const int KS = splitk_waves(p.K / kGroup);
+    const int SP0 = (sh.top_k + 1) / 2;
+    const int SP = SP0 <= 1 ? 1 : SP0 <= 2 ? 2 : SP0 <= 4 ? 4 : 8;
+    const size_t lds = (size_t)sh.top_k * p.K * 2;
+    const long long items = (long long)sh.num_tokens * (p.N / 16);
+    auto go = [&](auto kernel) {
+        const int threads = KS * SP * 64;
+        const long long grid = resident_grid(reinterpret_cast<const void *>(kernel), threads, lds, items);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), lds, st, p);
+    };
+#define MOE_DEC_DC(KS_, SP_) \
+    if (KS == KS_ && SP == SP_) { go(decode_down_combine_kernel<KS_, SP_>); return hipGetLastError(); }
+    MOE_DEC_DC(1, 1) MOE_DEC_DC(1, 2) MOE_DEC_DC(1, 4) MOE_DEC_DC(1, 8)
+    MOE_DEC_DC(2, 1) MOE_DEC_DC(2, 2) MOE_DEC_DC(2, 4) MOE_DEC_DC(2, 8)
+    MOE_DEC_DC(4, 1) MOE_DEC_DC(4, 2) MOE_DEC_DC(4, 4)
+    MOE_DEC_DC(8, 1) MOE_DEC_DC(8, 2)
+#undef MOE_DEC_DC
+    return hipErrorInvalidValue;                          // decode_combine_fits() rules this out
+}
+
+}  // namespace moe

@@ -31,7 +31,7 @@ namespace {
 // experts): nsh <= kMaxShared rows per token at y row R + s*T + t, R =
 // *shared_row0 (the routed row count), each added with weight 1 after the
 // routed slots: acc = acc + v, or v as the token's first term.
-constexpr int kMaxShared = 4;
+constexpr int kMaxShared = kMaxSharedExperts;
 
 template <bool Y_F32, bool OUT_F32, int KMAX, bool Y_SLOT, bool SHARED>
 __global__ __launch_bounds__(256) void finalize_kernel(int T, int k, int H,

@@ -1,0 +1,198 @@
+// gemm_core.hpp -- device building blocks shared by the grouped-GEMM kernels
+// (gemm_w4a16.hip) and the small-batch layer kernels (decode.hip): buffer
+// loads, the int4 unpack, the MFMA step, and the split-K tile body. The
+// split-K body is one function used by every kernel that computes a tile
+// that way, so they produce the same bits for the same tile.
+//
+// Method (pages): GC-MoE abstract (4-bit weights decoded in registers and fed
+// straight to the matrix unit); Cloudflare "Unweight" post, section on the
+// reconstructive matmul (weights rebuilt on chip, never written back).
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+constexpr uint32_t kNeg136 = 0xC308C308u;  // bf16 pair (-136, -136)
+constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every descriptor
+constexpr int kXcds = 8;                         // MI355X: 8 XCDs of 32 CUs, one L2 each
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Cache policy of the weight-code stream. NT: non-temporal (the nt bit of
+// the buffer instruction), for launches where each expert's codes are read
+// about once (at most one chunk per expert): the streaming policy keeps
+// them from evicting the activation rows, which the other blocks of a chunk
+// read again from L2. Measured on MI355X (Qwen3-30B-A3B decode, 16-256
+// tokens; the EP shard): both grouped GEMMs 6-9% faster. Where several
+// chunks of an expert re-read its codes (prefill, a dense GEMM of many rows)
+// the default policy keeps them in L2 for the next chunk (nt: 3-14% slower).
+template <bool NT>
+__device__ __forceinline__ u32x4 bload16_codes(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? 2 : 0));
+}
+
+// Raw bf16 bits of a scale; converted where it is used, so that the load can
+// stay in flight until then (a conversion next to the load would wait for it).
+__device__ __forceinline__ uint32_t bload_scale(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
+// Nibbles j and j+4 -> bf16 pair j (128 + (q+8)): K order (0,4,1,5,..) for
+// plain codes, column order for tiled ones.
+__device__ __forceinline__ bf16x8 unpack8(uint32_t w)
+{
+    u32x4 o;
+    o.x = (w & 0x000F000Fu) ^ 0x43084308u;
+    o.y = ((w >> 4) & 0x000F000Fu) ^ 0x43084308u;
+    o.z = ((w >> 8) & 0x000F000Fu) ^ 0x43084308u;
+    o.w = ((w >> 12) & 0x000F000Fu) ^ 0x43084308u;
+    return __builtin_bit_cast(bf16x8, o);
+}
+
+// Eight consecutive bf16 activations -> the (0,4,1,5,2,6,3,7) order of
+// plain codes.
+__device__ __forceinline__ u32x4 permute_act(u32x4 d)
+{
+    u32x4 o;
+    o.x = __builtin_amdgcn_perm(d.z, d.x, 0x05040100u);
+    o.y = __builtin_amdgcn_perm(d.z, d.x, 0x07060302u);
+    o.z = __builtin_amdgcn_perm(d.w, d.y, 0x05040100u);
+    o.w = __builtin_amdgcn_perm(d.w, d.y, 0x07060302u);
+    return o;
+}
+
+__device__ __forceinline__ floatx4 mfma(u32x4 a, bf16x8 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// silu for a value that is rounded to bf16 next: hardware exp2 and reciprocal
+// (errors of a few fp32 ulp, far below the bf16 rounding step).
+__device__ __forceinline__ float silu_fast(float g)
+{
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
+// Value of lane (l ^ 8) within each 16-lane row (DPP row rotate by 8).
+__device__ __forceinline__ float row_swap8(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ bf16x8 neg136_operand()
+{
+    const u32x4 v = {kNeg136, kNeg136, kNeg136, kNeg136};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Group range [g0, g1) of wave `wave` when NW waves split G groups.
+__device__ __forceinline__ void splitk_groups(int wave, int G, int NW, int &g0, int &g1)
+{
+    g0 = wave * G / NW;
+    g1 = (wave + 1) * G / NW;
+}
+
+// One 128-wide group of a 16-row weight tile: the chain of the -136 * sum(x)
+// correction MFMAs followed by the four code MFMAs (activation fragments a,
+// already in the codes' K order), times the group's scale, added to tot.
+__device__ __forceinline__ void splitk_group(const u32x4 (&a)[4], u32x4 wv, uint32_t sc, floatx4 &tot)
+{
+    const bf16x8 neg136 = neg136_operand();
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc = mfma(a[i], neg136, acc);
+    acc = mfma(a[0], unpack8(wv.x), acc);
+    acc = mfma(a[1], unpack8(wv.y), acc);
+    acc = mfma(a[2], unpack8(wv.z), acc);
+    acc = mfma(a[3], unpack8(wv.w), acc);
+    const float scale = bf16_to_f32(sc);
+    tot.x = __builtin_fmaf(scale, acc.x, tot.x);
+    tot.y = __builtin_fmaf(scale, acc.y, tot.y);
+    tot.z = __builtin_fmaf(scale, acc.z, tot.z);
+    tot.w = __builtin_fmaf(scale, acc.w, tot.w);
+}
+
+// One wave's share of a 16-row weight tile over groups [g0, g1): the sum over
+// those groups, in ascending order, of scale_g * (chain of group g), the
+// chain being the -136 * sum(x) correction MFMAs followed by the four code
+// MFMAs (the per-group contraction is exact for integer activations).
+// Loads go out GB groups at a time, all before the first is used; groups
+// past g1 are not loaded. Activation fragments come from `ra` at voff_x
+// (+16 per MFMA step, +256 per group; an out-of-range voff_x gives zeros).
+template <int GB>
+__device__ __forceinline__ floatx4 splitk_wave_sum(__amdgpu_buffer_rsrc_t rw, uint32_t voff_w, uint32_t gstride,
+                                                   __amdgpu_buffer_rsrc_t rs, uint32_t voff_s,
+                                                   __amdgpu_buffer_rsrc_t ra, uint32_t voff_x, int g0, int g1,
+                                                   bool w_tiled)
+{
+    floatx4 tot = {0.f, 0.f, 0.f, 0.f};
+    for (int gb = g0; gb < g1; gb += GB) {
+        u32x4 wv[GB];
+        uint32_t sc[GB];
+        u32x4 xa[GB][4];
+#pragma unroll
+        for (int j = 0; j < GB; ++j) {
+            if (gb + j < g1) {
+                const uint32_t g = gb + j;
+                wv[j] = bload16_codes<true>(rw, voff_w, g * gstride);
+                sc[j] = bload_scale(rs, voff_s, g * 2);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xa[j][i] = bload16(ra, voff_x + i * 16, g * kGroup * 2);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < GB; ++j) {
+            if (gb + j >= g1)
+                break;
+            u32x4 a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[i] = w_tiled ? xa[j][i] : permute_act(xa[j][i]);
+            splitk_group(a, wv[j], sc[j], tot);
+        }
+    }
+    return tot;
+}
+
+// Sum of the NW waves' shares in wave order (s_red[0] + s_red[1] + ...),
+// valid in wave 0. Block-wide (two barriers): every wave must call it.
+template <int NW>
+__device__ __forceinline__ floatx4 splitk_reduce(floatx4 tot, floatx4 (*s_red)[64], int wave, int lane)
+{
+    s_red[wave][lane] = tot;
+    __syncthreads();
+    floatx4 sum = s_red[0][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        const floatx4 v = s_red[w][lane];
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
+    }
+    __syncthreads();
+    return sum;
+}
+
+// K-group count -> waves of a split-K tile (at least 2 groups per wave from
+// 4 groups on; 8 waves once there are 24 groups or more).
+constexpr int splitk_waves(int G) { return G >= 24 ? 8 : G >= 8 ? 4 : G >= 4 ? 2 : 1; }
+
+}  // namespace moe

@@ -53,7 +53,7 @@
 //    the grid never depends on the counts and the host never synchronises.
 //    Subtiles past the chunk's valid rows are skipped (runtime N); rows past
 //    the last valid token are neither read nor written.
-#include "common.hpp"
+#include "gemm_core.hpp"
 
 #include <map>
 #include <type_traits>
@@ -63,10 +63,6 @@
 namespace moe {
 
 namespace {
-
-constexpr uint32_t kNeg136 = 0xC308C308u;  // bf16 pair (-136, -136)
-constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every descriptor
-constexpr int kXcds = 8;                         // MI355X: 8 XCDs of 32 CUs, one L2 each
 
 struct GemmArgs {
     const uint16_t *a;
@@ -105,88 +101,6 @@ __device__ __forceinline__ uint32_t code_offset(const GemmArgs &p, int tile, uin
 
 __device__ __forceinline__ uint32_t group_stride(const GemmArgs &p) { return p.w_tiled ? 8192u : 64u; }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
-// Cache policy of the weight-code stream. NT: non-temporal (the nt bit of
-// the buffer instruction), for launches where each expert's codes are read
-// about once (at most one chunk per expert): the streaming policy keeps
-// them from evicting the activation rows, which the other blocks of a chunk
-// read again from L2. Measured on MI355X (Qwen3-30B-A3B decode, 16-256
-// tokens; the EP shard): both grouped GEMMs 6-9% faster. Where several
-// chunks of an expert re-read its codes (prefill, a dense GEMM of many rows)
-// the default policy keeps them in L2 for the next chunk (nt: 3-14% slower).
-template <bool NT>
-__device__ __forceinline__ u32x4 bload16_codes(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? 2 : 0));
-}
-
-// Raw bf16 bits of a scale; converted where it is used, so that the load can
-// stay in flight until then (a conversion next to the load would wait for it).
-__device__ __forceinline__ uint32_t bload_scale(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-}
-
-// Nibbles j and j+4 -> bf16 pair j (128 + (q+8)): K order (0,4,1,5,..) for
-// plain codes, column order for tiled ones.
-__device__ __forceinline__ bf16x8 unpack8(uint32_t w)
-{
-    u32x4 o;
-    o.x = (w & 0x000F000Fu) ^ 0x43084308u;
-    o.y = ((w >> 4) & 0x000F000Fu) ^ 0x43084308u;
-    o.z = ((w >> 8) & 0x000F000Fu) ^ 0x43084308u;
-    o.w = ((w >> 12) & 0x000F000Fu) ^ 0x43084308u;
-    return __builtin_bit_cast(bf16x8, o);
-}
-
-// Eight consecutive bf16 activations -> the (0,4,1,5,2,6,3,7) order of
-// plain codes.
-__device__ __forceinline__ u32x4 permute_act(u32x4 d)
-{
-    u32x4 o;
-    o.x = __builtin_amdgcn_perm(d.z, d.x, 0x05040100u);
-    o.y = __builtin_amdgcn_perm(d.z, d.x, 0x07060302u);
-    o.z = __builtin_amdgcn_perm(d.w, d.y, 0x05040100u);
-    o.w = __builtin_amdgcn_perm(d.w, d.y, 0x07060302u);
-    return o;
-}
-
-__device__ __forceinline__ floatx4 mfma(u32x4 a, bf16x8 b, floatx4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
-
-// silu for a value that is rounded to bf16 next: hardware exp2 and reciprocal
-// (errors of a few fp32 ulp, far below the bf16 rounding step).
-__device__ __forceinline__ float silu_fast(float g)
-{
-    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
-}
-
-// Value of lane (l ^ 8) within each 16-lane row (DPP row rotate by 8).
-__device__ __forceinline__ float row_swap8(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ bf16x8 neg136_operand()
-{
-    const u32x4 v = {kNeg136, kNeg136, kNeg136, kNeg136};
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Codes and scales of expert e: the routed arrays, or past e_routed the
 // shared experts' arrays (e is uniform: a scalar select, no branch).
@@ -614,7 +528,7 @@ template <int KIND, int NWAVES, int GB>
 __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
 {
     constexpr int CS = 16;
-    __shared__ int s_prefix[kMaxExperts + 1];
+    __shared__ int s_prefix[kMaxExperts + kMaxSharedExperts + 1];   // routed + shared experts
     __shared__ int s_wtot[NWAVES];
     __shared__ floatx4 s_red[NWAVES][64];
 
@@ -629,10 +543,9 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
     const int ntiles = p.N >> 4;
     const int total_items = s_prefix[E] * ntiles;
     const int G = p.K / kGroup;
-    const int g0 = wave * G / NWAVES;
-    const int g1 = (wave + 1) * G / NWAVES;
+    int g0, g1;
+    splitk_groups(wave, G, NWAVES, g0, g1);
     const uint32_t row_bytes = (uint32_t)(p.K >> 1);
-    const bf16x8 neg136 = neg136_operand();
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c_row_index, p.c_row_bytes);
     const uint32_t gstride = group_stride(p);
@@ -659,61 +572,10 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
             const uint32_t src = p.a_row_index ? (uint32_t)(p.a_row_index[r] / p.top_k) : (uint32_t)r;
             voff_x = src * (uint32_t)p.K * 2 + kq * 64;
         }
-
-        floatx4 tot = {0.f, 0.f, 0.f, 0.f};
-        for (int gb = g0; gb < g1; gb += GB) {
-            u32x4 wv[GB];
-            uint32_t sc[GB];
-            u32x4 xa[GB][4];
-#pragma unroll
-            for (int j = 0; j < GB; ++j) {
-                if (gb + j < g1) {
-                    const uint32_t g = gb + j;
-                    wv[j] = bload16_codes<true>(rw, voff_w, g * gstride);
-                    sc[j] = bload_scale(rs, voff_s, g * 2);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        xa[j][i] = bload16(ra, voff_x + i * 16, g * kGroup * 2);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < GB; ++j) {
-                if (gb + j >= g1)
-                    break;
-                u32x4 a[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a[i] = p.w_tiled ? xa[j][i] : permute_act(xa[j][i]);
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc = mfma(a[i], neg136, acc);
-                acc = mfma(a[0], unpack8(wv[j].x), acc);
-                acc = mfma(a[1], unpack8(wv[j].y), acc);
-                acc = mfma(a[2], unpack8(wv[j].z), acc);
-                acc = mfma(a[3], unpack8(wv[j].w), acc);
-                const float scale = bf16_to_f32(sc[j]);
-                tot.x = __builtin_fmaf(scale, acc.x, tot.x);
-                tot.y = __builtin_fmaf(scale, acc.y, tot.y);
-                tot.z = __builtin_fmaf(scale, acc.z, tot.z);
-                tot.w = __builtin_fmaf(scale, acc.w, tot.w);
-            }
-        }
-        s_red[wave][lane] = tot;
-        __syncthreads();
-        if (wave == 0) {
-            floatx4 sum = s_red[0][lane];
-#pragma unroll
-            for (int w = 1; w < NWAVES; ++w) {
-                const floatx4 v = s_red[w][lane];
-                sum.x += v.x;
-                sum.y += v.y;
-                sum.z += v.z;
-                sum.w += v.w;
-            }
+        const floatx4 tot = splitk_wave_sum<GB>(rw, voff_w, gstride, rs, voff_s, ra, voff_x, g0, g1, p.w_tiled != 0);
+        const floatx4 sum = splitk_reduce<NWAVES>(tot, s_red, wave, lane);
+        if (wave == 0)
             store_tile<KIND>(p, sum, tile, row0, kq * 4, nvalid, n16, c_rows);
-        }
-        __syncthreads();
     }
 }
 
@@ -737,9 +599,9 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
 //  * The +136 offset is removed once per item instead of once per group and
 //    tile: per group, waves w and w+4 add 136 * sum(x) of subtile w's two
 //    halves of K to column g of one MFMA tile (operand B one-hot on column
-//    g), and after the last group one MFMA per (subtile, tile) adds
-//    sum_g s[n][g] * (-136 * sum_g x), each sum split into two bf16 terms
-//    (hi + lo, 16 significant bits). Needs G <= 16 (one column per group).
+//    g), and after the last group two MFMAs per (subtile, tile) add
+//    sum_g s[n][g] * (-136 * sum_g x), each sum split exactly into three
+//    bf16 terms (hi + mid + lo). Needs G <= 16 (one column per group).
 //  * Tiled codes only: they unpack in column order, matching the
 //    activations as they lie in memory.
 // ---------------------------------------------------------------------------
@@ -1141,17 +1003,28 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
                 const floatx4 v0 = *reinterpret_cast<const floatx4 *>(s_sx + sb * 256 + n16 * 16 + kq * 4);
                 const floatx4 v1 = *reinterpret_cast<const floatx4 *>(s_sx + (sb + NS) * 256 + n16 * 16 + kq * 4);
                 const float vv[4] = {v0.x + v1.x, v0.y + v1.y, v0.z + v1.z, v0.w + v1.w};
-                uint32_t d[4];
+                // -136 * sum(x) split into three bf16 terms hi + mid + lo that
+                // add up to the binary32 value exactly (each remainder is exact
+                // and has at most 8 fewer significant bits than the last), so
+                // the correction is as accurate as the per-group one of the
+                // streaming kernel whatever the size of sum(x)
+                uint32_t d[4], dl[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float nv = -vv[j];
                     const float hi = __uint_as_float(bf16_pair(nv, 0.f) << 16);
-                    d[j] = bf16_pair(hi, nv - hi);
+                    const float r1 = nv - hi;
+                    const float mid = __uint_as_float(bf16_pair(r1, 0.f) << 16);
+                    d[j] = bf16_pair(hi, mid);
+                    dl[j] = bf16_pair(r1 - mid, 0.f);
                 }
                 const u32x4 acorr = {d[0], d[1], d[2], d[3]};
+                const u32x4 acorr_lo = {dl[0], dl[1], dl[2], dl[3]};
 #pragma unroll
-                for (int t = 0; t < TPW; ++t)
+                for (int t = 0; t < TPW; ++t) {
                     tot[t][sb] = mfma(acorr, __builtin_bit_cast(bf16x8, bcorr[t]), tot[t][sb]);
+                    tot[t][sb] = mfma(acorr_lo, __builtin_bit_cast(bf16x8, bcorr[t]), tot[t][sb]);
+                }
             }
         }
 
@@ -1312,14 +1185,12 @@ hipError_t launch_kind(const GemmArgs &a, int max_rows, int mode, int tpw, int n
     if (mode == 3)
         return launch_tile<KIND, 4, 2>(a, max_rows, st);
     if (mode == 0) {
-        const int G = a.K / kGroup;
-        if (G >= 24)
-            return launch_splitk<KIND, 8>(a, max_rows, st);
-        if (G >= 8)
-            return launch_splitk<KIND, 4>(a, max_rows, st);
-        if (G >= 4)
-            return launch_splitk<KIND, 2>(a, max_rows, st);
-        return launch_splitk<KIND, 1>(a, max_rows, st);
+        switch (splitk_waves(a.K / kGroup)) {
+        case 8: return launch_splitk<KIND, 8>(a, max_rows, st);
+        case 4: return launch_splitk<KIND, 4>(a, max_rows, st);
+        case 2: return launch_splitk<KIND, 2>(a, max_rows, st);
+        default: return launch_splitk<KIND, 1>(a, max_rows, st);
+        }
     }
 #define MOE_STREAM(T, S, B, R)                                \
     if (tpw == T && nsub == S && kseg == B && ring == R)      \
@@ -1418,6 +1289,11 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     while (tpw > 1 && chunks * ntiles / tpw <= fill)
         tpw >>= 1;
     int mode = chunks * ntiles / tpw > fill ? 1 : 0;
+    // At most 16 tokens (every expert then holds at most one 16-row chunk):
+    // the split-K kernel, whose tiles the layer's small-batch path computes
+    // with the same arithmetic, so the layer equals these GEMMs composed.
+    if (g.offsets && T <= 16.0)
+        mode = 0;
     int kseg = 4;
     int ring = (g.K >= 4096 || m < 3.0) ? 4 : 2;
     if (g.K >= 4096)
@@ -1429,20 +1305,21 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     // GEMM (measured on MI355X, Qwen3-30B-A3B shapes: at 64 rows per expert
     // 7% faster for the down GEMM, 5% slower for the gate/up GEMM; at 16 rows
     // slower for both). The 4-wave variant (32-row chunks, two workgroups per
-    // CU, MOE_GEMM_MODE=3) came out within run-to-run spread of the
+    // CU, forced with gemm_mode 3) came out within run-to-run spread of the
     // streaming kernel from 16 to 64 rows per expert and is not chosen.
     if (m >= (g.kind == MOE_GEMM_W2 ? 64.0 : 96.0) && tile_fits(g, 8))
         mode = 2;
-    if (const char *env = getenv("MOE_GEMM_MODE"))
-        mode = atoi(env);
-    if (const char *env = getenv("MOE_GEMM_TPW"))
-        tpw = atoi(env);
-    if (const char *env = getenv("MOE_GEMM_NSUB"))
-        nsub = atoi(env);
-    if (const char *env = getenv("MOE_GEMM_KSEG"))
-        kseg = atoi(env);
-    if (const char *env = getenv("MOE_GEMM_RING"))
-        ring = atoi(env);
+    const moe_launch_override ov = launch_override();
+    if (ov.gemm_mode >= 0)
+        mode = ov.gemm_mode;
+    if (ov.gemm_tiles_per_wave > 0)
+        tpw = ov.gemm_tiles_per_wave;
+    if (ov.gemm_subtiles > 0)
+        nsub = ov.gemm_subtiles;
+    if (ov.gemm_kseg > 0)
+        kseg = ov.gemm_kseg;
+    if (ov.gemm_ring > 0)
+        ring = ov.gemm_ring;
     while (tpw > 1 && ntiles % (4 * tpw) != 0)
         tpw >>= 1;
     // LDS: 2 buffers x KSEG groups x NSUB subtiles x 4 KiB <= 64 KiB
@@ -1456,10 +1333,10 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
         mode = 0;                                         // shapes the streaming tiles do not divide
     // non-temporal code loads while most experts fit one chunk (their codes
     // are then read once): routed loads vary around m, a dense GEMM has
-    // exactly m rows. MOE_GEMM_NT overrides
+    // exactly m rows
     bool nt = m <= (g.num_experts == 1 ? 1.0 : 0.75) * 16.0 * nsub;
-    if (const char *env = getenv("MOE_GEMM_NT"))
-        nt = atoi(env) != 0;
+    if (ov.gemm_nontemporal >= 0)
+        nt = ov.gemm_nontemporal != 0;
     if (g.kind == MOE_GEMM_W13_SWIGLU)
         return launch_kind<MOE_GEMM_W13_SWIGLU>(a, g.max_rows, mode, tpw, nsub, kseg, ring, nt, st);
     return launch_kind<MOE_GEMM_W2>(a, g.max_rows, mode, tpw, nsub, kseg, ring, nt, st);

@@ -15,7 +15,6 @@
 #include "common.hpp"
 #include "route_core.hpp"
 
-#include <cstdlib>
 #include <mutex>
 
 namespace moe {
@@ -415,17 +414,15 @@ static int chunk_tokens_for(int E)
     return c;
 }
 
-// Past this many tokens (MOE_PERMUTE_PARALLEL_MIN_T overrides) the
-// permutation runs over nb token ranges in two launches (per-range
-// histograms, then a scatter whose workgroups each scan the histograms for
-// their own first rows) instead of one workgroup; at most 64 ranges, so that
-// scan reads few partial counts per expert.
+// Past this many tokens (the launch override's permute_parallel_min_tokens
+// can change it) the permutation runs over nb token ranges in two launches
+// (per-range histograms, then a scatter whose workgroups each scan the
+// histograms for their own first rows) instead of one workgroup; at most 64
+// ranges, so that scan reads few partial counts per expert.
 static int parallel_ranges(const moe_shape &sh)
 {
-    static const int min_t = [] {
-        const char *env = getenv("MOE_PERMUTE_PARALLEL_MIN_T");
-        return env ? atoi(env) : 384;
-    }();
+    const int ov = launch_override().permute_parallel_min_tokens;
+    const int min_t = ov >= 0 ? ov : 384;
     const int T = sh.num_tokens;
     if (T <= min_t || T < 2)
         return 0;
@@ -491,11 +488,9 @@ bool route_permute_fusable(const moe_shape &sh)
     const size_t lds = (size_t)E * (chunk / 32) * 8 + (size_t)sh.num_tokens * sh.top_k * 4;
     // One workgroup routes every token: it pays while routing is one pass of
     // its 16 waves (4 tokens each) and at most two waves share a SIMD; past that the separate routing launch,
-    // spread over many CUs, is faster. MOE_ROUTE_FUSE_MAX_T overrides.
-    static const int max_t = [] {
-        const char *env = getenv("MOE_ROUTE_FUSE_MAX_T");
-        return env ? atoi(env) : 32;
-    }();
+    // spread over many CUs, is faster. The launch override's route_fuse_max_tokens can change it.
+    const int ov = launch_override().route_fuse_max_tokens;
+    const int max_t = ov >= 0 ? ov : 32;
     return sh.num_experts <= 256 && sh.num_tokens <= max_t && lds <= kDynLdsMax;
 }
 

@@ -123,6 +123,9 @@ __device__ __forceinline__ void route_token(const float *__restrict__ row, int E
     // ranges lose no accuracy before the exponential. The normaliser is a
     // DPP row sum over the 16 lanes holding the slots (k <= 16; lanes q >= k
     // add 0); every lane of the row ends with the same sum.
+    // A slot whose difference is not finite (a -inf logit, i.e. a masked
+    // expert, or l_q - l_0 overflowing to -inf) has exp(d) = 0 exactly; the
+    // correction term is then NaN (inf - inf) and is not applied.
     float ex = 0.0f;
     if (q < k) {
         const float a = my_v, b = -l0;
@@ -131,7 +134,7 @@ __device__ __forceinline__ void route_token(const float *__restrict__ row, int E
         const float bp = d - ap;
         const float r = (a - ap) + (b - bp);
         const float ed = expf(d);
-        ex = __builtin_fmaf(ed, r, ed);
+        ex = __builtin_isfinite(d) ? __builtin_fmaf(ed, r, ed) : ed;
     }
     float z = ex;
 #define MOE_DPP_ADD(ctrl) z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), ctrl, 0xF, 0xF, false));

@@ -28,7 +28,8 @@ _STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUP
 EXPORTED = ["moe_status_str", "moe_w4a16_check_shape", "moe_w4a16_is_supported",
             "moe_w4a16_workspace_size", "moe_w4a16_forward", "moe_route", "moe_permute_workspace_size",
             "moe_permute", "moe_grouped_gemm_w4a16", "moe_finalize", "moe_w4a16_pack_weights",
-            "moe_w4a16_dense_gemm", "moe_w4a16_workspace_size_shared", "moe_w4a16_forward_shared"]
+            "moe_w4a16_dense_gemm", "moe_w4a16_workspace_size_shared", "moe_w4a16_forward_shared",
+            "moe_w4a16_set_launch_override"]
 
 
 class MoeShape(ctypes.Structure):
@@ -36,6 +37,14 @@ class MoeShape(ctypes.Structure):
                 ("num_experts", ctypes.c_int32), ("expert_begin", ctypes.c_int32),
                 ("num_local_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
+
+
+class LaunchOverride(ctypes.Structure):
+    _fields_ = [("gemm_mode", ctypes.c_int32), ("gemm_tiles_per_wave", ctypes.c_int32),
+                ("gemm_subtiles", ctypes.c_int32), ("gemm_kseg", ctypes.c_int32), ("gemm_ring", ctypes.c_int32),
+                ("gemm_nontemporal", ctypes.c_int32), ("permute_parallel_min_tokens", ctypes.c_int32),
+                ("route_fuse_max_tokens", ctypes.c_int32), ("decode_max_tokens", ctypes.c_int32),
+                ("decode_combine_max_tokens", ctypes.c_int32)]
 
 
 class MoeError(ValueError):
@@ -88,6 +97,8 @@ def load_library(path: str = LIB_PATH):
         lib.moe_w4a16_workspace_size_shared.restype = Z
         lib.moe_w4a16_forward_shared.argtypes = [S, ctypes.c_int32] + [P] * 12 + [Z, P]
         lib.moe_w4a16_forward_shared.restype = I
+        lib.moe_w4a16_set_launch_override.argtypes = [ctypes.POINTER(LaunchOverride)]
+        lib.moe_w4a16_set_launch_override.restype = I
         _lib = lib
         return lib
 
@@ -130,6 +141,32 @@ def _need(t, dtype, name):
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def set_launch_override(**fields) -> None:
+    """Force launch-shape choices (see moe_launch_override in the C header);
+    fields not given stay automatic (-1). No fields: back to automatic."""
+    ov = LaunchOverride(*([-1] * len(LaunchOverride._fields_)))
+    for k, v in fields.items():
+        if k not in dict(LaunchOverride._fields_):
+            raise ValueError(f"unknown launch override field {k}")
+        setattr(ov, k, int(v))
+    _check(load_library().moe_w4a16_set_launch_override(ctypes.byref(ov) if fields else None))
+
+
+class launch_override:
+    """Context manager: set_launch_override(**fields) inside, automatic after."""
+
+    def __init__(self, **fields):
+        self.fields = fields
+
+    def __enter__(self):
+        set_launch_override(**self.fields)
+        return self
+
+    def __exit__(self, *exc):
+        set_launch_override()
+        return False
 
 
 def check_shape(shape: MoeShape) -> int:
@@ -285,14 +322,29 @@ def finalize(y: torch.Tensor, topk_w: torch.Tensor, inv_perm: torch.Tensor, *,
 
 
 _ws_cache: dict = {}
+_ws_lock = threading.Lock()
 
 
-def _workspace(nbytes: int, device) -> torch.Tensor:
-    key = (device.index if device.index is not None else torch.cuda.current_device())
-    buf = _ws_cache.get(key)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _ws_cache[key] = buf
+def _workspace(nbytes: int, device, stream) -> torch.Tensor:
+    """Default layer workspace, one per (device, stream): forwards in flight on
+    different streams never share one. It is allocated while its stream is
+    current, so when it grows the caching allocator reuses the old block only
+    for work ordered after everything already queued on that stream."""
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    dev = device.index if device.index is not None else torch.cuda.current_device()
+    key = (dev, handle)
+    with _ws_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            if isinstance(stream, torch.cuda.Stream):
+                with torch.cuda.stream(stream):
+                    buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            else:
+                buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+                buf.record_stream(torch.cuda.ExternalStream(handle, device=device))
+            _ws_cache[key] = buf
     return buf
 
 
@@ -340,7 +392,7 @@ def moe_w4a16_forward(x: torch.Tensor, router_logits: torch.Tensor, w13_q: torch
         if nbytes == 0:
             _check(int(lib.moe_w4a16_check_shape(ctypes.byref(sh))) or 3)
         if workspace is None:
-            workspace = _workspace(nbytes, x.device)
+            workspace = _workspace(nbytes, x.device, stream)
         _check(lib.moe_w4a16_forward_shared(ctypes.byref(sh), nsh, _ptr(x), _ptr(router_logits), _ptr(w13_q),
                                             _ptr(s13), _ptr(w2_q), _ptr(s2), _ptr(w13s), _ptr(s13s), _ptr(w2s),
                                             _ptr(s2s), _ptr(out), _ptr(workspace),
@@ -350,8 +402,9 @@ def moe_w4a16_forward(x: torch.Tensor, router_logits: torch.Tensor, w13_q: torch
     if nbytes == 0:
         _check(int(lib.moe_w4a16_check_shape(ctypes.byref(sh))) or 2)
     if workspace is None:
-        workspace = _workspace(nbytes, x.device)
+        workspace = _workspace(nbytes, x.device, stream)
     _check(lib.moe_w4a16_forward(ctypes.byref(sh), _ptr(x), _ptr(router_logits), _ptr(w13_q), _ptr(s13),
                                  _ptr(w2_q), _ptr(s2), _ptr(out), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
