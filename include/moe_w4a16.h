@@ -155,6 +155,24 @@ moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const fl
                              size_t workspace_bytes, void *stream);
 
 /*
+ * The layer for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and result as moe_w4a16_forward, with the workspace taken
+ * from a fixed device array inside the library, MOE_NOALLOC_SCRATCH_BYTES
+ * per GPU (each GPU the library runs on holds one until the process ends).
+ * It allocates nothing. A shape whose moe_w4a16_workspace_size exceeds the
+ * array returns MOE_ERR_WORKSPACE before any launch (for the Qwen3-30B-A3B
+ * expert shape, up to 1484 tokens). Every call on one GPU shares that GPU's
+ * array, so calls that overlap on one GPU (two streams, two host threads)
+ * race: the caller must order them. The array keeps the last call's
+ * intermediates; nothing in it has to start at zero.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_w4a16_forward_noalloc(const moe_shape *shape, const uint16_t *x, const float *router_logits,
+                                     const uint8_t *w13_q, const uint16_t *s13, const uint8_t *w2_q,
+                                     const uint16_t *s2, uint16_t *out, void *stream);
+
+/*
  * The layer with shared experts ([GC] abstract: optional, fused shared
  * experts; the reading taken): num_shared (1..4) always-on experts with the
  * routed experts' shape and formats run on every token, and each one's bf16

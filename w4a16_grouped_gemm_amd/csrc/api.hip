@@ -481,6 +481,61 @@ moe_status moe_w4a16_forward(const moe_shape *shape, const uint16_t *x, const fl
                         workspace, workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// The layer without a caller workspace: its intermediates live in a
+// file-scope device array (one copy per GPU, held until the process ends).
+// Host code never passes the array's name to a kernel: that name is only a
+// host-side stand-in. Its device address is looked up once per device, with
+// that device current, and kept; kernels get that address as their workspace.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static void *g_scratch_ptr[kMaxDevices];
+static hipError_t g_scratch_err[kMaxDevices];
+static std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of this device's scratch array (NULL on failure, with the
+// HIP error in *err). The lookup runs on the first call on each device.
+static void *scratch_address(hipError_t *err)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *ptr = nullptr;
+        const hipError_t r = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_err[dev] = r;
+        g_scratch_ptr[dev] = r == hipSuccess ? ptr : nullptr;
+    });
+    *err = g_scratch_err[dev];
+    return g_scratch_ptr[dev];
+}
+
+moe_status moe_w4a16_forward_noalloc(const moe_shape *shape, const uint16_t *x, const float *router_logits,
+                                     const uint8_t *w13_q, const uint16_t *s13, const uint8_t *w2_q,
+                                     const uint16_t *s2, uint16_t *out, void *stream)
+{
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK)
+        return st;
+    if (carve(*shape, nullptr).bytes > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+        return MOE_ERR_WORKSPACE;                         // beyond the fixed scratch array
+    if (shape->num_tokens == 0)
+        return MOE_OK;
+    hipError_t err = hipSuccess;
+    void *ws = scratch_address(&err);
+    if (!ws)
+        return MOE_ERR_HIP;
+    // nothing in the workspace has to start at zero: every kernel of the
+    // layer writes each intermediate before any kernel reads it
+    return forward_impl(shape, 0, x, router_logits, w13_q, s13, w2_q, s2, nullptr, nullptr, nullptr, nullptr, out,
+                        ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 moe_status moe_w4a16_forward_shared(const moe_shape *shape, int32_t num_shared, const uint16_t *x,
                                     const float *router_logits, const uint8_t *w13_q, const uint16_t *s13,
                                     const uint8_t *w2_q, const uint16_t *s2, const uint8_t *w13_sh,

@@ -29,7 +29,7 @@ EXPORTED = ["moe_status_str", "moe_w4a16_check_shape", "moe_w4a16_is_supported",
             "moe_w4a16_workspace_size", "moe_w4a16_forward", "moe_route", "moe_permute_workspace_size",
             "moe_permute", "moe_grouped_gemm_w4a16", "moe_finalize", "moe_w4a16_pack_weights",
             "moe_w4a16_dense_gemm", "moe_w4a16_workspace_size_shared", "moe_w4a16_forward_shared",
-            "moe_w4a16_set_launch_override"]
+            "moe_w4a16_set_launch_override", "moe_w4a16_forward_noalloc"]
 
 
 class MoeShape(ctypes.Structure):
@@ -99,6 +99,8 @@ def load_library(path: str = LIB_PATH):
         lib.moe_w4a16_forward_shared.restype = I
         lib.moe_w4a16_set_launch_override.argtypes = [ctypes.POINTER(LaunchOverride)]
         lib.moe_w4a16_set_launch_override.restype = I
+        lib.moe_w4a16_forward_noalloc.argtypes = [S, P, P, P, P, P, P, P, P]
+        lib.moe_w4a16_forward_noalloc.restype = I
         _lib = lib
         return lib
 
@@ -408,3 +410,27 @@ def moe_w4a16_forward(x: torch.Tensor, router_logits: torch.Tensor, w13_q: torch
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of the C header
+
+
+def moe_w4a16_forward_noalloc(x: torch.Tensor, router_logits: torch.Tensor, w13_q: torch.Tensor,
+                              s13: torch.Tensor, w2_q: torch.Tensor, s2: torch.Tensor, top_k: int,
+                              out: torch.Tensor, stream=None, *, expert_begin: int = 0,
+                              weight_layout: int = WEIGHTS_PLAIN) -> torch.Tensor:
+    """The layer through moe_w4a16_forward_noalloc: no workspace, nothing
+    allocated (the caller passes `out`); the library's fixed per-GPU scratch
+    array holds the intermediates. Calls that overlap on one GPU race."""
+    for t, d, n in ((x, torch.bfloat16, "x"), (router_logits, torch.float32, "router_logits"),
+                    (w13_q, torch.uint8, "w13_q"), (s13, torch.bfloat16, "s13"), (w2_q, torch.uint8, "w2_q"),
+                    (s2, torch.bfloat16, "s2"), (out, torch.bfloat16, "out")):
+        _need(t, d, n)
+    T, H = x.shape
+    E_loc, N13, _ = w13_q.shape
+    sh = make_shape(T, H, N13 // 2, router_logits.shape[1], E_loc, top_k, expert_begin,
+                    weight_layout=weight_layout)
+    if tuple(out.shape) != (T, H):
+        raise ValueError("out must be [T, H]")
+    _check(load_library().moe_w4a16_forward_noalloc(ctypes.byref(sh), _ptr(x), _ptr(router_logits), _ptr(w13_q),
+                                                    _ptr(s13), _ptr(w2_q), _ptr(s2), _ptr(out), _stream(stream)))
+    return out
