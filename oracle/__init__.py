@@ -19,6 +19,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
+_SRCS = [_SRC, os.path.join(_HERE, "mxfp4_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 
 W13_SWIGLU, W2, RAW = 0, 1, 2
@@ -31,7 +32,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+               "-fPIC", "-shared", "-o", tmp, *_SRCS, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -41,7 +42,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(os.path.getmtime(f) for f in _SRCS):
         build(force=True)
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
@@ -56,6 +57,14 @@ def _load():
     lib.oracle_finalize.argtypes = [I, I, I, P, I, P, P, I, P, P, P, I]
     lib.oracle_layer.argtypes = [I] * 8 + [P] * 6 + [I] + [P] * 4 + [P] + [P] * 10
     lib.oracle_layer_bruteforce.argtypes = [I] * 7 + [P] * 7 + [I] + [P] * 4 + [P] * 2
+    lib.oracle_e2m1_value.argtypes = [I]
+    lib.oracle_e2m1_value.restype = ctypes.c_double
+    lib.oracle_e8m0_value.argtypes = [I]
+    lib.oracle_e8m0_value.restype = ctypes.c_double
+    lib.oracle_mx_quantize.argtypes = [ctypes.c_int64, I, P, P, P]
+    lib.oracle_grouped_gemm_mxfp4.argtypes = [I, I, I, I, P, P, P, I, P, P, P, P, P, I]
+    lib.oracle_layer_w4a4.argtypes = [I] * 7 + [P] * 7 + [P] * 13
+    lib.oracle_layer_w4a4_bruteforce.argtypes = [I] * 6 + [P] * 7 + [P] * 2
     _lib = lib
     return lib
 
@@ -211,3 +220,86 @@ def layer_bruteforce(x, topk_ids, topk_w, w13_q, s13, w2_q, s2, *, expert_begin:
 def _shared_ptrs(shared):
     nsh, w13s, s13s, w2s, s2s = _shared_args(shared)
     return nsh, _ptr(w13s), _ptr(s13s), _ptr(w2s), _ptr(s2s)
+
+
+# ---------------------------------------------------------------------------
+# W4A4 (MXFP4) variant -- see mxfp4_oracle.c for the format reading
+# ---------------------------------------------------------------------------
+
+def e2m1_value(code: int) -> float:
+    return float(_load().oracle_e2m1_value(int(code)))
+
+
+def e8m0_value(s: int) -> float:
+    return float(_load().oracle_e8m0_value(int(s)))
+
+
+def mx_quantize(x: np.ndarray):
+    """bf16 rows [R, K] (K % 32 == 0) -> (codes uint8 [R, K/2], scales uint8 [R, K/32])."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    R, K = x.shape
+    codes = np.empty((R, K // 2), np.uint8)
+    scales = np.empty((R, K // 32), np.uint8)
+    _load().oracle_mx_quantize(R, K, _ptr(x), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def grouped_gemm_mxfp4(kind: int, a_codes, a_scales, offsets, wq, ws, *, rows: int, a_row_index=None,
+                       top_k: int = 1, out_f32: bool = False, row_sel=None):
+    """Grouped GEMM on MXFP4 activations and weights (oracle_grouped_gemm_mxfp4)."""
+    E_loc, N, K2 = wq.shape
+    K = 2 * K2
+    out_cols = N // 2 if kind == W13_SWIGLU else N
+    out = np.zeros((rows, out_cols), np.float32 if out_f32 else np.uint16)
+    idx = None if a_row_index is None else np.ascontiguousarray(a_row_index, dtype=np.int32)
+    sel = None if row_sel is None else np.ascontiguousarray(row_sel, dtype=np.uint8)
+    _load().oracle_grouped_gemm_mxfp4(kind, E_loc, N, K, _ptr(np.ascontiguousarray(a_codes)),
+                                      _ptr(np.ascontiguousarray(a_scales)), _ptr(idx), top_k,
+                                      _ptr(np.ascontiguousarray(offsets, dtype=np.int32)),
+                                      _ptr(np.ascontiguousarray(wq)), _ptr(np.ascontiguousarray(ws)), _ptr(sel),
+                                      _ptr(out), 1 if out_f32 else 0)
+    return out
+
+
+def layer_w4a4(x, logits, w13_q, w13_s, w2_q, w2_s, *, top_k: int, expert_begin: int = 0, tok_sel=None):
+    """The W4A4 (MXFP4) layer through the permutation; a dict of every stage."""
+    T, H = x.shape
+    E_g = logits.shape[1]
+    E_loc, N13, _ = w13_q.shape
+    I = N13 // 2
+    S = T * top_k
+    r = dict(topk_ids=np.empty((T, top_k), np.int32), topk_w=np.empty((T, top_k), np.float32),
+             counts=np.empty(E_loc, np.int32), offsets=np.empty(E_loc + 1, np.int32),
+             perm=np.empty(S, np.int32), inv_perm=np.empty((T, top_k), np.int32),
+             xq=np.zeros((T, H // 2), np.uint8), xs=np.zeros((T, H // 32), np.uint8),
+             h=np.zeros((S, I), np.uint16), hq=np.zeros((S, I // 2), np.uint8), hs=np.zeros((S, I // 32), np.uint8),
+             y=np.zeros((S, H), np.uint16), out=np.zeros((T, H), np.uint16))
+    sel = None if tok_sel is None else np.ascontiguousarray(tok_sel, dtype=np.uint8)
+    _load().oracle_layer_w4a4(T, E_g, top_k, expert_begin, E_loc, H, I,
+                              _ptr(np.ascontiguousarray(x, dtype=np.uint16)),
+                              _ptr(np.ascontiguousarray(logits, dtype=np.float32)),
+                              _ptr(np.ascontiguousarray(w13_q)), _ptr(np.ascontiguousarray(w13_s)),
+                              _ptr(np.ascontiguousarray(w2_q)), _ptr(np.ascontiguousarray(w2_s)), _ptr(sel),
+                              _ptr(r["topk_ids"]), _ptr(r["topk_w"]), _ptr(r["counts"]), _ptr(r["offsets"]),
+                              _ptr(r["perm"]), _ptr(r["inv_perm"]), _ptr(r["xq"]), _ptr(r["xs"]), _ptr(r["h"]),
+                              _ptr(r["hq"]), _ptr(r["hs"]), _ptr(r["y"]), _ptr(r["out"]))
+    return r
+
+
+def layer_w4a4_bruteforce(x, topk_ids, topk_w, w13_q, w13_s, w2_q, w2_s, *, expert_begin: int = 0,
+                          tok_sel=None):
+    """Per (token, slot) W4A4 expert FFNs + ordered combine; no permutation."""
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    E_loc, N13, _ = w13_q.shape
+    I = N13 // 2
+    out = np.zeros((T, H), np.uint16)
+    sel = None if tok_sel is None else np.ascontiguousarray(tok_sel, dtype=np.uint8)
+    _load().oracle_layer_w4a4_bruteforce(T, k, expert_begin, E_loc, H, I,
+                                         _ptr(np.ascontiguousarray(x, dtype=np.uint16)),
+                                         _ptr(np.ascontiguousarray(topk_ids, dtype=np.int32)),
+                                         _ptr(np.ascontiguousarray(topk_w, dtype=np.float32)),
+                                         _ptr(np.ascontiguousarray(w13_q)), _ptr(np.ascontiguousarray(w13_s)),
+                                         _ptr(np.ascontiguousarray(w2_q)), _ptr(np.ascontiguousarray(w2_s)),
+                                         _ptr(sel), _ptr(out))
+    return out

@@ -167,6 +167,46 @@ def make_shared_weights(workload: str | Workload, num_shared: int, seed: int | N
 
 
 @dataclass
+class Mxfp4LayerInputs:
+    """The W4A4 variant's layer inputs: x and logits as in make_layer_inputs,
+    weights as MXFP4 (E2M1 codes in the int4 byte layout, E8M0 scales per 32
+    along K)."""
+    workload: Workload
+    tokens: int
+    x: np.ndarray        # uint16 (bf16) [T, H]
+    logits: np.ndarray   # float32 [T, E_g]
+    w13_q: np.ndarray    # uint8 E2M1 codes [E_loc, 2I, H/2]
+    w13_s: np.ndarray    # uint8 E8M0 [E_loc, 2I, H/32]
+    w2_q: np.ndarray     # uint8 E2M1 codes [E_loc, H, I/2]
+    w2_s: np.ndarray     # uint8 E8M0 [E_loc, H, I/32]
+
+
+MX_BLOCK = 32
+MX_SCALE_RANGE = (119, 121)   # E8M0 bytes: scales 2^-8 .. 2^-6, the W4A16 scales' magnitude
+
+
+def make_mxfp4_layer_inputs(workload: str | Workload, tokens: int, seed: int | None = None) -> Mxfp4LayerInputs:
+    """x and logits drawn exactly as make_layer_inputs draws them (same seed,
+    same order), then w13 codes, w13 scales, w2 codes, w2 scales: every code
+    byte uniform (two independent uniform E2M1 codes), every scale byte
+    uniform over MX_SCALE_RANGE."""
+    wl = WORKLOADS[workload] if isinstance(workload, str) else workload
+    T, H, I, E, El = tokens, wl.hidden, wl.inter, wl.num_experts, wl.num_local_experts
+    rng = np.random.Generator(np.random.PCG64(seed_for(wl.index, T) if seed is None else seed))
+    x = bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    if wl.routing == "zipf":
+        logits = zipf_logits(rng, T, E)
+    else:
+        logits = rng.standard_normal((T, E), dtype=np.float32)
+    lo, hi = MX_SCALE_RANGE
+    w13_q = rng.integers(0, 256, size=(El, 2 * I, H // 2), dtype=np.uint8)
+    w13_s = rng.integers(lo, hi + 1, size=(El, 2 * I, H // MX_BLOCK), dtype=np.uint8)
+    w2_q = rng.integers(0, 256, size=(El, H, I // 2), dtype=np.uint8)
+    w2_s = rng.integers(lo, hi + 1, size=(El, H, I // MX_BLOCK), dtype=np.uint8)
+    return Mxfp4LayerInputs(wl, T, x, logits, w13_q, w13_s, w2_q, w2_s)
+
+
+@dataclass
 class FinalizeStressInputs:
     logits: np.ndarray      # float32 [T, E]: route these with top_k to get ids / weights
     zero_mask: np.ndarray   # bool [T, k]: routing weights forced to +0.0
