@@ -315,6 +315,76 @@ def shared_weights(ops, wl, L, torch, layout, S=1):
 
 
 # ---------------------------------------------------------------------------
+# the W4A4 (MXFP4) variant
+# ---------------------------------------------------------------------------
+
+FP4_MFMA_PEAK_TFLOPS = 10100.0
+
+
+def mx_weight_bytes_per_expert(H: int, I: int):
+    """E2M1 codes + E8M0 scales (one byte per 32 along K) of one expert: (w13, w2)."""
+    return 2 * I * H // 2 + 2 * I * (H // 32), H * I // 2 + H * (I // 32)
+
+
+def make_mx_weights(wl, L, torch, seed_base):
+    from w4a16_grouped_gemm_amd.inputs import MX_SCALE_RANGE, make_mxfp4_layer_inputs
+    dev = torch.device("cuda")
+    H, I, El = wl.hidden, wl.inter, wl.num_local_experts
+    inp = make_mxfp4_layer_inputs(wl, 1)
+    reps = [dict(w13=torch.from_numpy(inp.w13_q).to(dev), s13=torch.from_numpy(inp.w13_s).to(dev),
+                 w2=torch.from_numpy(inp.w2_q).to(dev), s2=torch.from_numpy(inp.w2_s).to(dev))]
+    g = torch.Generator(device=dev)
+    lo, hi = MX_SCALE_RANGE
+    for i in range(1, L):
+        g.manual_seed(seed_base * 1000 + i)
+        reps.append(dict(
+            w13=torch.randint(0, 256, (El, 2 * I, H // 2), generator=g, device=dev, dtype=torch.uint8),
+            s13=torch.randint(lo, hi + 1, (El, 2 * I, H // 32), generator=g, device=dev, dtype=torch.uint8),
+            w2=torch.randint(0, 256, (El, H, I // 2), generator=g, device=dev, dtype=torch.uint8),
+            s2=torch.randint(lo, hi + 1, (El, H, I // 32), generator=g, device=dev, dtype=torch.uint8)))
+    return reps
+
+
+def w4a4_point(ops, wl, weights, T, torch, seed, prefill=False):
+    """The W4A4 layer at T tokens: median per call; weight bytes of the
+    active experts (decode) or flops against the dense FP4 MFMA peak (prefill)."""
+    import ctypes
+    probe = make_batches(wl, T, 4, torch, seed)
+    w13b, w2b = mx_weight_bytes_per_expert(wl.hidden, wl.inter)
+    act0 = sum(s["active"] for s in routing_stats(ops, wl, probe, torch)) / len(probe)
+    calls = 8 if prefill else n_calls_for(act0 * (w13b + w2b))
+    batches = make_batches(wl, T, calls, torch, seed)
+    st = routing_stats(ops, wl, batches, torch)
+    act = sum(s["active"] for s in st) / calls
+    shape = ops.make_shape(T, wl.hidden, wl.inter, wl.num_experts, wl.num_local_experts, wl.top_k,
+                           wl.expert_begin, group_size=32)
+    ws = torch.empty(max(int(ops.load_library().moe_w4a4_workspace_size(ctypes.byref(shape))), 256),
+                     dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((T, wl.hidden), dtype=torch.bfloat16, device="cuda") for _ in range(calls)]
+
+    def fwd(i):
+        w, b = weights[i % len(weights)], batches[i]
+        ops.moe_w4a4_forward(b["x"], b["logits"], w["w13"], w["s13"], w["w2"], w["s2"], wl.top_k, out=outs[i],
+                             expert_begin=wl.expert_begin, workspace=ws)
+    g = capture(torch, [lambda i=i: fwd(i) for i in range(calls)])
+    r = replay_stats(torch, g, calls)
+    del g
+    us = r["median_us"]
+    rec = {"tokens": T, "us_per_layer": us, "tokens_per_s": round(T / (us * 1e-6), 1), "active_experts": act,
+           "timing": r}
+    if prefill:
+        flops = 6.0 * wl.inter * wl.hidden * T * wl.top_k
+        tf = flops / (us * 1e-6) / 1e12
+        rec.update(routing="zipf(1.1)", tflops=round(tf, 1), fp4_mfma_frac=round(tf / FP4_MFMA_PEAK_TFLOPS, 4),
+                   bf16_mfma_frac=round(tf / MFMA_PEAK_TFLOPS, 4))
+    else:
+        gbps = act * (w13b + w2b) / (us * 1e-6) / 1e9
+        rec.update(weight_bytes=round(act * (w13b + w2b)), weight_GBps=round(gbps, 1),
+                   hbm_frac=round(gbps / HBM_PEAK_GBPS, 4))
+    return rec
+
+
+# ---------------------------------------------------------------------------
 # the GEMMs alone (roofline of the dominant kernel)
 # ---------------------------------------------------------------------------
 
@@ -485,7 +555,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of extra workloads to time "
-                    "(decode,prefill,ep,shared,finalize,dense); default all")
+                    "(decode,prefill,ep,shared,finalize,dense,w4a4); default all")
     ap.add_argument("--weights", choices=["tiled", "plain"], default="tiled",
                     help="int4 code layout the layer reads (tiled: packed once before timing)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -504,7 +574,8 @@ def main():
     from w4a16_grouped_gemm_amd.inputs import WORKLOADS
 
     ops.load_library()
-    only = set(filter(None, args.only.split(","))) or {"decode", "prefill", "ep", "shared", "finalize", "dense"}
+    only = set(filter(None, args.only.split(","))) or {"decode", "prefill", "ep", "shared", "finalize", "dense",
+                                                        "w4a4"}
     if args.no_sweep:
         only = set()
     layout = ops.WEIGHTS_TILED if args.weights == "tiled" else ops.WEIGHTS_PLAIN
@@ -586,6 +657,16 @@ def main():
         log("dense W4A16 GEMM")
         dense = dense_points(ops, torch, layout)
 
+    w4a4 = None
+    if "w4a4" in only:
+        log("W4A4 (MXFP4) layer: decode 1/16/64/256 and prefill 2048")
+        wm = make_mx_weights(wl, 8, torch, seed_base=13)
+        w4a4 = {"workload": "qwen3_decode / qwen3_prefill shapes, MXFP4 weights and activations",
+                "decode": [w4a4_point(ops, wl, wm, ts, torch, seed=ts + 3) for ts in (1, 16, 64, 256)],
+                "prefill": w4a4_point(ops, WORKLOADS["qwen3_prefill"], wm, 2048, torch, seed=2049, prefill=True)}
+        del wm
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
@@ -619,6 +700,7 @@ def main():
         "ep_shard": ep,
         "finalize_stream": fin,
         "dense_gemm": dense,
+        "w4a4_mxfp4": w4a4,
     }
     print(json.dumps(rec), flush=True)
 

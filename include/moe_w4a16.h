@@ -312,6 +312,60 @@ moe_status moe_w4a16_pack_weights(const moe_shape *shape, moe_gemm_kind kind, co
                                   uint8_t *wq_tiled, void *stream);
 
 /*
+ * ---- The W4A4 variant: MXFP4 weights and activations ----------------------
+ * [FI] section 2 ("Arithmetic Alignment": W4A4 finalizers beside the W4A16
+ * ones) and its performance section (a W4A4 kernel); [GC] abstract (FP4
+ * block-scaled grouped GEMMs, activations requantized between the GEMMs).
+ * The pages fix no FP4 encoding; the format read is the OCP MX one, MXFP4:
+ *   element  E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa bit; a zero
+ *            exponent field is subnormal): magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+ *            codes two per byte, element k of a row in byte k/2, even k in the
+ *            low nibble (the int4 byte layout), rows K-contiguous;
+ *   scale    E8M0 byte s per 32 consecutive elements along K: 2^(s - 127);
+ *   weights  w13_q uint8 [E_loc][2*I][H/2], w13_s uint8 [E_loc][2*I][H/32],
+ *            w2_q  uint8 [E_loc][H][I/2],   w2_s  uint8 [E_loc][H][I/32].
+ * These entry points take moe_shape.group_size == 32 and weight_layout ==
+ * MOE_WEIGHTS_PLAIN (else MOE_ERR_UNSUPPORTED); H and I stay multiples of 128.
+ */
+
+/*
+ * Quantize rows x rows of K bf16 values (K a multiple of 32, <= 65536) to
+ * MXFP4: codes uint8 [rows][K/2], scales uint8 [rows][K/32]. Per block of 32:
+ * X = 2^(floor(log2 max|v|) - 2), the exponent clamped to [-127, 127]
+ * (an all-zero block gets s = 0); each v / X rounded to the nearest E2M1
+ * magnitude, ties to the even code, magnitudes past 6 held at 6, the sign of
+ * v kept. Bit-exact (every decision is taken on the exact binary32 value).
+ */
+moe_status moe_mxfp4_quantize(int64_t rows, int32_t K, const uint16_t *x, uint8_t *codes, uint8_t *scales,
+                              void *stream);
+
+/*
+ * Grouped GEMM on MXFP4 operands, the same row semantics as
+ * moe_grouped_gemm_w4a16: for local expert e and rows r in
+ * [offsets[e], offsets[e+1]) the activation row is row a_row_index[r] / top_k
+ * of (a_codes [T][K/2], a_scales [T][K/32]) when a_row_index != NULL, else
+ * row r of (a_codes [T*k][K/2], a_scales [T*k][K/32]). Kinds and outputs as
+ * moe_grouped_gemm_w4a16 (W13_SWIGLU: bf16 h = silu(g) * u; W2 / W13_RAW: bf16
+ * or f32). Accumulation is binary32 in the matrix unit over exact FP4 products
+ * with power-of-two block scales. No workspace.
+ */
+moe_status moe_grouped_gemm_mxfp4(const moe_shape *shape, moe_gemm_kind kind, const uint8_t *a_codes,
+                                  const uint8_t *a_scales, const int32_t *a_row_index, const int32_t *offsets,
+                                  const uint8_t *wq, const uint8_t *ws, void *c, moe_dtype c_dtype, void *stream);
+
+/*
+ * The W4A4 layer: route -> permute -> quantize x (per token, 32 along H) ->
+ * gate/up GEMM (h = bf16(silu(g) * u)) -> requantize h (32 along I) -> down
+ * GEMM (y bf16) -> finalize (the W4A16 layer's combine). Arguments as
+ * moe_w4a16_forward with MXFP4 weights; workspace >= moe_w4a4_workspace_size
+ * bytes (0 for an invalid shape), 256-B aligned.
+ */
+size_t moe_w4a4_workspace_size(const moe_shape *shape);
+moe_status moe_w4a4_forward(const moe_shape *shape, const uint16_t *x, const float *router_logits,
+                            const uint8_t *w13_q, const uint8_t *w13_s, const uint8_t *w2_q, const uint8_t *w2_s,
+                            uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Launch-shape override, for tests and tuning (not a passage of the pages: a
  * switch over this library's own kernel variants). Every field -1 keeps the
  * automatic choice. A field changes which kernel variant runs and how it

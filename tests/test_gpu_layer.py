@@ -199,7 +199,9 @@ def test_two_streams_default_workspaces():
 
 
 # (workload, T): the small-batch path's regimes -- down GEMM with the combine
-# (T <= 4), down GEMM then the finalize (5..16), and the edges: 128 slots
+# (T <= 2; forced up to 16 below), down GEMM then the finalize, both kernel
+# families (split-K on the EP shard at 1 token and on the tiny layer,
+# streaming elsewhere), and the edges: 128 slots
 # (T = 8 at k = 16), a token with no local slot (EP shard), 2 tokens sharing
 # experts (tiny: 8 experts, top-2)
 SMALL = [("qwen3_decode", 1), ("qwen3_decode", 2), ("qwen3_decode", 4), ("qwen3_decode", 5),
@@ -226,10 +228,13 @@ def test_small_batch_path_equals_general_path(wl, T):
     fast = _forward(inp)
     with ops.launch_override(decode_combine_max_tokens=0):
         no_combine = _forward(inp)
+    with ops.launch_override(decode_combine_max_tokens=16):
+        combine = _forward(inp)                          # the fused combine wherever it fits
     with ops.launch_override(decode_max_tokens=0):
         general = _forward(inp)
     assert np.array_equal(fast, general)
     assert np.array_equal(no_combine, general)
+    assert np.array_equal(combine, general)
     ref = oracle.layer(inp.x, inp.logits, inp.w13_q, inp.s13, inp.w2_q, inp.s2, top_k=inp.workload.top_k,
                        expert_begin=inp.workload.expert_begin)
     local = (ref["topk_ids"] >= inp.workload.expert_begin) & \

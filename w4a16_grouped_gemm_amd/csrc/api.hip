@@ -40,6 +40,30 @@ moe_launch_override launch_override()
     return g_override;
 }
 
+// The grouped GEMM descriptor of the layer's gate/up or down projection
+// (sizes, expected rows under uniform routing, code layout); the caller fills
+// in the pointers.
+GemmLaunch layer_gemm_args(const moe_shape &sh, moe_gemm_kind kind)
+{
+    GemmLaunch g{};
+    g.kind = kind;
+    g.top_k = sh.top_k;
+    g.num_experts = sh.num_local_experts;
+    g.max_rows = sh.num_tokens * sh.top_k;
+    // expected local rows: the routed slots that land on this GPU's experts
+    g.expected_rows = (int)((long long)g.max_rows * sh.num_local_experts / sh.num_experts);
+    if (kind == MOE_GEMM_W2) {
+        g.K = sh.inter;
+        g.N = sh.hidden;
+    } else {
+        g.K = sh.hidden;
+        g.N = 2 * sh.inter;
+    }
+    g.a_bytes = (size_t)g.max_rows * g.K * 2;
+    g.w_tiled = sh.weight_layout == MOE_WEIGHTS_TILED;
+    return g;
+}
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -124,28 +148,48 @@ Workspace carve(const moe_shape &sh, void *base, int nsh = 0)
 
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// The W4A4 (MXFP4) entry points: the same limits, with 32-element scale
+// blocks and plain (row-major) codes.
+moe_status check_shape_mx(const moe_shape *sh)
+{
+    if (!sh)
+        return MOE_ERR_NULL;
+    if (sh->group_size != 32 || sh->weight_layout != MOE_WEIGHTS_PLAIN)
+        return MOE_ERR_UNSUPPORTED;
+    moe_shape s = *sh;
+    s.group_size = kGroup;
+    return check_shape(&s);
+}
+
+// W4A4 layer workspace: the W4A16 layer's regions plus the quantized x and h.
+struct MxWorkspace {
+    Workspace base;
+    uint8_t *xq, *xs, *hq, *hs;
+    size_t bytes;
+};
+
+MxWorkspace carve_mx(const moe_shape &sh, void *p)
+{
+    MxWorkspace w{};
+    w.base = carve(sh, p);
+    char *b = static_cast<char *>(p);
+    size_t off = w.base.bytes;
+    auto take = [&](size_t bytes) {
+        char *r = b ? b + off : nullptr;
+        off += align_up(bytes);
+        return reinterpret_cast<uint8_t *>(r);
+    };
+    const size_t T = (size_t)sh.num_tokens, S = T * sh.top_k;
+    w.xq = take(T * sh.hidden / 2);
+    w.xs = take(T * sh.hidden / 32);
+    w.hq = take(S * sh.inter / 2);
+    w.hs = take(S * sh.inter / 32);
+    w.bytes = off;
+    return w;
+}
+
 constexpr int32_t kMaxDenseDim = 65536;   // N and K of the dense GEMM
 
-GemmLaunch gemm_args(const moe_shape &sh, moe_gemm_kind kind)
-{
-    GemmLaunch g{};
-    g.kind = kind;
-    g.top_k = sh.top_k;
-    g.num_experts = sh.num_local_experts;
-    g.max_rows = sh.num_tokens * sh.top_k;
-    // expected local rows: the routed slots that land on this GPU's experts
-    g.expected_rows = (int)((long long)g.max_rows * sh.num_local_experts / sh.num_experts);
-    if (kind == MOE_GEMM_W2) {
-        g.K = sh.inter;
-        g.N = sh.hidden;
-    } else {
-        g.K = sh.hidden;
-        g.N = 2 * sh.inter;
-    }
-    g.a_bytes = (size_t)g.max_rows * g.K * 2;
-    g.w_tiled = sh.weight_layout == MOE_WEIGHTS_TILED;
-    return g;
-}
 
 }  // namespace
 }  // namespace moe
@@ -272,7 +316,7 @@ moe_status moe_grouped_gemm_w4a16(const moe_shape *shape, moe_gemm_kind kind, co
     if (!aligned(a, 16) || !aligned(wq, 16) || !aligned(c, 16) || !aligned(s, 2) ||
         !aligned(offsets, 4) || (a_row_index && !aligned(a_row_index, 4)))
         return MOE_ERR_ALIGN;
-    GemmLaunch g = gemm_args(*shape, kind);
+    GemmLaunch g = layer_gemm_args(*shape, kind);
     g.a = a;
     g.a_row_index = a_row_index;
     if (a_row_index)
@@ -437,7 +481,7 @@ static moe_status forward_impl(const moe_shape *shape, int nsh, const uint16_t *
         g.s_sh = s_sh;
     };
     if (e == hipSuccess) {
-        GemmLaunch g = gemm_args(sh, MOE_GEMM_W13_SWIGLU);
+        GemmLaunch g = layer_gemm_args(sh, MOE_GEMM_W13_SWIGLU);
         with_shared(g, w13_sh, s13_sh);
         g.a = x;
         g.a_row_index = ws.perm;
@@ -453,7 +497,7 @@ static moe_status forward_impl(const moe_shape *shape, int nsh, const uint16_t *
     // order and the finalize reads it without the inv_perm indirection
     const bool y_slot = sh.num_local_experts == sh.num_experts && nsh == 0;
     if (e == hipSuccess) {
-        GemmLaunch g = gemm_args(sh, MOE_GEMM_W2);
+        GemmLaunch g = layer_gemm_args(sh, MOE_GEMM_W2);
         with_shared(g, w2_sh, s2_sh);
         g.a = ws.h;
         g.a_row_index = nullptr;
@@ -534,6 +578,151 @@ moe_status moe_w4a16_forward_noalloc(const moe_shape *shape, const uint16_t *x, 
     // layer writes each intermediate before any kernel reads it
     return forward_impl(shape, 0, x, router_logits, w13_q, s13, w2_q, s2, nullptr, nullptr, nullptr, nullptr, out,
                         ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+moe_status moe_mxfp4_quantize(int64_t rows, int32_t K, const uint16_t *x, uint8_t *codes, uint8_t *scales,
+                              void *stream)
+{
+    if (rows < 0 || K < 32 || K % 32 != 0 || K > 65536)
+        return MOE_ERR_SHAPE;
+    if (rows * (int64_t)K * 2 >= (1LL << 40))
+        return MOE_ERR_UNSUPPORTED;
+    if (rows == 0)
+        return MOE_OK;
+    if (!x || !codes || !scales)
+        return MOE_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(codes, 16))
+        return MOE_ERR_ALIGN;
+    return from_hip(launch_mx_quantize(rows, K, x, codes, scales, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_gemm_mxfp4(const moe_shape *shape, moe_gemm_kind kind, const uint8_t *a_codes,
+                                  const uint8_t *a_scales, const int32_t *a_row_index, const int32_t *offsets,
+                                  const uint8_t *wq, const uint8_t *ws, void *c, moe_dtype c_dtype, void *stream)
+{
+    moe_status st = check_shape_mx(shape);
+    if (st != MOE_OK)
+        return st;
+    if (kind != MOE_GEMM_W13_SWIGLU && kind != MOE_GEMM_W2 && kind != MOE_GEMM_W13_RAW)
+        return MOE_ERR_UNSUPPORTED;
+    if ((c_dtype != MOE_BF16 && c_dtype != MOE_F32) || (kind == MOE_GEMM_W13_SWIGLU && c_dtype != MOE_BF16))
+        return MOE_ERR_UNSUPPORTED;
+    if (shape->num_tokens == 0)
+        return MOE_OK;
+    if (!a_codes || !a_scales || !offsets || !wq || !ws || !c)
+        return MOE_ERR_NULL;
+    if (!aligned(a_codes, 16) || !aligned(wq, 16) || !aligned(c, 16) || !aligned(a_scales, 4) || !aligned(ws, 4) ||
+        !aligned(offsets, 4) || (a_row_index && !aligned(a_row_index, 4)))
+        return MOE_ERR_ALIGN;
+    GemmLaunch g0 = layer_gemm_args(*shape, kind);
+    MxGemmLaunch g{};
+    g.kind = kind;
+    g.a = a_codes;
+    g.as = a_scales;
+    g.a_row_index = a_row_index;
+    g.a_rows = a_row_index ? shape->num_tokens : (long long)shape->num_tokens * shape->top_k;
+    g.top_k = shape->top_k;
+    g.offsets = offsets;
+    g.num_experts = shape->num_local_experts;
+    g.wq = wq;
+    g.ws = ws;
+    g.c = c;
+    g.c_f32 = c_dtype == MOE_F32;
+    g.K = g0.K;
+    g.N = g0.N;
+    g.max_rows = g0.max_rows;
+    g.expected_rows = g0.expected_rows;
+    return from_hip(launch_mx_grouped_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_w4a4_workspace_size(const moe_shape *shape)
+{
+    if (check_shape_mx(shape) != MOE_OK)
+        return 0;
+    moe_shape s = *shape;
+    s.group_size = kGroup;
+    return carve_mx(s, nullptr).bytes;
+}
+
+moe_status moe_w4a4_forward(const moe_shape *shape, const uint16_t *x, const float *router_logits,
+                            const uint8_t *w13_q, const uint8_t *w13_s, const uint8_t *w2_q, const uint8_t *w2_s,
+                            uint16_t *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    moe_status st = check_shape_mx(shape);
+    if (st != MOE_OK)
+        return st;
+    moe_shape sh = *shape;
+    sh.group_size = kGroup;                               // the shared launchers read no group size
+    if (sh.num_tokens == 0)
+        return MOE_OK;
+    if (!x || !router_logits || !w13_q || !w13_s || !w2_q || !w2_s || !out || !workspace)
+        return MOE_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w13_q, 16) || !aligned(w2_q, 16) || !aligned(w13_s, 4) ||
+        !aligned(w2_s, 4) || !aligned(router_logits, 4) || !aligned(workspace, kAlign))
+        return MOE_ERR_ALIGN;
+    MxWorkspace mw = carve_mx(sh, workspace);
+    if (workspace_bytes < mw.bytes)
+        return MOE_ERR_WORKSPACE;
+    const Workspace &ws = mw.base;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (route_permute_fusable(sh)) {
+        e = launch_route_permute(sh, router_logits, ws.ids, ws.w, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s, 0);
+    } else {
+        e = launch_route(sh, router_logits, ws.ids, ws.w, s);
+        if (e == hipSuccess)
+            e = launch_permute(sh, ws.ids, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s, 0, ws.part);
+    }
+    if (e == hipSuccess)
+        e = launch_mx_quantize(sh.num_tokens, sh.hidden, x, mw.xq, mw.xs, nullptr, s);
+    const int S = sh.num_tokens * sh.top_k;
+    if (e == hipSuccess) {
+        const GemmLaunch g0 = layer_gemm_args(sh, MOE_GEMM_W13_SWIGLU);
+        MxGemmLaunch g{};
+        g.kind = MOE_GEMM_W13_SWIGLU;
+        g.a = mw.xq;
+        g.as = mw.xs;
+        g.a_row_index = ws.perm;
+        g.a_rows = sh.num_tokens;
+        g.top_k = sh.top_k;
+        g.offsets = ws.offsets;
+        g.num_experts = sh.num_local_experts;
+        g.wq = w13_q;
+        g.ws = w13_s;
+        g.c = ws.h;
+        g.K = g0.K;
+        g.N = g0.N;
+        g.max_rows = g0.max_rows;
+        g.expected_rows = g0.expected_rows;
+        e = launch_mx_grouped_gemm(g, s);
+    }
+    // requantize h: only the R routed rows (R = offsets[E_loc], read on the device)
+    if (e == hipSuccess)
+        e = launch_mx_quantize(S, sh.inter, ws.h, mw.hq, mw.hs, ws.offsets + sh.num_local_experts, s);
+    const bool y_slot = sh.num_local_experts == sh.num_experts;
+    if (e == hipSuccess) {
+        const GemmLaunch g0 = layer_gemm_args(sh, MOE_GEMM_W2);
+        MxGemmLaunch g{};
+        g.kind = MOE_GEMM_W2;
+        g.a = mw.hq;
+        g.as = mw.hs;
+        g.a_rows = S;
+        g.top_k = sh.top_k;
+        g.offsets = ws.offsets;
+        g.num_experts = sh.num_local_experts;
+        g.wq = w2_q;
+        g.ws = w2_s;
+        g.c = ws.y;
+        g.c_row_index = y_slot ? ws.perm : nullptr;
+        g.K = g0.K;
+        g.N = g0.N;
+        g.max_rows = g0.max_rows;
+        g.expected_rows = g0.expected_rows;
+        e = launch_mx_grouped_gemm(g, s);
+    }
+    if (e == hipSuccess)
+        e = launch_finalize(sh, ws.y, false, ws.w, ws.inv_perm, out, false, s, y_slot);
+    return from_hip(e);
 }
 
 moe_status moe_w4a16_forward_shared(const moe_shape *shape, int32_t num_shared, const uint16_t *x,

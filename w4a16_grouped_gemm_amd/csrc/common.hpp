@@ -109,6 +109,30 @@ hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const
                            bool y_slot = false, int num_shared = 0,
                            const int32_t *shared_row0 = nullptr);
 
+// The grouped GEMM's launch choice for a shape: kernel family (0 split-K,
+// 1 streaming, 2 / 3 tile kernel) and the streaming tiling. The families
+// sum in different orders; within a family every tiling gives the same bits.
+struct LaunchChoice {
+    int mode, tpw, nsub, kseg, ring;
+    bool nt;
+};
+LaunchChoice choose_launch(const GemmLaunch &g);
+GemmLaunch layer_gemm_args(const moe_shape &sh, moe_gemm_kind kind);
+
+// Item source of the small-batch path on the streaming kernel: src 1 routes
+// inside the kernel (gate/up; writes ids / w / pres), src 2 reads the stored
+// slot table (down). T tokens, E_g logit columns, local experts from begin.
+struct DecodeSource {
+    int src;
+    const float *logits;
+    int T, E_g, begin;
+    int32_t *ids;
+    float *w;
+    int32_t *pres;
+};
+hipError_t launch_decode_stream(const GemmLaunch &g, const DecodeSource &d, hipStream_t st);
+bool decode_stream_supported(const GemmLaunch &g);
+
 // The layer's small-batch path (decode.hip): up to 16 tokens, no shared
 // experts, E_g <= 256. h and y are in slot order; pres[t*k + j] is the slot
 // index when the slot's expert is local, else -1.
@@ -122,6 +146,29 @@ hipError_t launch_decode_down(const moe_shape &sh, const int32_t *ids, const int
 hipError_t launch_decode_down_combine(const moe_shape &sh, const int32_t *ids, const float *w, const int32_t *pres,
                                       const uint16_t *h, const uint8_t *w2, const uint16_t *s2, uint16_t *out,
                                       hipStream_t st);
+
+// The W4A4 variant (gemm_mxfp4.hip): MXFP4 operands, E8M0 scale per 32 along K.
+struct MxGemmLaunch {
+    moe_gemm_kind kind;
+    const uint8_t *a;            // activation codes [a_rows][K/2]
+    const uint8_t *as;           // activation scales [a_rows][K/32]
+    const int32_t *a_row_index;  // NULL, or row r reads activation row a_row_index[r] / top_k
+    long long a_rows;
+    int top_k;
+    const int32_t *offsets;      // [E+1] on the device
+    int num_experts;
+    const uint8_t *wq;           // [E][N][K/2]
+    const uint8_t *ws;           // [E][N][K/32]
+    void *c;
+    const int32_t *c_row_index;  // NULL, or result row r is stored at row c_row_index[r]
+    bool c_f32;
+    int K, N;
+    int max_rows, expected_rows;
+};
+hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st);
+// rows_dev (nullable): the device-side row count to quantize (at most rows)
+hipError_t launch_mx_quantize(long long rows, int K, const uint16_t *x, uint8_t *codes, uint8_t *scales,
+                              const int32_t *rows_dev, hipStream_t st);
 
 int device_cu_count();
 

@@ -11,7 +11,8 @@
 // With at most 16 tokens every expert holds at most 16 routed rows, one
 // MFMA subtile, so no permutation is needed: a workgroup that knows the
 // routing can list an expert's rows itself.
-//  * decode_gate_up_kernel: every workgroup routes all T tokens itself (the
+//  * gate/up (decode_gate_up_kernel, or the streaming kernel with routing
+//    inside): every workgroup routes all T tokens itself (the
 //    logits are a few KiB), so routing costs no launch and no memory round
 //    trip of its own. The "leader" of an expert is its first slot in slot
 //    order; items are (leader, 16-row weight tile). An item's rows are the
@@ -19,19 +20,22 @@
 //    to h in slot order (row t*k + j). Workgroup 0 also writes each slot's
 //    expert id, routing weight and presence (slot index, or -1 when the
 //    expert is not local).
-//  * decode_down_kernel (4 < T <= 16): the same items from the stored slot
+//  * down (decode_down_kernel, or the streaming kernel on the stored slot
+//    table; otherwise): the same items from the stored slot
 //    table; y in slot order, then the finalize kernel reads y[t*k + j].
-//  * decode_down_combine_kernel (T <= 4): items are (token, 16-column tile);
+//  * decode_down_combine_kernel (T <= 2, few h bytes per token): items are
+//    (token, 16-column tile);
 //    the workgroup computes the tile for each of the token's present slots
 //    and combines them in slot order (multiply, then FMA), so the finalize
 //    needs no launch of its own. An expert used by several of the tokens is
 //    then streamed once per token (at 4 tokens of top-8 over 128 experts,
 //    about 12% more down-projection bytes than once per expert).
-// Every tile is computed with the split-K body of gemm_core.hpp and the same
-// wave count per K-group count as the standalone grouped GEMM's split-K
-// kernel (which takes 16 tokens and fewer), and the combine repeats the
-// finalize kernel's operations, so the path is bit-identical to the
-// standalone entry points composed.
+// Every tile repeats the arithmetic of the kernel family the standalone
+// grouped GEMM picks for the same shape: the split-K body of gemm_core.hpp
+// with the same wave split (the kernels here), or the streaming kernel itself
+// with the slot table as its item source (gemm_w4a16.hip); the combine
+// repeats the finalize kernel's operations. The path is therefore
+// bit-identical to the standalone entry points composed.
 #include "gemm_core.hpp"
 #include "route_core.hpp"
 
@@ -42,8 +46,6 @@
 namespace moe {
 
 namespace {
-
-constexpr int kDecMaxSlots = 128;       // T * k of the small-batch path
 
 struct DecodeArgs {
     int T, k, E_g, begin, E_loc;
@@ -74,47 +76,6 @@ __device__ __forceinline__ uint32_t dec_code_offset(const DecodeArgs &p, int til
     if (p.w_tiled)
         return (uint32_t)((tile >> 3) * G * 8 + (tile & 7)) * 1024u + (uint32_t)lane * 16u;
     return row * (uint32_t)(p.K >> 1) + (uint32_t)(lane >> 4) * 16u;
-}
-
-// Slot of row r of an expert whose slots are the set bits of (m0, m1): the
-// r-th set bit, or -1 past the last.
-__device__ __forceinline__ int nth_slot(uint64_t m0, uint64_t m1, int r)
-{
-    const int c0 = __popcll(m0);
-    uint64_t m = r < c0 ? m0 : m1;
-    int rr = r < c0 ? r : r - c0;
-    if (rr >= __popcll(m))
-        return -1;
-    for (int i = 0; i < rr; ++i)
-        m &= m - 1;
-    return (r < c0 ? 0 : 64) + __builtin_ctzll(m);
-}
-
-// Shared slot bookkeeping of the two expert-major kernels, after s_loc[s]
-// (local expert of slot s, or -1) is in LDS: s_first[e] = first slot of
-// expert e, then the leaders in slot order in s_lead. Block-wide.
-template <int NT>
-__device__ void build_leaders(int S, int E_loc, const int *s_loc, int *s_first, int *s_lead, int *s_nlead)
-{
-    const int tid = threadIdx.x, lane = tid & 63;
-    for (int s = tid; s < S; s += NT)
-        if (s_loc[s] >= 0)
-            atomicMin(&s_first[s_loc[s]], s);
-    __syncthreads();
-    if (tid < 64) {
-        int base = 0;
-        for (int s0 = 0; s0 < S; s0 += 64) {
-            const int s = s0 + lane;
-            const bool lead = s < S && s_loc[s] >= 0 && s_first[s_loc[s]] == s;
-            const uint64_t m = __ballot(lead);
-            if (lead)
-                s_lead[base + __popcll(m & ((1ull << lane) - 1ull))] = s;
-            base += __popcll(m);
-        }
-        if (lane == 0)
-            *s_nlead = base;
-    }
-    __syncthreads();
 }
 
 // One expert-major item: expert e (leader slot `lead`), 16-row tile `tile`.
@@ -246,16 +207,24 @@ __global__ __launch_bounds__(NW * 64) void decode_down_kernel(DecodeArgs p)
 }
 
 // Down projection and combine, token-major. Item = (token t, 16-column tile).
-// KS waves split K exactly as the split-K kernel does; SP such wave groups
-// take the token's slots j = sp, sp + SP (at most two each, so k <= 2 SP).
-// The token's h rows are staged in LDS (k * K bf16); each wave prefetches the
-// codes and scales of both its slots before computing either. Partial sums of
-// result row 0 go to LDS; wave 0 reduces them in wave order, rounds y to
-// bf16 and combines the present slots in slot order.
-constexpr int kCombineMaxHBytes = 64 * 1024;            // k * K * 2 bytes of staged h rows
-constexpr int kCombineMaxGroups = 4;                    // groups per wave (G / KS)
+// The tile of each of the token's present slots is computed with the
+// arithmetic of the standalone down GEMM's kernel family: KS waves split K
+// as the split-K kernel does (KS = 1: one wave sums every group in order,
+// which is also the streaming kernel's per-element sum). SP wave groups take
+// slots j = sp + u SP (u < SPW), so k <= SP * SPW. The token's h rows are
+// staged in LDS (k * K bf16); each wave prefetches the codes and scales of
+// its slots (at most GMAX groups each) before computing any. Partial sums of
+// result row 0 go to LDS; wave 0 reduces them in wave order, rounds y to bf16
+// and combines the present slots in slot order, as the finalize kernel does.
+// The combine kernel re-stages the token's h rows for every 16-column tile,
+// so it pays only while those rows are few: measured on MI355X it matches
+// the down GEMM + finalize at 1-2 Qwen3-30B-A3B tokens (12 KiB of rows) and
+// loses from 4 tokens, and on the EP shard (32 KiB of rows) already at 1.
+constexpr int kCombineMaxHBytes = 64 * 1024;            // k * K * 2 bytes of staged h rows (LDS)
+constexpr int kCombineAutoHBytes = 16 * 1024;           // the automatic choice's limits
+constexpr int kCombineAutoTokens = 2;
 
-template <int KS, int SP>
+template <int KS, int SP, int SPW, int GMAX>
 __global__ __launch_bounds__(KS * SP * 64) void decode_down_combine_kernel(DecodeArgs p)
 {
     constexpr int NW = KS * SP;
@@ -269,6 +238,7 @@ __global__ __launch_bounds__(KS * SP * 64) void decode_down_combine_kernel(Decod
     splitk_groups(ks, G, KS, g0, g1);
     const int ntiles = p.N >> 4;
     const uint32_t wbytes = (uint32_t)p.N * (uint32_t)(K >> 1);
+    const uint32_t gstride = p.w_tiled ? 8192u : 64u;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
     const int chunks = k * K / 8;                         // 16-byte pieces of the token's h rows
     for (int item = blockIdx.x; item < p.T * ntiles; item += gridDim.x) {
@@ -287,53 +257,53 @@ __global__ __launch_bounds__(KS * SP * 64) void decode_down_combine_kernel(Decod
             *reinterpret_cast<u32x4 *>(s_h + (size_t)c * 8) = bload16(ra, vo, 0);
         }
         // this wave's slots: codes and scales of groups g0..g1 (absent: zeros, no traffic)
-        u32x4 wv[2][kCombineMaxGroups];
-        uint32_t sc[2][kCombineMaxGroups];
-        int jj[2];
-        bool present[2];
+        u32x4 wv[SPW][GMAX];
+        uint32_t sc[SPW][GMAX];
+        int jj[SPW];
+        bool present[SPW];
         const uint32_t row = (uint32_t)(tile * 16 + n16);
         const uint32_t voff_w = p.w_tiled ? (uint32_t)((tile >> 3) * G * 8 + (tile & 7)) * 1024u + (uint32_t)lane * 16u
                                           : row * (uint32_t)(K >> 1) + (uint32_t)(lane >> 4) * 16u;
         const uint32_t voff_s = row * (uint32_t)G * 2;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < SPW; ++u) {
             const int j = sp + u * SP;
             jj[u] = j;
             const int pj = __shfl(pres_l, min(j, k - 1), 64);
             present[u] = j < k && pj >= 0;
-            const int e = present[u] ? __shfl(id_l, j, 64) - p.begin : 0;
+            const int e = present[u] ? __shfl(id_l, min(j, k - 1), 64) - p.begin : 0;
             const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (size_t)uniform(e) * wbytes, present[u] ? wbytes : 0u);
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc(p.s + (size_t)uniform(e) * p.N * G, present[u] ? (uint32_t)p.N * G * 2 : 0u);
 #pragma unroll
-            for (int q = 0; q < kCombineMaxGroups; ++q) {
+            for (int q = 0; q < GMAX; ++q) {
                 const int g = g0 + q;
                 const uint32_t oor = g < g1 ? 0u : kOutOfRange;
-                wv[u][q] = bload16_codes<true>(rw, voff_w | oor, (uint32_t)(g < g1 ? g : 0) * (p.w_tiled ? 8192u : 64u));
+                wv[u][q] = bload16_codes<true>(rw, voff_w | oor, (uint32_t)(g < g1 ? g : 0) * gstride);
                 sc[u][q] = bload_scale(rs, voff_s | oor, (uint32_t)(g < g1 ? g : 0) * 2u);
             }
         }
         __syncthreads();                                  // h rows staged
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < SPW; ++u) {
             if (!uniform(present[u]))
                 continue;
             floatx4 tot = {0.f, 0.f, 0.f, 0.f};
             const uint16_t *hrow = s_h + (size_t)jj[u] * K;
 #pragma unroll
-            for (int q = 0; q < kCombineMaxGroups; ++q) {
+            for (int q = 0; q < GMAX; ++q) {
                 const int g = g0 + q;
-                if (g >= g1)
-                    break;
-                u32x4 a[4];
+                if (g < g1) {
+                    u32x4 a[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(hrow + g * kGroup + kq * 32 + i * 8);
-                    const u32x4 z = {0u, 0u, 0u, 0u};
-                    const u32x4 va = n16 == 0 ? v : z;        // row 0 only: the token's h row
-                    a[i] = p.w_tiled ? va : permute_act(va);
+                    for (int i = 0; i < 4; ++i) {
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(hrow + g * kGroup + kq * 32 + i * 8);
+                        const u32x4 z = {0u, 0u, 0u, 0u};
+                        const u32x4 va = n16 == 0 ? v : z;    // row 0 only: the token's h row
+                        a[i] = p.w_tiled ? va : permute_act(va);
+                    }
+                    splitk_group(a, wv[u][q], sc[u][q], tot);
                 }
-                splitk_group(a, wv[u][q], sc[u][q], tot);
             }
             if (kq == 0)
                 s_part[jj[u]][ks][n16] = tot.x;
@@ -390,29 +360,76 @@ long long resident_grid(const void *kernel, int threads, size_t lds, long long i
 
 }  // namespace
 
+// Kernel family of the layer's standalone gate/up and down GEMMs at this
+// shape: the small-batch path repeats that family's arithmetic (split-K: the
+// split-K body with the same wave split; streaming: the streaming kernel with
+// the slot-table item source), so the layer equals the GEMMs composed.
+static int gemm_family(const moe_shape &sh, moe_gemm_kind kind)
+{
+    return choose_launch(layer_gemm_args(sh, kind)).mode;
+}
+
+// The combine kernel's shape for this layer: waves splitting K (the down
+// GEMM's split-K wave count, 1 for the streaming family), slot groups, slots
+// per wave, and the most groups a wave holds.
+struct CombineShape {
+    int KS, SP, SPW, GMAX;
+};
+
+static CombineShape combine_shape(const moe_shape &sh)
+{
+    const int G = sh.inter / kGroup;
+    CombineShape c{};
+    c.KS = gemm_family(sh, MOE_GEMM_W2) == 0 ? splitk_waves(G) : 1;
+    c.SPW = c.KS == 1 ? 1 : 2;
+    c.GMAX = c.KS == 1 ? 16 : 4;
+    const int need = (sh.top_k + c.SPW - 1) / c.SPW;
+    c.SP = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+    return c;
+}
+
 bool decode_path_fits(const moe_shape &sh, int nsh)
 {
     const moe_launch_override ov = launch_override();
     const int max_t = ov.decode_max_tokens >= 0 ? ov.decode_max_tokens : 16;
-    return nsh == 0 && sh.num_tokens <= max_t && sh.num_tokens * sh.top_k <= kDecMaxSlots &&
-           sh.num_experts <= 256;
+    if (!(nsh == 0 && sh.num_tokens <= max_t && sh.num_tokens * sh.top_k <= kDecMaxSlots && sh.num_experts <= 256))
+        return false;
+    const GemmLaunch g1 = layer_gemm_args(sh, MOE_GEMM_W13_SWIGLU), g2 = layer_gemm_args(sh, MOE_GEMM_W2);
+    const int f1 = choose_launch(g1).mode, f2 = choose_launch(g2).mode;
+    if (f1 > 1 || f2 > 1)
+        return false;                                     // a tile-kernel shape: the general path
+    if (f1 == 1 && !decode_stream_supported(g1))
+        return false;
+    return decode_combine_fits(sh) || f2 == 0 || decode_stream_supported(g2);
 }
 
 bool decode_combine_fits(const moe_shape &sh)
 {
     const moe_launch_override ov = launch_override();
-    const int max_t = ov.decode_combine_max_tokens >= 0 ? ov.decode_combine_max_tokens : 4;
-    const int G = sh.inter / kGroup, KS = splitk_waves(G);
-    const int SP = (sh.top_k + 1) / 2;
-    const int sp2 = SP <= 1 ? 1 : SP <= 2 ? 2 : SP <= 4 ? 4 : 8;
-    return sh.num_tokens <= max_t && (G + KS - 1) / KS <= kCombineMaxGroups && KS * sp2 <= 16 &&
-           (size_t)sh.top_k * sh.inter * 2 <= (size_t)kCombineMaxHBytes;
+    const bool forced = ov.decode_combine_max_tokens >= 0;
+    const int max_t = forced ? ov.decode_combine_max_tokens : kCombineAutoTokens;
+    const size_t max_h = forced ? kCombineMaxHBytes : kCombineAutoHBytes;
+    const int G = sh.inter / kGroup;
+    const CombineShape c = combine_shape(sh);
+    return sh.num_tokens <= max_t && gemm_family(sh, MOE_GEMM_W2) <= 1 && (G + c.KS - 1) / c.KS <= c.GMAX &&
+           c.KS * c.SP <= 16 && (size_t)sh.top_k * sh.inter * 2 <= max_h;
 }
 
 hipError_t launch_decode_gate_up(const moe_shape &sh, const float *logits, const uint16_t *x, const uint8_t *w13,
                                  const uint16_t *s13, int32_t *ids, float *w, int32_t *pres, uint16_t *h,
                                  hipStream_t st)
 {
+    GemmLaunch g = layer_gemm_args(sh, MOE_GEMM_W13_SWIGLU);
+    if (choose_launch(g).mode == 1) {
+        g.a = x;
+        g.a_bytes = (size_t)sh.num_tokens * sh.hidden * 2;
+        g.wq = w13;
+        g.s = s13;
+        g.c = h;
+        g.c_f32 = false;
+        const DecodeSource d{1, logits, sh.num_tokens, sh.num_experts, sh.expert_begin, ids, w, pres};
+        return launch_decode_stream(g, d, st);
+    }
     DecodeArgs p{};
     p.T = sh.num_tokens;
     p.k = sh.top_k;
@@ -481,6 +498,18 @@ static DecodeArgs down_args(const moe_shape &sh, const int32_t *ids, const float
 hipError_t launch_decode_down(const moe_shape &sh, const int32_t *ids, const int32_t *pres, const uint16_t *h,
                               const uint8_t *w2, const uint16_t *s2, uint16_t *y, hipStream_t st)
 {
+    GemmLaunch g = layer_gemm_args(sh, MOE_GEMM_W2);
+    if (choose_launch(g).mode == 1) {
+        g.a = h;
+        g.a_bytes = (size_t)sh.num_tokens * sh.top_k * sh.inter * 2;
+        g.wq = w2;
+        g.s = s2;
+        g.c = y;
+        g.c_f32 = false;
+        const DecodeSource d{2, nullptr, sh.num_tokens, sh.num_experts, sh.expert_begin,
+                             const_cast<int32_t *>(ids), nullptr, const_cast<int32_t *>(pres)};
+        return launch_decode_stream(g, d, st);
+    }
     const DecodeArgs p = down_args(sh, ids, nullptr, pres, h, w2, s2, y);
     const long long items = (long long)sh.num_tokens * sh.top_k * (p.N / 16);
     auto go = [&](auto kernel, int nw) {
@@ -501,22 +530,24 @@ hipError_t launch_decode_down_combine(const moe_shape &sh, const int32_t *ids, c
                                       hipStream_t st)
 {
     const DecodeArgs p = down_args(sh, ids, w, pres, h, w2, s2, out);
-    const int KS = splitk_waves(p.K / kGroup);
-    const int SP0 = (sh.top_k + 1) / 2;
-    const int SP = SP0 <= 1 ? 1 : SP0 <= 2 ? 2 : SP0 <= 4 ? 4 : 8;
+    const CombineShape c = combine_shape(sh);
     const size_t lds = (size_t)sh.top_k * p.K * 2;
     const long long items = (long long)sh.num_tokens * (p.N / 16);
     auto go = [&](auto kernel) {
-        const int threads = KS * SP * 64;
+        const int threads = c.KS * c.SP * 64;
         const long long grid = resident_grid(reinterpret_cast<const void *>(kernel), threads, lds, items);
         hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), lds, st, p);
     };
-#define MOE_DEC_DC(KS_, SP_) \
-    if (KS == KS_ && SP == SP_) { go(decode_down_combine_kernel<KS_, SP_>); return hipGetLastError(); }
-    MOE_DEC_DC(1, 1) MOE_DEC_DC(1, 2) MOE_DEC_DC(1, 4) MOE_DEC_DC(1, 8)
-    MOE_DEC_DC(2, 1) MOE_DEC_DC(2, 2) MOE_DEC_DC(2, 4) MOE_DEC_DC(2, 8)
-    MOE_DEC_DC(4, 1) MOE_DEC_DC(4, 2) MOE_DEC_DC(4, 4)
-    MOE_DEC_DC(8, 1) MOE_DEC_DC(8, 2)
+#define MOE_DEC_DC(KS_, SP_, SPW_, GM_)                                                 \
+    if (c.KS == KS_ && c.SP == SP_ && c.SPW == SPW_ && c.GMAX == GM_) {                  \
+        go(decode_down_combine_kernel<KS_, SP_, SPW_, GM_>);                           \
+        return hipGetLastError();                                                      \
+    }
+    MOE_DEC_DC(1, 1, 1, 16) MOE_DEC_DC(1, 2, 1, 16) MOE_DEC_DC(1, 4, 1, 16) MOE_DEC_DC(1, 8, 1, 16)
+    MOE_DEC_DC(1, 16, 1, 16)
+    MOE_DEC_DC(2, 1, 2, 4) MOE_DEC_DC(2, 2, 2, 4) MOE_DEC_DC(2, 4, 2, 4) MOE_DEC_DC(2, 8, 2, 4)
+    MOE_DEC_DC(4, 1, 2, 4) MOE_DEC_DC(4, 2, 2, 4) MOE_DEC_DC(4, 4, 2, 4)
+    MOE_DEC_DC(8, 1, 2, 4) MOE_DEC_DC(8, 2, 2, 4)
 #undef MOE_DEC_DC
     return hipErrorInvalidValue;                          // decode_combine_fits() rules this out
 }

@@ -191,6 +191,118 @@ __device__ __forceinline__ floatx4 splitk_reduce(floatx4 tot, floatx4 (*s_red)[6
     return sum;
 }
 
+// Row offset of expert e: offsets[e], or for a dense GEMM (offsets NULL,
+// one expert) 0 and dense_rows.
+__device__ __forceinline__ int expert_offset(const int32_t *offsets, int dense_rows, int e)
+{
+    return offsets ? offsets[e] : (e == 0 ? 0 : dense_rows);
+}
+
+// Chunk prefix over experts: s_prefix[e] = chunks of experts < e (chunk =
+// up to CS rows of one expert), s_prefix[E] = total. Block-wide.
+// When s_off is given it receives offsets[0..E] as well.
+template <int NT>
+__device__ void build_chunk_prefix(const int32_t *offsets, int dense_rows, int E, int CS, int *s_prefix,
+                                   int *s_wtot, int *s_off = nullptr)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int carry = 0;
+    for (int base = 0; base < E; base += NT) {
+        const int e = base + tid;
+        int v = 0;
+        if (e < E) {
+            const int o0 = expert_offset(offsets, dense_rows, e), o1 = expert_offset(offsets, dense_rows, e + 1);
+            if (s_off) {
+                s_off[e] = o0;
+                if (e == E - 1)
+                    s_off[E] = o1;
+            }
+            const int cnt = o1 - o0;
+            v = (cnt + CS - 1) / CS;
+        }
+        int wt;
+        const int ex = wave_exclusive_scan(v, wt);
+        if (lane == 0)
+            s_wtot[wave] = wt;
+        __syncthreads();
+        int wbase = 0, all = 0;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) {
+            wbase += (w < wave) ? s_wtot[w] : 0;
+            all += s_wtot[w];
+        }
+        if (e < E)
+            s_prefix[e] = carry + wbase + ex;
+        carry += all;
+        __syncthreads();
+    }
+    if (tid == 0)
+        s_prefix[E] = carry;
+    __syncthreads();
+}
+
+// Expert owning chunk `chunk`: the last e with s_prefix[e] <= chunk.
+__device__ __forceinline__ int chunk_expert(const int *s_prefix, int E, int chunk)
+{
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_prefix[mid] <= chunk)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// ---- the layer's small-batch path: slot tables ------------------------------
+// With at most 16 tokens every expert holds at most 16 routed rows, so a
+// workgroup that knows each slot's local expert (s_loc[s], -1 when not local;
+// slot s = t * k + j) can list an expert's rows itself: the "leader" of an
+// expert is its first slot; its rows are its slots in slot order.
+constexpr int kDecMaxSlots = 128;                   // T * k of the small-batch path
+
+// Slot of row r of an expert whose slots are the set bits of (m0, m1): the
+// r-th set bit, or -1 past the last.
+__device__ __forceinline__ int nth_slot(uint64_t m0, uint64_t m1, int r)
+{
+    const int c0 = __popcll(m0);
+    uint64_t m = r < c0 ? m0 : m1;
+    int rr = r < c0 ? r : r - c0;
+    if (rr >= __popcll(m))
+        return -1;
+    for (int i = 0; i < rr; ++i)
+        m &= m - 1;
+    return (r < c0 ? 0 : 64) + __builtin_ctzll(m);
+}
+
+// Shared slot bookkeeping of the two expert-major kernels, after s_loc[s]
+// (local expert of slot s, or -1) is in LDS: s_first[e] = first slot of
+// expert e, then the leaders in slot order in s_lead. Block-wide.
+template <int NT>
+__device__ void build_leaders(int S, int E_loc, const int *s_loc, int *s_first, int *s_lead, int *s_nlead)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    for (int s = tid; s < S; s += NT)
+        if (s_loc[s] >= 0)
+            atomicMin(&s_first[s_loc[s]], s);
+    __syncthreads();
+    if (tid < 64) {
+        int base = 0;
+        for (int s0 = 0; s0 < S; s0 += 64) {
+            const int s = s0 + lane;
+            const bool lead = s < S && s_loc[s] >= 0 && s_first[s_loc[s]] == s;
+            const uint64_t m = __ballot(lead);
+            if (lead)
+                s_lead[base + __popcll(m & ((1ull << lane) - 1ull))] = s;
+            base += __popcll(m);
+        }
+        if (lane == 0)
+            *s_nlead = base;
+    }
+    __syncthreads();
+}
+
 // K-group count -> waves of a split-K tile (at least 2 groups per wave from
 // 4 groups on; 8 waves once there are 24 groups or more).
 constexpr int splitk_waves(int G) { return G >= 24 ? 8 : G >= 8 ? 4 : G >= 4 ? 2 : 1; }

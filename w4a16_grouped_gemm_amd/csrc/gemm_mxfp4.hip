@@ -1,0 +1,386 @@
+// gemm_mxfp4.hip -- the W4A4 variant: MXFP4 activations and weights on the
+// gfx950 block-scaled matrix unit.
+//
+// Pages: FlashInfer PR #7196 analysis, section 2 ("Arithmetic Alignment":
+// W4A4 finalizers beside the W4A16 ones) and its performance section (a
+// W4A4 kernel beside the W4A16 one); GC-MoE abstract (FP4 block-scaled
+// grouped GEMMs, 4-bit operands decoded in the matrix unit, activations
+// requantized between the GEMMs). The pages fix no FP4 encoding; the format
+// is the OCP MX one, MXFP4: E2M1 elements (magnitudes 0, 0.5, 1, 1.5, 2, 3,
+// 4, 6) with one E8M0 scale 2^(s-127) per 32 elements along K.
+//
+// gfx950 design:
+//  * v_mfma_scale_f32_16x16x128_f8f6f4 with both operands in FP4: lane l
+//    holds 32 consecutive K elements (16 bytes, element k of the lane in
+//    nibble k % 8 of dword k / 8) of row / column l % 16 of K block l / 16,
+//    and one scale byte for them. That is the storage layout itself (two
+//    elements per byte, even k in the low nibble, rows K-contiguous) and the
+//    MX block of 32, so codes and scales go from memory to the matrix unit
+//    unchanged: one MFMA per 16x16 tile and 128 K, no unpack, no scale FMA.
+//  * Operand A = 16 routed rows of one expert (the activations), operand B =
+//    16 weight rows; the result lane holds 4 rows x 1 weight row, as in the
+//    W4A16 kernels, so the SwiGLU and row-index epilogue is the same.
+//  * Everything streams HBM -> VGPR (codes 16 bytes per lane and group, the
+//    group's four scale bytes as one dword); activations are as small as the
+//    weights, so there is no LDS staging and no barrier in the K loop.
+//  * Work items (expert chunk of up to 16 NSUB rows, block of 4 waves x TPW
+//    tiles) come from the chunk prefix over `offsets`, as in the W4A16
+//    streaming kernel.
+//  * mx_quantize_kernel: one thread per 32-element block: the block maximum,
+//    the shared exponent floor(log2 amax) - 2 (clamped to the E8M0 range),
+//    and each element / 2^e rounded to the nearest E2M1 value with ties to
+//    the even code and saturation at 6, by comparisons against the midpoints
+//    (exact in binary32: the division by a power of two is exact).
+#include "gemm_core.hpp"
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+namespace moe {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+struct MxArgs {
+    const uint8_t *a;            // activation codes [rows][K/2]
+    const uint8_t *as;           // activation scales [rows][K/32]
+    const int32_t *a_row_index;  // row r reads a row a_row_index[r] / top_k (NULL: row r)
+    uint32_t a_bytes, as_bytes;
+    const int32_t *offsets;      // [E+1]
+    const uint8_t *wq;           // weight codes [E][N][K/2]
+    const uint8_t *ws;           // weight scales [E][N][K/32]
+    void *c;
+    const int32_t *c_row_index;  // output row of result row r (NULL: r)
+    uint32_t c_row_bytes;
+    int top_k, num_experts, K, N, ldc, half, c_f32;
+};
+
+__device__ __forceinline__ floatx4 mfma_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32_t sb, floatx4 c)
+{
+    const v8i va = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    const v8i vb = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, vb, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+template <int KIND>
+__device__ __forceinline__ uint32_t mx_tile_row(const MxArgs &p, int tile, int n16)
+{
+    if (KIND == MOE_GEMM_W13_SWIGLU)
+        return (uint32_t)(n16 < 8 ? tile * 8 + n16 : p.half + tile * 8 + (n16 - 8));
+    return (uint32_t)(tile * 16 + n16);
+}
+
+template <int KIND, int TPW, int NSUB, int RING>
+__global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p)
+{
+    constexpr int CS = 16 * NSUB;
+    constexpr int BT = 4 * TPW;
+    extern __shared__ __align__(16) unsigned char s_dyn[];
+    const int E = p.num_experts;
+    int *s_prefix = reinterpret_cast<int *>(s_dyn);
+    int *s_wtot = s_prefix + (E + 1);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n16 = lane & 15, kq = lane >> 4;
+    build_chunk_prefix<256>(p.offsets, 0, E, CS, s_prefix, s_wtot);
+
+    const int ntiles = p.N >> 4;
+    const int nblocks = ntiles / BT;
+    const int total_items = s_prefix[E] * nblocks;
+    const int G = p.K / kGroup;
+    const uint32_t row_bytes = (uint32_t)(p.K >> 1), srow_bytes = (uint32_t)(p.K >> 5);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+    const __amdgpu_buffer_rsrc_t ras = make_rsrc(p.as, p.as_bytes);
+    const uint32_t sh = 8u * (uint32_t)kq;             // this lane's scale byte within a group's dword
+    const int nx = (int)gridDim.x >= kXcds ? kXcds : 1;  // XCD-aware item ranges, as in the W4A16 kernels
+    const int xcd = blockIdx.x % nx;
+    const int i_end = (int)((long long)total_items * (xcd + 1) / nx);
+    for (int item = (int)((long long)total_items * xcd / nx) + blockIdx.x / nx; item < i_end;
+         item += gridDim.x / nx) {
+        const int chunk = item / nblocks;
+        const int block = item - chunk * nblocks;
+        const int e = uniform(chunk_expert(s_prefix, E, chunk));
+        const int row0 = uniform(p.offsets[e] + (chunk - s_prefix[e]) * CS);
+        const int nvalid = uniform(min(CS, p.offsets[e + 1] - row0));
+        const int nsub = (nvalid + 15) >> 4;
+        const int tile0 = block * BT + wave * TPW;
+        const uint32_t wbytes = (uint32_t)p.N * row_bytes, wsbytes = (uint32_t)p.N * srow_bytes;
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (size_t)e * wbytes, wbytes);
+        const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.ws + (size_t)e * wsbytes, wsbytes);
+        uint32_t vw[TPW], vws[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const uint32_t row = mx_tile_row<KIND>(p, tile0 + t, n16);
+            vw[t] = row * row_bytes + (uint32_t)kq * 16u;
+            vws[t] = row * srow_bytes;
+        }
+        uint32_t va[NSUB], vas[NSUB];
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb) {
+            const int m = sb * 16 + n16;
+            const int r = row0 + min(m, nvalid - 1);
+            const uint32_t src = p.a_row_index ? (uint32_t)(p.a_row_index[r] / p.top_k) : (uint32_t)r;
+            const bool ok = m < nvalid;
+            va[sb] = ok ? src * row_bytes + (uint32_t)kq * 16u : kOutOfRange;
+            vas[sb] = ok ? src * srow_bytes : kOutOfRange;
+        }
+        floatx4 acc[TPW][NSUB];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb)
+                acc[t][sb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        u32x4 wv[RING][TPW], av[RING][NSUB];
+        uint32_t wsv[RING][TPW], asv[RING][NSUB];
+        // group g -> ring slot g % RING; groups past G read out of range (zeros)
+        auto load = [&](int g, int b) {
+            const uint32_t oor = g < G ? 0u : kOutOfRange;
+            const uint32_t gc = (uint32_t)(g < G ? g : 0);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                wv[b][t] = bload16_codes<true>(rw, vw[t] | oor, gc * 64u);
+                wsv[b][t] = __builtin_amdgcn_raw_buffer_load_b32(rws, vws[t] | oor, gc * 4u, 0);
+            }
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb) {
+                av[b][sb] = bload16(ra, va[sb] | oor, gc * 64u);
+                asv[b][sb] = __builtin_amdgcn_raw_buffer_load_b32(ras, vas[sb] | oor, gc * 4u, 0);
+            }
+        };
+#pragma unroll
+        for (int r = 0; r < RING - 1; ++r)
+            load(r, r);
+        for (int g0 = 0; g0 < G; g0 += RING) {
+#pragma unroll
+            for (int j = 0; j < RING; ++j) {
+                const int g = g0 + j;
+                load(g + RING - 1, (j + RING - 1) % RING);
+                if (g < G) {
+#pragma unroll
+                    for (int sb = 0; sb < NSUB; ++sb) {
+                        if (sb < nsub) {
+#pragma unroll
+                            for (int t = 0; t < TPW; ++t)
+                                acc[t][sb] = mfma_fp4(av[j][sb], asv[j][sb] >> sh, wv[j][t], wsv[j][t] >> sh,
+                                                      acc[t][sb]);
+                        }
+                    }
+                }
+            }
+        }
+        // epilogue: result lane (n16, kq) holds rows 4kq + i of weight row n16
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c_row_index, p.c_row_bytes);
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb) {
+            if (sb >= nsub)
+                break;
+            int orow[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = sb * 16 + kq * 4 + i;
+                const int r = row0 + min(m, nvalid - 1);
+                orow[i] = p.c_row_index ? (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)r * 4u, 0, 0) : r;
+            }
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const floatx4 v = acc[t][sb];
+                const float rr[4] = {v.x, v.y, v.z, v.w};
+                if (KIND == MOE_GEMM_W13_SWIGLU) {
+                    float u[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        u[i] = __shfl_xor(rr[i], 8, 64);
+                    if (n16 < 8) {
+                        uint16_t *c = static_cast<uint16_t *>(p.c);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (sb * 16 + kq * 4 + i < nvalid)
+                                c[(size_t)orow[i] * p.ldc + (tile0 + t) * 8 + n16] =
+                                    (uint16_t)f32_to_bf16_rne(silu(rr[i]) * u[i]);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (sb * 16 + kq * 4 + i < nvalid) {
+                            const size_t off = (size_t)orow[i] * p.ldc + (tile0 + t) * 16 + n16;
+                            if (p.c_f32)
+                                static_cast<float *>(p.c)[off] = rr[i];
+                            else
+                                static_cast<uint16_t *>(p.c)[off] = (uint16_t)f32_to_bf16_rne(rr[i]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// E2M1 code of |p| (p already divided by the block scale): nearest of 0, 0.5,
+// 1, 1.5, 2, 3, 4, 6; a midpoint goes to the even code; past 6 stays at 6.
+__device__ __forceinline__ uint32_t e2m1_code(float m)
+{
+    return m <= 0.25f ? 0u : m < 0.75f ? 1u : m <= 1.25f ? 2u : m < 1.75f ? 3u
+         : m <= 2.5f ? 4u : m < 3.5f ? 5u : m <= 5.0f ? 6u : 7u;
+}
+
+// rows x (K/32) blocks; `rows_dev` (nullable) bounds the rows on the device.
+__global__ __launch_bounds__(256) void mx_quantize_kernel(long long rows, int K, const uint16_t *__restrict__ x,
+                                                          uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                          const int32_t *__restrict__ rows_dev)
+{
+    const int nb = K >> 5;
+    const long long R = rows_dev ? (long long)rows_dev[0] : rows;
+    const long long total = (R < rows ? R : rows) * nb;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (long long)gridDim.x * blockDim.x) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(x + i * 32);
+        uint32_t w[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 d = src[q];
+            w[4 * q] = d.x;
+            w[4 * q + 1] = d.y;
+            w[4 * q + 2] = d.z;
+            w[4 * q + 3] = d.w;
+        }
+        // the block maximum on the magnitude bits (bf16 orders like its magnitude)
+        uint32_t amax = 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const uint32_t lo = w[q] & 0x7FFFu, hi = (w[q] >> 16) & 0x7FFFu;
+            amax = lo > amax ? lo : amax;
+            amax = hi > amax ? hi : amax;
+        }
+        int ex = -127;
+        if (amax != 0) {
+            const int bexp = (int)(amax >> 7);              // biased exponent of the bf16 maximum
+            const int fl = bexp > 0 ? bexp - 127 : -133 + (31 - __builtin_clz(amax & 0x7Fu));   // floor(log2)
+            ex = fl - 2;
+            ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+        }
+        scales[i] = (uint8_t)(ex + 127);
+        // 2^-ex as a binary32 power of two: a finite bf16 maximum is below
+        // 2^128, so ex <= 125 and 2^-ex is a normal number (exponent field
+        // 127 - ex in [2, 254]); |v| * 2^-ex is then exact or, far below the
+        // first midpoint 0.25, rounds harmlessly
+        const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);
+        uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+#pragma unroll
+            for (int hlf = 0; hlf < 2; ++hlf) {
+                const uint32_t b = hlf ? (w[q] >> 16) : (w[q] & 0xFFFFu);
+                const float v = __uint_as_float(b << 16);
+                const uint32_t code = e2m1_code(fabsf(v) * inv) | ((b >> 12) & 8u);
+                const int k = 2 * q + hlf;                 // element of the block
+                out[k >> 3] |= code << (4 * (k & 7));
+            }
+        }
+        *reinterpret_cast<u32x4 *>(codes + i * 16) = u32x4{out[0], out[1], out[2], out[3]};
+    }
+}
+
+template <typename F>
+int mx_resident_per_cu(F kernel, size_t lds)
+{
+    static std::mutex mu;
+    static std::map<std::pair<const void *, size_t>, int> cache;
+    const auto key = std::make_pair(reinterpret_cast<const void *>(kernel), lds);
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end())
+        return it->second;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, lds) != hipSuccess || n < 1)
+        n = 1;
+    cache[key] = n;
+    return n;
+}
+
+template <int KIND, int TPW, int NSUB, int RING>
+hipError_t mx_launch(const MxArgs &a, int max_rows, hipStream_t st)
+{
+    auto kernel = mx_gemm_kernel<KIND, TPW, NSUB, RING>;
+    const size_t lds = sizeof(int) * (a.num_experts + 1 + 4);
+    const int per_cu = mx_resident_per_cu(kernel, lds);
+    const int nblocks = (a.N >> 4) / (4 * TPW);
+    const long long chunks = (long long)min(a.num_experts, max_rows) + max_rows / (16 * NSUB);
+    long long grid = chunks * nblocks;
+    const long long cap = (long long)device_cu_count() * per_cu;
+    grid = grid < cap ? grid : cap;
+    grid = grid < 1 ? 1 : grid;
+    if (grid >= kXcds)
+        grid -= grid % kXcds;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), lds, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mx_quantize(long long rows, int K, const uint16_t *x, uint8_t *codes, uint8_t *scales,
+                              const int32_t *rows_dev, hipStream_t st)
+{
+    const long long blocks_total = rows * (K / 32);
+    long long grid = (blocks_total + 255) / 256;
+    const long long cap = (long long)device_cu_count() * 8;
+    grid = grid < cap ? grid : cap;
+    grid = grid < 1 ? 1 : grid;
+    hipLaunchKernelGGL(mx_quantize_kernel, dim3((unsigned)grid), dim3(256), 0, st, rows, K, x, codes, scales, rows_dev);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st)
+{
+    MxArgs a{};
+    a.a = g.a;
+    a.as = g.as;
+    a.a_row_index = g.a_row_index;
+    a.a_bytes = (uint32_t)((size_t)g.a_rows * (g.K / 2));
+    a.as_bytes = (uint32_t)((size_t)g.a_rows * (g.K / 32));
+    a.offsets = g.offsets;
+    a.wq = g.wq;
+    a.ws = g.ws;
+    a.c = g.c;
+    a.c_row_index = g.c_row_index;
+    a.c_row_bytes = g.c_row_index ? (uint32_t)g.max_rows * 4u : 0u;
+    a.top_k = g.top_k;
+    a.num_experts = g.num_experts;
+    a.K = g.K;
+    a.N = g.N;
+    a.half = g.N / 2;
+    a.ldc = g.kind == MOE_GEMM_W13_SWIGLU ? g.N / 2 : g.N;
+    a.c_f32 = g.c_f32 ? 1 : 0;
+    // rows per active expert under uniform routing: one subtile for decode,
+    // four (64-row chunks) once experts hold many rows; tiles per wave from
+    // how many items the grid gets
+    const double E = g.num_experts > 0 ? g.num_experts : 1;
+    const double R = g.expected_rows > 0 ? g.expected_rows : 1;
+    const double T = g.max_rows / (double)(g.top_k > 0 ? g.top_k : 1);
+    const double ps = R / (T * E);
+    const double active = E * (1.0 - pow(1.0 - (ps < 1.0 ? ps : 1.0), T));
+    const double m = R / (active > 1.0 ? active : 1.0);
+    const int ntiles = g.N / 16;
+    const int nsub = m > 40.0 ? 4 : m > 12.0 ? 2 : 1;
+    int tpw = 4;
+    const double chunks = fmax(active, R / (16.0 * nsub));
+    while (tpw > 1 && (ntiles % (4 * tpw) != 0 || chunks * ntiles / tpw <= 2.0 * device_cu_count()))
+        tpw >>= 1;
+    if (ntiles % (4 * tpw) != 0)
+        return hipErrorInvalidValue;                   // N is a multiple of 128: 4 waves x 2 tiles always divide
+    auto go = [&](auto kindc) -> hipError_t {
+        constexpr int KIND = decltype(kindc)::value;
+#define MOE_MX(TP, NS) \
+        if (tpw == TP && nsub == NS) return mx_launch<KIND, TP, NS, (NS == 4 ? 2 : 4)>(a, g.max_rows, st);
+        MOE_MX(1, 1) MOE_MX(2, 1) MOE_MX(4, 1) MOE_MX(1, 2) MOE_MX(2, 2) MOE_MX(4, 2) MOE_MX(1, 4) MOE_MX(2, 4)
+        MOE_MX(4, 4)
+#undef MOE_MX
+        return hipErrorInvalidValue;
+    };
+    if (g.kind == MOE_GEMM_W13_SWIGLU)
+        return go(std::integral_constant<int, MOE_GEMM_W13_SWIGLU>());
+    if (g.kind == MOE_GEMM_W2)
+        return go(std::integral_constant<int, MOE_GEMM_W2>());
+    return go(std::integral_constant<int, MOE_GEMM_W13_RAW>());
+}
+
+}  // namespace moe

@@ -54,6 +54,7 @@
 //    Subtiles past the chunk's valid rows are skipped (runtime N); rows past
 //    the last valid token are neither read nor written.
 #include "gemm_core.hpp"
+#include "route_core.hpp"
 
 #include <map>
 #include <type_traits>
@@ -88,7 +89,19 @@ struct GemmArgs {
     int half;       // SwiGLU: row offset of the up projection (= I)
     int c_f32;
     int w_tiled;    // codes in the tiled layout: tile t, group g at ((t/8)*G*8 + t%8)*1 KiB + g*8 KiB
+    // the layer's small-batch item sources (gemm_stream_kernel with SRC != 0):
+    // each expert's rows are its slots, listed from a slot table in LDS
+    const float *logits;  // SRC_ROUTE: router logits [T][E_g]
+    int T, E_g, begin;    // tokens, logit columns, global id of local expert 0
+    int32_t *ids;         // per slot t*k+j: global expert id (SRC_ROUTE writes, SRC_SLOTS reads)
+    float *wts;           // SRC_ROUTE writes the routing weights
+    int32_t *pres;        // per slot: the slot index if its expert is local, else -1
 };
+
+// Item sources of the streaming kernel: the chunk prefix over `offsets`
+// (the grouped GEMM), or the small-batch layer's slot table, built by
+// routing inside the kernel (gate/up) or read from the stored table (down).
+enum { SRC_OFFSETS = 0, SRC_ROUTE = 1, SRC_SLOTS = 2 };
 
 // Lane offset of a tile's codes and the byte step from one group to the next.
 __device__ __forceinline__ uint32_t code_offset(const GemmArgs &p, int tile, uint32_t row, int G, uint32_t row_bytes,
@@ -112,70 +125,6 @@ __device__ __forceinline__ const uint8_t *expert_codes(const GemmArgs &p, int e,
 __device__ __forceinline__ const uint16_t *expert_scales(const GemmArgs &p, int e, uint32_t n)
 {
     return e < p.e_routed ? p.s + (size_t)e * n : p.s_sh + (size_t)(e - p.e_routed) * n;
-}
-
-// Row offset of expert e: offsets[e], or for a dense GEMM (offsets NULL,
-// one expert) 0 and dense_rows.
-__device__ __forceinline__ int expert_offset(const int32_t *offsets, int dense_rows, int e)
-{
-    return offsets ? offsets[e] : (e == 0 ? 0 : dense_rows);
-}
-
-// Chunk prefix over experts: s_prefix[e] = chunks of experts < e (chunk =
-// up to CS rows of one expert), s_prefix[E] = total. Block-wide.
-// When s_off is given it receives offsets[0..E] as well.
-template <int NT>
-__device__ void build_chunk_prefix(const int32_t *offsets, int dense_rows, int E, int CS, int *s_prefix,
-                                   int *s_wtot, int *s_off = nullptr)
-{
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int carry = 0;
-    for (int base = 0; base < E; base += NT) {
-        const int e = base + tid;
-        int v = 0;
-        if (e < E) {
-            const int o0 = expert_offset(offsets, dense_rows, e), o1 = expert_offset(offsets, dense_rows, e + 1);
-            if (s_off) {
-                s_off[e] = o0;
-                if (e == E - 1)
-                    s_off[E] = o1;
-            }
-            const int cnt = o1 - o0;
-            v = (cnt + CS - 1) / CS;
-        }
-        int wt;
-        const int ex = wave_exclusive_scan(v, wt);
-        if (lane == 0)
-            s_wtot[wave] = wt;
-        __syncthreads();
-        int wbase = 0, all = 0;
-#pragma unroll
-        for (int w = 0; w < NT / 64; ++w) {
-            wbase += (w < wave) ? s_wtot[w] : 0;
-            all += s_wtot[w];
-        }
-        if (e < E)
-            s_prefix[e] = carry + wbase + ex;
-        carry += all;
-        __syncthreads();
-    }
-    if (tid == 0)
-        s_prefix[E] = carry;
-    __syncthreads();
-}
-
-// Expert owning chunk `chunk`: the last e with s_prefix[e] <= chunk.
-__device__ __forceinline__ int chunk_expert(const int *s_prefix, int E, int chunk)
-{
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_prefix[mid] <= chunk)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
 }
 
 // Weight row of lane n16 in 16-row tile `tile`: for SwiGLU rows 0..7 are gate
@@ -258,9 +207,10 @@ __device__ __forceinline__ int act_slot(int step, int lane)
     return lane ^ ((4 * step + (lane >> 4)) & 15);
 }
 
-template <int KIND, int TPW, int NSUB, int KSEG, int RING, bool NT>
+template <int KIND, int TPW, int NSUB, int KSEG, int RING, bool NT, int SRC = SRC_OFFSETS, int PL = 8>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
 {
+    static_assert(SRC == SRC_OFFSETS || NSUB == 1, "small-batch items hold at most 16 rows");
     static_assert((2 * KSEG) % RING == 0, "the weight ring slot of group g is g % RING, static per segment parity");
     static_assert(KSEG == 1 || KSEG % 2 == 0, "scales are loaded as dwords of two groups");
     constexpr int SD = (KSEG + 1) / 2;                 // scale dwords per tile and segment
@@ -274,17 +224,56 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
     int *s_prefix = reinterpret_cast<int *>(s_dyn + stream_act_bytes<NSUB, KSEG>());
     int *s_off = s_prefix + (E + 1);
     int *s_wtot = s_off + (E + 1);
+    // small-batch slot tables (SRC != 0), in the same region
+    int *s_loc = s_prefix;
+    int *s_lead = s_loc + kDecMaxSlots;
+    int *s_nlead = s_lead + kDecMaxSlots;
+    int *s_first = s_nlead + 4;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int n16 = lane & 15;
     const int kq = lane >> 4;
-    build_chunk_prefix<256>(p.offsets, p.dense_rows, E, CS, s_prefix, s_wtot, s_off);
-
     const int ntiles = p.N >> 4;
     const int nblocks = ntiles / BT;
-    const int total_items = s_prefix[E] * nblocks;
+    const int S_slots = p.T * p.top_k;
+    int total_items;
+    if constexpr (SRC == SRC_OFFSETS) {
+        build_chunk_prefix<256>(p.offsets, p.dense_rows, E, CS, s_prefix, s_wtot, s_off);
+        total_items = s_prefix[E] * nblocks;
+    } else {
+        for (int e = tid; e < E; e += 256)
+            s_first[e] = kDecMaxSlots;
+        if constexpr (SRC == SRC_ROUTE) {
+            // every workgroup routes all tokens: one DPP row of 16 lanes per token
+            for (int t0 = wave * 4; t0 < p.T; t0 += 16) {
+                const int t = t0 + (lane >> 4);
+                if (t < p.T) {
+                    int eg;
+                    float wt;
+                    route_token<16, PL>(p.logits + (size_t)t * p.E_g, p.E_g, p.top_k, n16, eg, wt);
+                    if (n16 < p.top_k) {
+                        const int sl = t * p.top_k + n16;
+                        const int le = eg - p.begin;
+                        const int loc = (le >= 0 && le < E) ? le : -1;
+                        s_loc[sl] = loc;
+                        if (blockIdx.x == 0) {
+                            p.ids[sl] = eg;
+                            p.wts[sl] = wt;
+                            p.pres[sl] = loc >= 0 ? sl : -1;
+                        }
+                    }
+                }
+            }
+        } else {
+            for (int sl = tid; sl < S_slots; sl += 256)
+                s_loc[sl] = p.pres[sl] >= 0 ? p.ids[sl] - p.begin : -1;
+        }
+        __syncthreads();
+        build_leaders<256>(S_slots, E, s_loc, s_first, s_lead, s_nlead);
+        total_items = s_nlead[0] * nblocks;
+    }
     const int G = p.K / kGroup;
     const int nseg = G / KSEG;                         // host guarantees KSEG | G
     const uint32_t row_bytes = (uint32_t)(p.K >> 1);
@@ -321,9 +310,19 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
          item += gridDim.x / nx) {
         const int chunk = item / nblocks;
         const int block = item - chunk * nblocks;
-        const int e = uniform(chunk_expert(s_prefix, E, chunk));
-        const int row0 = uniform(s_off[e] + (chunk - s_prefix[e]) * CS);
-        const int nvalid = uniform(min(CS, s_off[e + 1] - row0));
+        int e, row0, nvalid;
+        uint64_t m0 = 0, m1 = 0;                          // small batch: the expert's slots
+        if constexpr (SRC == SRC_OFFSETS) {
+            e = uniform(chunk_expert(s_prefix, E, chunk));
+            row0 = uniform(s_off[e] + (chunk - s_prefix[e]) * CS);
+            nvalid = uniform(min(CS, s_off[e + 1] - row0));
+        } else {
+            e = uniform(s_loc[s_lead[chunk]]);
+            m0 = __ballot(lane < S_slots && s_loc[lane] == e);
+            m1 = __ballot(64 + lane < S_slots && s_loc[64 + lane] == e);
+            row0 = 0;
+            nvalid = uniform(__popcll(m0) + __popcll(m1));
+        }
         const int nsub = (nvalid + 15) >> 4;
         const int tile0 = block * BT + wave * TPW;
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(expert_codes(p, e, (uint32_t)p.N * row_bytes), (uint32_t)p.N * row_bytes);
@@ -337,15 +336,28 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
             voff_s[t] = row * (uint32_t)G * 2;
         }
         // output row of the one result row this lane stores in the LDS
-        // epilogue, read now (no load under a branch; zeros when unused)
-        const int32_t c_row = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
-            rc, (uint32_t)(row0 + min(epi_m, nvalid - 1)) * 4u, 0, 0);
+        // epilogue, read now (no load under a branch; zeros when unused);
+        // small batch: that row's slot
+        int32_t c_row;
+        if constexpr (SRC == SRC_OFFSETS)
+            c_row = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(row0 + min(epi_m, nvalid - 1)) * 4u,
+                                                                  0, 0);
+        else
+            c_row = nth_slot(m0, m1, min(epi_m, nvalid - 1));
         uint32_t voff_x[NSUB];
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb) {
             const int m = sb * 16 + st_tok;
-            const int r = row0 + min(m, nvalid - 1);       // always a valid row: no branch around the load
-            const uint32_t src = p.a_row_index ? (uint32_t)(p.a_row_index[r] / p.top_k) : (uint32_t)r;
+            uint32_t src;
+            if constexpr (SRC == SRC_OFFSETS) {
+                const int r = row0 + min(m, nvalid - 1);   // always a valid row: no branch around the load
+                src = p.a_row_index ? (uint32_t)(p.a_row_index[r] / p.top_k) : (uint32_t)r;
+            } else {
+                // row m of the expert is its m-th slot: gate/up reads that
+                // slot's token, down reads the slot's own h row
+                const int sl = nth_slot(m0, m1, min(m, nvalid - 1));
+                src = SRC == SRC_ROUTE ? (uint32_t)(sl / p.top_k) : (uint32_t)sl;
+            }
             voff_x[sb] = (m < nvalid) ? src * (uint32_t)p.K * 2 + st_c16 * 16 : kOutOfRange;
         }
 
@@ -504,7 +516,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
                 const int m = sb * 16 + rr;
                 if (b < NBLK && sb < nsub && m < nvalid) {
                     const u32x4 d = *reinterpret_cast<const u32x4 *>(so + (b * 16 + rr) * COLS + part * 8);
-                    const int orow = !p.c_row_index ? row0 + m : (EPI_ONE_ROW ? c_row : p.c_row_index[row0 + m]);
+                    const int orow = SRC != SRC_OFFSETS ? c_row
+                                     : !p.c_row_index ? row0 + m : (EPI_ONE_ROW ? c_row : p.c_row_index[row0 + m]);
                     *reinterpret_cast<u32x4 *>(c + (size_t)orow * p.ldc + (tile0 + t) * COLS + part * 8) = d;
                 }
             }
@@ -1135,16 +1148,20 @@ int resident_per_cu(F kernel, size_t lds = 0)
     return n;
 }
 
-template <int KIND, int TPW, int NSUB, int KSEG, int RING, bool NT>
+template <int KIND, int TPW, int NSUB, int KSEG, int RING, bool NT, int SRC = SRC_OFFSETS, int PL = 8>
 hipError_t launch_stream(const GemmArgs &a, int max_rows, hipStream_t st)
 {
     constexpr int CS = 16 * NSUB;
-    auto kernel = gemm_stream_kernel<KIND, TPW, NSUB, KSEG, RING, NT>;
-    const size_t lds = stream_act_bytes<NSUB, KSEG>() + sizeof(int) * (2 * (a.num_experts + 1) + 4);
+    auto kernel = gemm_stream_kernel<KIND, TPW, NSUB, KSEG, RING, NT, SRC, PL>;
+    const size_t tables = SRC == SRC_OFFSETS ? sizeof(int) * (2 * (a.num_experts + 1) + 4)
+                                             : sizeof(int) * (2 * kDecMaxSlots + 4 + a.num_experts);
+    const size_t lds = stream_act_bytes<NSUB, KSEG>() + tables;
     const int per_cu = resident_per_cu(kernel, lds);
     // persistent grid: at most the resident slots, at most the item bound
+    // (small batch: at most one item per slot and block)
     const int nblocks = (a.N >> 4) / (4 * TPW);
-    const long long chunks = (long long)min(a.num_experts, max_rows) + max_rows / CS;
+    const long long chunks = SRC != SRC_OFFSETS ? (long long)min(a.num_experts, max_rows)
+                                                : (long long)min(a.num_experts, max_rows) + max_rows / CS;
     long long grid = grid_for(chunks * nblocks, per_cu);
     if (grid >= kXcds)
         grid -= grid % kXcds;                          // whole XCD shares (see the kernel)
@@ -1211,6 +1228,20 @@ hipError_t launch_kind(const GemmArgs &a, int max_rows, int mode, int tpw, int n
 
 }  // namespace
 
+// Streaming kernel instances (tiles per wave, subtiles, K segment, ring depth).
+static bool stream_instance(int tpw, int nsub, int kseg, int ring)
+{
+    static const int list[][4] = {{1, 1, 2, 2}, {1, 1, 4, 2}, {1, 1, 4, 4}, {1, 1, 8, 4}, {1, 2, 2, 2}, {1, 2, 4, 2},
+                                  {1, 2, 4, 4}, {1, 4, 2, 2}, {2, 1, 2, 2}, {2, 1, 4, 2}, {2, 1, 4, 4}, {2, 1, 8, 4},
+                                  {2, 2, 2, 2}, {2, 2, 4, 2}, {2, 2, 4, 4}, {2, 4, 2, 2}, {4, 1, 2, 2}, {4, 1, 4, 2},
+                                  {4, 1, 4, 4}, {4, 1, 8, 4}, {4, 2, 2, 2}, {4, 2, 4, 2}, {4, 2, 4, 4}, {4, 4, 2, 2},
+                                  {2, 4, 1, 2}, {4, 4, 1, 2}};
+    for (const auto &l : list)
+        if (l[0] == tpw && l[1] == nsub && l[2] == kseg && l[3] == ring)
+            return true;
+    return false;
+}
+
 // Shapes the tile kernel takes: tiled codes, K/128 even, at least 4 (the
 // next item's first groups are copied during groups G-3 and G-2) and at most
 // 16 (one correction column per group), 512-row blocks, expert tables in the
@@ -1224,9 +1255,9 @@ static bool tile_fits(const GemmLaunch &g, int waves)
            (size_t)g.max_rows * (size_t)ldc * 2 < 0x80000000u;
 }
 
-hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
+static GemmArgs make_args(const GemmLaunch &g)
 {
-    GemmArgs a;
+    GemmArgs a{};
     a.a = g.a;
     a.a_row_index = g.a_row_index;
     a.offsets = g.offsets;
@@ -1253,7 +1284,13 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
         const size_t cb = (size_t)g.max_rows * (size_t)a.ldc * 2;
         a.c_bytes = cb < 0x80000000u ? (uint32_t)cb : 0u;   // 0: too large for the tile kernel
     }
+    return a;
+}
 
+// The launch the grouped GEMM takes for this shape: kernel family (mode 0
+// split-K, 1 streaming, 2 / 3 tile kernel) and its tiling.
+LaunchChoice choose_launch(const GemmLaunch &g)
+{
     // Expected rows per active expert (uniform routing estimate) picks the
     // kernel and the tile shape. Only the launch shape depends on it, never
     // the result.
@@ -1289,11 +1326,6 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     while (tpw > 1 && chunks * ntiles / tpw <= fill)
         tpw >>= 1;
     int mode = chunks * ntiles / tpw > fill ? 1 : 0;
-    // At most 16 tokens (every expert then holds at most one 16-row chunk):
-    // the split-K kernel, whose tiles the layer's small-batch path computes
-    // with the same arithmetic, so the layer equals these GEMMs composed.
-    if (g.offsets && T <= 16.0)
-        mode = 0;
     int kseg = 4;
     int ring = (g.K >= 4096 || m < 3.0) ? 4 : 2;
     if (g.K >= 4096)
@@ -1329,7 +1361,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
         ring = 2;
     if ((mode == 2 && !tile_fits(g, 8)) || (mode == 3 && !tile_fits(g, 4)))
         mode = 1;
-    if (mode == 1 && (ntiles % (4 * tpw) != 0 || G % kseg != 0))
+    if (mode == 1 && (ntiles % (4 * tpw) != 0 || G % kseg != 0 || !stream_instance(tpw, nsub, kseg, ring)))
         mode = 0;                                         // shapes the streaming tiles do not divide
     // non-temporal code loads while most experts fit one chunk (their codes
     // are then read once): routed loads vary around m, a dense GEMM has
@@ -1337,9 +1369,66 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
     bool nt = m <= (g.num_experts == 1 ? 1.0 : 0.75) * 16.0 * nsub;
     if (ov.gemm_nontemporal >= 0)
         nt = ov.gemm_nontemporal != 0;
+    LaunchChoice c;
+    c.mode = mode;
+    c.tpw = tpw;
+    c.nsub = nsub;
+    c.kseg = kseg;
+    c.ring = ring;
+    c.nt = nt;
+    return c;
+}
+
+hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
+{
+    const GemmArgs a = make_args(g);
+    const LaunchChoice c = choose_launch(g);
     if (g.kind == MOE_GEMM_W13_SWIGLU)
-        return launch_kind<MOE_GEMM_W13_SWIGLU>(a, g.max_rows, mode, tpw, nsub, kseg, ring, nt, st);
-    return launch_kind<MOE_GEMM_W2>(a, g.max_rows, mode, tpw, nsub, kseg, ring, nt, st);
+        return launch_kind<MOE_GEMM_W13_SWIGLU>(a, g.max_rows, c.mode, c.tpw, c.nsub, c.kseg, c.ring, c.nt, st);
+    return launch_kind<MOE_GEMM_W2>(a, g.max_rows, c.mode, c.tpw, c.nsub, c.kseg, c.ring, c.nt, st);
+}
+
+// The layer's small-batch path on the streaming kernel: the item source is
+// the slot table (SRC_ROUTE: routing inside, gate/up; SRC_SLOTS: the stored
+// table, down). The tiling follows choose_launch with one 16-row subtile;
+// every streaming tiling computes the same bits.
+hipError_t launch_decode_stream(const GemmLaunch &g, const DecodeSource &d, hipStream_t st)
+{
+    GemmArgs a = make_args(g);
+    a.logits = d.logits;
+    a.T = d.T;
+    a.E_g = d.E_g;
+    a.begin = d.begin;
+    a.ids = d.ids;
+    a.wts = d.w;
+    a.pres = d.pres;
+    const LaunchChoice c = choose_launch(g);
+    const int tpw = c.tpw > 2 ? 2 : c.tpw;
+    const int ntiles = g.N / 16;
+    if (ntiles % (4 * tpw) != 0 || g.c_f32)
+        return hipErrorInvalidValue;
+#define MOE_DEC_STREAM(T_, KS_, RG_)                                                                         \
+    if (tpw == T_ && c.kseg == KS_ && c.ring == RG_) {                                                     \
+        if (d.src == SRC_ROUTE && g.kind == MOE_GEMM_W13_SWIGLU)                                          \
+            return launch_stream<MOE_GEMM_W13_SWIGLU, T_, 1, KS_, RG_, true, SRC_ROUTE, 16>(a, g.max_rows, st); \
+        if (d.src == SRC_SLOTS && g.kind == MOE_GEMM_W2)                                                  \
+            return launch_stream<MOE_GEMM_W2, T_, 1, KS_, RG_, true, SRC_SLOTS, 8>(a, g.max_rows, st);     \
+        return hipErrorInvalidValue;                                                                      \
+    }
+    MOE_DEC_STREAM(1, 2, 2) MOE_DEC_STREAM(1, 4, 2) MOE_DEC_STREAM(1, 4, 4) MOE_DEC_STREAM(1, 8, 4)
+    MOE_DEC_STREAM(2, 2, 2) MOE_DEC_STREAM(2, 4, 2) MOE_DEC_STREAM(2, 4, 4) MOE_DEC_STREAM(2, 8, 4)
+#undef MOE_DEC_STREAM
+    return hipErrorInvalidValue;
+}
+
+// Whether launch_decode_stream has an instance for this GEMM.
+bool decode_stream_supported(const GemmLaunch &g)
+{
+    const LaunchChoice c = choose_launch(g);
+    const int tpw = c.tpw > 2 ? 2 : c.tpw;
+    if (c.mode != 1 || (g.N / 16) % (4 * tpw) != 0 || g.c_f32)
+        return false;
+    return (c.kseg == 2 && c.ring == 2) || (c.kseg == 4 && (c.ring == 2 || c.ring == 4)) || (c.kseg == 8 && c.ring == 4);
 }
 
 }  // namespace moe

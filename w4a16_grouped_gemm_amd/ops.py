@@ -29,7 +29,8 @@ EXPORTED = ["moe_status_str", "moe_w4a16_check_shape", "moe_w4a16_is_supported",
             "moe_w4a16_workspace_size", "moe_w4a16_forward", "moe_route", "moe_permute_workspace_size",
             "moe_permute", "moe_grouped_gemm_w4a16", "moe_finalize", "moe_w4a16_pack_weights",
             "moe_w4a16_dense_gemm", "moe_w4a16_workspace_size_shared", "moe_w4a16_forward_shared",
-            "moe_w4a16_set_launch_override", "moe_w4a16_forward_noalloc"]
+            "moe_w4a16_set_launch_override", "moe_w4a16_forward_noalloc", "moe_mxfp4_quantize",
+            "moe_grouped_gemm_mxfp4", "moe_w4a4_workspace_size", "moe_w4a4_forward"]
 
 
 class MoeShape(ctypes.Structure):
@@ -101,6 +102,14 @@ def load_library(path: str = LIB_PATH):
         lib.moe_w4a16_set_launch_override.restype = I
         lib.moe_w4a16_forward_noalloc.argtypes = [S, P, P, P, P, P, P, P, P]
         lib.moe_w4a16_forward_noalloc.restype = I
+        lib.moe_mxfp4_quantize.argtypes = [ctypes.c_int64, ctypes.c_int32, P, P, P, P]
+        lib.moe_mxfp4_quantize.restype = I
+        lib.moe_grouped_gemm_mxfp4.argtypes = [S, I, P, P, P, P, P, P, P, I, P]
+        lib.moe_grouped_gemm_mxfp4.restype = I
+        lib.moe_w4a4_workspace_size.argtypes = [S]
+        lib.moe_w4a4_workspace_size.restype = Z
+        lib.moe_w4a4_forward.argtypes = [S, P, P, P, P, P, P, P, P, Z, P]
+        lib.moe_w4a4_forward.restype = I
         _lib = lib
         return lib
 
@@ -433,4 +442,80 @@ def moe_w4a16_forward_noalloc(x: torch.Tensor, router_logits: torch.Tensor, w13_
         raise ValueError("out must be [T, H]")
     _check(load_library().moe_w4a16_forward_noalloc(ctypes.byref(sh), _ptr(x), _ptr(router_logits), _ptr(w13_q),
                                                     _ptr(s13), _ptr(w2_q), _ptr(s2), _ptr(out), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# the W4A4 (MXFP4) variant
+# ---------------------------------------------------------------------------
+
+def mxfp4_quantize(x: torch.Tensor, *, stream=None):
+    """bf16 [R, K] -> (codes uint8 [R, K/2], scales uint8 [R, K/32]), MXFP4."""
+    _need(x, torch.bfloat16, "x")
+    R, K = x.shape
+    codes = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+    _check(load_library().moe_mxfp4_quantize(int(R), int(K), _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def grouped_gemm_mxfp4(kind: int, a_codes: torch.Tensor, a_scales: torch.Tensor, offsets: torch.Tensor,
+                       wq: torch.Tensor, ws: torch.Tensor, *, num_tokens: int, top_k: int,
+                       a_row_index: torch.Tensor | None = None, out_dtype=torch.bfloat16,
+                       num_experts: int | None = None, out: torch.Tensor | None = None, stream=None):
+    """Grouped GEMM on MXFP4 activations and weights; returns c [num_tokens*top_k, cols]."""
+    _need(a_codes, torch.uint8, "a_codes")
+    _need(a_scales, torch.uint8, "a_scales")
+    _need(offsets, torch.int32, "offsets")
+    _need(wq, torch.uint8, "wq")
+    _need(ws, torch.uint8, "ws")
+    E_loc, N, K2 = wq.shape
+    K = 2 * K2
+    if ws.shape != (E_loc, N, K // 32) or a_codes.shape[-1] != K // 2 or a_scales.shape[-1] != K // 32:
+        raise ValueError("MXFP4 operand shapes do not match")
+    if kind == W2:
+        H, I, cols = N, K, N
+    else:
+        H, I = K, N // 2
+        cols = I if kind == W13_SWIGLU else N
+    if out is None:
+        out = torch.empty((num_tokens * top_k, cols), dtype=out_dtype, device=a_codes.device)
+    dt = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}.get(out.dtype)
+    if dt is None:
+        raise ValueError("out dtype must be bfloat16 or float32")
+    if a_row_index is not None:
+        _need(a_row_index, torch.int32, "a_row_index")
+    sh = make_shape(num_tokens, H, I, num_experts or E_loc, E_loc, top_k, group_size=32)
+    _check(load_library().moe_grouped_gemm_mxfp4(ctypes.byref(sh), int(kind), _ptr(a_codes), _ptr(a_scales),
+                                                 _ptr(a_row_index), _ptr(offsets), _ptr(wq), _ptr(ws), _ptr(out),
+                                                 dt, _stream(stream)))
+    return out
+
+
+def moe_w4a4_forward(x: torch.Tensor, router_logits: torch.Tensor, w13_q: torch.Tensor, w13_s: torch.Tensor,
+                     w2_q: torch.Tensor, w2_s: torch.Tensor, top_k: int, out: torch.Tensor | None = None,
+                     stream=None, *, expert_begin: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The W4A4 (MXFP4) MoE expert layer: MXFP4 weights, activations quantized on the fly."""
+    _need(x, torch.bfloat16, "x")
+    _need(router_logits, torch.float32, "router_logits")
+    for t, n in ((w13_q, "w13_q"), (w13_s, "w13_s"), (w2_q, "w2_q"), (w2_s, "w2_s")):
+        _need(t, torch.uint8, n)
+    T, H = x.shape
+    E_loc, N13, H2 = w13_q.shape
+    I = N13 // 2
+    if (H2 * 2 != H or w2_q.shape != (E_loc, H, I // 2) or w13_s.shape != (E_loc, 2 * I, H // 32)
+            or w2_s.shape != (E_loc, H, I // 32)):
+        raise ValueError("MXFP4 weight shapes do not match x")
+    sh = make_shape(T, H, I, router_logits.shape[1], E_loc, top_k, expert_begin, group_size=32)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    lib = load_library()
+    nbytes = int(lib.moe_w4a4_workspace_size(ctypes.byref(sh)))
+    if nbytes == 0 and T > 0:
+        raise MoeError(2, "shape not supported by the W4A4 layer")
+    if workspace is None:
+        workspace = _workspace(nbytes, x.device, stream)
+    _check(lib.moe_w4a4_forward(ctypes.byref(sh), _ptr(x), _ptr(router_logits), _ptr(w13_q), _ptr(w13_s),
+                                _ptr(w2_q), _ptr(w2_s), _ptr(out), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
