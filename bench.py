@@ -41,7 +41,8 @@ METRIC = "MoE-layer tokens/s; weight HBM GB/s % peak (decode), MFMA % (prefill)"
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["w4a16_grouped_gemm_amd/csrc/gemm_w4a16.hip", "w4a16_grouped_gemm_amd/csrc/common.hpp"]
+KERNEL_SOURCES = ["w4a16_grouped_gemm_amd/csrc/gemm_w4a16.hip", "w4a16_grouped_gemm_amd/csrc/gemm_core.hpp",
+                  "w4a16_grouped_gemm_amd/csrc/common.hpp"]
 WARM_REPLAYS = 10
 TIMED_REPLAYS = 50
 CACHE_BYTES = 256e6          # Infinity Cache (MALL); the L2s (8 x 4 MB) are smaller
@@ -556,6 +557,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="", help="comma list of extra workloads to time "
                     "(decode,prefill,ep,shared,finalize,dense,w4a4); default all")
+    ap.add_argument("--decode-tokens", default="1,16,64,256",
+                    help="token counts of the decode sweep (comma list)")
     ap.add_argument("--weights", choices=["tiled", "plain"], default="tiled",
                     help="int4 code layout the layer reads (tiled: packed once before timing)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -628,7 +631,7 @@ def main():
 
     sweep, prefill, ep, shared, fin, dense = [], None, [], None, None, None
     if "decode" in only:
-        for ts in (1, 16, 64, 256):
+        for ts in [int(v) for v in args.decode_tokens.split(",") if v]:
             log(f"decode T={ts}")
             sweep.append(decode_point(ops, wl, weights, ts, torch, layout, seed=ts))
     if "prefill" in only:

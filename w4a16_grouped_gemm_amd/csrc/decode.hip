@@ -248,14 +248,12 @@ __global__ __launch_bounds__(KS * SP * 64) void decode_down_combine_kernel(Decod
         const int pres_l = p.pres[t * k + js];
         const int id_l = p.ids[t * k + js];
         const float w_l = p.w[t * k + js];
-        // stage the present slots' h rows (absent rows read as zeros)
-        for (int c = tid; c < chunks; c += NW * 64) {
-            const int j = c / (K / 8);
-            const int pj = __shfl(pres_l, j, 64);
-            const uint32_t vo = pj >= 0 ? ((uint32_t)(t * k + j) * (uint32_t)K + (uint32_t)(c % (K / 8)) * 8u) * 2u
-                                        : kOutOfRange;
-            *reinterpret_cast<u32x4 *>(s_h + (size_t)c * 8) = bload16(ra, vo, 0);
-        }
+        // stage the token's k h rows, issued together with the slot-table
+        // loads above (no dependence on them: rows of absent slots are staged
+        // too and never read)
+        for (int c = tid; c < chunks; c += NW * 64)
+            *reinterpret_cast<u32x4 *>(s_h + (size_t)c * 8) =
+                bload16(ra, ((uint32_t)t * (uint32_t)k * (uint32_t)K + (uint32_t)c * 8u) * 2u, 0);
         // this wave's slots: codes and scales of groups g0..g1 (absent: zeros, no traffic)
         u32x4 wv[SPW][GMAX];
         uint32_t sc[SPW][GMAX];
