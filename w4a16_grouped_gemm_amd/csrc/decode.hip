@@ -136,10 +136,16 @@ __device__ __forceinline__ void expert_item(const DecodeArgs &p, const int *s_lo
     }
 }
 
-// Gate/up with routing inside: every workgroup routes all tokens (PL logits
-// per lane, 16 lanes per token, E_g <= 256), builds the slot table and the
-// leaders, then runs its share of the (leader, tile) items.
-template <int NW, int PL>
+// Gate/up with routing inside: every workgroup routes all tokens (TL lanes
+// per token, PL logits per lane, E_g <= TL * PL), builds the slot table and
+// the leaders, then runs its share of the (leader, tile) items. With at most
+// one token per wave a whole wave routes each token (TL = 64): the k rounds
+// of the selection are the routing's serial part, and 64 lanes of PL = 2
+// logits (128 experts) take about half the instructions per round of 16
+// lanes of 8. The selection and the weights are those of the 16-lane shape
+// bit for bit (the same comparisons; the slot weights are formed in lanes
+// 0..k-1, one DPP row, as there).
+template <int NW, int TL, int PL>
 __global__ __launch_bounds__(NW * 64) void decode_gate_up_kernel(DecodeArgs p)
 {
     __shared__ int s_loc[kDecMaxSlots];
@@ -147,19 +153,19 @@ __global__ __launch_bounds__(NW * 64) void decode_gate_up_kernel(DecodeArgs p)
     __shared__ int s_lead[kDecMaxSlots];
     __shared__ int s_nlead;
     __shared__ floatx4 s_red[NW][64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n16 = lane & 15;
+    constexpr int TPWV = 64 / TL;                      // tokens per wave and pass
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane % TL;
     const int S = p.T * p.k;
     for (int e = tid; e < p.E_loc; e += NW * 64)
         s_first[e] = kDecMaxSlots;
-    // four tokens per wave and pass, one DPP row (16 lanes) each
-    for (int t0 = wave * 4; t0 < p.T; t0 += NW * 4) {
-        const int t = t0 + (lane >> 4);
+    for (int t0 = wave * TPWV; t0 < p.T; t0 += NW * TPWV) {
+        const int t = t0 + lane / TL;
         if (t < p.T) {
             int eg;
             float wt;
-            route_token<16, PL>(p.logits + (size_t)t * p.E_g, p.E_g, p.k, n16, eg, wt);
-            if (n16 < p.k) {
-                const int s = t * p.k + n16;
+            route_token<TL, PL>(p.logits + (size_t)t * p.E_g, p.E_g, p.k, q, eg, wt);
+            if (q < p.k) {
+                const int s = t * p.k + q;
                 const int le = eg - p.begin;
                 const int loc = (le >= 0 && le < p.E_loc) ? le : -1;
                 s_loc[s] = loc;
@@ -228,6 +234,10 @@ template <int KS, int SP, int SPW, int GMAX>
 __global__ __launch_bounds__(KS * SP * 64) void decode_down_combine_kernel(DecodeArgs p)
 {
     constexpr int NW = KS * SP;
+    // h pieces (16 bytes) per thread loaded in one batch: the automatic
+    // choice's h rows (kCombineAutoHBytes) in one pass
+    constexpr int CPT = (kCombineAutoHBytes / 16) / (NW * 64) < 1 ? 1
+                        : (kCombineAutoHBytes / 16) / (NW * 64) > 8 ? 8 : (kCombineAutoHBytes / 16) / (NW * 64);
     extern __shared__ __align__(16) unsigned char s_dyn[];
     uint16_t *s_h = reinterpret_cast<uint16_t *>(s_dyn);                     // [k][K]
     __shared__ float s_part[kMaxTopK][KS][16];
@@ -248,12 +258,18 @@ __global__ __launch_bounds__(KS * SP * 64) void decode_down_combine_kernel(Decod
         const int pres_l = p.pres[t * k + js];
         const int id_l = p.ids[t * k + js];
         const float w_l = p.w[t * k + js];
-        // stage the token's k h rows, issued together with the slot-table
-        // loads above (no dependence on them: rows of absent slots are staged
-        // too and never read)
-        for (int c = tid; c < chunks; c += NW * 64)
-            *reinterpret_cast<u32x4 *>(s_h + (size_t)c * 8) =
-                bload16(ra, ((uint32_t)t * (uint32_t)k * (uint32_t)K + (uint32_t)c * 8u) * 2u, 0);
+        // the token's k h rows: the first CPT pieces of each thread go out
+        // with the slot-table loads above (no dependence on them: rows of
+        // absent slots are loaded too and never read) and land in LDS after
+        // the weight loads below have been issued, so the whole item costs
+        // one round trip after the slot table
+        const uint32_t hoff = (uint32_t)t * (uint32_t)k * (uint32_t)K * 2u;
+        u32x4 hv[CPT];
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int c = tid + u * NW * 64;
+            hv[u] = bload16(ra, c < chunks ? hoff + (uint32_t)c * 16u : kOutOfRange, 0);
+        }
         // this wave's slots: codes and scales of groups g0..g1 (absent: zeros, no traffic)
         u32x4 wv[SPW][GMAX];
         uint32_t sc[SPW][GMAX];
@@ -281,6 +297,14 @@ __global__ __launch_bounds__(KS * SP * 64) void decode_down_combine_kernel(Decod
                 sc[u][q] = bload_scale(rs, voff_s | oor, (uint32_t)(g < g1 ? g : 0) * 2u);
             }
         }
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            const int c = tid + u * NW * 64;
+            if (c < chunks)
+                *reinterpret_cast<u32x4 *>(s_h + (size_t)c * 8) = hv[u];
+        }
+        for (int c = tid + CPT * NW * 64; c < chunks; c += NW * 64)   // rows past the batch (large k * K)
+            *reinterpret_cast<u32x4 *>(s_h + (size_t)c * 8) = bload16(ra, hoff + (uint32_t)c * 16u, 0);
         __syncthreads();                                  // h rows staged
 #pragma unroll
         for (int u = 0; u < SPW; ++u) {
@@ -453,13 +477,21 @@ hipError_t launch_decode_gate_up(const moe_shape &sh, const float *logits, const
         hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(nw * 64), 0, st, p);
     };
     const int E = sh.num_experts;
+    // a wave per token while every wave routes at most one (see the kernel)
 #define MOE_DEC_GU(NW)                                                                     \
-    if (E <= 64)                                                                           \
-        go(decode_gate_up_kernel<NW, 4>, NW);                                              \
+    if (sh.num_tokens <= NW) {                                                             \
+        if (E <= 64)                                                                       \
+            go(decode_gate_up_kernel<NW, 64, 1>, NW);                                      \
+        else if (E <= 128)                                                                 \
+            go(decode_gate_up_kernel<NW, 64, 2>, NW);                                      \
+        else                                                                               \
+            go(decode_gate_up_kernel<NW, 64, 4>, NW);                                      \
+    } else if (E <= 64)                                                                    \
+        go(decode_gate_up_kernel<NW, 16, 4>, NW);                                          \
     else if (E <= 128)                                                                     \
-        go(decode_gate_up_kernel<NW, 8>, NW);                                              \
+        go(decode_gate_up_kernel<NW, 16, 8>, NW);                                          \
     else                                                                                   \
-        go(decode_gate_up_kernel<NW, 16>, NW);
+        go(decode_gate_up_kernel<NW, 16, 16>, NW);
     switch (splitk_waves(G)) {
     case 8: MOE_DEC_GU(8) break;
     case 4: MOE_DEC_GU(4) break;

@@ -1306,14 +1306,18 @@ LaunchChoice choose_launch(const GemmLaunch &g)
     // tokens, dense GEMMs of 1..1024 rows):
     //  * a second 16-token subtile once experts average more than 12 rows
     //    (each expert's weights are then streamed once instead of twice);
-    //  * tiles per wave: 4 with two subtiles (the correction MFMAs and the
-    //    LDS activation reads of a subtile serve four tiles), else 2, halved
-    //    while the streaming kernel would not have more than two waves per
-    //    CU (chunks x tiles / tiles-per-wave); split-K only when even one
-    //    tile per wave cannot fill the chip (one or two active experts);
-    //  * 4-group K segments (8 for K >= 4096); a 4-deep weight ring for long
-    //    K or few rows per expert, else 2, and 2 with four tiles per wave
-    //    (a deeper ring would not fit two waves per SIMD);
+    //  * tiles per wave: 4 (the correction MFMAs and the LDS activation
+    //    reads of a subtile serve four tiles), halved while the streaming
+    //    kernel would not have more than two waves per CU with two subtiles
+    //    (chunks x tiles / tiles-per-wave), four with one; split-K only when
+    //    even one tile per wave cannot fill the chip (one or two active
+    //    experts). With one subtile, 4 tiles per wave against 2: 16 tokens
+    //    27.1 vs 29.6 us (GEMM1), 64 tokens 37.9 vs 39.9 us; the EP shard at
+    //    64 and 256 tokens 5-7% faster;
+    //  * 4-group K segments (8 for K >= 4096); a 4-deep weight ring for
+    //    K >= 4096, else 2 (at 16 and 64 tokens a 2-deep ring is 3-5% faster
+    //    than a 4-deep one), and 2 with four tiles and two subtiles (a
+    //    deeper ring would not fit two waves per SIMD);
     //  * prefill (2048 tokens) runs best with the two-subtile shape: four
     //    subtiles with one group per segment came out 8% slower.
     const double fill = 2.0 * device_cu_count();
@@ -1322,12 +1326,20 @@ LaunchChoice choose_launch(const GemmLaunch &g)
     const int nsub0 = (g.num_experts == 1 ? m > 16.0 : m > 12.0) ? 2 : 1;
     const double chunks = fmax(active, R / (16.0 * nsub0));
     int nsub = nsub0;
-    int tpw = nsub == 2 ? 4 : 2;
-    while (tpw > 1 && chunks * ntiles / tpw <= fill)
+    int tpw = 4;
+    const double keep = nsub == 2 ? fill : 2.0 * fill;
+    while (tpw > 1 && chunks * ntiles / tpw <= keep)
         tpw >>= 1;
     int mode = chunks * ntiles / tpw > fill ? 1 : 0;
+    // at most 16 routed rows of about one row per expert (one or two decode
+    // tokens of top-8): split-K, whose waves issue all their code loads
+    // before the first MFMA. Measured on MI355X (Qwen3-30B-A3B layer): 1
+    // token 18.3 vs 20.7 us, 2 tokens 21.9 vs 23.4 us; from 4 tokens on (32
+    // rows) the streaming kernel is faster (29.6 vs 37.8 us).
+    if (g.num_experts > 1 && g.max_rows <= 16 && m < 1.5)
+        mode = 0;
     int kseg = 4;
-    int ring = (g.K >= 4096 || m < 3.0) ? 4 : 2;
+    int ring = g.K >= 4096 ? 4 : 2;
     if (g.K >= 4096)
         kseg = 8;
     if (tpw == 4 && nsub == 2)
@@ -1414,7 +1426,9 @@ hipError_t launch_decode_stream(const GemmLaunch &g, const DecodeSource &d, hipS
 #define MOE_DEC_STREAM(T_, KS_, RG_)                                                                         \
     if (tpw == T_ && c.kseg == KS_ && c.ring == RG_) {                                                     \
         if (d.src == SRC_ROUTE && g.kind == MOE_GEMM_W13_SWIGLU)                                          \
-            return launch_stream<MOE_GEMM_W13_SWIGLU, T_, 1, KS_, RG_, true, SRC_ROUTE, 16>(a, g.max_rows, st); \
+            return d.E_g <= 128                                                                           \
+                       ? launch_stream<MOE_GEMM_W13_SWIGLU, T_, 1, KS_, RG_, true, SRC_ROUTE, 8>(a, g.max_rows, st) \
+                       : launch_stream<MOE_GEMM_W13_SWIGLU, T_, 1, KS_, RG_, true, SRC_ROUTE, 16>(a, g.max_rows, st); \
         if (d.src == SRC_SLOTS && g.kind == MOE_GEMM_W2)                                                  \
             return launch_stream<MOE_GEMM_W2, T_, 1, KS_, RG_, true, SRC_SLOTS, 8>(a, g.max_rows, st);     \
         return hipErrorInvalidValue;                                                                      \

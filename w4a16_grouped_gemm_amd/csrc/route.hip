@@ -1,6 +1,7 @@
 // route.hip -- wavefront-level top-k routing with softmax renormalisation.
 //
-// 16 lanes per token (a DPP row) for E <= 256, a whole wave for larger E;
+// A whole wave per token up to 4096 tokens, else 16 lanes per token (a DPP
+// row) for E <= 256 and a whole wave for larger E;
 // lane q holds logits q, q+TL, ... . Each of k rounds takes the largest
 // remaining logit (on an order-preserving integer image; -0 is folded to +0
 // so equal logits tie exactly as IEEE equality says), then the lowest expert
@@ -45,7 +46,19 @@ hipError_t launch_route(const moe_shape &sh, const float *logits, int32_t *ids, 
     const int k = sh.top_k;
     const dim3 block(kRouteWaves * 64);
     auto grid = [&](int tl) { return dim3((T + kRouteWaves * (64 / tl) - 1) / (kRouteWaves * (64 / tl))); };
-    if (E <= 64 && k <= 16)
+    // A whole wave per token while that still leaves the GPU short of waves
+    // (up to 4096 tokens: 1024 workgroups): the k selection rounds are the
+    // serial part of routing, and 64 lanes of 2 logits (128 experts) take
+    // about half the instructions per round of 16 lanes of 8. Same
+    // selection and weights bit for bit (route_core.hpp).
+    if (T <= 4096 && E <= 256 && k <= 16) {
+        if (E <= 64)
+            hipLaunchKernelGGL((route_kernel<64, 1>), grid(64), block, 0, st, T, E, k, logits, ids, w);
+        else if (E <= 128)
+            hipLaunchKernelGGL((route_kernel<64, 2>), grid(64), block, 0, st, T, E, k, logits, ids, w);
+        else
+            hipLaunchKernelGGL((route_kernel<64, 4>), grid(64), block, 0, st, T, E, k, logits, ids, w);
+    } else if (E <= 64 && k <= 16)
         hipLaunchKernelGGL((route_kernel<16, 4>), grid(16), block, 0, st, T, E, k, logits, ids, w);
     else if (E <= 128 && k <= 16)
         hipLaunchKernelGGL((route_kernel<16, 8>), grid(16), block, 0, st, T, E, k, logits, ids, w);
