@@ -20,9 +20,22 @@
 //  * Operand A = 16 routed rows of one expert (the activations), operand B =
 //    16 weight rows; the result lane holds 4 rows x 1 weight row, as in the
 //    W4A16 kernels, so the SwiGLU and row-index epilogue is the same.
-//  * Everything streams HBM -> VGPR (codes 16 bytes per lane and group, the
-//    group's four scale bytes as one dword); activations are as small as the
-//    weights, so there is no LDS staging and no barrier in the K loop.
+//  * Code loads use the default cache policy: a lane's 16 bytes are a
+//    quarter of a row's 64 bytes of one group, so each 128-byte line holds two
+//    groups of a row, and the streaming (non-temporal) policy let lines go
+//    before their second half was read (measured on MI355X, Qwen3-30B-A3B
+//    gate/up at 256 tokens: 305 MB fetched for 210 MB of data, 58.5 us;
+//    default policy 228 MB, 54.7 us).
+//  * K <= 2048 (mx_gemm_lds_kernel): each item stages its chunk's
+//    activation codes and scales for the whole K in LDS once (coalesced row
+//    reads), the four waves read their fragments there, the weight scales of
+//    a tile are loaded once per item, and only the weight codes stream
+//    through a register ring. Per-wave gathers of 16 activation rows and of
+//    16 rows' scale bytes for every group had made the address unit the
+//    bottleneck (Qwen3-30B-A3B gate/up at 256 tokens: 82 -> 55 us).
+//  * Larger K (mx_gemm_kernel): everything streams HBM -> VGPR (codes 16
+//    bytes per lane and group, the group's four scale bytes as one dword),
+//    no LDS staging and no barrier in the K loop.
 //  * Work items (expert chunk of up to 16 NSUB rows, block of 4 waves x TPW
 //    tiles) come from the chunk prefix over `offsets`, as in the W4A16
 //    streaming kernel.
@@ -70,6 +83,58 @@ __device__ __forceinline__ uint32_t mx_tile_row(const MxArgs &p, int tile, int n
     if (KIND == MOE_GEMM_W13_SWIGLU)
         return (uint32_t)(n16 < 8 ? tile * 8 + n16 : p.half + tile * 8 + (n16 - 8));
     return (uint32_t)(tile * 16 + n16);
+}
+
+// Epilogue of one item: result lane (n16, kq) holds rows 4kq + i of weight
+// row n16 of each (tile, subtile); SwiGLU pairs gate row n16 with up row
+// n16 + 8 (lane n16 ^ 8).
+template <int KIND, int TPW, int NSUB>
+__device__ __forceinline__ void mx_store(const MxArgs &p, const floatx4 (&acc)[TPW][NSUB], int tile0, int row0,
+                                         int nvalid, int nsub, int n16, int kq)
+{
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c_row_index, p.c_row_bytes);
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+        if (sb >= nsub)
+            break;
+        int orow[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = sb * 16 + kq * 4 + i;
+            const int r = row0 + min(m, nvalid - 1);
+            orow[i] = p.c_row_index ? (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)r * 4u, 0, 0) : r;
+        }
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const floatx4 v = acc[t][sb];
+            const float rr[4] = {v.x, v.y, v.z, v.w};
+            if (KIND == MOE_GEMM_W13_SWIGLU) {
+                float u[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    u[i] = __shfl_xor(rr[i], 8, 64);
+                if (n16 < 8) {
+                    uint16_t *c = static_cast<uint16_t *>(p.c);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (sb * 16 + kq * 4 + i < nvalid)
+                            c[(size_t)orow[i] * p.ldc + (tile0 + t) * 8 + n16] =
+                                (uint16_t)f32_to_bf16_rne(silu(rr[i]) * u[i]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (sb * 16 + kq * 4 + i < nvalid) {
+                        const size_t off = (size_t)orow[i] * p.ldc + (tile0 + t) * 16 + n16;
+                        if (p.c_f32)
+                            static_cast<float *>(p.c)[off] = rr[i];
+                        else
+                            static_cast<uint16_t *>(p.c)[off] = (uint16_t)f32_to_bf16_rne(rr[i]);
+                    }
+                }
+            }
+        }
+    }
 }
 
 template <int KIND, int TPW, int NSUB, int RING>
@@ -138,7 +203,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p)
             const uint32_t gc = (uint32_t)(g < G ? g : 0);
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
-                wv[b][t] = bload16_codes<true>(rw, vw[t] | oor, gc * 64u);
+                wv[b][t] = bload16_codes<false>(rw, vw[t] | oor, gc * 64u);
                 wsv[b][t] = __builtin_amdgcn_raw_buffer_load_b32(rws, vws[t] | oor, gc * 4u, 0);
             }
 #pragma unroll
@@ -168,50 +233,177 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p)
                 }
             }
         }
-        // epilogue: result lane (n16, kq) holds rows 4kq + i of weight row n16
-        const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c_row_index, p.c_row_bytes);
+        mx_store<KIND, TPW, NSUB>(p, acc, tile0, row0, nvalid, nsub, n16, kq);
+    }
+}
+
+// The same items with the chunk's activations staged in LDS: the 16*NSUB
+// rows' codes and scales for the whole K are copied once per item, rows
+// contiguous (coalesced global reads, one row segment per 64 lanes), and the
+// four waves read their MFMA fragments from there, instead of each wave
+// gathering 16 rows per load instruction for every group. The weight scales
+// of a tile's 16 rows are loaded once per item (lane (n16, kq): the dwords of
+// groups 4kq .. 4kq+3 of row n16) and each group's byte is taken from the
+// owning lane with ds_bpermute. Only weight codes stream through the
+// register ring. K <= 2048 (16 groups: one 16-byte scale load per lane).
+// Row strides: K/2 + 16 bytes for codes (a 16-row fragment read spreads over
+// all banks), K/32 + 4 for scales.
+__host__ __device__ constexpr int mx_code_stride(int K) { return K / 2 + 16; }
+__host__ __device__ constexpr int mx_scale_stride(int K) { return K / 32 + 4; }
+constexpr int kMxStageBatch = 8;                     // staging loads a thread issues before storing
+
+template <int KIND, int TPW, int NSUB, int RING>
+__global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
+{
+    constexpr int CS = 16 * NSUB;
+    constexpr int BT = 4 * TPW;
+    extern __shared__ __align__(16) unsigned char s_dyn[];
+    const int E = p.num_experts;
+    const int K = p.K, G = K / kGroup;
+    const int AST = mx_code_stride(K), ASS = mx_scale_stride(K);
+    uint8_t *s_a = s_dyn;                                        // [CS][AST]
+    uint8_t *s_as = s_a + CS * AST;                              // [CS][ASS]
+    int *s_src = reinterpret_cast<int *>(s_as + CS * ASS);       // [CS] activation row of each chunk row
+    int *s_prefix = s_src + CS;                                  // [E+1], then the scan scratch
+    int *s_wtot = s_prefix + (E + 1);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n16 = lane & 15, kq = lane >> 4;
+    build_chunk_prefix<256>(p.offsets, 0, E, CS, s_prefix, s_wtot);
+
+    const int ntiles = p.N >> 4;
+    const int nblocks = ntiles / BT;
+    const int total_items = s_prefix[E] * nblocks;
+    const uint32_t row_bytes = (uint32_t)(K >> 1), srow_bytes = (uint32_t)(K >> 5);
+    const int ppr = K >> 5;                                      // 16-byte code pieces per row
+    const int spr = K >> 7;                                      // scale dwords per row
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+    const __amdgpu_buffer_rsrc_t ras = make_rsrc(p.as, p.as_bytes);
+    const uint32_t sh = 8u * (uint32_t)kq;
+    const int nx = (int)gridDim.x >= kXcds ? kXcds : 1;
+    const int xcd = blockIdx.x % nx;
+    const int i_end = (int)((long long)total_items * (xcd + 1) / nx);
+    for (int item = (int)((long long)total_items * xcd / nx) + blockIdx.x / nx; item < i_end;
+         item += gridDim.x / nx) {
+        const int chunk = item / nblocks;
+        const int block = item - chunk * nblocks;
+        const int e = uniform(chunk_expert(s_prefix, E, chunk));
+        const int row0 = uniform(p.offsets[e] + (chunk - s_prefix[e]) * CS);
+        const int nvalid = uniform(min(CS, p.offsets[e + 1] - row0));
+        const int nsub = (nvalid + 15) >> 4;
+        const int tile0 = block * BT + wave * TPW;
+        const uint32_t wbytes = (uint32_t)p.N * row_bytes, wsbytes = (uint32_t)p.N * srow_bytes;
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (size_t)e * wbytes, wbytes);
+        const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.ws + (size_t)e * wsbytes, wsbytes);
+        // activation row of chunk row tid (gather index read now, stored after the barrier)
+        int src = 0;
+        if (tid < CS && tid < nvalid)
+            src = p.a_row_index ? p.a_row_index[row0 + tid] / p.top_k : row0 + tid;
+        // weight scales of this wave's tiles, and the first RING-1 groups of codes
+        uint32_t vw[TPW];
+        u32x4 wsc[TPW];
 #pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb) {
-            if (sb >= nsub)
-                break;
-            int orow[4];
+        for (int t = 0; t < TPW; ++t) {
+            const uint32_t row = mx_tile_row<KIND>(p, tile0 + t, n16);
+            vw[t] = row * row_bytes + (uint32_t)kq * 16u;
+            // dword d of the lane: group 4kq + d (dwords past G are not read:
+            // a row's scales end inside the lane's 16 bytes when G % 4 != 0)
+            const uint32_t so = row * srow_bytes + (uint32_t)kq * 16u;
+            uint32_t d4[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = sb * 16 + kq * 4 + i;
-                const int r = row0 + min(m, nvalid - 1);
-                orow[i] = p.c_row_index ? (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)r * 4u, 0, 0) : r;
+            for (int d = 0; d < 4; ++d)
+                d4[d] = __builtin_amdgcn_raw_buffer_load_b32(rws, 4 * kq + d < G ? so + 4u * d : kOutOfRange, 0, 0);
+            wsc[t] = u32x4{d4[0], d4[1], d4[2], d4[3]};
+        }
+        u32x4 wv[RING][TPW];
+        auto load_w = [&](int g, int b) {
+            const uint32_t oor = g < G ? 0u : kOutOfRange;
+            const uint32_t gc = (uint32_t)(g < G ? g : 0);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+                wv[b][t] = bload16_codes<false>(rw, vw[t] | oor, gc * 64u);
+        };
+#pragma unroll
+        for (int r = 0; r < RING - 1; ++r)
+            load_w(r, r);
+        __syncthreads();                                         // the previous item is done with s_a
+        if (tid < CS)
+            s_src[tid] = src;
+        __syncthreads();
+        // stage the chunk's codes and scales: a batch of loads per thread goes
+        // out before any is stored (rows past nvalid are left as they are:
+        // their results are never stored)
+        for (int base = 0; base < nvalid * ppr; base += kMxStageBatch * 256) {
+            u32x4 v[kMxStageBatch];
+            uint32_t sv[kMxStageBatch / 4];
+#pragma unroll
+            for (int u = 0; u < kMxStageBatch; ++u) {
+                const int q = base + u * 256 + tid;
+                const int r = q / ppr, c = q - r * ppr;
+                const uint32_t off = q < nvalid * ppr ? (uint32_t)s_src[min(r, CS - 1)] * row_bytes + (uint32_t)c * 16u
+                                                      : kOutOfRange;
+                v[u] = bload16(ra, off, 0);
+            }
+            // scale dwords: one per 4 code pieces (spr = ppr / 4)
+#pragma unroll
+            for (int u = 0; u < kMxStageBatch / 4; ++u) {
+                const int q = base / 4 + u * 256 + tid;
+                const int r = q / spr, c = q - r * spr;
+                const bool ok = q < min(nvalid * spr, (base + kMxStageBatch * 256) / 4);
+                sv[u] = __builtin_amdgcn_raw_buffer_load_b32(
+                    ras, ok ? (uint32_t)s_src[min(r, CS - 1)] * srow_bytes + (uint32_t)c * 4u : kOutOfRange, 0, 0);
             }
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const floatx4 v = acc[t][sb];
-                const float rr[4] = {v.x, v.y, v.z, v.w};
-                if (KIND == MOE_GEMM_W13_SWIGLU) {
-                    float u[4];
+            for (int u = 0; u < kMxStageBatch; ++u) {
+                const int q = base + u * 256 + tid;
+                const int r = q / ppr, c = q - r * ppr;
+                if (q < nvalid * ppr)
+                    *reinterpret_cast<u32x4 *>(s_a + r * AST + c * 16) = v[u];
+            }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        u[i] = __shfl_xor(rr[i], 8, 64);
-                    if (n16 < 8) {
-                        uint16_t *c = static_cast<uint16_t *>(p.c);
+            for (int u = 0; u < kMxStageBatch / 4; ++u) {
+                const int q = base / 4 + u * 256 + tid;
+                const int r = q / spr, c = q - r * spr;
+                if (q < min(nvalid * spr, (base + kMxStageBatch * 256) / 4))
+                    *reinterpret_cast<uint32_t *>(s_as + r * ASS + c * 4) = sv[u];
+            }
+        }
+        __syncthreads();
+
+        floatx4 acc[TPW][NSUB];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (sb * 16 + kq * 4 + i < nvalid)
-                                c[(size_t)orow[i] * p.ldc + (tile0 + t) * 8 + n16] =
-                                    (uint16_t)f32_to_bf16_rne(silu(rr[i]) * u[i]);
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int sb = 0; sb < NSUB; ++sb)
+                acc[t][sb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int g0 = 0; g0 < G; g0 += RING) {
+#pragma unroll
+            for (int j = 0; j < RING; ++j) {
+                const int g = g0 + j;
+                load_w(g + RING - 1, (j + RING - 1) % RING);
+                if (g < G) {
+                    // weight scale byte kq of (row n16, group g): lane n16 + 16 (g / 4), dword g % 4
+                    const int src_lane = (n16 + 16 * (g >> 2)) * 4;
+                    uint32_t wsg[TPW];
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t) {
+                        const int gq = g & 3;
+                        const uint32_t d = gq == 0 ? wsc[t].x : gq == 1 ? wsc[t].y : gq == 2 ? wsc[t].z : wsc[t].w;
+                        wsg[t] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)d) >> sh;
                     }
-                } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if (sb * 16 + kq * 4 + i < nvalid) {
-                            const size_t off = (size_t)orow[i] * p.ldc + (tile0 + t) * 16 + n16;
-                            if (p.c_f32)
-                                static_cast<float *>(p.c)[off] = rr[i];
-                            else
-                                static_cast<uint16_t *>(p.c)[off] = (uint16_t)f32_to_bf16_rne(rr[i]);
+                    for (int sb = 0; sb < NSUB; ++sb) {
+                        if (sb < nsub) {
+                            const int m = sb * 16 + n16;
+                            const u32x4 a = *reinterpret_cast<const u32x4 *>(s_a + m * AST + g * 64 + kq * 16);
+                            const uint32_t as = *reinterpret_cast<const uint32_t *>(s_as + m * ASS + g * 4) >> sh;
+#pragma unroll
+                            for (int t = 0; t < TPW; ++t)
+                                acc[t][sb] = mfma_fp4(a, as, wv[j][t], wsg[t], acc[t][sb]);
                         }
                     }
                 }
             }
         }
+        mx_store<KIND, TPW, NSUB>(p, acc, tile0, row0, nvalid, nsub, n16, kq);
     }
 }
 
@@ -315,6 +507,35 @@ hipError_t mx_launch(const MxArgs &a, int max_rows, hipStream_t st)
     return hipGetLastError();
 }
 
+// The LDS-staged kernel when the whole K of a chunk fits (K <= 2048, the
+// one-load weight scales), else the register-streaming one.
+template <int KIND, int TPW, int NSUB, int RING>
+hipError_t mx_launch_any(const MxArgs &a, int max_rows, hipStream_t st)
+{
+    constexpr int CS = 16 * NSUB;
+    const size_t lds = (size_t)CS * (mx_code_stride(a.K) + mx_scale_stride(a.K) + 4) +
+                       sizeof(int) * (a.num_experts + 1 + 4);
+    if (a.K > 2048 || lds > 150 * 1024)
+        return mx_launch<KIND, TPW, NSUB, RING>(a, max_rows, st);
+    auto kernel = mx_gemm_lds_kernel<KIND, TPW, NSUB, RING>;
+    static std::once_flag once;
+    std::call_once(once, [&] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  150 * 1024);
+    });
+    const int per_cu = mx_resident_per_cu(kernel, lds);
+    const int nblocks = (a.N >> 4) / (4 * TPW);
+    const long long chunks = (long long)min(a.num_experts, max_rows) + max_rows / CS;
+    long long grid = chunks * nblocks;
+    const long long cap = (long long)device_cu_count() * per_cu;
+    grid = grid < cap ? grid : cap;
+    grid = grid < 1 ? 1 : grid;
+    if (grid >= kXcds)
+        grid -= grid % kXcds;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), lds, st, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_mx_quantize(long long rows, int K, const uint16_t *x, uint8_t *codes, uint8_t *scales,
@@ -370,7 +591,7 @@ hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st)
     auto go = [&](auto kindc) -> hipError_t {
         constexpr int KIND = decltype(kindc)::value;
 #define MOE_MX(TP, NS) \
-        if (tpw == TP && nsub == NS) return mx_launch<KIND, TP, NS, (NS == 4 ? 2 : 4)>(a, g.max_rows, st);
+        if (tpw == TP && nsub == NS) return mx_launch_any<KIND, TP, NS, (NS == 4 ? 2 : 4)>(a, g.max_rows, st);
         MOE_MX(1, 1) MOE_MX(2, 1) MOE_MX(4, 1) MOE_MX(1, 2) MOE_MX(2, 2) MOE_MX(4, 2) MOE_MX(1, 4) MOE_MX(2, 4)
         MOE_MX(4, 4)
 #undef MOE_MX
