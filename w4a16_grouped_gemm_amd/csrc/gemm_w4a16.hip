@@ -1402,8 +1402,8 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st)
 
 // The layer's small-batch path on the streaming kernel: the item source is
 // the slot table (SRC_ROUTE: routing inside, gate/up; SRC_SLOTS: the stored
-// table, down). The tiling follows choose_launch with one 16-row subtile;
-// every streaming tiling computes the same bits. Deeper weight rings (all 16
+// table, down). The tiling is choose_launch's (one 16-row subtile at these
+// row counts); every streaming tiling computes the same bits. Deeper weight rings (all 16
 // groups of a tile in flight) were measured on MI355X and did not pay: one
 // token's gate/up kernel went from 11.5 to 12.4 us and 16 tokens' layer from
 // 50.7 to 56.1 us, so the launch is latency-chained rather than short of
@@ -1419,7 +1419,7 @@ hipError_t launch_decode_stream(const GemmLaunch &g, const DecodeSource &d, hipS
     a.wts = d.w;
     a.pres = d.pres;
     const LaunchChoice c = choose_launch(g);
-    const int tpw = c.tpw > 2 ? 2 : c.tpw;
+    const int tpw = c.tpw;
     const int ntiles = g.N / 16;
     if (ntiles % (4 * tpw) != 0 || g.c_f32)
         return hipErrorInvalidValue;
@@ -1435,6 +1435,7 @@ hipError_t launch_decode_stream(const GemmLaunch &g, const DecodeSource &d, hipS
     }
     MOE_DEC_STREAM(1, 2, 2) MOE_DEC_STREAM(1, 4, 2) MOE_DEC_STREAM(1, 4, 4) MOE_DEC_STREAM(1, 8, 4)
     MOE_DEC_STREAM(2, 2, 2) MOE_DEC_STREAM(2, 4, 2) MOE_DEC_STREAM(2, 4, 4) MOE_DEC_STREAM(2, 8, 4)
+    MOE_DEC_STREAM(4, 2, 2) MOE_DEC_STREAM(4, 4, 2) MOE_DEC_STREAM(4, 4, 4) MOE_DEC_STREAM(4, 8, 4)
 #undef MOE_DEC_STREAM
     return hipErrorInvalidValue;
 }
@@ -1443,8 +1444,7 @@ hipError_t launch_decode_stream(const GemmLaunch &g, const DecodeSource &d, hipS
 bool decode_stream_supported(const GemmLaunch &g)
 {
     const LaunchChoice c = choose_launch(g);
-    const int tpw = c.tpw > 2 ? 2 : c.tpw;
-    if (c.mode != 1 || (g.N / 16) % (4 * tpw) != 0 || g.c_f32)
+    if (c.mode != 1 || (g.N / 16) % (4 * c.tpw) != 0 || g.c_f32)
         return false;
     return (c.kseg == 2 && c.ring == 2) || (c.kseg == 4 && (c.ring == 2 || c.ring == 4)) || (c.kseg == 8 && c.ring == 4);
 }
