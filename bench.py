@@ -327,7 +327,9 @@ def mx_weight_bytes_per_expert(H: int, I: int):
     return 2 * I * H // 2 + 2 * I * (H // 32), H * I // 2 + H * (I // 32)
 
 
-def make_mx_weights(wl, L, torch, seed_base):
+def make_mx_weights(ops, wl, L, torch, seed_base):
+    """L replicas of the layer's MXFP4 weights, codes in the tiled layout
+    (moe_mxfp4_pack_weights), so that a wave's code load covers whole lines."""
     from w4a16_grouped_gemm_amd.inputs import MX_SCALE_RANGE, make_mxfp4_layer_inputs
     dev = torch.device("cuda")
     H, I, El = wl.hidden, wl.inter, wl.num_local_experts
@@ -343,6 +345,10 @@ def make_mx_weights(wl, L, torch, seed_base):
             s13=torch.randint(lo, hi + 1, (El, 2 * I, H // 32), generator=g, device=dev, dtype=torch.uint8),
             w2=torch.randint(0, 256, (El, H, I // 2), generator=g, device=dev, dtype=torch.uint8),
             s2=torch.randint(lo, hi + 1, (El, H, I // 32), generator=g, device=dev, dtype=torch.uint8)))
+    for r in reps:
+        r["w13"] = ops.mxfp4_pack_weights(ops.W13_SWIGLU, r["w13"])
+        r["w2"] = ops.mxfp4_pack_weights(ops.W2, r["w2"])
+    torch.cuda.synchronize()
     return reps
 
 
@@ -366,7 +372,7 @@ def w4a4_point(ops, wl, weights, T, torch, seed, prefill=False):
     def fwd(i):
         w, b = weights[i % len(weights)], batches[i]
         ops.moe_w4a4_forward(b["x"], b["logits"], w["w13"], w["s13"], w["w2"], w["s2"], wl.top_k, out=outs[i],
-                             expert_begin=wl.expert_begin, workspace=ws)
+                             expert_begin=wl.expert_begin, workspace=ws, weight_layout=ops.WEIGHTS_TILED)
     g = capture(torch, [lambda i=i: fwd(i) for i in range(calls)])
     r = replay_stats(torch, g, calls)
     del g
@@ -663,8 +669,8 @@ def main():
     w4a4 = None
     if "w4a4" in only:
         log("W4A4 (MXFP4) layer: decode 1/16/64/256 and prefill 2048")
-        wm = make_mx_weights(wl, 8, torch, seed_base=13)
-        w4a4 = {"workload": "qwen3_decode / qwen3_prefill shapes, MXFP4 weights and activations",
+        wm = make_mx_weights(ops, wl, 8, torch, seed_base=13)
+        w4a4 = {"workload": "qwen3_decode / qwen3_prefill shapes, MXFP4 weights (tiled codes) and activations",
                 "decode": [w4a4_point(ops, wl, wm, ts, torch, seed=ts + 3) for ts in (1, 16, 64, 256)],
                 "prefill": w4a4_point(ops, WORKLOADS["qwen3_prefill"], wm, 2048, torch, seed=2049, prefill=True)}
         del wm

@@ -324,8 +324,13 @@ moe_status moe_w4a16_pack_weights(const moe_shape *shape, moe_gemm_kind kind, co
  *   scale    E8M0 byte s per 32 consecutive elements along K: 2^(s - 127);
  *   weights  w13_q uint8 [E_loc][2*I][H/2], w13_s uint8 [E_loc][2*I][H/32],
  *            w2_q  uint8 [E_loc][H][I/2],   w2_s  uint8 [E_loc][H][I/32].
- * These entry points take moe_shape.group_size == 32 and weight_layout ==
- * MOE_WEIGHTS_PLAIN (else MOE_ERR_UNSUPPORTED); H and I stay multiples of 128.
+ * These entry points take moe_shape.group_size == 32 (else
+ * MOE_ERR_UNSUPPORTED); H and I stay multiples of 128. weight_layout ==
+ * MOE_WEIGHTS_TILED selects the tiled MXFP4 code layout (scales stay plain):
+ * the int4 tiled layout's runs without the word shuffle (a lane's 16 bytes
+ * are its operand of the scaled matrix instruction as they lie),
+ *   tiled[e][b][g][i][l][0 .. 16) = plain[e][row(16*(8*b+i), l%16)][64*g + 16*(l/16) .. +16)
+ * with b, g, i, l and row() as above; moe_mxfp4_pack_weights writes it.
  */
 
 /*
@@ -352,6 +357,16 @@ moe_status moe_mxfp4_quantize(int64_t rows, int32_t K, const uint16_t *x, uint8_
 moe_status moe_grouped_gemm_mxfp4(const moe_shape *shape, moe_gemm_kind kind, const uint8_t *a_codes,
                                   const uint8_t *a_scales, const int32_t *a_row_index, const int32_t *offsets,
                                   const uint8_t *wq, const uint8_t *ws, void *c, moe_dtype c_dtype, void *stream);
+
+/*
+ * Reorder one MXFP4 weight matrix's codes from the plain layout into the
+ * tiled MXFP4 layout above (for callers whose weights are fixed: each code
+ * load of the GEMMs then reads 1 KiB contiguously). Arguments and errors as
+ * moe_w4a16_pack_weights, with an MXFP4 shape (group_size 32;
+ * weight_layout is ignored). Bit-exact byte permutation.
+ */
+moe_status moe_mxfp4_pack_weights(const moe_shape *shape, moe_gemm_kind kind, const uint8_t *wq, uint8_t *wq_tiled,
+                                  void *stream);
 
 /*
  * The W4A4 layer: route -> permute -> quantize x (per token, 32 along H) ->

@@ -69,11 +69,11 @@ def shuffle_words(b):
     return out.view(np.uint8).reshape(b.shape)
 
 
-def tiled_codes(wq, kind, inter):
-    """The tiled code layout written out from its definition in the C header:
-    tiled[e][b][g][i][l] = shuffle(plain[e][row(16*(8b+i), l%16)][64g + 16(l//16) : +16]),
-    each 4-byte word shuffled. kind 0 (W13_SWIGLU) pairs gate row 8t+n with
-    up row I+8t+n in tile t."""
+def tiled_runs(wq, kind, inter):
+    """The tiled layout's runs before any word shuffle (the tiled MXFP4 code
+    layout as it is), from the definition in the C header:
+    tiled[e][b][g][i][l] = plain[e][row(16*(8b+i), l%16)][64g + 16(l//16) : +16].
+    kind 0 (W13_SWIGLU) pairs gate row 8t+n with up row I+8t+n in tile t."""
     wq = np.asarray(wq, np.uint8)
     E, N, K2 = wq.shape
     G = (2 * K2) // 128
@@ -89,4 +89,10 @@ def tiled_codes(wq, kind, inter):
                 for g in range(G):
                     for kq in range(4):
                         out[:, b, g, i, 16 * kq + n, :] = wq[:, row, 64 * g + 16 * kq: 64 * g + 16 * kq + 16]
-    return shuffle_words(out).reshape(E, N, K2)
+    return out.reshape(E, N, K2)
+
+
+def tiled_codes(wq, kind, inter):
+    """The tiled int4 code layout from its definition in the C header: the
+    runs of tiled_runs, each 4-byte word shuffled."""
+    return shuffle_words(tiled_runs(wq, kind, inter)).reshape(np.asarray(wq).shape)

@@ -10,12 +10,16 @@
 - moe_w4a4_forward: within the layer tolerance of the oracle's W4A4 layer
   (max |d| <= 2e-2 max |ref|, sum |d| / sum |ref| <= 5e-3), and equal to its
   entry points composed.
+- The tiled MXFP4 code layout: moe_mxfp4_pack_weights equals the layout's
+  definition (a byte permutation written out in numpy); the GEMMs on tiled
+  codes equal the oracle exactly like the plain ones, and the layer on tiled
+  codes equals the layer on plain codes bit for bit.
 """
 import numpy as np
 import pytest
 
 import oracle
-from helpers import assert_layer_close, bf16_dev, bf16_to_f64, say, to_dev, to_np_u16
+from helpers import assert_layer_close, bf16_dev, bf16_to_f64, say, tiled_runs, to_dev, to_np_u16
 from w4a16_grouped_gemm_amd.inputs import bf16_bits, make_mxfp4_layer_inputs
 
 pytestmark = pytest.mark.gpu
@@ -60,10 +64,11 @@ RAGGED = np.array([0, 1, 17, 40, 3, 0, 70, 16, 33, 128])
 
 @pytest.mark.parametrize("kind,H,I", [(2, 2048, 768), (1, 2048, 768), (2, 256, 512), (1, 7168, 2048)])
 @pytest.mark.parametrize("gather", [False, True])
-def test_gemm_exact(kind, H, I, gather):
+@pytest.mark.parametrize("tiled", [False, True])
+def test_gemm_exact(kind, H, I, gather, tiled):
     import torch
     from w4a16_grouped_gemm_amd import ops
-    say(f"mxfp4 gemm exact kind={kind} H={H} I={I} gather={gather}")
+    say(f"mxfp4 gemm exact kind={kind} H={H} I={I} gather={gather} tiled={tiled}")
     rng = np.random.default_rng(H + I + kind + gather)
     counts = RAGGED
     E = len(counts)
@@ -83,9 +88,13 @@ def test_gemm_exact(kind, H, I, gather):
     if gather:
         idx = np.full(T * k, -1, np.int32)
         idx[:R] = rng.permutation(T * k)[:R].astype(np.int32)
-    got = ops.grouped_gemm_mxfp4(kind, to_dev(aq), to_dev(as_), to_dev(offsets), to_dev(wq), to_dev(ws),
+    wdev = to_dev(wq)
+    if tiled:
+        wdev = ops.mxfp4_pack_weights(kind, wdev)
+    got = ops.grouped_gemm_mxfp4(kind, to_dev(aq), to_dev(as_), to_dev(offsets), wdev, to_dev(ws),
                                  num_tokens=T, top_k=k, a_row_index=None if idx is None else to_dev(idx),
-                                 out_dtype=torch.float32)
+                                 out_dtype=torch.float32,
+                                 weight_layout=ops.WEIGHTS_TILED if tiled else ops.WEIGHTS_PLAIN)
     torch.cuda.synchronize()
     ref = oracle.grouped_gemm_mxfp4(oracle.RAW, aq, as_, offsets, wq, ws, rows=T * k, a_row_index=idx, top_k=k,
                                     out_f32=True)
@@ -187,3 +196,31 @@ def test_w4a4_forward_equals_entry_points_composed(wl, T):
     torch.cuda.synchronize()
     assert R > 0
     assert np.array_equal(_w4a4_forward(inp), to_np_u16(composed))
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_mxfp4_pack_matches_layout_definition(kind):
+    from w4a16_grouped_gemm_amd import ops
+    say(f"mxfp4 pack layout kind={kind}")
+    rng = np.random.default_rng(40 + kind)
+    E, H, I = 3, 256, 384
+    N, K = (H, I) if kind == ops.W2 else (2 * I, H)
+    wq = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    got = ops.mxfp4_pack_weights(kind, to_dev(wq)).cpu().numpy()
+    ref = tiled_runs(wq, 0 if kind == ops.W13_SWIGLU else 1, I)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("wl,T", [("qwen3_decode", 16), ("qwen3_decode", 256), ("ep_shard_decode", 64)])
+def test_w4a4_forward_tiled_equals_plain(wl, T):
+    import torch
+    from w4a16_grouped_gemm_amd import ops
+    say(f"w4a4 forward tiled vs plain {wl} T={T}")
+    inp = make_mxfp4_layer_inputs(wl, T)
+    w = inp.workload
+    w13t = ops.mxfp4_pack_weights(ops.W13_SWIGLU, to_dev(inp.w13_q))
+    w2t = ops.mxfp4_pack_weights(ops.W2, to_dev(inp.w2_q))
+    o = ops.moe_w4a4_forward(bf16_dev(inp.x), to_dev(inp.logits), w13t, to_dev(inp.w13_s), w2t, to_dev(inp.w2_s),
+                             w.top_k, expert_begin=w.expert_begin, weight_layout=ops.WEIGHTS_TILED)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np_u16(o), _w4a4_forward(inp))

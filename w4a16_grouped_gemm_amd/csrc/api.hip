@@ -154,7 +154,7 @@ moe_status check_shape_mx(const moe_shape *sh)
 {
     if (!sh)
         return MOE_ERR_NULL;
-    if (sh->group_size != 32 || sh->weight_layout != MOE_WEIGHTS_PLAIN)
+    if (sh->group_size != 32 || (sh->weight_layout != MOE_WEIGHTS_PLAIN && sh->weight_layout != MOE_WEIGHTS_TILED))
         return MOE_ERR_UNSUPPORTED;
     moe_shape s = *sh;
     s.group_size = kGroup;
@@ -632,7 +632,30 @@ moe_status moe_grouped_gemm_mxfp4(const moe_shape *shape, moe_gemm_kind kind, co
     g.N = g0.N;
     g.max_rows = g0.max_rows;
     g.expected_rows = g0.expected_rows;
+    g.w_tiled = shape->weight_layout == MOE_WEIGHTS_TILED;
     return from_hip(launch_mx_grouped_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_mxfp4_pack_weights(const moe_shape *shape, moe_gemm_kind kind, const uint8_t *wq, uint8_t *wq_tiled,
+                                  void *stream)
+{
+    moe_status st = check_shape_mx(shape);
+    if (st != MOE_OK)
+        return st;
+    if (kind != MOE_GEMM_W13_SWIGLU && kind != MOE_GEMM_W2 && kind != MOE_GEMM_W13_RAW)
+        return MOE_ERR_UNSUPPORTED;
+    if (!wq || !wq_tiled)
+        return MOE_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(wq_tiled, 16))
+        return MOE_ERR_ALIGN;
+    const int N = kind == MOE_GEMM_W2 ? shape->hidden : 2 * shape->inter;
+    const int K = kind == MOE_GEMM_W2 ? shape->inter : shape->hidden;
+    const size_t bytes = (size_t)shape->num_local_experts * N * (K / 2);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(wq), b = reinterpret_cast<uintptr_t>(wq_tiled);
+    if (a < b + bytes && b < a + bytes)
+        return MOE_ERR_UNSUPPORTED;                       // in place or overlapping
+    return from_hip(launch_pack_weights(shape->num_local_experts, N, K, shape->inter, kind == MOE_GEMM_W13_SWIGLU,
+                                        wq, wq_tiled, static_cast<hipStream_t>(stream), false));
 }
 
 size_t moe_w4a4_workspace_size(const moe_shape *shape)
@@ -694,6 +717,7 @@ moe_status moe_w4a4_forward(const moe_shape *shape, const uint16_t *x, const flo
         g.N = g0.N;
         g.max_rows = g0.max_rows;
         g.expected_rows = g0.expected_rows;
+        g.w_tiled = sh.weight_layout == MOE_WEIGHTS_TILED;
         e = launch_mx_grouped_gemm(g, s);
     }
     // requantize h: only the R routed rows (R = offsets[E_loc], read on the device)
@@ -718,6 +742,7 @@ moe_status moe_w4a4_forward(const moe_shape *shape, const uint16_t *x, const flo
         g.N = g0.N;
         g.max_rows = g0.max_rows;
         g.expected_rows = g0.expected_rows;
+        g.w_tiled = sh.weight_layout == MOE_WEIGHTS_TILED;
         e = launch_mx_grouped_gemm(g, s);
     }
     if (e == hipSuccess)

@@ -103,7 +103,7 @@ hipError_t launch_gather(const moe_shape &sh, const uint16_t *x, const int32_t *
                          const int32_t *offsets, uint16_t *x_perm, hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st);
 hipError_t launch_pack_weights(int E, int N, int K, int half, bool pair_rows, const uint8_t *wq,
-                               uint8_t *wq_tiled, hipStream_t st);
+                               uint8_t *wq_tiled, hipStream_t st, bool shuffle = true);
 hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const float *w,
                            const int32_t *inv_perm, void *out, bool out_f32, hipStream_t st,
                            bool y_slot = false, int num_shared = 0,
@@ -164,6 +164,7 @@ struct MxGemmLaunch {
     bool c_f32;
     int K, N;
     int max_rows, expected_rows;
+    bool w_tiled;                // codes in the tiled layout (scales plain)
 };
 hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st);
 // rows_dev (nullable): the device-side row count to quantize (at most rows)

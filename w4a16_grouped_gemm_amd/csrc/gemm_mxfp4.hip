@@ -68,7 +68,18 @@ struct MxArgs {
     const int32_t *c_row_index;  // output row of result row r (NULL: r)
     uint32_t c_row_bytes;
     int top_k, num_experts, K, N, ldc, half, c_f32;
+    int w_tiled;                 // codes tiled: tile t, group g at ((t/8)*G*8 + t%8)*1 KiB + g*8 KiB
 };
+
+// Lane offset of tile `tile`'s codes (row `row` of the plain layout) and the
+// byte step from one 128-wide group to the next.
+__device__ __forceinline__ uint32_t mx_code_offset(const MxArgs &p, int tile, uint32_t row, int lane, int kq)
+{
+    if (p.w_tiled)
+        return (uint32_t)((tile >> 3) * (p.K >> 7) * 8 + (tile & 7)) * 1024u + (uint32_t)lane * 16u;
+    return row * (uint32_t)(p.K >> 1) + (uint32_t)kq * 16u;
+}
+__device__ __forceinline__ uint32_t mx_group_stride(const MxArgs &p) { return p.w_tiled ? 8192u : 64u; }
 
 __device__ __forceinline__ floatx4 mfma_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32_t sb, floatx4 c)
 {
@@ -176,9 +187,10 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p)
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const uint32_t row = mx_tile_row<KIND>(p, tile0 + t, n16);
-            vw[t] = row * row_bytes + (uint32_t)kq * 16u;
+            vw[t] = mx_code_offset(p, tile0 + t, row, lane, kq);
             vws[t] = row * srow_bytes;
         }
+        const uint32_t gstride = mx_group_stride(p);
         uint32_t va[NSUB], vas[NSUB];
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb) {
@@ -203,7 +215,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p)
             const uint32_t gc = (uint32_t)(g < G ? g : 0);
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
-                wv[b][t] = bload16_codes<false>(rw, vw[t] | oor, gc * 64u);
+                wv[b][t] = bload16_codes<false>(rw, vw[t] | oor, gc * gstride);
                 wsv[b][t] = __builtin_amdgcn_raw_buffer_load_b32(rws, vws[t] | oor, gc * 4u, 0);
             }
 #pragma unroll
@@ -303,7 +315,7 @@ __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const uint32_t row = mx_tile_row<KIND>(p, tile0 + t, n16);
-            vw[t] = row * row_bytes + (uint32_t)kq * 16u;
+            vw[t] = mx_code_offset(p, tile0 + t, row, lane, kq);
             // dword d of the lane: group 4kq + d (dwords past G are not read:
             // a row's scales end inside the lane's 16 bytes when G % 4 != 0)
             const uint32_t so = row * srow_bytes + (uint32_t)kq * 16u;
@@ -314,12 +326,13 @@ __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
             wsc[t] = u32x4{d4[0], d4[1], d4[2], d4[3]};
         }
         u32x4 wv[RING][TPW];
+        const uint32_t gstride = mx_group_stride(p);
         auto load_w = [&](int g, int b) {
             const uint32_t oor = g < G ? 0u : kOutOfRange;
             const uint32_t gc = (uint32_t)(g < G ? g : 0);
 #pragma unroll
             for (int t = 0; t < TPW; ++t)
-                wv[b][t] = bload16_codes<false>(rw, vw[t] | oor, gc * 64u);
+                wv[b][t] = bload16_codes<false>(rw, vw[t] | oor, gc * gstride);
         };
 #pragma unroll
         for (int r = 0; r < RING - 1; ++r)
@@ -571,6 +584,7 @@ hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st)
     a.half = g.N / 2;
     a.ldc = g.kind == MOE_GEMM_W13_SWIGLU ? g.N / 2 : g.N;
     a.c_f32 = g.c_f32 ? 1 : 0;
+    a.w_tiled = g.w_tiled ? 1 : 0;
     // rows per active expert under uniform routing: one subtile for decode,
     // four (64-row chunks) once experts hold many rows; tiles per wave from
     // how many items the grid gets

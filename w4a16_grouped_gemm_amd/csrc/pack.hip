@@ -28,8 +28,9 @@ __device__ __forceinline__ uint32_t shuffle_word(uint32_t d)
 
 // One thread per 16-byte unit of the output: unit u of expert e is
 // (((b * G + g) * 8 + i) * 64 + l), read from plain row row(16*(8b+i), l%16),
-// bytes [64g + 16(l/16), +16), each word shuffled.
-__global__ __launch_bounds__(256) void pack_kernel(int E, int N, int K, int half, int pair_rows,
+// bytes [64g + 16(l/16), +16), each word shuffled (int4 codes) or as it is
+// (MXFP4 codes: a lane's 16 bytes already are its matrix-unit operand).
+__global__ __launch_bounds__(256) void pack_kernel(int E, int N, int K, int half, int pair_rows, int shuffle,
                                                    const uint8_t *__restrict__ src, uint8_t *__restrict__ dst)
 {
     const int G = K / kGroup;
@@ -52,14 +53,14 @@ __global__ __launch_bounds__(256) void pack_kernel(int E, int N, int K, int half
         const uint8_t *s = src + ((long long)e * N + row) * row_bytes + 64 * g + 16 * (l >> 4);
         const u32x4 v = *reinterpret_cast<const u32x4 *>(s);
         *reinterpret_cast<u32x4 *>(dst + u * 16) =
-            u32x4{shuffle_word(v.x), shuffle_word(v.y), shuffle_word(v.z), shuffle_word(v.w)};
+            shuffle ? u32x4{shuffle_word(v.x), shuffle_word(v.y), shuffle_word(v.z), shuffle_word(v.w)} : v;
     }
 }
 
 }  // namespace
 
 hipError_t launch_pack_weights(int E, int N, int K, int half, bool pair_rows, const uint8_t *wq,
-                               uint8_t *wq_tiled, hipStream_t st)
+                               uint8_t *wq_tiled, hipStream_t st, bool shuffle)
 {
     const long long total = (long long)E * N * (K / 2) / 16;
     long long blocks = (total + 255) / 256;
@@ -69,7 +70,7 @@ hipError_t launch_pack_weights(int E, int N, int K, int half, bool pair_rows, co
     if (blocks < 1)
         blocks = 1;
     hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, st, E, N, K, half, pair_rows ? 1 : 0,
-                       wq, wq_tiled);
+                       shuffle ? 1 : 0, wq, wq_tiled);
     return hipGetLastError();
 }
 

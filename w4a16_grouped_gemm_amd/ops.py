@@ -30,7 +30,8 @@ EXPORTED = ["moe_status_str", "moe_w4a16_check_shape", "moe_w4a16_is_supported",
             "moe_permute", "moe_grouped_gemm_w4a16", "moe_finalize", "moe_w4a16_pack_weights",
             "moe_w4a16_dense_gemm", "moe_w4a16_workspace_size_shared", "moe_w4a16_forward_shared",
             "moe_w4a16_set_launch_override", "moe_w4a16_forward_noalloc", "moe_mxfp4_quantize",
-            "moe_grouped_gemm_mxfp4", "moe_w4a4_workspace_size", "moe_w4a4_forward"]
+            "moe_grouped_gemm_mxfp4", "moe_w4a4_workspace_size", "moe_w4a4_forward",
+            "moe_mxfp4_pack_weights"]
 
 
 class MoeShape(ctypes.Structure):
@@ -110,6 +111,8 @@ def load_library(path: str = LIB_PATH):
         lib.moe_w4a4_workspace_size.restype = Z
         lib.moe_w4a4_forward.argtypes = [S, P, P, P, P, P, P, P, P, Z, P]
         lib.moe_w4a4_forward.restype = I
+        lib.moe_mxfp4_pack_weights.argtypes = [S, I, P, P, P]
+        lib.moe_mxfp4_pack_weights.restype = I
         _lib = lib
         return lib
 
@@ -459,10 +462,28 @@ def mxfp4_quantize(x: torch.Tensor, *, stream=None):
     return codes, scales
 
 
+def mxfp4_pack_weights(kind: int, wq: torch.Tensor, *, stream=None) -> torch.Tensor:
+    """Plain -> tiled MXFP4 codes of one weight matrix (same shape and dtype).
+
+    kind: W13_SWIGLU (w13 for the layer / SwiGLU GEMM), W13_RAW or W2."""
+    _need(wq, torch.uint8, "wq")
+    E_loc, N, K2 = wq.shape
+    if kind == W2:
+        H, I = N, 2 * K2
+    else:
+        H, I = 2 * K2, N // 2
+    out = torch.empty_like(wq)
+    sh = make_shape(0, H, I, E_loc, E_loc, 1, group_size=32)
+    _check(load_library().moe_mxfp4_pack_weights(ctypes.byref(sh), int(kind), _ptr(wq), _ptr(out),
+                                                 _stream(stream)))
+    return out
+
+
 def grouped_gemm_mxfp4(kind: int, a_codes: torch.Tensor, a_scales: torch.Tensor, offsets: torch.Tensor,
                        wq: torch.Tensor, ws: torch.Tensor, *, num_tokens: int, top_k: int,
                        a_row_index: torch.Tensor | None = None, out_dtype=torch.bfloat16,
-                       num_experts: int | None = None, out: torch.Tensor | None = None, stream=None):
+                       num_experts: int | None = None, out: torch.Tensor | None = None, stream=None,
+                       weight_layout: int = WEIGHTS_PLAIN):
     """Grouped GEMM on MXFP4 activations and weights; returns c [num_tokens*top_k, cols]."""
     _need(a_codes, torch.uint8, "a_codes")
     _need(a_scales, torch.uint8, "a_scales")
@@ -485,7 +506,8 @@ def grouped_gemm_mxfp4(kind: int, a_codes: torch.Tensor, a_scales: torch.Tensor,
         raise ValueError("out dtype must be bfloat16 or float32")
     if a_row_index is not None:
         _need(a_row_index, torch.int32, "a_row_index")
-    sh = make_shape(num_tokens, H, I, num_experts or E_loc, E_loc, top_k, group_size=32)
+    sh = make_shape(num_tokens, H, I, num_experts or E_loc, E_loc, top_k, group_size=32,
+                    weight_layout=weight_layout)
     _check(load_library().moe_grouped_gemm_mxfp4(ctypes.byref(sh), int(kind), _ptr(a_codes), _ptr(a_scales),
                                                  _ptr(a_row_index), _ptr(offsets), _ptr(wq), _ptr(ws), _ptr(out),
                                                  dt, _stream(stream)))
@@ -494,8 +516,10 @@ def grouped_gemm_mxfp4(kind: int, a_codes: torch.Tensor, a_scales: torch.Tensor,
 
 def moe_w4a4_forward(x: torch.Tensor, router_logits: torch.Tensor, w13_q: torch.Tensor, w13_s: torch.Tensor,
                      w2_q: torch.Tensor, w2_s: torch.Tensor, top_k: int, out: torch.Tensor | None = None,
-                     stream=None, *, expert_begin: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """The W4A4 (MXFP4) MoE expert layer: MXFP4 weights, activations quantized on the fly."""
+                     stream=None, *, expert_begin: int = 0, workspace: torch.Tensor | None = None,
+                     weight_layout: int = WEIGHTS_PLAIN) -> torch.Tensor:
+    """The W4A4 (MXFP4) MoE expert layer: MXFP4 weights, activations quantized on the fly.
+    weight_layout WEIGHTS_TILED: w13_q and w2_q from mxfp4_pack_weights (W13_SWIGLU / W2)."""
     _need(x, torch.bfloat16, "x")
     _need(router_logits, torch.float32, "router_logits")
     for t, n in ((w13_q, "w13_q"), (w13_s, "w13_s"), (w2_q, "w2_q"), (w2_s, "w2_s")):
@@ -506,7 +530,8 @@ def moe_w4a4_forward(x: torch.Tensor, router_logits: torch.Tensor, w13_q: torch.
     if (H2 * 2 != H or w2_q.shape != (E_loc, H, I // 2) or w13_s.shape != (E_loc, 2 * I, H // 32)
             or w2_s.shape != (E_loc, H, I // 32)):
         raise ValueError("MXFP4 weight shapes do not match x")
-    sh = make_shape(T, H, I, router_logits.shape[1], E_loc, top_k, expert_begin, group_size=32)
+    sh = make_shape(T, H, I, router_logits.shape[1], E_loc, top_k, expert_begin, group_size=32,
+                    weight_layout=weight_layout)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     lib = load_library()
