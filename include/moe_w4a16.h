@@ -404,6 +404,9 @@ typedef struct {
                                             (routing inside the gate/up GEMM; 0: never) */
     int32_t decode_combine_max_tokens;   /* small-batch path: down GEMM and combine in one
                                             launch up to this T (0: never)              */
+    int32_t perm_in_gemm_max_tokens;     /* general path: the gate/up GEMM builds the
+                                            permutation from the routing ids up to this T
+                                            (no permutation launch; 0: never)           */
 } moe_launch_override;
 
 moe_status moe_w4a16_set_launch_override(const moe_launch_override *ov);

@@ -145,6 +145,33 @@ def test_forward_equals_the_entry_points_composed(wl, T):
     assert np.array_equal(_forward(inp), to_np_u16(composed))
 
 
+# (workload, T): the general path where the gate/up GEMM builds the
+# permutation from the routing ids itself, against the permutation launch
+# (routing inside it up to 32 tokens, T = 20 and 24 here): the largest T it
+# takes, token counts that are not a multiple of 32 (partial bitmap words),
+# slots of non-local experts (EP shard), top-2 of 8 experts (one and two
+# tiles per wave), top-16 (k16_e64), two subtiles per chunk (256 and 512)
+PERM_IN_GEMM = [("qwen3_decode", 20), ("qwen3_decode", 33), ("qwen3_decode", 100), ("qwen3_decode", 256),
+                ("qwen3_decode", 512), ("ep_shard_decode", 24), ("ep_shard_decode", 64), ("ep_shard_decode", 256),
+                ("tiny", 200), ("k16_e64", 40)]
+
+
+@pytest.mark.parametrize("wl,T", PERM_IN_GEMM)
+def test_permutation_in_gemm_equals_separate_permutation(wl, T):
+    # the layer with the permutation built inside the gate/up GEMM against
+    # the layer with the separate permutation launch: bit for bit (the down
+    # GEMM and the finalize read the tables the GEMM stored)
+    from w4a16_grouped_gemm_amd import ops
+    say(f"permutation in gemm {wl} T={T}")
+    inp = _small_inputs(wl, T)
+    with ops.launch_override(perm_in_gemm_max_tokens=4096):
+        fused = _forward(inp)
+    with ops.launch_override(perm_in_gemm_max_tokens=0):
+        separate = _forward(inp)
+    assert np.array_equal(fused, separate)
+    assert np.any(fused != 0)
+
+
 @pytest.mark.parametrize("wl,T", [("tiny", 16), ("qwen3_decode", 16), ("qwen3_decode", 64)])
 def test_masked_experts(wl, T):
     # router logits of -inf (masked experts), and tokens with fewer finite

@@ -102,6 +102,17 @@ hipError_t launch_route_permute(const moe_shape &sh, const float *logits, int32_
 hipError_t launch_gather(const moe_shape &sh, const uint16_t *x, const int32_t *perm,
                          const int32_t *offsets, uint16_t *x_perm, hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st);
+// The layer's gate/up GEMM with the permutation built inside it from the
+// routing ids (no permutation launch): g as for launch_grouped_gemm with
+// a_row_index unused; the permutation's tables (as moe_permute stores them)
+// go to the IdsSource outputs.
+struct IdsSource {
+    const int32_t *ids;       // [T*k] global expert ids
+    int T, begin;             // tokens; global id of local expert 0
+    int32_t *counts, *offsets, *perm, *inv_perm;
+};
+bool gemm_ids_supported(const GemmLaunch &g, int T);
+hipError_t launch_gemm_ids(const GemmLaunch &g, const IdsSource &src, hipStream_t st);
 hipError_t launch_pack_weights(int E, int N, int K, int half, bool pair_rows, const uint8_t *wq,
                                uint8_t *wq_tiled, hipStream_t st, bool shuffle = true);
 hipError_t launch_finalize(const moe_shape &sh, const void *y, bool y_f32, const float *w,

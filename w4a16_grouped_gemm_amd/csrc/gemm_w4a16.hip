@@ -96,12 +96,15 @@ struct GemmArgs {
     int32_t *ids;         // per slot t*k+j: global expert id (SRC_ROUTE writes, SRC_SLOTS reads)
     float *wts;           // SRC_ROUTE writes the routing weights
     int32_t *pres;        // per slot: the slot index if its expert is local, else -1
+    // SRC_IDS: the permutation's tables, stored by workgroup 0 as moe_permute would
+    int32_t *cnt_out, *off_out, *perm_out, *inv_out;
 };
 
 // Item sources of the streaming kernel: the chunk prefix over `offsets`
-// (the grouped GEMM), or the small-batch layer's slot table, built by
-// routing inside the kernel (gate/up) or read from the stored table (down).
-enum { SRC_OFFSETS = 0, SRC_ROUTE = 1, SRC_SLOTS = 2 };
+// (the grouped GEMM), the small-batch layer's slot table, built by routing
+// inside the kernel (gate/up) or read from the stored table (down), or the
+// layer's permutation built from the routing ids inside the kernel (gate/up).
+enum { SRC_OFFSETS = 0, SRC_ROUTE = 1, SRC_SLOTS = 2, SRC_IDS = 3 };
 
 // Lane offset of a tile's codes and the byte step from one group to the next.
 __device__ __forceinline__ uint32_t code_offset(const GemmArgs &p, int tile, uint32_t row, int G, uint32_t row_bytes,
@@ -183,6 +186,118 @@ __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx4 v, int til
 }
 
 // ---------------------------------------------------------------------------
+// SRC_IDS: the layer's stable expert permutation (moe_permute's result) built
+// by every workgroup in LDS from the routing ids, so that the gate/up GEMM
+// needs no permutation launch before it (InfiniLM PR #500 report, section
+// 2.2: counts, offsets and a permutation from the routing ids). A token's k
+// experts are distinct, so the rows of local expert e are its slots in token
+// order: row(slot s of token t) = offsets[e] + #{tokens t' < t routed to e},
+// counted from per-expert token bitmaps. Fills s_off / s_prefix as
+// build_chunk_prefix does from `offsets`, and s_row[r] = slot of row r;
+// workgroup 0 also stores counts, offsets, perm and inv_perm (-1 for a slot
+// whose expert is not local). The bitmaps and word prefixes are scratch
+// (dead after the last barrier). Needs E <= NT and T * k <= kIdsPerThread * NT.
+// ---------------------------------------------------------------------------
+constexpr int kIdsPerThread = 16;                 // slots per thread: T * k <= 16 * 256
+
+template <int NT>
+__device__ void build_from_ids(const GemmArgs &p, int CS, uint32_t *s_bits, int *s_wpre, uint16_t *s_row,
+                               int *s_prefix, int *s_off, int *s_wtot)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = p.num_experts, k = p.top_k;
+    const int S = p.T * k, words = (p.T + 31) >> 5;
+    const bool store = blockIdx.x == 0;
+    // every id load of the thread goes out before the first is used (one
+    // memory round trip; slots past S read out of range, as zeros)
+    const __amdgpu_buffer_rsrc_t rids = make_rsrc(p.ids, (uint32_t)S * 4u);
+    int le[kIdsPerThread], tk[kIdsPerThread];          // local expert (-1: none) and token of each slot
+#pragma unroll
+    for (int j = 0; j < kIdsPerThread; ++j)
+        le[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rids, (uint32_t)(tid + j * NT) * 4u, 0, 0);
+    for (int i = tid; i < E * words; i += NT)
+        s_bits[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kIdsPerThread; ++j) {
+        const int s = tid + j * NT;
+        const int e = le[j] - p.begin;
+        le[j] = (s < S && e >= 0 && e < E) ? e : -1;
+        tk[j] = s / k;
+        if (le[j] >= 0)
+            atomicOr(&s_bits[le[j] * words + (tk[j] >> 5)], 1u << (tk[j] & 31));
+    }
+    __syncthreads();
+    // thread e: its row count and word prefixes, then one scan over the
+    // experts of (rows, chunks of CS rows)
+    int cnt = 0, ch = 0;
+    if (tid < E) {
+        for (int w = 0; w < words; ++w) {
+            s_wpre[tid * words + w] = cnt;
+            cnt += __popc(s_bits[tid * words + w]);
+        }
+        ch = (cnt + CS - 1) / CS;
+    }
+    int tc, tch;
+    const int xc = wave_exclusive_scan(cnt, tc);
+    const int xch = wave_exclusive_scan(ch, tch);
+    if (lane == 0) {
+        s_wtot[wave] = tc;
+        s_wtot[NT / 64 + wave] = tch;
+    }
+    __syncthreads();
+    int bc = 0, bch = 0, ac = 0, ach = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        bc += w < wave ? s_wtot[w] : 0;
+        bch += w < wave ? s_wtot[NT / 64 + w] : 0;
+        ac += s_wtot[w];
+        ach += s_wtot[NT / 64 + w];
+    }
+    if (tid < E) {
+        s_off[tid] = bc + xc;
+        s_prefix[tid] = bch + xch;
+        if (store) {
+            p.cnt_out[tid] = cnt;
+            p.off_out[tid] = bc + xc;
+        }
+    }
+    if (tid == 0) {
+        s_off[E] = ac;
+        s_prefix[E] = ach;
+        if (store)
+            p.off_out[E] = ac;
+    }
+    __syncthreads();
+    // the row of every slot first (LDS reads only, all independent), then the stores
+    int row[kIdsPerThread];
+#pragma unroll
+    for (int j = 0; j < kIdsPerThread; ++j) {
+        const int e = le[j] >= 0 ? le[j] : 0, w = le[j] >= 0 ? tk[j] >> 5 : 0;
+        const uint32_t below = s_bits[e * words + w] & ((1u << (tk[j] & 31)) - 1u);
+        row[j] = s_off[e] + s_wpre[e * words + w] + __popc(below);
+    }
+#pragma unroll
+    for (int j = 0; j < kIdsPerThread; ++j) {
+        const int s = tid + j * NT;
+        if (le[j] >= 0) {
+            s_row[row[j]] = (uint16_t)s;
+            if (store)
+                p.perm_out[row[j]] = s;
+        }
+        if (store && s < S)
+            p.inv_out[s] = le[j] >= 0 ? row[j] : -1;
+    }
+    __syncthreads();
+}
+
+// SRC_IDS scratch inside the activation buffers (bitmaps, word prefixes).
+constexpr size_t ids_scratch_bytes(int E, int T)
+{
+    return (size_t)E * ((T + 31) / 32) * 8;
+}
+
+// ---------------------------------------------------------------------------
 // gemm_stream_kernel
 //
 // No load sits under a branch: tiles past N never occur (the host launches
@@ -210,7 +325,8 @@ __device__ __forceinline__ int act_slot(int step, int lane)
 template <int KIND, int TPW, int NSUB, int KSEG, int RING, bool NT, int SRC = SRC_OFFSETS, int PL = 8>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
 {
-    static_assert(SRC == SRC_OFFSETS || NSUB == 1, "small-batch items hold at most 16 rows");
+    static_assert(SRC == SRC_OFFSETS || SRC == SRC_IDS || NSUB == 1, "small-batch items hold at most 16 rows");
+    constexpr bool CHUNKED = SRC == SRC_OFFSETS || SRC == SRC_IDS;   // items from the chunk prefix
     static_assert((2 * KSEG) % RING == 0, "the weight ring slot of group g is g % RING, static per segment parity");
     static_assert(KSEG == 1 || KSEG % 2 == 0, "scales are loaded as dwords of two groups");
     constexpr int SD = (KSEG + 1) / 2;                 // scale dwords per tile and segment
@@ -229,6 +345,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
     int *s_lead = s_loc + kDecMaxSlots;
     int *s_nlead = s_lead + kDecMaxSlots;
     int *s_first = s_nlead + 4;
+    // SRC_IDS: slot of each permuted row, after the scan scratch (2 x 4 ints)
+    uint16_t *s_row = reinterpret_cast<uint16_t *>(s_wtot + 8);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -241,6 +359,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
     int total_items;
     if constexpr (SRC == SRC_OFFSETS) {
         build_chunk_prefix<256>(p.offsets, p.dense_rows, E, CS, s_prefix, s_wtot, s_off);
+        total_items = s_prefix[E] * nblocks;
+    } else if constexpr (SRC == SRC_IDS) {
+        uint32_t *s_bits = reinterpret_cast<uint32_t *>(s_dyn);
+        const int words = (p.T + 31) >> 5;
+        int *s_wpre = reinterpret_cast<int *>(s_bits + E * words);
+        build_from_ids<256>(p, CS, s_bits, s_wpre, s_row, s_prefix, s_off, s_wtot);
         total_items = s_prefix[E] * nblocks;
     } else {
         for (int e = tid; e < E; e += 256)
@@ -312,7 +436,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         const int block = item - chunk * nblocks;
         int e, row0, nvalid;
         uint64_t m0 = 0, m1 = 0;                          // small batch: the expert's slots
-        if constexpr (SRC == SRC_OFFSETS) {
+        if constexpr (CHUNKED) {
             e = uniform(chunk_expert(s_prefix, E, chunk));
             row0 = uniform(s_off[e] + (chunk - s_prefix[e]) * CS);
             nvalid = uniform(min(CS, s_off[e + 1] - row0));
@@ -339,7 +463,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         // epilogue, read now (no load under a branch; zeros when unused);
         // small batch: that row's slot
         int32_t c_row;
-        if constexpr (SRC == SRC_OFFSETS)
+        if constexpr (CHUNKED)
             c_row = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(row0 + min(epi_m, nvalid - 1)) * 4u,
                                                                   0, 0);
         else
@@ -352,6 +476,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
             if constexpr (SRC == SRC_OFFSETS) {
                 const int r = row0 + min(m, nvalid - 1);   // always a valid row: no branch around the load
                 src = p.a_row_index ? (uint32_t)(p.a_row_index[r] / p.top_k) : (uint32_t)r;
+            } else if constexpr (SRC == SRC_IDS) {
+                src = (uint32_t)(s_row[row0 + min(m, nvalid - 1)] / p.top_k);   // the row's token
             } else {
                 // row m of the expert is its m-th slot: gate/up reads that
                 // slot's token, down reads the slot's own h row
@@ -516,7 +642,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
                 const int m = sb * 16 + rr;
                 if (b < NBLK && sb < nsub && m < nvalid) {
                     const u32x4 d = *reinterpret_cast<const u32x4 *>(so + (b * 16 + rr) * COLS + part * 8);
-                    const int orow = SRC != SRC_OFFSETS ? c_row
+                    const int orow = !CHUNKED ? c_row
                                      : !p.c_row_index ? row0 + m : (EPI_ONE_ROW ? c_row : p.c_row_index[row0 + m]);
                     *reinterpret_cast<u32x4 *>(c + (size_t)orow * p.ldc + (tile0 + t) * COLS + part * 8) = d;
                 }
@@ -1154,14 +1280,16 @@ hipError_t launch_stream(const GemmArgs &a, int max_rows, hipStream_t st)
     constexpr int CS = 16 * NSUB;
     auto kernel = gemm_stream_kernel<KIND, TPW, NSUB, KSEG, RING, NT, SRC, PL>;
     const size_t tables = SRC == SRC_OFFSETS ? sizeof(int) * (2 * (a.num_experts + 1) + 4)
+                          : SRC == SRC_IDS   ? sizeof(int) * (2 * (a.num_experts + 1) + 8) + 2 * (size_t)a.T * a.top_k
                                              : sizeof(int) * (2 * kDecMaxSlots + 4 + a.num_experts);
     const size_t lds = stream_act_bytes<NSUB, KSEG>() + tables;
     const int per_cu = resident_per_cu(kernel, lds);
     // persistent grid: at most the resident slots, at most the item bound
     // (small batch: at most one item per slot and block)
     const int nblocks = (a.N >> 4) / (4 * TPW);
-    const long long chunks = SRC != SRC_OFFSETS ? (long long)min(a.num_experts, max_rows)
-                                                : (long long)min(a.num_experts, max_rows) + max_rows / CS;
+    const long long chunks = (SRC == SRC_ROUTE || SRC == SRC_SLOTS)
+                                 ? (long long)min(a.num_experts, max_rows)
+                                 : (long long)min(a.num_experts, max_rows) + max_rows / CS;
     long long grid = grid_for(chunks * nblocks, per_cu);
     if (grid >= kXcds)
         grid -= grid % kXcds;                          // whole XCD shares (see the kernel)
@@ -1439,6 +1567,59 @@ hipError_t launch_decode_stream(const GemmLaunch &g, const DecodeSource &d, hipS
 #undef MOE_DEC_STREAM
     return hipErrorInvalidValue;
 }
+
+// The layer's gate/up GEMM on the streaming kernel with the permutation
+// built inside it from the routing ids (SRC_IDS); the GEMM is the one
+// launch_grouped_gemm runs for g (same tiling, same bits), and workgroup 0
+// stores the permutation's tables for the down GEMM and the finalize.
+#define MOE_IDS_STREAM_LIST(X) X(4, 1, 4, 2) X(4, 2, 4, 2) X(4, 1, 8, 4) X(4, 1, 4, 4) X(4, 1, 2, 2) \
+    X(4, 2, 2, 2) X(2, 1, 4, 2) X(2, 2, 4, 2) X(2, 1, 8, 4) X(2, 1, 2, 2) X(2, 2, 2, 2) X(1, 1, 2, 2)  \
+    X(1, 1, 4, 2) X(1, 2, 2, 2)
+
+static bool ids_instance(const LaunchChoice &c)
+{
+#define MOE_IDS_HAS(T_, S_, B_, R_) if (c.tpw == T_ && c.nsub == S_ && c.kseg == B_ && c.ring == R_) return true;
+    MOE_IDS_STREAM_LIST(MOE_IDS_HAS)
+#undef MOE_IDS_HAS
+    return false;
+}
+
+bool gemm_ids_supported(const GemmLaunch &g, int T)
+{
+    if (g.kind != MOE_GEMM_W13_SWIGLU || g.wq_sh || g.c_f32 || g.num_experts > 256 || g.offsets == nullptr)
+        return false;
+    const LaunchChoice c = choose_launch(g);
+    if (c.mode != 1 || !ids_instance(c) || g.max_rows > kIdsPerThread * 256)
+        return false;
+    // the bitmaps, word prefixes and local ids fit the activation buffers
+    const size_t act = sizeof(u32x4) * 2 * c.kseg * c.nsub * 4 * 64;
+    return ids_scratch_bytes(g.num_experts, T) <= act;
+}
+
+hipError_t launch_gemm_ids(const GemmLaunch &g, const IdsSource &src, hipStream_t st)
+{
+    if (!gemm_ids_supported(g, src.T))
+        return hipErrorInvalidValue;
+    GemmArgs a = make_args(g);
+    a.a_row_index = nullptr;
+    a.a_row_bytes = 0;
+    a.ids = const_cast<int32_t *>(src.ids);
+    a.T = src.T;
+    a.begin = src.begin;
+    a.cnt_out = src.counts;
+    a.off_out = src.offsets;
+    a.perm_out = src.perm;
+    a.inv_out = src.inv_perm;
+    const LaunchChoice c = choose_launch(g);
+#define MOE_IDS_LAUNCH(T_, S_, B_, R_)                                                                 \
+    if (c.tpw == T_ && c.nsub == S_ && c.kseg == B_ && c.ring == R_)                                 \
+        return c.nt ? launch_stream<MOE_GEMM_W13_SWIGLU, T_, S_, B_, R_, true, SRC_IDS>(a, g.max_rows, st) \
+                    : launch_stream<MOE_GEMM_W13_SWIGLU, T_, S_, B_, R_, false, SRC_IDS>(a, g.max_rows, st);
+    MOE_IDS_STREAM_LIST(MOE_IDS_LAUNCH)
+#undef MOE_IDS_LAUNCH
+    return hipErrorInvalidValue;
+}
+#undef MOE_IDS_STREAM_LIST
 
 // Whether launch_decode_stream has an instance for this GEMM.
 bool decode_stream_supported(const GemmLaunch &g)

@@ -46,7 +46,7 @@ class LaunchOverride(ctypes.Structure):
                 ("gemm_subtiles", ctypes.c_int32), ("gemm_kseg", ctypes.c_int32), ("gemm_ring", ctypes.c_int32),
                 ("gemm_nontemporal", ctypes.c_int32), ("permute_parallel_min_tokens", ctypes.c_int32),
                 ("route_fuse_max_tokens", ctypes.c_int32), ("decode_max_tokens", ctypes.c_int32),
-                ("decode_combine_max_tokens", ctypes.c_int32)]
+                ("decode_combine_max_tokens", ctypes.c_int32), ("perm_in_gemm_max_tokens", ctypes.c_int32)]
 
 
 class MoeError(ValueError):
