@@ -174,7 +174,12 @@ def test_w4a4_layer_matches_oracle(wl, T, n):
         assert_layer_close(got[keep], ref["out"][keep], f"w4a4 {wl} T={T}")
 
 
-@pytest.mark.parametrize("wl,T", [("qwen3_decode", 16), ("ep_shard_decode", 64)])
+# the forward quantizes x inside its routing launch (the fused route +
+# permutation up to 32 tokens, the routing kernel past that) and h inside the
+# gate/up GEMM's epilogue where that GEMM stages activations in LDS (K <=
+# 2048), else with the quantize kernel after it (the EP shard's K = 7168)
+@pytest.mark.parametrize("wl,T", [("qwen3_decode", 1), ("qwen3_decode", 16), ("qwen3_decode", 256), ("tiny", 40),
+                                  ("ep_shard_decode", 16), ("ep_shard_decode", 64)])
 def test_w4a4_forward_equals_entry_points_composed(wl, T):
     import torch
     from w4a16_grouped_gemm_amd import ops

@@ -713,15 +713,15 @@ moe_status moe_w4a4_forward(const moe_shape *shape, const uint16_t *x, const flo
     const Workspace &ws = mw.base;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
+    // x is quantized by the routing launch (the quantize kernel's bits)
     if (route_permute_fusable(sh)) {
-        e = launch_route_permute(sh, router_logits, ws.ids, ws.w, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s, 0);
+        e = launch_route_permute(sh, router_logits, ws.ids, ws.w, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s, 0,
+                                 x, mw.xq, mw.xs);
     } else {
-        e = launch_route(sh, router_logits, ws.ids, ws.w, s);
+        e = launch_route(sh, router_logits, ws.ids, ws.w, s, x, mw.xq, mw.xs);
         if (e == hipSuccess)
             e = launch_permute(sh, ws.ids, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s, 0, ws.part);
     }
-    if (e == hipSuccess)
-        e = launch_mx_quantize(sh.num_tokens, sh.hidden, x, mw.xq, mw.xs, nullptr, s);
     const int S = sh.num_tokens * sh.top_k;
     if (e == hipSuccess) {
         const GemmLaunch g0 = layer_gemm_args(sh, MOE_GEMM_W13_SWIGLU);
@@ -742,11 +742,12 @@ moe_status moe_w4a4_forward(const moe_shape *shape, const uint16_t *x, const flo
         g.max_rows = g0.max_rows;
         g.expected_rows = g0.expected_rows;
         g.w_tiled = sh.weight_layout == MOE_WEIGHTS_TILED;
+        // h requantized (only the R routed rows, R = offsets[E_loc] on the
+        // device): in the GEMM's epilogue, or by the quantize kernel after it
+        g.cq = mw.hq;
+        g.cs = mw.hs;
         e = launch_mx_grouped_gemm(g, s);
     }
-    // requantize h: only the R routed rows (R = offsets[E_loc], read on the device)
-    if (e == hipSuccess)
-        e = launch_mx_quantize(S, sh.inter, ws.h, mw.hq, mw.hs, ws.offsets + sh.num_local_experts, s);
     const bool y_slot = sh.num_local_experts == sh.num_experts;
     if (e == hipSuccess) {
         const GemmLaunch g0 = layer_gemm_args(sh, MOE_GEMM_W2);

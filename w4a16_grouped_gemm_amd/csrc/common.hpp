@@ -86,8 +86,11 @@ struct GemmLaunch {
     bool w_tiled;             // codes in the tiled layout (1 KiB per tile and group)
 };
 
+// x non-NULL (the W4A4 layer): the launch also quantizes x [T][H] to MXFP4
+// codes xq [T][H/2] and scales xs [T][H/32] (the quantize kernel's bits)
 hipError_t launch_route(const moe_shape &sh, const float *logits, int32_t *ids, float *w,
-                        hipStream_t st);
+                        hipStream_t st, const uint16_t *x = nullptr, uint8_t *xq = nullptr,
+                        uint8_t *xs = nullptr);
 // part: workspace of permute_workspace_bytes(sh) (the per-range counts of
 // the parallel path for many tokens; NULL when that size is 0)
 hipError_t launch_permute(const moe_shape &sh, const int32_t *ids, int32_t *counts,
@@ -98,7 +101,8 @@ bool route_permute_fusable(const moe_shape &sh);
 hipError_t launch_route_permute(const moe_shape &sh, const float *logits, int32_t *ids, float *w,
                                 int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
                                 hipStream_t st,
-                                int num_shared = 0);
+                                int num_shared = 0, const uint16_t *x = nullptr, uint8_t *xq = nullptr,
+                                uint8_t *xs = nullptr);
 hipError_t launch_gather(const moe_shape &sh, const uint16_t *x, const int32_t *perm,
                          const int32_t *offsets, uint16_t *x_perm, hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st);
@@ -176,6 +180,10 @@ struct MxGemmLaunch {
     int K, N;
     int max_rows, expected_rows;
     bool w_tiled;                // codes in the tiled layout (scales plain)
+    // SwiGLU only, non-NULL: h also stored requantized to MXFP4 ([max_rows][N/4]
+    // codes, [max_rows][N/64] scales; the routed rows, counted on the device);
+    // c is then scratch for bf16 h
+    uint8_t *cq, *cs;
 };
 hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st);
 // rows_dev (nullable): the device-side row count to quantize (at most rows)

@@ -45,6 +45,7 @@
 //    the even code and saturation at 6, by comparisons against the midpoints
 //    (exact in binary32: the division by a power of two is exact).
 #include "gemm_core.hpp"
+#include "mx_quant.hpp"
 
 #include <map>
 #include <mutex>
@@ -69,6 +70,7 @@ struct MxArgs {
     uint32_t c_row_bytes;
     int top_k, num_experts, K, N, ldc, half, c_f32;
     int w_tiled;                 // codes tiled: tile t, group g at ((t/8)*G*8 + t%8)*1 KiB + g*8 KiB
+    uint8_t *cq, *cs;            // non-NULL (SwiGLU, LDS kernel): h stored as MXFP4 codes and scales
 };
 
 // Lane offset of tile `tile`'s codes (row `row` of the plain layout) and the
@@ -144,6 +146,62 @@ __device__ __forceinline__ void mx_store(const MxArgs &p, const floatx4 (&acc)[T
                     }
                 }
             }
+        }
+    }
+}
+
+// SwiGLU epilogue that stores h already requantized (the down GEMM's MXFP4
+// activations): the item's bf16 h values, rounded as mx_store rounds them, go
+// to an LDS tile of CS rows x 32 TPW features (s_h, over the staged
+// activations), then each thread quantizes one row's block of 32 features
+// with the shared block quantizer and stores its 16 code bytes and scale
+// byte: the same bits as storing bf16 h and quantizing it afterwards.
+template <int TPW, int NSUB>
+__host__ __device__ constexpr int mx_h_stride() { return 32 * TPW + 8; }   // bf16 elements per LDS row
+
+template <int TPW, int NSUB>
+__device__ __forceinline__ void mx_store_quant(const MxArgs &p, const floatx4 (&acc)[TPW][NSUB], int block, int row0,
+                                               int nvalid, int nsub, int n16, int kq, int wave, int tid,
+                                               uint16_t *s_h)
+{
+    constexpr int CS = 16 * NSUB, HST = mx_h_stride<TPW, NSUB>();
+    __syncthreads();                                   // every wave is done with the staged activations
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+        if (sb >= nsub)
+            break;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const floatx4 v = acc[t][sb];
+            const float rr[4] = {v.x, v.y, v.z, v.w};
+            float u[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                u[i] = __shfl_xor(rr[i], 8, 64);       // partner lane holds the up row
+            if (n16 < 8) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    s_h[(sb * 16 + kq * 4 + i) * HST + (wave * TPW + t) * 8 + n16] =
+                        (uint16_t)f32_to_bf16_rne(silu(rr[i]) * u[i]);
+            }
+        }
+    }
+    __syncthreads();
+    const int ldq = p.ldc >> 1, lds_ = p.ldc >> 5;     // bytes per h row: codes, scales
+    for (int q = tid; q < CS * TPW; q += 256) {
+        const int r = q / TPW, b = q - r * TPW;
+        if (r < nvalid) {
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(s_h + r * HST + b * 32);
+            uint32_t w[16];
+#pragma unroll
+            for (int d = 0; d < 16; ++d)
+                w[d] = src[d];
+            uint32_t out[4];
+            const uint32_t sc = mx_quant_block(w, out);
+            const int orow = p.c_row_index ? p.c_row_index[row0 + r] : row0 + r;
+            const int f0 = block * 32 * TPW + b * 32;  // first feature of the block
+            *reinterpret_cast<u32x4 *>(p.cq + (size_t)orow * ldq + (f0 >> 1)) = u32x4{out[0], out[1], out[2], out[3]};
+            p.cs[(size_t)orow * lds_ + (f0 >> 5)] = (uint8_t)sc;
         }
     }
 }
@@ -416,16 +474,12 @@ __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
                 }
             }
         }
-        mx_store<KIND, TPW, NSUB>(p, acc, tile0, row0, nvalid, nsub, n16, kq);
+        if (KIND == MOE_GEMM_W13_SWIGLU && p.cq)
+            mx_store_quant<TPW, NSUB>(p, acc, block, row0, nvalid, nsub, n16, kq, wave, tid,
+                                      reinterpret_cast<uint16_t *>(s_a));
+        else
+            mx_store<KIND, TPW, NSUB>(p, acc, tile0, row0, nvalid, nsub, n16, kq);
     }
-}
-
-// E2M1 code of |p| (p already divided by the block scale): nearest of 0, 0.5,
-// 1, 1.5, 2, 3, 4, 6; a midpoint goes to the even code; past 6 stays at 6.
-__device__ __forceinline__ uint32_t e2m1_code(float m)
-{
-    return m <= 0.25f ? 0u : m < 0.75f ? 1u : m <= 1.25f ? 2u : m < 1.75f ? 3u
-         : m <= 2.5f ? 4u : m < 3.5f ? 5u : m <= 5.0f ? 6u : 7u;
 }
 
 // rows x (K/32) blocks; `rows_dev` (nullable) bounds the rows on the device.
@@ -448,39 +502,8 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(long long rows, int K,
             w[4 * q + 2] = d.z;
             w[4 * q + 3] = d.w;
         }
-        // the block maximum on the magnitude bits (bf16 orders like its magnitude)
-        uint32_t amax = 0;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const uint32_t lo = w[q] & 0x7FFFu, hi = (w[q] >> 16) & 0x7FFFu;
-            amax = lo > amax ? lo : amax;
-            amax = hi > amax ? hi : amax;
-        }
-        int ex = -127;
-        if (amax != 0) {
-            const int bexp = (int)(amax >> 7);              // biased exponent of the bf16 maximum
-            const int fl = bexp > 0 ? bexp - 127 : -133 + (31 - __builtin_clz(amax & 0x7Fu));   // floor(log2)
-            ex = fl - 2;
-            ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
-        }
-        scales[i] = (uint8_t)(ex + 127);
-        // 2^-ex as a binary32 power of two: a finite bf16 maximum is below
-        // 2^128, so ex <= 125 and 2^-ex is a normal number (exponent field
-        // 127 - ex in [2, 254]); |v| * 2^-ex is then exact or, far below the
-        // first midpoint 0.25, rounds harmlessly
-        const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);
-        uint32_t out[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-#pragma unroll
-            for (int hlf = 0; hlf < 2; ++hlf) {
-                const uint32_t b = hlf ? (w[q] >> 16) : (w[q] & 0xFFFFu);
-                const float v = __uint_as_float(b << 16);
-                const uint32_t code = e2m1_code(fabsf(v) * inv) | ((b >> 12) & 8u);
-                const int k = 2 * q + hlf;                 // element of the block
-                out[k >> 3] |= code << (4 * (k & 7));
-            }
-        }
+        uint32_t out[4];
+        scales[i] = (uint8_t)mx_quant_block(w, out);
         *reinterpret_cast<u32x4 *>(codes + i * 16) = u32x4{out[0], out[1], out[2], out[3]};
     }
 }
@@ -522,13 +545,30 @@ hipError_t mx_launch(const MxArgs &a, int max_rows, hipStream_t st)
 
 // The LDS-staged kernel when the whole K of a chunk fits (K <= 2048, the
 // one-load weight scales), else the register-streaming one.
+template <int TPW, int NSUB>
+size_t mx_lds_bytes(int K, int num_experts)
+{
+    constexpr int CS = 16 * NSUB;
+    size_t stage = (size_t)CS * (mx_code_stride(K) + mx_scale_stride(K) + 4);
+    const size_t h = (size_t)CS * mx_h_stride<TPW, NSUB>() * 2;    // the requantizing epilogue's tile
+    stage = stage > h ? stage : h;
+    return stage + sizeof(int) * (num_experts + 1 + 4);
+}
+
+// Whether the LDS-staged kernel takes the launch (K <= 2048, the one-load
+// weight scales, and its LDS).
+template <int TPW, int NSUB>
+bool mx_lds_fits(int K, int num_experts)
+{
+    return K <= 2048 && mx_lds_bytes<TPW, NSUB>(K, num_experts) <= 150 * 1024;
+}
+
 template <int KIND, int TPW, int NSUB, int RING>
 hipError_t mx_launch_any(const MxArgs &a, int max_rows, hipStream_t st)
 {
     constexpr int CS = 16 * NSUB;
-    const size_t lds = (size_t)CS * (mx_code_stride(a.K) + mx_scale_stride(a.K) + 4) +
-                       sizeof(int) * (a.num_experts + 1 + 4);
-    if (a.K > 2048 || lds > 150 * 1024)
+    const size_t lds = mx_lds_bytes<TPW, NSUB>(a.K, a.num_experts);
+    if (!mx_lds_fits<TPW, NSUB>(a.K, a.num_experts))
         return mx_launch<KIND, TPW, NSUB, RING>(a, max_rows, st);
     auto kernel = mx_gemm_lds_kernel<KIND, TPW, NSUB, RING>;
     static std::once_flag once;
@@ -585,6 +625,8 @@ hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st)
     a.ldc = g.kind == MOE_GEMM_W13_SWIGLU ? g.N / 2 : g.N;
     a.c_f32 = g.c_f32 ? 1 : 0;
     a.w_tiled = g.w_tiled ? 1 : 0;
+    a.cq = g.kind == MOE_GEMM_W13_SWIGLU ? g.cq : nullptr;
+    a.cs = g.kind == MOE_GEMM_W13_SWIGLU ? g.cs : nullptr;
     // rows per active expert under uniform routing: one subtile for decode,
     // four (64-row chunks) once experts hold many rows; tiles per wave from
     // how many items the grid gets
@@ -604,8 +646,22 @@ hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st)
         return hipErrorInvalidValue;                   // N is a multiple of 128: 4 waves x 2 tiles always divide
     auto go = [&](auto kindc) -> hipError_t {
         constexpr int KIND = decltype(kindc)::value;
-#define MOE_MX(TP, NS) \
-        if (tpw == TP && nsub == NS) return mx_launch_any<KIND, TP, NS, (NS == 4 ? 2 : 4)>(a, g.max_rows, st);
+        // h requantized in the epilogue where the LDS kernel runs; otherwise
+        // bf16 h, then the quantize kernel over the routed rows (same bits)
+#define MOE_MX(TP, NS)                                                                                      \
+        if (tpw == TP && nsub == NS) {                                                                      \
+            if (a.cq && !mx_lds_fits<TP, NS>(a.K, a.num_experts)) {                                        \
+                MxArgs b = a;                                                                               \
+                b.cq = nullptr;                                                                             \
+                b.cs = nullptr;                                                                             \
+                const hipError_t e = mx_launch_any<KIND, TP, NS, (NS == 4 ? 2 : 4)>(b, g.max_rows, st);    \
+                if (e != hipSuccess)                                                                        \
+                    return e;                                                                               \
+                return launch_mx_quantize(g.max_rows, a.ldc, static_cast<const uint16_t *>(a.c), a.cq, a.cs, \
+                                          g.offsets + g.num_experts, st);                                   \
+            }                                                                                               \
+            return mx_launch_any<KIND, TP, NS, (NS == 4 ? 2 : 4)>(a, g.max_rows, st);                       \
+        }
         MOE_MX(1, 1) MOE_MX(2, 1) MOE_MX(4, 1) MOE_MX(1, 2) MOE_MX(2, 2) MOE_MX(4, 2) MOE_MX(1, 4) MOE_MX(2, 4)
         MOE_MX(4, 4)
 #undef MOE_MX

@@ -13,6 +13,7 @@
 // copy only the valid rows, with wide vectors; rows are 16-byte aligned here
 // because H is a multiple of 128.
 #include "common.hpp"
+#include "mx_quant.hpp"
 #include "route_core.hpp"
 
 #include <mutex>
@@ -37,14 +38,18 @@ constexpr size_t kDynLdsMax = 144 * 1024; // dynamic LDS of one launch: bitmaps 
 // permutation (b = blockIdx.x); bases[b'*E + e] holds the slots of expert e
 // in each range b' (permute_hist_kernel), from which every workgroup forms
 // its own first rows (the parallel path for many tokens).
-template <bool IDS_IN_LDS, bool ROUTE = false, int TL = 16, int PL = 8>
+// QX (with ROUTE; the W4A4 layer): the workgroup also quantizes x [T][H]
+// to MXFP4 (xq, xs); each thread's first blocks are loaded before routing.
+template <bool IDS_IN_LDS, bool ROUTE = false, int TL = 16, int PL = 8, bool QX = false>
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int T, int k, int begin, int E, const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm,
     int chunk_tokens, const float *__restrict__ logits = nullptr, int E_g = 0,
     int32_t *__restrict__ ids_out = nullptr, float *__restrict__ w_out = nullptr, int num_shared = 0,
-    const int32_t *__restrict__ bases = nullptr, int tpb = 0)
+    const int32_t *__restrict__ bases = nullptr, int tpb = 0, const uint16_t *__restrict__ xsrc = nullptr,
+    int H = 0, uint8_t *__restrict__ xq = nullptr, uint8_t *__restrict__ xs = nullptr)
 {
+    static_assert(!QX || ROUTE, "x is quantized by the routing workgroup");
     static_assert(!ROUTE || IDS_IN_LDS, "routing in the kernel keeps the ids in LDS");
     __shared__ int s_count[kMaxExperts];
     __shared__ int s_cursor[kMaxExperts];
@@ -71,6 +76,11 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     if (one_chunk)
         for (int i = tid; i < E * words; i += kPermThreads)
             s_mask[i] = 0u;
+    constexpr int kQB = 2;                            // x blocks a thread loads before routing
+    uint32_t xw[QX ? kQB : 1][16];
+    const long long nblk = QX ? (long long)T * (H >> 5) : 0;
+    if constexpr (QX)
+        mx_blocks_load<kQB>(xsrc, nblk, tid, kPermThreads, xw);
     if (ROUTE) {
         // 64 / TL tokens per wave and pass; a token's TL lanes form whole DPP rows
         constexpr int TPWV = 64 / TL;
@@ -89,6 +99,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
                 }
             }
         }
+        if constexpr (QX)
+            mx_blocks_finish<kQB>(xw, xsrc, nblk, tid, kPermThreads, xq, xs);
     } else if (IDS_IN_LDS) {
         // local expert index (or -1) of every slot; four loads per thread go
         // out before the first is used (clamped indices, no branch)
@@ -496,7 +508,7 @@ bool route_permute_fusable(const moe_shape &sh)
 
 hipError_t launch_route_permute(const moe_shape &sh, const float *logits, int32_t *ids, float *w,
                                 int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
-                                hipStream_t st, int num_shared)
+                                hipStream_t st, int num_shared, const uint16_t *x, uint8_t *xq, uint8_t *xs)
 {
     const int E = sh.num_local_experts;
     int chunk = chunk_tokens_for(E);
@@ -509,9 +521,16 @@ hipError_t launch_route_permute(const moe_shape &sh, const float *logits, int32_
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDynLdsMax);
         hipLaunchKernelGGL(kernel, dim3(1), dim3(kPermThreads), dyn, st, sh.num_tokens, sh.top_k,
                            sh.expert_begin, E, nullptr, counts, offsets, perm, inv_perm, chunk, logits,
-                           sh.num_experts, ids, w, num_shared, nullptr, 0);
+                           sh.num_experts, ids, w, num_shared, nullptr, 0, x, sh.hidden, xq, xs);
     };
-    if (sh.num_experts <= 64)
+    if (x) {
+        if (sh.num_experts <= 64)
+            launch(permute_kernel<true, true, 16, 4, true>);
+        else if (sh.num_experts <= 128)
+            launch(permute_kernel<true, true, 16, 8, true>);
+        else
+            launch(permute_kernel<true, true, 16, 16, true>);
+    } else if (sh.num_experts <= 64)
         launch(permute_kernel<true, true, 16, 4>);
     else if (sh.num_experts <= 128)
         launch(permute_kernel<true, true, 16, 8>);
