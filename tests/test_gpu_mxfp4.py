@@ -229,3 +229,21 @@ def test_w4a4_forward_tiled_equals_plain(wl, T):
                              w.top_k, expert_begin=w.expert_begin, weight_layout=ops.WEIGHTS_TILED)
     torch.cuda.synchronize()
     assert np.array_equal(to_np_u16(o), _w4a4_forward(inp))
+
+
+# the W4A4 gate/up GEMM builds the permutation from the routing ids where it
+# stages activations in LDS (K <= 2048): against the separate permutation
+# launch (routing inside it up to 32 tokens), bit for bit; the EP shard (K =
+# 7168) keeps the permutation launch either way
+@pytest.mark.parametrize("wl,T", [("qwen3_decode", 20), ("qwen3_decode", 33), ("qwen3_decode", 256),
+                                  ("qwen3_decode", 512), ("tiny", 200), ("ep_shard_decode", 64)])
+def test_w4a4_permutation_in_gemm_equals_separate_permutation(wl, T):
+    from w4a16_grouped_gemm_amd import ops
+    say(f"w4a4 permutation in gemm {wl} T={T}")
+    inp = make_mxfp4_layer_inputs(wl, T)
+    with ops.launch_override(perm_in_gemm_max_tokens=4096):
+        fused = _w4a4_forward(inp)
+    with ops.launch_override(perm_in_gemm_max_tokens=0):
+        separate = _w4a4_forward(inp)
+    assert np.array_equal(fused, separate)
+    assert np.any(fused != 0)

@@ -713,8 +713,46 @@ moe_status moe_w4a4_forward(const moe_shape *shape, const uint16_t *x, const flo
     const Workspace &ws = mw.base;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
+    const int S = sh.num_tokens * sh.top_k;
+    // the gate/up GEMM; h requantized (only the R routed rows, R =
+    // offsets[E_loc] on the device): in the GEMM's epilogue, or by the
+    // quantize kernel after it
+    const GemmLaunch g0 = layer_gemm_args(sh, MOE_GEMM_W13_SWIGLU);
+    MxGemmLaunch g1{};
+    g1.kind = MOE_GEMM_W13_SWIGLU;
+    g1.a = mw.xq;
+    g1.as = mw.xs;
+    g1.a_row_index = ws.perm;
+    g1.a_rows = sh.num_tokens;
+    g1.top_k = sh.top_k;
+    g1.offsets = ws.offsets;
+    g1.num_experts = sh.num_local_experts;
+    g1.wq = w13_q;
+    g1.ws = w13_s;
+    g1.c = ws.h;
+    g1.K = g0.K;
+    g1.N = g0.N;
+    g1.max_rows = g0.max_rows;
+    g1.expected_rows = g0.expected_rows;
+    g1.w_tiled = sh.weight_layout == MOE_WEIGHTS_TILED;
+    g1.cq = mw.hq;
+    g1.cs = mw.hs;
+    // as in the W4A16 layer: up to a few hundred tokens the gate/up GEMM
+    // builds the permutation from the routing ids (no permutation launch)
+    const bool perm_in_gemm = perm_in_gemm_fits(sh) && mx_gemm_ids_supported(g1, sh.num_tokens);
+    if (perm_in_gemm) {
+        g1.ids = ws.ids;
+        g1.T = sh.num_tokens;
+        g1.begin = sh.expert_begin;
+        g1.counts_out = ws.counts;
+        g1.offsets_out = ws.offsets;
+        g1.perm_out = ws.perm;
+        g1.inv_perm_out = ws.inv_perm;
+    }
     // x is quantized by the routing launch (the quantize kernel's bits)
-    if (route_permute_fusable(sh)) {
+    if (perm_in_gemm) {
+        e = launch_route(sh, router_logits, ws.ids, ws.w, s, x, mw.xq, mw.xs);
+    } else if (route_permute_fusable(sh)) {
         e = launch_route_permute(sh, router_logits, ws.ids, ws.w, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s, 0,
                                  x, mw.xq, mw.xs);
     } else {
@@ -722,32 +760,8 @@ moe_status moe_w4a4_forward(const moe_shape *shape, const uint16_t *x, const flo
         if (e == hipSuccess)
             e = launch_permute(sh, ws.ids, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s, 0, ws.part);
     }
-    const int S = sh.num_tokens * sh.top_k;
-    if (e == hipSuccess) {
-        const GemmLaunch g0 = layer_gemm_args(sh, MOE_GEMM_W13_SWIGLU);
-        MxGemmLaunch g{};
-        g.kind = MOE_GEMM_W13_SWIGLU;
-        g.a = mw.xq;
-        g.as = mw.xs;
-        g.a_row_index = ws.perm;
-        g.a_rows = sh.num_tokens;
-        g.top_k = sh.top_k;
-        g.offsets = ws.offsets;
-        g.num_experts = sh.num_local_experts;
-        g.wq = w13_q;
-        g.ws = w13_s;
-        g.c = ws.h;
-        g.K = g0.K;
-        g.N = g0.N;
-        g.max_rows = g0.max_rows;
-        g.expected_rows = g0.expected_rows;
-        g.w_tiled = sh.weight_layout == MOE_WEIGHTS_TILED;
-        // h requantized (only the R routed rows, R = offsets[E_loc] on the
-        // device): in the GEMM's epilogue, or by the quantize kernel after it
-        g.cq = mw.hq;
-        g.cs = mw.hs;
-        e = launch_mx_grouped_gemm(g, s);
-    }
+    if (e == hipSuccess)
+        e = launch_mx_grouped_gemm(g1, s);
     const bool y_slot = sh.num_local_experts == sh.num_experts;
     if (e == hipSuccess) {
         const GemmLaunch g0 = layer_gemm_args(sh, MOE_GEMM_W2);

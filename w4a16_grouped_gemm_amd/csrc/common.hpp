@@ -184,8 +184,15 @@ struct MxGemmLaunch {
     // codes, [max_rows][N/64] scales; the routed rows, counted on the device);
     // c is then scratch for bf16 h
     uint8_t *cq, *cs;
+    // non-NULL: the permutation is built inside the GEMM from these routing
+    // ids ([T*k], global expert ids; offsets and a_row_index unused) and its
+    // tables (as moe_permute stores them) go to the outputs below
+    const int32_t *ids;
+    int T, begin;
+    int32_t *counts_out, *offsets_out, *perm_out, *inv_perm_out;
 };
 hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st);
+bool mx_gemm_ids_supported(const MxGemmLaunch &g, int T);
 // rows_dev (nullable): the device-side row count to quantize (at most rows)
 hipError_t launch_mx_quantize(long long rows, int K, const uint16_t *x, uint8_t *codes, uint8_t *scales,
                               const int32_t *rows_dev, hipStream_t st);

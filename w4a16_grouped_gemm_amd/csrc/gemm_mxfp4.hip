@@ -71,6 +71,11 @@ struct MxArgs {
     int top_k, num_experts, K, N, ldc, half, c_f32;
     int w_tiled;                 // codes tiled: tile t, group g at ((t/8)*G*8 + t%8)*1 KiB + g*8 KiB
     uint8_t *cq, *cs;            // non-NULL (SwiGLU, LDS kernel): h stored as MXFP4 codes and scales
+    // non-NULL (LDS kernel): the permutation is built in LDS from these
+    // routing ids (offsets and a_row_index unused); workgroup 0 stores its tables
+    const int32_t *ids;
+    int T, begin;
+    int32_t *cnt_out, *off_out, *perm_out, *inv_out;
 };
 
 // Lane offset of tile `tile`'s codes (row `row` of the plain layout) and the
@@ -334,10 +339,20 @@ __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
     uint8_t *s_a = s_dyn;                                        // [CS][AST]
     uint8_t *s_as = s_a + CS * AST;                              // [CS][ASS]
     int *s_src = reinterpret_cast<int *>(s_as + CS * ASS);       // [CS] activation row of each chunk row
-    int *s_prefix = s_src + CS;                                  // [E+1], then the scan scratch
-    int *s_wtot = s_prefix + (E + 1);
+    int *s_prefix = s_src + CS;                                  // [E+1] chunk prefix
+    int *s_off = s_prefix + (E + 1);                             // [E+1] expert row offsets
+    int *s_wtot = s_off + (E + 1);                               // [8] scan scratch
+    uint16_t *s_row = reinterpret_cast<uint16_t *>(s_wtot + 8);  // ids: slot of each permuted row
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n16 = lane & 15, kq = lane >> 4;
-    build_chunk_prefix<256>(p.offsets, 0, E, CS, s_prefix, s_wtot);
+    if (p.ids) {
+        // the permutation from the routing ids; its scratch is the staging area
+        uint32_t *s_bits = reinterpret_cast<uint32_t *>(s_dyn);
+        int *s_wpre = reinterpret_cast<int *>(s_bits + E * ((p.T + 31) >> 5));
+        const IdsTables it{p.ids, p.T, p.top_k, p.begin, E, p.cnt_out, p.off_out, p.perm_out, p.inv_out};
+        build_from_ids<256>(it, CS, s_bits, s_wpre, s_row, s_prefix, s_off, s_wtot);
+    } else {
+        build_chunk_prefix<256>(p.offsets, 0, E, CS, s_prefix, s_wtot, s_off);
+    }
 
     const int ntiles = p.N >> 4;
     const int nblocks = ntiles / BT;
@@ -356,8 +371,8 @@ __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
         const int chunk = item / nblocks;
         const int block = item - chunk * nblocks;
         const int e = uniform(chunk_expert(s_prefix, E, chunk));
-        const int row0 = uniform(p.offsets[e] + (chunk - s_prefix[e]) * CS);
-        const int nvalid = uniform(min(CS, p.offsets[e + 1] - row0));
+        const int row0 = uniform(s_off[e] + (chunk - s_prefix[e]) * CS);
+        const int nvalid = uniform(min(CS, s_off[e + 1] - row0));
         const int nsub = (nvalid + 15) >> 4;
         const int tile0 = block * BT + wave * TPW;
         const uint32_t wbytes = (uint32_t)p.N * row_bytes, wsbytes = (uint32_t)p.N * srow_bytes;
@@ -366,7 +381,8 @@ __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
         // activation row of chunk row tid (gather index read now, stored after the barrier)
         int src = 0;
         if (tid < CS && tid < nvalid)
-            src = p.a_row_index ? p.a_row_index[row0 + tid] / p.top_k : row0 + tid;
+            src = p.ids ? s_row[row0 + tid] / p.top_k
+                        : p.a_row_index ? p.a_row_index[row0 + tid] / p.top_k : row0 + tid;
         // weight scales of this wave's tiles, and the first RING-1 groups of codes
         uint32_t vw[TPW];
         u32x4 wsc[TPW];
@@ -545,31 +561,43 @@ hipError_t mx_launch(const MxArgs &a, int max_rows, hipStream_t st)
 
 // The LDS-staged kernel when the whole K of a chunk fits (K <= 2048, the
 // one-load weight scales), else the register-streaming one.
+// LDS of the LDS-staged kernel: the staging area (also the requantizing
+// epilogue's tile and the permutation scratch), then the tables; `slots`:
+// T * k with the permutation built from the ids, else 0.
 template <int TPW, int NSUB>
-size_t mx_lds_bytes(int K, int num_experts)
+size_t mx_lds_bytes(int K, int num_experts, int slots)
 {
     constexpr int CS = 16 * NSUB;
     size_t stage = (size_t)CS * (mx_code_stride(K) + mx_scale_stride(K) + 4);
     const size_t h = (size_t)CS * mx_h_stride<TPW, NSUB>() * 2;    // the requantizing epilogue's tile
     stage = stage > h ? stage : h;
-    return stage + sizeof(int) * (num_experts + 1 + 4);
+    return stage + sizeof(int) * (2 * (num_experts + 1) + 8) + 2 * (size_t)slots;
 }
 
 // Whether the LDS-staged kernel takes the launch (K <= 2048, the one-load
-// weight scales, and its LDS).
+// weight scales, and its LDS); with the permutation built from the ids, also
+// whether its scratch fits the staging area.
 template <int TPW, int NSUB>
-bool mx_lds_fits(int K, int num_experts)
+bool mx_lds_fits(int K, int num_experts, int T = 0, int slots = 0)
 {
-    return K <= 2048 && mx_lds_bytes<TPW, NSUB>(K, num_experts) <= 150 * 1024;
+    constexpr int CS = 16 * NSUB;
+    if (K > 2048 || mx_lds_bytes<TPW, NSUB>(K, num_experts, slots) > 150 * 1024)
+        return false;
+    return slots == 0 || (num_experts <= 256 && slots <= kIdsPerThread * 256 &&
+                          ids_scratch_bytes(num_experts, T) <= (size_t)CS * (mx_code_stride(K) + mx_scale_stride(K)));
 }
 
 template <int KIND, int TPW, int NSUB, int RING>
 hipError_t mx_launch_any(const MxArgs &a, int max_rows, hipStream_t st)
 {
     constexpr int CS = 16 * NSUB;
-    const size_t lds = mx_lds_bytes<TPW, NSUB>(a.K, a.num_experts);
-    if (!mx_lds_fits<TPW, NSUB>(a.K, a.num_experts))
+    const int slots = a.ids ? a.T * a.top_k : 0;
+    const size_t lds = mx_lds_bytes<TPW, NSUB>(a.K, a.num_experts, slots);
+    if (!mx_lds_fits<TPW, NSUB>(a.K, a.num_experts, a.T, slots)) {
+        if (a.ids)
+            return hipErrorInvalidValue;                 // mx_gemm_ids_supported() rules this out
         return mx_launch<KIND, TPW, NSUB, RING>(a, max_rows, st);
+    }
     auto kernel = mx_gemm_lds_kernel<KIND, TPW, NSUB, RING>;
     static std::once_flag once;
     std::call_once(once, [&] {
@@ -603,6 +631,40 @@ hipError_t launch_mx_quantize(long long rows, int K, const uint16_t *x, uint8_t 
     return hipGetLastError();
 }
 
+// Tiling of an MXFP4 grouped GEMM: rows per active expert under uniform
+// routing pick one subtile for decode, four (64-row chunks) once experts hold
+// many rows; tiles per wave from how many items the grid gets.
+static void mx_choose(const MxGemmLaunch &g, int &tpw, int &nsub)
+{
+    const double E = g.num_experts > 0 ? g.num_experts : 1;
+    const double R = g.expected_rows > 0 ? g.expected_rows : 1;
+    const double T = g.max_rows / (double)(g.top_k > 0 ? g.top_k : 1);
+    const double ps = R / (T * E);
+    const double active = E * (1.0 - pow(1.0 - (ps < 1.0 ? ps : 1.0), T));
+    const double m = R / (active > 1.0 ? active : 1.0);
+    const int ntiles = g.N / 16;
+    nsub = m > 40.0 ? 4 : m > 12.0 ? 2 : 1;
+    tpw = 4;
+    const double chunks = fmax(active, R / (16.0 * nsub));
+    while (tpw > 1 && (ntiles % (4 * tpw) != 0 || chunks * ntiles / tpw <= 2.0 * device_cu_count()))
+        tpw >>= 1;
+}
+
+bool mx_gemm_ids_supported(const MxGemmLaunch &g, int T)
+{
+    int tpw, nsub;
+    mx_choose(g, tpw, nsub);
+    const int slots = T * g.top_k;
+    if (g.c_f32 || slots > g.max_rows || (g.N / 16) % (4 * tpw) != 0)
+        return false;
+#define MOE_MX_FITS(TP, NS) \
+    if (tpw == TP && nsub == NS) return mx_lds_fits<TP, NS>(g.K, g.num_experts, T, slots);
+    MOE_MX_FITS(1, 1) MOE_MX_FITS(2, 1) MOE_MX_FITS(4, 1) MOE_MX_FITS(1, 2) MOE_MX_FITS(2, 2) MOE_MX_FITS(4, 2)
+    MOE_MX_FITS(1, 4) MOE_MX_FITS(2, 4) MOE_MX_FITS(4, 4)
+#undef MOE_MX_FITS
+    return false;
+}
+
 hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st)
 {
     MxArgs a{};
@@ -627,22 +689,21 @@ hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st)
     a.w_tiled = g.w_tiled ? 1 : 0;
     a.cq = g.kind == MOE_GEMM_W13_SWIGLU ? g.cq : nullptr;
     a.cs = g.kind == MOE_GEMM_W13_SWIGLU ? g.cs : nullptr;
-    // rows per active expert under uniform routing: one subtile for decode,
-    // four (64-row chunks) once experts hold many rows; tiles per wave from
-    // how many items the grid gets
-    const double E = g.num_experts > 0 ? g.num_experts : 1;
-    const double R = g.expected_rows > 0 ? g.expected_rows : 1;
-    const double T = g.max_rows / (double)(g.top_k > 0 ? g.top_k : 1);
-    const double ps = R / (T * E);
-    const double active = E * (1.0 - pow(1.0 - (ps < 1.0 ? ps : 1.0), T));
-    const double m = R / (active > 1.0 ? active : 1.0);
-    const int ntiles = g.N / 16;
-    const int nsub = m > 40.0 ? 4 : m > 12.0 ? 2 : 1;
-    int tpw = 4;
-    const double chunks = fmax(active, R / (16.0 * nsub));
-    while (tpw > 1 && (ntiles % (4 * tpw) != 0 || chunks * ntiles / tpw <= 2.0 * device_cu_count()))
-        tpw >>= 1;
-    if (ntiles % (4 * tpw) != 0)
+    if (g.ids) {
+        if (!mx_gemm_ids_supported(g, g.T))
+            return hipErrorInvalidValue;
+        a.ids = g.ids;
+        a.T = g.T;
+        a.begin = g.begin;
+        a.cnt_out = g.counts_out;
+        a.off_out = g.offsets_out;
+        a.perm_out = g.perm_out;
+        a.inv_out = g.inv_perm_out;
+        a.a_row_index = nullptr;
+    }
+    int tpw, nsub;
+    mx_choose(g, tpw, nsub);
+    if ((g.N / 16) % (4 * tpw) != 0)
         return hipErrorInvalidValue;                   // N is a multiple of 128: 4 waves x 2 tiles always divide
     auto go = [&](auto kindc) -> hipError_t {
         constexpr int KIND = decltype(kindc)::value;
@@ -650,7 +711,7 @@ hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st)
         // bf16 h, then the quantize kernel over the routed rows (same bits)
 #define MOE_MX(TP, NS)                                                                                      \
         if (tpw == TP && nsub == NS) {                                                                      \
-            if (a.cq && !mx_lds_fits<TP, NS>(a.K, a.num_experts)) {                                        \
+            if (a.cq && !mx_lds_fits<TP, NS>(a.K, a.num_experts, a.T, a.ids ? a.T * a.top_k : 0)) {        \
                 MxArgs b = a;                                                                               \
                 b.cq = nullptr;                                                                             \
                 b.cs = nullptr;                                                                             \

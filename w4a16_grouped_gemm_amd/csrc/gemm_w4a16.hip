@@ -186,118 +186,6 @@ __device__ __forceinline__ void store_tile(const GemmArgs &p, floatx4 v, int til
 }
 
 // ---------------------------------------------------------------------------
-// SRC_IDS: the layer's stable expert permutation (moe_permute's result) built
-// by every workgroup in LDS from the routing ids, so that the gate/up GEMM
-// needs no permutation launch before it (InfiniLM PR #500 report, section
-// 2.2: counts, offsets and a permutation from the routing ids). A token's k
-// experts are distinct, so the rows of local expert e are its slots in token
-// order: row(slot s of token t) = offsets[e] + #{tokens t' < t routed to e},
-// counted from per-expert token bitmaps. Fills s_off / s_prefix as
-// build_chunk_prefix does from `offsets`, and s_row[r] = slot of row r;
-// workgroup 0 also stores counts, offsets, perm and inv_perm (-1 for a slot
-// whose expert is not local). The bitmaps and word prefixes are scratch
-// (dead after the last barrier). Needs E <= NT and T * k <= kIdsPerThread * NT.
-// ---------------------------------------------------------------------------
-constexpr int kIdsPerThread = 16;                 // slots per thread: T * k <= 16 * 256
-
-template <int NT>
-__device__ void build_from_ids(const GemmArgs &p, int CS, uint32_t *s_bits, int *s_wpre, uint16_t *s_row,
-                               int *s_prefix, int *s_off, int *s_wtot)
-{
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int E = p.num_experts, k = p.top_k;
-    const int S = p.T * k, words = (p.T + 31) >> 5;
-    const bool store = blockIdx.x == 0;
-    // every id load of the thread goes out before the first is used (one
-    // memory round trip; slots past S read out of range, as zeros)
-    const __amdgpu_buffer_rsrc_t rids = make_rsrc(p.ids, (uint32_t)S * 4u);
-    int le[kIdsPerThread], tk[kIdsPerThread];          // local expert (-1: none) and token of each slot
-#pragma unroll
-    for (int j = 0; j < kIdsPerThread; ++j)
-        le[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rids, (uint32_t)(tid + j * NT) * 4u, 0, 0);
-    for (int i = tid; i < E * words; i += NT)
-        s_bits[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kIdsPerThread; ++j) {
-        const int s = tid + j * NT;
-        const int e = le[j] - p.begin;
-        le[j] = (s < S && e >= 0 && e < E) ? e : -1;
-        tk[j] = s / k;
-        if (le[j] >= 0)
-            atomicOr(&s_bits[le[j] * words + (tk[j] >> 5)], 1u << (tk[j] & 31));
-    }
-    __syncthreads();
-    // thread e: its row count and word prefixes, then one scan over the
-    // experts of (rows, chunks of CS rows)
-    int cnt = 0, ch = 0;
-    if (tid < E) {
-        for (int w = 0; w < words; ++w) {
-            s_wpre[tid * words + w] = cnt;
-            cnt += __popc(s_bits[tid * words + w]);
-        }
-        ch = (cnt + CS - 1) / CS;
-    }
-    int tc, tch;
-    const int xc = wave_exclusive_scan(cnt, tc);
-    const int xch = wave_exclusive_scan(ch, tch);
-    if (lane == 0) {
-        s_wtot[wave] = tc;
-        s_wtot[NT / 64 + wave] = tch;
-    }
-    __syncthreads();
-    int bc = 0, bch = 0, ac = 0, ach = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        bc += w < wave ? s_wtot[w] : 0;
-        bch += w < wave ? s_wtot[NT / 64 + w] : 0;
-        ac += s_wtot[w];
-        ach += s_wtot[NT / 64 + w];
-    }
-    if (tid < E) {
-        s_off[tid] = bc + xc;
-        s_prefix[tid] = bch + xch;
-        if (store) {
-            p.cnt_out[tid] = cnt;
-            p.off_out[tid] = bc + xc;
-        }
-    }
-    if (tid == 0) {
-        s_off[E] = ac;
-        s_prefix[E] = ach;
-        if (store)
-            p.off_out[E] = ac;
-    }
-    __syncthreads();
-    // the row of every slot first (LDS reads only, all independent), then the stores
-    int row[kIdsPerThread];
-#pragma unroll
-    for (int j = 0; j < kIdsPerThread; ++j) {
-        const int e = le[j] >= 0 ? le[j] : 0, w = le[j] >= 0 ? tk[j] >> 5 : 0;
-        const uint32_t below = s_bits[e * words + w] & ((1u << (tk[j] & 31)) - 1u);
-        row[j] = s_off[e] + s_wpre[e * words + w] + __popc(below);
-    }
-#pragma unroll
-    for (int j = 0; j < kIdsPerThread; ++j) {
-        const int s = tid + j * NT;
-        if (le[j] >= 0) {
-            s_row[row[j]] = (uint16_t)s;
-            if (store)
-                p.perm_out[row[j]] = s;
-        }
-        if (store && s < S)
-            p.inv_out[s] = le[j] >= 0 ? row[j] : -1;
-    }
-    __syncthreads();
-}
-
-// SRC_IDS scratch inside the activation buffers (bitmaps, word prefixes).
-constexpr size_t ids_scratch_bytes(int E, int T)
-{
-    return (size_t)E * ((T + 31) / 32) * 8;
-}
-
-// ---------------------------------------------------------------------------
 // gemm_stream_kernel
 //
 // No load sits under a branch: tiles past N never occur (the host launches
@@ -364,7 +252,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         uint32_t *s_bits = reinterpret_cast<uint32_t *>(s_dyn);
         const int words = (p.T + 31) >> 5;
         int *s_wpre = reinterpret_cast<int *>(s_bits + E * words);
-        build_from_ids<256>(p, CS, s_bits, s_wpre, s_row, s_prefix, s_off, s_wtot);
+        const IdsTables it{p.ids, p.T, p.top_k, p.begin, E, p.cnt_out, p.off_out, p.perm_out, p.inv_out};
+        build_from_ids<256>(it, CS, s_bits, s_wpre, s_row, s_prefix, s_off, s_wtot);
         total_items = s_prefix[E] * nblocks;
     } else {
         for (int e = tid; e < E; e += 256)
