@@ -15,6 +15,8 @@
   codes equal the oracle exactly like the plain ones, and the layer on tiled
   codes equals the layer on plain codes bit for bit.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -247,3 +249,51 @@ def test_w4a4_permutation_in_gemm_equals_separate_permutation(wl, T):
         separate = _w4a4_forward(inp)
     assert np.array_equal(fused, separate)
     assert np.any(fused != 0)
+
+
+# (workload, T): the W4A4 small-batch path (routing and the quantization of x
+# inside the gate/up GEMM, slot-ordered h and y, no permutation): one and
+# two tokens, a token count between, the largest T, 8 experts of top-2 (two
+# tokens sharing experts), 128 slots at top-16 (k16_e64), and the EP shard,
+# whose K = 7168 keeps the general path either way
+def _mx_small_inputs(wl, T):
+    from w4a16_grouped_gemm_amd.inputs import Workload
+    if wl == "k16_e64":
+        wl = Workload("k16_e64", 21, 64, 64, 0, 16, 256, 256, (3, 8))
+    return make_mxfp4_layer_inputs(wl, T)
+
+
+@pytest.mark.parametrize("wl,T", [("qwen3_decode", 1), ("qwen3_decode", 2), ("qwen3_decode", 5),
+                                  ("qwen3_decode", 16), ("tiny", 2), ("tiny", 7), ("k16_e64", 8),
+                                  ("ep_shard_decode", 3)])
+def test_w4a4_small_batch_path_equals_general_path(wl, T):
+    from w4a16_grouped_gemm_amd import ops
+    say(f"w4a4 small-batch path {wl} T={T}")
+    inp = _mx_small_inputs(wl, T)
+    fast = _w4a4_forward(inp)
+    with ops.launch_override(decode_max_tokens=0):
+        general = _w4a4_forward(inp)
+    assert np.array_equal(fast, general)
+    w = inp.workload
+    ref = oracle.layer_w4a4(inp.x, inp.logits, inp.w13_q, inp.w13_s, inp.w2_q, inp.w2_s, top_k=w.top_k,
+                            expert_begin=w.expert_begin)
+    local = (ref["topk_ids"] >= w.expert_begin) & (ref["topk_ids"] < w.expert_begin + w.num_local_experts)
+    none = ~local.any(axis=1)
+    assert np.all(fast[none] == 0)
+    if (~none).any():
+        assert_layer_close(fast[~none], ref["out"][~none], f"w4a4 small {wl} T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_w4a4_small_batch_masked_experts(T):
+    # -inf logits (masked experts) on the small-batch path: the experts
+    # selected with weight 0 must not disturb the output
+    say(f"w4a4 small-batch masked experts T={T}")
+    inp = make_mxfp4_layer_inputs("qwen3_decode", T)
+    lg = np.full_like(inp.logits, -np.inf)
+    lg[:, :3] = inp.logits[:, :3]                        # 3 finite logits, 8 slots
+    inp = dataclasses.replace(inp, logits=lg)
+    got = _w4a4_forward(inp)
+    ref = oracle.layer_w4a4(inp.x, inp.logits, inp.w13_q, inp.w13_s, inp.w2_q, inp.w2_s, top_k=8)
+    assert np.all(np.isfinite(bf16_to_f64(got)))
+    assert_layer_close(got, ref["out"], f"w4a4 small masked T={T}")

@@ -714,6 +714,7 @@ moe_status moe_w4a4_forward(const moe_shape *shape, const uint16_t *x, const flo
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     const int S = sh.num_tokens * sh.top_k;
+    const bool y_slot = sh.num_local_experts == sh.num_experts;
     // the gate/up GEMM; h requantized (only the R routed rows, R =
     // offsets[E_loc] on the device): in the GEMM's epilogue, or by the
     // quantize kernel after it
@@ -737,6 +738,41 @@ moe_status moe_w4a4_forward(const moe_shape *shape, const uint16_t *x, const flo
     g1.w_tiled = sh.weight_layout == MOE_WEIGHTS_TILED;
     g1.cq = mw.hq;
     g1.cs = mw.hs;
+    // the down GEMM: the requantized h, y bf16
+    const GemmLaunch gd = layer_gemm_args(sh, MOE_GEMM_W2);
+    MxGemmLaunch g2{};
+    g2.kind = MOE_GEMM_W2;
+    g2.a = mw.hq;
+    g2.as = mw.hs;
+    g2.a_rows = S;
+    g2.top_k = sh.top_k;
+    g2.offsets = ws.offsets;
+    g2.num_experts = sh.num_local_experts;
+    g2.wq = w2_q;
+    g2.ws = w2_s;
+    g2.c = ws.y;
+    g2.c_row_index = y_slot ? ws.perm : nullptr;
+    g2.K = gd.K;
+    g2.N = gd.N;
+    g2.max_rows = gd.max_rows;
+    g2.expected_rows = gd.expected_rows;
+    g2.w_tiled = sh.weight_layout == MOE_WEIGHTS_TILED;
+    // Small batch (as in the W4A16 layer): the gate/up GEMM routes the tokens
+    // and quantizes their x rows itself, h and y rows are the slots t*k + j,
+    // no permutation; three launches.
+    const moe_launch_override ov = launch_override();
+    const int small_max = ov.decode_max_tokens >= 0 ? ov.decode_max_tokens : 16;
+    if (sh.num_tokens <= small_max && S <= kDecMaxSlots && sh.num_experts <= 256 && mx_small_supported(g1) &&
+        mx_small_supported(g2)) {
+        e = launch_mx_small(g1, MxSmallSource{router_logits, sh.num_experts, sh.num_tokens, sh.expert_begin, x,
+                                              ws.ids, ws.w, ws.pres}, s);
+        if (e == hipSuccess)
+            e = launch_mx_small(g2, MxSmallSource{nullptr, sh.num_experts, sh.num_tokens, sh.expert_begin, nullptr,
+                                                  ws.ids, ws.w, ws.pres}, s);
+        if (e == hipSuccess)
+            e = launch_finalize(sh, ws.y, false, ws.w, ws.pres, out, false, s, true);
+        return from_hip(e);
+    }
     // as in the W4A16 layer: up to a few hundred tokens the gate/up GEMM
     // builds the permutation from the routing ids (no permutation launch)
     const bool perm_in_gemm = perm_in_gemm_fits(sh) && mx_gemm_ids_supported(g1, sh.num_tokens);
@@ -762,28 +798,8 @@ moe_status moe_w4a4_forward(const moe_shape *shape, const uint16_t *x, const flo
     }
     if (e == hipSuccess)
         e = launch_mx_grouped_gemm(g1, s);
-    const bool y_slot = sh.num_local_experts == sh.num_experts;
-    if (e == hipSuccess) {
-        const GemmLaunch g0 = layer_gemm_args(sh, MOE_GEMM_W2);
-        MxGemmLaunch g{};
-        g.kind = MOE_GEMM_W2;
-        g.a = mw.hq;
-        g.as = mw.hs;
-        g.a_rows = S;
-        g.top_k = sh.top_k;
-        g.offsets = ws.offsets;
-        g.num_experts = sh.num_local_experts;
-        g.wq = w2_q;
-        g.ws = w2_s;
-        g.c = ws.y;
-        g.c_row_index = y_slot ? ws.perm : nullptr;
-        g.K = g0.K;
-        g.N = g0.N;
-        g.max_rows = g0.max_rows;
-        g.expected_rows = g0.expected_rows;
-        g.w_tiled = sh.weight_layout == MOE_WEIGHTS_TILED;
-        e = launch_mx_grouped_gemm(g, s);
-    }
+    if (e == hipSuccess)
+        e = launch_mx_grouped_gemm(g2, s);
     if (e == hipSuccess)
         e = launch_finalize(sh, ws.y, false, ws.w, ws.inv_perm, out, false, s, y_slot);
     return from_hip(e);

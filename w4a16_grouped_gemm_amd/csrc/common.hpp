@@ -110,6 +110,8 @@ hipError_t launch_grouped_gemm(const GemmLaunch &g, hipStream_t st);
 // routing ids (no permutation launch): g as for launch_grouped_gemm with
 // a_row_index unused; the permutation's tables (as moe_permute stores them)
 // go to the IdsSource outputs.
+constexpr int kDecMaxSlots = 128;                   // T * k of the layers' small-batch paths
+
 struct IdsSource {
     const int32_t *ids;       // [T*k] global expert ids
     int T, begin;             // tokens; global id of local expert 0
@@ -193,6 +195,22 @@ struct MxGemmLaunch {
 };
 hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st);
 bool mx_gemm_ids_supported(const MxGemmLaunch &g, int T);
+// The W4A4 layer's small-batch path (T * k <= 128): the gate/up GEMM routes
+// the tokens itself (logits non-NULL: writes ids, w, pres) and quantizes
+// their x rows while staging them, its outputs h rows t*k + j (requantized,
+// g.cq / g.cs); the down GEMM (logits NULL) reads that stored slot table and
+// writes y rows t*k + j. g as for launch_mx_grouped_gemm (offsets,
+// a_row_index, c_row_index unused).
+struct MxSmallSource {
+    const float *logits;      // [T][E_g] (gate/up) or NULL (down)
+    int E_g, T, begin;
+    const uint16_t *x;        // bf16 x [T][H] (gate/up)
+    int32_t *ids;             // [T*k] global expert ids
+    float *w;                 // [T*k] routing weights
+    int32_t *pres;            // [T*k] slot if local, else -1
+};
+bool mx_small_supported(const MxGemmLaunch &g);
+hipError_t launch_mx_small(const MxGemmLaunch &g, const MxSmallSource &src, hipStream_t st);
 // rows_dev (nullable): the device-side row count to quantize (at most rows)
 hipError_t launch_mx_quantize(long long rows, int K, const uint16_t *x, uint8_t *codes, uint8_t *scales,
                               const int32_t *rows_dev, hipStream_t st);

@@ -379,7 +379,6 @@ constexpr size_t ids_scratch_bytes(int E, int T)
 // workgroup that knows each slot's local expert (s_loc[s], -1 when not local;
 // slot s = t * k + j) can list an expert's rows itself: the "leader" of an
 // expert is its first slot; its rows are its slots in slot order.
-constexpr int kDecMaxSlots = 128;                   // T * k of the small-batch path
 
 // Slot of row r of an expert whose slots are the set bits of (m0, m1): the
 // r-th set bit, or -1 past the last.

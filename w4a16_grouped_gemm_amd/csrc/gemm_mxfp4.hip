@@ -46,6 +46,7 @@
 //    (exact in binary32: the division by a power of two is exact).
 #include "gemm_core.hpp"
 #include "mx_quant.hpp"
+#include "route_core.hpp"
 
 #include <map>
 #include <mutex>
@@ -76,7 +77,22 @@ struct MxArgs {
     const int32_t *ids;
     int T, begin;
     int32_t *cnt_out, *off_out, *perm_out, *inv_out;
+    // the W4A4 layer's small-batch path (LDS kernel, SRC != MX_SRC_CHUNKS):
+    // items from a slot table, built by routing inside the gate/up GEMM
+    // (which also quantizes the tokens' x rows while staging them) or read
+    // from the stored table (down); rows are slots t*k + j
+    const float *logits;         // [T][E_g]
+    int E_g;
+    const uint16_t *x;           // bf16 x [T][K] (gate/up)
+    int32_t *slot_ids;           // [T*k]: global expert id of each slot (gate/up writes, down reads)
+    float *slot_w;               // [T*k]: routing weight (gate/up writes)
+    int32_t *pres;               // [T*k]: the slot if its expert is local, else -1
 };
+
+// Item sources of the LDS kernel: the chunk prefix (offsets or the routing
+// ids), the small-batch slot table built by routing in the kernel, or the
+// stored slot table.
+enum { MX_SRC_CHUNKS = 0, MX_SRC_ROUTE = 1, MX_SRC_SLOTS = 2 };
 
 // Lane offset of tile `tile`'s codes (row `row` of the plain layout) and the
 // byte step from one 128-wide group to the next.
@@ -108,7 +124,7 @@ __device__ __forceinline__ uint32_t mx_tile_row(const MxArgs &p, int tile, int n
 // n16 + 8 (lane n16 ^ 8).
 template <int KIND, int TPW, int NSUB>
 __device__ __forceinline__ void mx_store(const MxArgs &p, const floatx4 (&acc)[TPW][NSUB], int tile0, int row0,
-                                         int nvalid, int nsub, int n16, int kq)
+                                         int nvalid, int nsub, int n16, int kq, const int *s_orow = nullptr)
 {
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c_row_index, p.c_row_bytes);
 #pragma unroll
@@ -120,7 +136,8 @@ __device__ __forceinline__ void mx_store(const MxArgs &p, const floatx4 (&acc)[T
         for (int i = 0; i < 4; ++i) {
             const int m = sb * 16 + kq * 4 + i;
             const int r = row0 + min(m, nvalid - 1);
-            orow[i] = p.c_row_index ? (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)r * 4u, 0, 0) : r;
+            orow[i] = s_orow ? s_orow[min(m, nvalid - 1)]
+                    : p.c_row_index ? (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)r * 4u, 0, 0) : r;
         }
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
@@ -167,7 +184,7 @@ __host__ __device__ constexpr int mx_h_stride() { return 32 * TPW + 8; }   // bf
 template <int TPW, int NSUB>
 __device__ __forceinline__ void mx_store_quant(const MxArgs &p, const floatx4 (&acc)[TPW][NSUB], int block, int row0,
                                                int nvalid, int nsub, int n16, int kq, int wave, int tid,
-                                               uint16_t *s_h)
+                                               uint16_t *s_h, const int *s_orow = nullptr)
 {
     constexpr int CS = 16 * NSUB, HST = mx_h_stride<TPW, NSUB>();
     __syncthreads();                                   // every wave is done with the staged activations
@@ -203,7 +220,7 @@ __device__ __forceinline__ void mx_store_quant(const MxArgs &p, const floatx4 (&
                 w[d] = src[d];
             uint32_t out[4];
             const uint32_t sc = mx_quant_block(w, out);
-            const int orow = p.c_row_index ? p.c_row_index[row0 + r] : row0 + r;
+            const int orow = s_orow ? s_orow[r] : p.c_row_index ? p.c_row_index[row0 + r] : row0 + r;
             const int f0 = block * 32 * TPW + b * 32;  // first feature of the block
             *reinterpret_cast<u32x4 *>(p.cq + (size_t)orow * ldq + (f0 >> 1)) = u32x4{out[0], out[1], out[2], out[3]};
             p.cs[(size_t)orow * lds_ + (f0 >> 5)] = (uint8_t)sc;
@@ -326,10 +343,12 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p)
 __host__ __device__ constexpr int mx_code_stride(int K) { return K / 2 + 16; }
 __host__ __device__ constexpr int mx_scale_stride(int K) { return K / 32 + 4; }
 constexpr int kMxStageBatch = 8;                     // staging loads a thread issues before storing
+constexpr int kMxQuantBatch = 4;                     // x blocks a thread loads before quantizing (small batch)
 
-template <int KIND, int TPW, int NSUB, int RING>
+template <int KIND, int TPW, int NSUB, int RING, int SRC = MX_SRC_CHUNKS, int PL = 8>
 __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
 {
+    static_assert(SRC == MX_SRC_CHUNKS || NSUB == 1, "small-batch items hold at most 16 rows");
     constexpr int CS = 16 * NSUB;
     constexpr int BT = 4 * TPW;
     extern __shared__ __align__(16) unsigned char s_dyn[];
@@ -338,25 +357,68 @@ __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
     const int AST = mx_code_stride(K), ASS = mx_scale_stride(K);
     uint8_t *s_a = s_dyn;                                        // [CS][AST]
     uint8_t *s_as = s_a + CS * AST;                              // [CS][ASS]
-    int *s_src = reinterpret_cast<int *>(s_as + CS * ASS);       // [CS] activation row of each chunk row
-    int *s_prefix = s_src + CS;                                  // [E+1] chunk prefix
+    // the staging area also holds the requantizing epilogue's h tile
+    const int stage = max(CS * (AST + ASS), CS * mx_h_stride<TPW, NSUB>() * 2);
+    int *s_src = reinterpret_cast<int *>(s_dyn + stage);         // [CS] activation row of each chunk row
+    int *s_orow = s_src + CS;                                    // [CS] small batch: output row (slot)
+    int *s_prefix = s_orow + CS;                                 // [E+1] chunk prefix
     int *s_off = s_prefix + (E + 1);                             // [E+1] expert row offsets
     int *s_wtot = s_off + (E + 1);                               // [8] scan scratch
     uint16_t *s_row = reinterpret_cast<uint16_t *>(s_wtot + 8);  // ids: slot of each permuted row
+    // small-batch slot tables, in the same region
+    int *s_loc = s_prefix;                                       // [kDecMaxSlots] local expert per slot, -1
+    int *s_lead = s_loc + kDecMaxSlots;                          // [kDecMaxSlots] leaders in slot order
+    int *s_nlead = s_lead + kDecMaxSlots;                        // [4]
+    int *s_first = s_nlead + 4;                                  // [E] each expert's first slot
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n16 = lane & 15, kq = lane >> 4;
-    if (p.ids) {
-        // the permutation from the routing ids; its scratch is the staging area
-        uint32_t *s_bits = reinterpret_cast<uint32_t *>(s_dyn);
-        int *s_wpre = reinterpret_cast<int *>(s_bits + E * ((p.T + 31) >> 5));
-        const IdsTables it{p.ids, p.T, p.top_k, p.begin, E, p.cnt_out, p.off_out, p.perm_out, p.inv_out};
-        build_from_ids<256>(it, CS, s_bits, s_wpre, s_row, s_prefix, s_off, s_wtot);
-    } else {
-        build_chunk_prefix<256>(p.offsets, 0, E, CS, s_prefix, s_wtot, s_off);
-    }
-
+    const int S_slots = p.T * p.top_k;
     const int ntiles = p.N >> 4;
     const int nblocks = ntiles / BT;
-    const int total_items = s_prefix[E] * nblocks;
+    int total_items;
+    if constexpr (SRC == MX_SRC_CHUNKS) {
+        if (p.ids) {
+            // the permutation from the routing ids; its scratch is the staging area
+            uint32_t *s_bits = reinterpret_cast<uint32_t *>(s_dyn);
+            int *s_wpre = reinterpret_cast<int *>(s_bits + E * ((p.T + 31) >> 5));
+            const IdsTables it{p.ids, p.T, p.top_k, p.begin, E, p.cnt_out, p.off_out, p.perm_out, p.inv_out};
+            build_from_ids<256>(it, CS, s_bits, s_wpre, s_row, s_prefix, s_off, s_wtot);
+        } else {
+            build_chunk_prefix<256>(p.offsets, 0, E, CS, s_prefix, s_wtot, s_off);
+        }
+        total_items = s_prefix[E] * nblocks;
+    } else {
+        // the small-batch slot table, as the W4A16 streaming kernel builds it
+        for (int e = tid; e < E; e += 256)
+            s_first[e] = kDecMaxSlots;
+        if constexpr (SRC == MX_SRC_ROUTE) {
+            // every workgroup routes all tokens: one DPP row of 16 lanes per token
+            for (int t0 = wave * 4; t0 < p.T; t0 += 16) {
+                const int t = t0 + (lane >> 4);
+                if (t < p.T) {
+                    int eg;
+                    float wt;
+                    route_token<16, PL>(p.logits + (size_t)t * p.E_g, p.E_g, p.top_k, n16, eg, wt);
+                    if (n16 < p.top_k) {
+                        const int sl = t * p.top_k + n16;
+                        const int le = eg - p.begin;
+                        const int loc = (le >= 0 && le < E) ? le : -1;
+                        s_loc[sl] = loc;
+                        if (blockIdx.x == 0) {
+                            p.slot_ids[sl] = eg;
+                            p.slot_w[sl] = wt;
+                            p.pres[sl] = loc >= 0 ? sl : -1;
+                        }
+                    }
+                }
+            }
+        } else {
+            for (int sl = tid; sl < S_slots; sl += 256)
+                s_loc[sl] = p.pres[sl] >= 0 ? p.slot_ids[sl] - p.begin : -1;
+        }
+        __syncthreads();
+        build_leaders<256>(S_slots, E, s_loc, s_first, s_lead, s_nlead);
+        total_items = s_nlead[0] * nblocks;
+    }
     const uint32_t row_bytes = (uint32_t)(K >> 1), srow_bytes = (uint32_t)(K >> 5);
     const int ppr = K >> 5;                                      // 16-byte code pieces per row
     const int spr = K >> 7;                                      // scale dwords per row
@@ -370,19 +432,36 @@ __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
          item += gridDim.x / nx) {
         const int chunk = item / nblocks;
         const int block = item - chunk * nblocks;
-        const int e = uniform(chunk_expert(s_prefix, E, chunk));
-        const int row0 = uniform(s_off[e] + (chunk - s_prefix[e]) * CS);
-        const int nvalid = uniform(min(CS, s_off[e + 1] - row0));
+        int e, row0, nvalid;
+        uint64_t m0 = 0, m1 = 0;                                 // small batch: the expert's slots
+        if constexpr (SRC == MX_SRC_CHUNKS) {
+            e = uniform(chunk_expert(s_prefix, E, chunk));
+            row0 = uniform(s_off[e] + (chunk - s_prefix[e]) * CS);
+            nvalid = uniform(min(CS, s_off[e + 1] - row0));
+        } else {
+            e = uniform(s_loc[s_lead[chunk]]);
+            m0 = __ballot(lane < S_slots && s_loc[lane] == e);
+            m1 = __ballot(64 + lane < S_slots && s_loc[64 + lane] == e);
+            row0 = 0;
+            nvalid = uniform(__popcll(m0) + __popcll(m1));
+        }
         const int nsub = (nvalid + 15) >> 4;
         const int tile0 = block * BT + wave * TPW;
         const uint32_t wbytes = (uint32_t)p.N * row_bytes, wsbytes = (uint32_t)p.N * srow_bytes;
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (size_t)e * wbytes, wbytes);
         const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.ws + (size_t)e * wsbytes, wsbytes);
-        // activation row of chunk row tid (gather index read now, stored after the barrier)
-        int src = 0;
-        if (tid < CS && tid < nvalid)
-            src = p.ids ? s_row[row0 + tid] / p.top_k
-                        : p.a_row_index ? p.a_row_index[row0 + tid] / p.top_k : row0 + tid;
+        // activation row of chunk row tid (gather index read now, stored after
+        // the barrier); small batch: row m is the m-th slot, its output row
+        int src = 0, orow = 0;
+        if (tid < CS && tid < nvalid) {
+            if constexpr (SRC == MX_SRC_CHUNKS) {
+                src = p.ids ? s_row[row0 + tid] / p.top_k
+                            : p.a_row_index ? p.a_row_index[row0 + tid] / p.top_k : row0 + tid;
+            } else {
+                orow = nth_slot(m0, m1, tid);
+                src = SRC == MX_SRC_ROUTE ? orow / p.top_k : orow;   // gate/up: the slot's token
+            }
+        }
         // weight scales of this wave's tiles, and the first RING-1 groups of codes
         uint32_t vw[TPW];
         u32x4 wsc[TPW];
@@ -412,13 +491,50 @@ __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
         for (int r = 0; r < RING - 1; ++r)
             load_w(r, r);
         __syncthreads();                                         // the previous item is done with s_a
-        if (tid < CS)
+        if (tid < CS) {
             s_src[tid] = src;
+            s_orow[tid] = orow;
+        }
         __syncthreads();
+        if constexpr (SRC == MX_SRC_ROUTE) {
+            // the rows' bf16 x, quantized here (the quantize kernel's bits)
+            // into the staging layout: block b of row r -> codes s_a[r][16b..],
+            // scale s_as[r][b]; every load of a batch before any store
+            const int nb = K >> 5;
+            for (int base = 0; base < nvalid * nb; base += kMxQuantBatch * 256) {
+                uint32_t w[kMxQuantBatch][16];
+#pragma unroll
+                for (int u = 0; u < kMxQuantBatch; ++u) {
+                    const int q = base + u * 256 + tid;
+                    if (q < nvalid * nb) {
+                        const int r = q / nb, b = q - r * nb;
+                        const u32x4 *xs4 = reinterpret_cast<const u32x4 *>(p.x + (size_t)s_src[r] * K + b * 32);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const u32x4 d = xs4[c];
+                            w[u][4 * c] = d.x;
+                            w[u][4 * c + 1] = d.y;
+                            w[u][4 * c + 2] = d.z;
+                            w[u][4 * c + 3] = d.w;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kMxQuantBatch; ++u) {
+                    const int q = base + u * 256 + tid;
+                    if (q < nvalid * nb) {
+                        const int r = q / nb, b = q - r * nb;
+                        uint32_t out[4];
+                        s_as[r * ASS + b] = (uint8_t)mx_quant_block(w[u], out);
+                        *reinterpret_cast<u32x4 *>(s_a + r * AST + b * 16) = u32x4{out[0], out[1], out[2], out[3]};
+                    }
+                }
+            }
+        }
         // stage the chunk's codes and scales: a batch of loads per thread goes
         // out before any is stored (rows past nvalid are left as they are:
         // their results are never stored)
-        for (int base = 0; base < nvalid * ppr; base += kMxStageBatch * 256) {
+        for (int base = 0; base < (SRC == MX_SRC_ROUTE ? 0 : nvalid * ppr); base += kMxStageBatch * 256) {
             u32x4 v[kMxStageBatch];
             uint32_t sv[kMxStageBatch / 4];
 #pragma unroll
@@ -490,11 +606,12 @@ __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
                 }
             }
         }
+        const int *orows = SRC == MX_SRC_CHUNKS ? nullptr : s_orow;
         if (KIND == MOE_GEMM_W13_SWIGLU && p.cq)
             mx_store_quant<TPW, NSUB>(p, acc, block, row0, nvalid, nsub, n16, kq, wave, tid,
-                                      reinterpret_cast<uint16_t *>(s_a));
+                                      reinterpret_cast<uint16_t *>(s_a), orows);
         else
-            mx_store<KIND, TPW, NSUB>(p, acc, tile0, row0, nvalid, nsub, n16, kq);
+            mx_store<KIND, TPW, NSUB>(p, acc, tile0, row0, nvalid, nsub, n16, kq, orows);
     }
 }
 
@@ -565,13 +682,22 @@ hipError_t mx_launch(const MxArgs &a, int max_rows, hipStream_t st)
 // epilogue's tile and the permutation scratch), then the tables; `slots`:
 // T * k with the permutation built from the ids, else 0.
 template <int TPW, int NSUB>
+size_t mx_stage_bytes(int K)
+{
+    constexpr int CS = 16 * NSUB;
+    const size_t a = (size_t)CS * (mx_code_stride(K) + mx_scale_stride(K));
+    const size_t h = (size_t)CS * mx_h_stride<TPW, NSUB>() * 2;    // the requantizing epilogue's tile
+    return a > h ? a : h;
+}
+
+template <int TPW, int NSUB>
 size_t mx_lds_bytes(int K, int num_experts, int slots)
 {
     constexpr int CS = 16 * NSUB;
-    size_t stage = (size_t)CS * (mx_code_stride(K) + mx_scale_stride(K) + 4);
-    const size_t h = (size_t)CS * mx_h_stride<TPW, NSUB>() * 2;    // the requantizing epilogue's tile
-    stage = stage > h ? stage : h;
-    return stage + sizeof(int) * (2 * (num_experts + 1) + 8) + 2 * (size_t)slots;
+    const size_t chunk_tables = sizeof(int) * (2 * (num_experts + 1) + 8) + 2 * (size_t)slots;
+    const size_t slot_tables = sizeof(int) * (2 * kDecMaxSlots + 4 + num_experts);   // small batch
+    return mx_stage_bytes<TPW, NSUB>(K) + sizeof(int) * 2 * CS +
+           (chunk_tables > slot_tables ? chunk_tables : slot_tables);
 }
 
 // Whether the LDS-staged kernel takes the launch (K <= 2048, the one-load
@@ -580,11 +706,10 @@ size_t mx_lds_bytes(int K, int num_experts, int slots)
 template <int TPW, int NSUB>
 bool mx_lds_fits(int K, int num_experts, int T = 0, int slots = 0)
 {
-    constexpr int CS = 16 * NSUB;
     if (K > 2048 || mx_lds_bytes<TPW, NSUB>(K, num_experts, slots) > 150 * 1024)
         return false;
     return slots == 0 || (num_experts <= 256 && slots <= kIdsPerThread * 256 &&
-                          ids_scratch_bytes(num_experts, T) <= (size_t)CS * (mx_code_stride(K) + mx_scale_stride(K)));
+                          ids_scratch_bytes(num_experts, T) <= mx_stage_bytes<TPW, NSUB>(K));
 }
 
 template <int KIND, int TPW, int NSUB, int RING>
@@ -608,6 +733,30 @@ hipError_t mx_launch_any(const MxArgs &a, int max_rows, hipStream_t st)
     const int nblocks = (a.N >> 4) / (4 * TPW);
     const long long chunks = (long long)min(a.num_experts, max_rows) + max_rows / CS;
     long long grid = chunks * nblocks;
+    const long long cap = (long long)device_cu_count() * per_cu;
+    grid = grid < cap ? grid : cap;
+    grid = grid < 1 ? 1 : grid;
+    if (grid >= kXcds)
+        grid -= grid % kXcds;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), lds, st, a);
+    return hipGetLastError();
+}
+
+// The LDS kernel with a small-batch item source (at most one item per
+// expert and weight block).
+template <int KIND, int TPW, int SRC, int PL>
+hipError_t mx_launch_small(const MxArgs &a, int max_rows, hipStream_t st)
+{
+    auto kernel = mx_gemm_lds_kernel<KIND, TPW, 1, 4, SRC, PL>;
+    const size_t lds = mx_lds_bytes<TPW, 1>(a.K, a.num_experts, 0);
+    static std::once_flag once;
+    std::call_once(once, [&] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  150 * 1024);
+    });
+    const int per_cu = mx_resident_per_cu(kernel, lds);
+    const int nblocks = (a.N >> 4) / (4 * TPW);
+    long long grid = (long long)min(a.num_experts, max_rows) * nblocks;
     const long long cap = (long long)device_cu_count() * per_cu;
     grid = grid < cap ? grid : cap;
     grid = grid < 1 ? 1 : grid;
@@ -650,6 +799,66 @@ static void mx_choose(const MxGemmLaunch &g, int &tpw, int &nsub)
         tpw >>= 1;
 }
 
+static MxArgs mx_args(const MxGemmLaunch &g);
+
+// The W4A4 layer's small-batch path: the tiling mx_choose picks with one
+// subtile (at most 16 rows per expert), on the LDS kernel.
+static bool mx_small_tiling(const MxGemmLaunch &g, int &tpw)
+{
+    int nsub;
+    mx_choose(g, tpw, nsub);
+    if (g.c_f32 || (g.N / 16) % (4 * tpw) != 0)
+        return false;
+    if (tpw == 4)
+        return mx_lds_fits<4, 1>(g.K, g.num_experts);
+    if (tpw == 2)
+        return mx_lds_fits<2, 1>(g.K, g.num_experts);
+    return mx_lds_fits<1, 1>(g.K, g.num_experts);
+}
+
+bool mx_small_supported(const MxGemmLaunch &g)
+{
+    int tpw;
+    return mx_small_tiling(g, tpw);
+}
+
+hipError_t launch_mx_small(const MxGemmLaunch &g, const MxSmallSource &src, hipStream_t st)
+{
+    int tpw;
+    if (!mx_small_tiling(g, tpw) || src.T * g.top_k > kDecMaxSlots || src.E_g > 256 ||
+        (g.kind == MOE_GEMM_W13_SWIGLU) != (src.logits != nullptr))
+        return hipErrorInvalidValue;
+    MxArgs a = mx_args(g);
+    a.T = src.T;
+    a.begin = src.begin;
+    a.logits = src.logits;
+    a.E_g = src.E_g;
+    a.x = src.x;
+    a.slot_ids = src.ids;
+    a.slot_w = src.w;
+    a.pres = src.pres;
+    a.a_row_index = nullptr;
+    a.c_row_index = nullptr;
+    const int R = g.max_rows;
+    if (g.kind == MOE_GEMM_W13_SWIGLU) {
+#define MOE_MXS_ROUTE(TP)                                                                                    \
+        if (tpw == TP)                                                                                      \
+            return src.E_g <= 64    ? mx_launch_small<MOE_GEMM_W13_SWIGLU, TP, MX_SRC_ROUTE, 4>(a, R, st)   \
+                   : src.E_g <= 128 ? mx_launch_small<MOE_GEMM_W13_SWIGLU, TP, MX_SRC_ROUTE, 8>(a, R, st)   \
+                                    : mx_launch_small<MOE_GEMM_W13_SWIGLU, TP, MX_SRC_ROUTE, 16>(a, R, st);
+        MOE_MXS_ROUTE(1) MOE_MXS_ROUTE(2) MOE_MXS_ROUTE(4)
+#undef MOE_MXS_ROUTE
+    } else if (g.kind == MOE_GEMM_W2) {
+        if (tpw == 1)
+            return mx_launch_small<MOE_GEMM_W2, 1, MX_SRC_SLOTS, 8>(a, R, st);
+        if (tpw == 2)
+            return mx_launch_small<MOE_GEMM_W2, 2, MX_SRC_SLOTS, 8>(a, R, st);
+        if (tpw == 4)
+            return mx_launch_small<MOE_GEMM_W2, 4, MX_SRC_SLOTS, 8>(a, R, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 bool mx_gemm_ids_supported(const MxGemmLaunch &g, int T)
 {
     int tpw, nsub;
@@ -665,7 +874,7 @@ bool mx_gemm_ids_supported(const MxGemmLaunch &g, int T)
     return false;
 }
 
-hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st)
+static MxArgs mx_args(const MxGemmLaunch &g)
 {
     MxArgs a{};
     a.a = g.a;
@@ -689,6 +898,12 @@ hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st)
     a.w_tiled = g.w_tiled ? 1 : 0;
     a.cq = g.kind == MOE_GEMM_W13_SWIGLU ? g.cq : nullptr;
     a.cs = g.kind == MOE_GEMM_W13_SWIGLU ? g.cs : nullptr;
+    return a;
+}
+
+hipError_t launch_mx_grouped_gemm(const MxGemmLaunch &g, hipStream_t st)
+{
+    MxArgs a = mx_args(g);
     if (g.ids) {
         if (!mx_gemm_ids_supported(g, g.T))
             return hipErrorInvalidValue;
