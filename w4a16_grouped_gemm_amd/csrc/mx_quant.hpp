@@ -16,10 +16,13 @@ namespace moe {
 
 // E2M1 code of |p| (p already divided by the block scale): nearest of 0, 0.5,
 // 1, 1.5, 2, 3, 4, 6; a midpoint goes to the even code; past 6 stays at 6.
+// The code is 7 minus the number of midpoints that m does not pass (a tie
+// counts as not passing when the lower code is even), seven compares and no
+// branch; a NaN passes none of the tests and takes code 7.
 __device__ __forceinline__ uint32_t e2m1_code(float m)
 {
-    return m <= 0.25f ? 0u : m < 0.75f ? 1u : m <= 1.25f ? 2u : m < 1.75f ? 3u
-         : m <= 2.5f ? 4u : m < 3.5f ? 5u : m <= 5.0f ? 6u : 7u;
+    return 7u - ((uint32_t)(m <= 0.25f) + (uint32_t)(m < 0.75f) + (uint32_t)(m <= 1.25f) + (uint32_t)(m < 1.75f) +
+                 (uint32_t)(m <= 2.5f) + (uint32_t)(m < 3.5f) + (uint32_t)(m <= 5.0f));
 }
 
 // One block of 32 bf16 values (w[q] holds elements 2q and 2q + 1, low half
