@@ -2,7 +2,10 @@
 
 - moe_mxfp4_quantize: bit-exact against the oracle's quantization (codes and
   scales), on random blocks across wide magnitudes with planted grid
-  midpoints, signed zeros, all-zero blocks and subnormal maxima.
+  midpoints, signed zeros, all-zero blocks and subnormal maxima; and on
+  every finite bf16 bit pattern under block maxima from the largest finite
+  value down to the smallest subnormal (non-finite activations are outside
+  the quantizer's contract: the two sides give such blocks different scales).
 - moe_grouped_gemm_mxfp4: exact products and power-of-two block scales keep
   every sum exact in binary32 at these magnitudes, so RAW / W2 with f32
   output equal the oracle bit for bit (ragged experts, a gather through a
@@ -48,6 +51,32 @@ def test_quantize_bit_exact(rows, K):
     say(f"mxfp4 quantize rows={rows} K={K}")
     rng = np.random.default_rng(rows + K)
     xb = _blocks(rng, rows, K)
+    codes, scales = ops.mxfp4_quantize(bf16_dev(xb))
+    torch.cuda.synchronize()
+    rc, rs = oracle.mx_quantize(xb)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("amax_bits", [0x7F7F, 0x4730, 0x3FC0, 0x0080, 0x0041, 0x0001])
+def test_quantize_every_bf16_value(amax_bits):
+    # every bf16 bit pattern whose magnitude does not exceed the block maximum
+    # (a finite value), 31 to a block after that maximum, so each block
+    # exponent sees the whole range below it
+    from w4a16_grouped_gemm_amd import ops
+    import torch
+    say(f"mxfp4 quantize every bf16 value, block maximum 0x{amax_bits:04x}")
+    allv = np.arange(65536, dtype=np.uint32)
+    vals = allv[(allv & 0x7FFF) <= amax_bits]
+    nblk = -(-len(vals) // 31)
+    body = np.zeros(nblk * 31, np.uint16)
+    body[:len(vals)] = vals
+    blocks = np.concatenate([np.full((nblk, 1), amax_bits, np.uint16), body.reshape(nblk, 31)], axis=1)
+    K = 2048
+    rows = -(-nblk // (K // 32))
+    xb = np.zeros((rows * (K // 32), 32), np.uint16)
+    xb[:nblk] = blocks
+    xb = xb.reshape(rows, K)
     codes, scales = ops.mxfp4_quantize(bf16_dev(xb))
     torch.cuda.synchronize()
     rc, rs = oracle.mx_quantize(xb)

@@ -14,23 +14,20 @@
 
 namespace moe {
 
-// E2M1 code of |p| (p already divided by the block scale): nearest of 0, 0.5,
-// 1, 1.5, 2, 3, 4, 6; a midpoint goes to the even code; past 6 stays at 6.
-// The code is 7 minus the number of midpoints that m does not pass (a tie
-// counts as not passing when the lower code is even), seven compares and no
-// branch; a NaN passes none of the tests and takes code 7.
-__device__ __forceinline__ uint32_t e2m1_code(float m)
-{
-    return 7u - ((uint32_t)(m <= 0.25f) + (uint32_t)(m < 0.75f) + (uint32_t)(m <= 1.25f) + (uint32_t)(m < 1.75f) +
-                 (uint32_t)(m <= 2.5f) + (uint32_t)(m < 3.5f) + (uint32_t)(m <= 5.0f));
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // One block of 32 bf16 values (w[q] holds elements 2q and 2q + 1, low half
 // first) -> 16 bytes of codes (element k in nibble k % 8 of dword k / 8) and
 // the E8M0 scale byte: the shared exponent floor(log2 amax) - 2 (clamped to
 // the E8M0 range; an all-zero block takes 2^-127), each element / 2^e rounded
-// to the nearest E2M1 value by comparisons against the midpoints (exact in
-// binary32: the division by a power of two is exact), its sign kept.
+// to the nearest E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6; a midpoint to the
+// even code, past 6 to 6, a NaN or infinity to 6 with its sign).
+// The rounding is gfx950's scaled FP4 conversion (two bf16 elements -> one
+// code byte, divided by the scale operand): on every bf16 value, at scales
+// 2^-127 .. 2^127 (2^-127 a binary32 subnormal), it gives exactly the codes
+// of the midpoint comparisons above, NaN and infinity included (measured on
+// MI355X against that rule). The division by a power of two is exact, and a
+// finite block's elements / 2^e stay below 8.
 __device__ __forceinline__ uint32_t mx_quant_block(const uint32_t (&w)[16], uint32_t (&out)[4])
 {
     // the block maximum on the magnitude bits (bf16 orders like its magnitude)
@@ -48,24 +45,18 @@ __device__ __forceinline__ uint32_t mx_quant_block(const uint32_t (&w)[16], uint
         ex = fl - 2;
         ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
     }
-    // 2^-ex as a binary32 power of two: a finite bf16 maximum is below
-    // 2^128, so ex <= 125 and 2^-ex is a normal number (exponent field
-    // 127 - ex in [2, 254]); |v| * 2^-ex is then exact or, far below the
-    // first midpoint 0.25, rounds harmlessly
-    const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);
+    // 2^ex as a binary32 value: normal from 2^-126 on, 2^-127 the subnormal
+    // 0x00400000 (a finite bf16 maximum gives ex <= 125)
+    const float scale = __uint_as_float(ex >= -126 ? (uint32_t)(ex + 127) << 23 : 0x00400000u);
 #pragma unroll
     for (int d = 0; d < 4; ++d)
         out[d] = 0u;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-#pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf) {
-            const uint32_t b = hlf ? (w[q] >> 16) : (w[q] & 0xFFFFu);
-            const float v = __uint_as_float(b << 16);
-            const uint32_t code = e2m1_code(fabsf(v) * inv) | ((b >> 12) & 8u);
-            const int k = 2 * q + hlf;                 // element of the block
-            out[k >> 3] |= code << (4 * (k & 7));
-        }
+        // elements 2q, 2q + 1 -> byte q % 4 of dword q / 4 (low nibble first);
+        // with a zero destination and byte 0 selected the result's other bits are 0
+        const uint32_t byte = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2, w[q]), scale, 0);
+        out[q >> 2] |= byte << (8 * (q & 3));
     }
     return (uint32_t)(ex + 127);
 }
