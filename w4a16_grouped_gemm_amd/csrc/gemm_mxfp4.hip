@@ -147,14 +147,14 @@ __device__ __forceinline__ void mx_store(const MxArgs &p, const floatx4 (&acc)[T
                 float u[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    u[i] = __shfl_xor(rr[i], 8, 64);
+                    u[i] = row_swap8(rr[i]);
                 if (n16 < 8) {
                     uint16_t *c = static_cast<uint16_t *>(p.c);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (sb * 16 + kq * 4 + i < nvalid)
                             c[(size_t)orow[i] * p.ldc + (tile0 + t) * 8 + n16] =
-                                (uint16_t)f32_to_bf16_rne(silu(rr[i]) * u[i]);
+                                (uint16_t)f32_to_bf16_rne(silu_fast(rr[i]) * u[i]);
                 }
             } else {
 #pragma unroll
@@ -178,6 +178,52 @@ __device__ __forceinline__ void mx_store(const MxArgs &p, const floatx4 (&acc)[T
 // activations), then each thread quantizes one row's block of 32 features
 // with the shared block quantizer and stores its 16 code bytes and scale
 // byte: the same bits as storing bf16 h and quantizing it afterwards.
+// Epilogue of one item with bf16 output, through LDS: each wave writes one
+// subtile's TPW tiles (16 rows x 16 columns each) to its own LDS area, then
+// every lane stores one 16-byte run of an output row (two lanes per tile
+// row) instead of sixteen scattered 2-byte values. `s_area`: 4 * TPW * 512
+// bytes that no wave reads any more (the caller has passed a barrier).
+template <int TPW, int NSUB>
+__device__ __forceinline__ void mx_store_lds(const MxArgs &p, const floatx4 (&acc)[TPW][NSUB], int tile0, int row0,
+                                             int nvalid, int nsub, int n16, int kq, int wave, int lane,
+                                             uint16_t *s_area, const int *s_orow)
+{
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c_row_index, p.c_row_bytes);
+    uint16_t *so = s_area + wave * (TPW * 256);
+    uint16_t *c = static_cast<uint16_t *>(p.c);
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+        if (sb >= nsub)
+            break;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const floatx4 v = acc[t][sb];
+            const float rr[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                so[(t * 16 + kq * 4 + i) * 16 + n16] = (uint16_t)f32_to_bf16_rne(rr[i]);
+        }
+        __builtin_amdgcn_wave_barrier();
+        // lane: tile b0 + lane / 32, row (lane / 2) % 16, columns 8 (lane % 2) ..
+        const int rr = (lane >> 1) & 15, part = lane & 1;
+        const int m = sb * 16 + rr;
+        int orow = 0;
+        if (m < nvalid)
+            orow = s_orow ? s_orow[m]
+                 : p.c_row_index ? (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(row0 + m) * 4u, 0, 0)
+                                 : row0 + m;
+#pragma unroll
+        for (int b0 = 0; b0 < TPW; b0 += 2) {
+            const int t = b0 + (lane >> 5);
+            if (t < TPW && m < nvalid) {
+                const u32x4 d = *reinterpret_cast<const u32x4 *>(so + (t * 16 + rr) * 16 + part * 8);
+                *reinterpret_cast<u32x4 *>(c + (size_t)orow * p.ldc + (tile0 + t) * 16 + part * 8) = d;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();                 // the area is rewritten for the next subtile
+    }
+}
+
 template <int TPW, int NSUB>
 __host__ __device__ constexpr int mx_h_stride() { return 32 * TPW + 8; }   // bf16 elements per LDS row
 
@@ -199,12 +245,12 @@ __device__ __forceinline__ void mx_store_quant(const MxArgs &p, const floatx4 (&
             float u[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                u[i] = __shfl_xor(rr[i], 8, 64);       // partner lane holds the up row
+                u[i] = row_swap8(rr[i]);               // partner lane holds the up row
             if (n16 < 8) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     s_h[(sb * 16 + kq * 4 + i) * HST + (wave * TPW + t) * 8 + n16] =
-                        (uint16_t)f32_to_bf16_rne(silu(rr[i]) * u[i]);
+                        (uint16_t)f32_to_bf16_rne(silu_fast(rr[i]) * u[i]);
             }
         }
     }
@@ -610,7 +656,11 @@ __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
         if (KIND == MOE_GEMM_W13_SWIGLU && p.cq)
             mx_store_quant<TPW, NSUB>(p, acc, block, row0, nvalid, nsub, n16, kq, wave, tid,
                                       reinterpret_cast<uint16_t *>(s_a), orows);
-        else
+        else if (KIND != MOE_GEMM_W13_SWIGLU && !p.c_f32 && 4 * TPW * 512 <= stage) {
+            __syncthreads();                                     // every wave is done with the staged rows
+            mx_store_lds<TPW, NSUB>(p, acc, tile0, row0, nvalid, nsub, n16, kq, wave, lane,
+                                    reinterpret_cast<uint16_t *>(s_a), orows);
+        } else
             mx_store<KIND, TPW, NSUB>(p, acc, tile0, row0, nvalid, nsub, n16, kq, orows);
     }
 }
