@@ -178,34 +178,27 @@ __device__ __forceinline__ void mx_store(const MxArgs &p, const floatx4 (&acc)[T
 // activations), then each thread quantizes one row's block of 32 features
 // with the shared block quantizer and stores its 16 code bytes and scale
 // byte: the same bits as storing bf16 h and quantizing it afterwards.
-// Epilogue of one item with bf16 output, through LDS: each wave writes one
-// subtile's TPW tiles (16 rows x 16 columns each) to its own LDS area, then
-// every lane stores one 16-byte run of an output row (two lanes per tile
-// row) instead of sixteen scattered 2-byte values. `s_area`: 4 * TPW * 512
-// bytes that no wave reads any more (the caller has passed a barrier).
+// Epilogue of one item with bf16 output, through LDS: each wave writes two
+// tiles of a subtile (16 rows x 16 columns each) to its own 1 KiB of LDS,
+// then every lane stores one 16-byte run of an output row (two lanes per
+// tile row) instead of four scattered 2-byte values. `s_area`: 4 KiB that
+// no wave reads any more (the caller has passed a barrier).
+constexpr int kMxStoreLdsBytes = 4 * 1024;
+
 template <int TPW, int NSUB>
 __device__ __forceinline__ void mx_store_lds(const MxArgs &p, const floatx4 (&acc)[TPW][NSUB], int tile0, int row0,
                                              int nvalid, int nsub, int n16, int kq, int wave, int lane,
                                              uint16_t *s_area, const int *s_orow)
 {
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c_row_index, p.c_row_bytes);
-    uint16_t *so = s_area + wave * (TPW * 256);
+    uint16_t *so = s_area + wave * 512;
     uint16_t *c = static_cast<uint16_t *>(p.c);
+    // lane: tile pair + lane / 32, row (lane / 2) % 16, columns 8 (lane % 2) ..
+    const int rr = (lane >> 1) & 15, part = lane & 1, half = lane >> 5;
 #pragma unroll
     for (int sb = 0; sb < NSUB; ++sb) {
         if (sb >= nsub)
             break;
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const floatx4 v = acc[t][sb];
-            const float rr[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                so[(t * 16 + kq * 4 + i) * 16 + n16] = (uint16_t)f32_to_bf16_rne(rr[i]);
-        }
-        __builtin_amdgcn_wave_barrier();
-        // lane: tile b0 + lane / 32, row (lane / 2) % 16, columns 8 (lane % 2) ..
-        const int rr = (lane >> 1) & 15, part = lane & 1;
         const int m = sb * 16 + rr;
         int orow = 0;
         if (m < nvalid)
@@ -213,14 +206,25 @@ __device__ __forceinline__ void mx_store_lds(const MxArgs &p, const floatx4 (&ac
                  : p.c_row_index ? (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(row0 + m) * 4u, 0, 0)
                                  : row0 + m;
 #pragma unroll
-        for (int b0 = 0; b0 < TPW; b0 += 2) {
-            const int t = b0 + (lane >> 5);
+        for (int t0 = 0; t0 < TPW; t0 += 2) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (t0 + u < TPW) {
+                    const floatx4 v = acc[t0 + u][sb];
+                    const float r4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        so[(u * 16 + kq * 4 + i) * 16 + n16] = (uint16_t)f32_to_bf16_rne(r4[i]);
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            const int t = t0 + half;
             if (t < TPW && m < nvalid) {
-                const u32x4 d = *reinterpret_cast<const u32x4 *>(so + (t * 16 + rr) * 16 + part * 8);
+                const u32x4 d = *reinterpret_cast<const u32x4 *>(so + (half * 16 + rr) * 16 + part * 8);
                 *reinterpret_cast<u32x4 *>(c + (size_t)orow * p.ldc + (tile0 + t) * 16 + part * 8) = d;
             }
+            __builtin_amdgcn_wave_barrier();             // the area is rewritten for the next pair
         }
-        __builtin_amdgcn_wave_barrier();                 // the area is rewritten for the next subtile
     }
 }
 
@@ -656,7 +660,7 @@ __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
         if (KIND == MOE_GEMM_W13_SWIGLU && p.cq)
             mx_store_quant<TPW, NSUB>(p, acc, block, row0, nvalid, nsub, n16, kq, wave, tid,
                                       reinterpret_cast<uint16_t *>(s_a), orows);
-        else if (KIND != MOE_GEMM_W13_SWIGLU && !p.c_f32 && 4 * TPW * 512 <= stage) {
+        else if (KIND != MOE_GEMM_W13_SWIGLU && !p.c_f32 && kMxStoreLdsBytes <= stage) {
             __syncthreads();                                     // every wave is done with the staged rows
             mx_store_lds<TPW, NSUB>(p, acc, tile0, row0, nvalid, nsub, n16, kq, wave, lane,
                                     reinterpret_cast<uint16_t *>(s_a), orows);
