@@ -596,25 +596,20 @@ def main():
     w13b, w2b = weight_bytes_per_expert(wl.hidden, wl.inter)
 
     # ---- the headline: exactly --steps steps after --warmup, one step = one layer call
+    # (replica i % L); the warm-up steps and the timed steps are one HIP graph
+    # each, so a step pays no launch of its own
     log(f"timing {args.steps} steps at T={T}")
     fns = layer_fns(ops, wl, weights, batches, L, torch, layout)
-    graph_all = capture(torch, fns)
-    singles = [capture(torch, [f]) for f in fns]
-
-    def run(n):
-        full, rem = divmod(n, L)
-        for _ in range(full):
-            graph_all.replay()
-        for i in range(rem):
-            singles[i].replay()
-
-    run(args.warmup)
+    graph_warm = capture(torch, [fns[i % L] for i in range(args.warmup)]) if args.warmup > 0 else None
+    graph_steps = capture(torch, [fns[i % L] for i in range(args.steps)])
+    if graph_warm is not None:
+        graph_warm.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run(args.steps)
+    graph_steps.replay()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    del graph_all, singles
+    del graph_warm, graph_steps
     ms = dt / args.steps * 1e3
     tok_s = T * args.steps / dt
     st = routing_stats(ops, wl, batches, torch)
