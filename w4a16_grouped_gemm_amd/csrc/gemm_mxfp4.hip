@@ -441,23 +441,40 @@ __global__ __launch_bounds__(256) void mx_gemm_lds_kernel(MxArgs p)
         for (int e = tid; e < E; e += 256)
             s_first[e] = kDecMaxSlots;
         if constexpr (SRC == MX_SRC_ROUTE) {
-            // every workgroup routes all tokens: one DPP row of 16 lanes per token
-            for (int t0 = wave * 4; t0 < p.T; t0 += 16) {
-                const int t = t0 + (lane >> 4);
-                if (t < p.T) {
+            // every workgroup routes all tokens: one DPP row of 16 lanes per
+            // token, or a whole wave per token while there are at most four
+            // (the k rounds of the selection are the routing's serial part; 64
+            // lanes hold a quarter of the logits each; the same selection and
+            // weights bit for bit, the weights formed in lanes 0..k-1)
+            auto keep = [&](int t, int q, int eg, float wt) {
+                if (q < p.top_k) {
+                    const int sl = t * p.top_k + q;
+                    const int le = eg - p.begin;
+                    const int loc = (le >= 0 && le < E) ? le : -1;
+                    s_loc[sl] = loc;
+                    if (blockIdx.x == 0) {
+                        p.slot_ids[sl] = eg;
+                        p.slot_w[sl] = wt;
+                        p.pres[sl] = loc >= 0 ? sl : -1;
+                    }
+                }
+            };
+            if (p.T <= 4) {
+                if (wave < p.T) {
                     int eg;
                     float wt;
-                    route_token<16, PL>(p.logits + (size_t)t * p.E_g, p.E_g, p.top_k, n16, eg, wt);
-                    if (n16 < p.top_k) {
-                        const int sl = t * p.top_k + n16;
-                        const int le = eg - p.begin;
-                        const int loc = (le >= 0 && le < E) ? le : -1;
-                        s_loc[sl] = loc;
-                        if (blockIdx.x == 0) {
-                            p.slot_ids[sl] = eg;
-                            p.slot_w[sl] = wt;
-                            p.pres[sl] = loc >= 0 ? sl : -1;
-                        }
+                    route_token<64, (PL >= 4 ? PL / 4 : 1)>(p.logits + (size_t)wave * p.E_g, p.E_g, p.top_k, lane, eg,
+                                                           wt);
+                    keep(wave, lane, eg, wt);
+                }
+            } else {
+                for (int t0 = wave * 4; t0 < p.T; t0 += 16) {
+                    const int t = t0 + (lane >> 4);
+                    if (t < p.T) {
+                        int eg;
+                        float wt;
+                        route_token<16, PL>(p.logits + (size_t)t * p.E_g, p.E_g, p.top_k, n16, eg, wt);
+                        keep(t, n16, eg, wt);
                     }
                 }
             }
