@@ -172,17 +172,11 @@ __device__ __forceinline__ void mx_store(const MxArgs &p, const floatx4 (&acc)[T
     }
 }
 
-// SwiGLU epilogue that stores h already requantized (the down GEMM's MXFP4
-// activations): the item's bf16 h values, rounded as mx_store rounds them, go
-// to an LDS tile of CS rows x 32 TPW features (s_h, over the staged
-// activations), then each thread quantizes one row's block of 32 features
-// with the shared block quantizer and stores its 16 code bytes and scale
-// byte: the same bits as storing bf16 h and quantizing it afterwards.
 // Epilogue of one item with bf16 output, through LDS: each wave writes two
 // tiles of a subtile (16 rows x 16 columns each) to its own 1 KiB of LDS,
 // then every lane stores one 16-byte run of an output row (two lanes per
-// tile row) instead of four scattered 2-byte values. `s_area`: 4 KiB that
-// no wave reads any more (the caller has passed a barrier).
+// tile row) instead of four scattered 2-byte values per tile. `s_area`: 4 KiB
+// that no wave reads any more (the caller has passed a barrier).
 constexpr int kMxStoreLdsBytes = 4 * 1024;
 
 template <int TPW, int NSUB>
@@ -231,6 +225,12 @@ __device__ __forceinline__ void mx_store_lds(const MxArgs &p, const floatx4 (&ac
 template <int TPW, int NSUB>
 __host__ __device__ constexpr int mx_h_stride() { return 32 * TPW + 8; }   // bf16 elements per LDS row
 
+// SwiGLU epilogue that stores h already requantized (the down GEMM's MXFP4
+// activations): the item's bf16 h values, rounded as mx_store rounds them, go
+// to an LDS tile of CS rows x 32 TPW features (s_h, over the staged
+// activations), then each thread quantizes one row's block of 32 features
+// with the shared block quantizer and stores its 16 code bytes and scale
+// byte: the same bits as storing bf16 h and quantizing it afterwards.
 template <int TPW, int NSUB>
 __device__ __forceinline__ void mx_store_quant(const MxArgs &p, const floatx4 (&acc)[TPW][NSUB], int block, int row0,
                                                int nvalid, int nsub, int n16, int kq, int wave, int tid,
