@@ -439,6 +439,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         corr = mfma(a[i], neg136, corr);
+                    // tile t's scale FMAs go out among tile t + 1's MFMAs
+                    // and stay in this group (no sinking past the loads
+                    // that follow), so only the last tile's trail it
+                    floatx4 accp = corr;
+                    float scp = 0.f;
 #pragma unroll
                     for (int t = 0; t < TPW; ++t) {
                         floatx4 acc = corr;
@@ -446,14 +451,24 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
                         acc = mfma(a[1], unpack8(wv[b][t].y), acc);
                         acc = mfma(a[2], unpack8(wv[b][t].z), acc);
                         acc = mfma(a[3], unpack8(wv[b][t].w), acc);
+                        if (t > 0) {
+                            tot[t - 1][sb].x = __builtin_fmaf(scp, accp.x, tot[t - 1][sb].x);
+                            tot[t - 1][sb].y = __builtin_fmaf(scp, accp.y, tot[t - 1][sb].y);
+                            tot[t - 1][sb].z = __builtin_fmaf(scp, accp.z, tot[t - 1][sb].z);
+                            tot[t - 1][sb].w = __builtin_fmaf(scp, accp.w, tot[t - 1][sb].w);
+                        }
                         const uint32_t d = sv[buf][t][j >> 1];
                         const int hi = KSEG == 1 ? buf : (j & 1);
-                        const float sc = __uint_as_float(hi ? (d & 0xFFFF0000u) : (d << 16));
-                        tot[t][sb].x = __builtin_fmaf(sc, acc.x, tot[t][sb].x);
-                        tot[t][sb].y = __builtin_fmaf(sc, acc.y, tot[t][sb].y);
-                        tot[t][sb].z = __builtin_fmaf(sc, acc.z, tot[t][sb].z);
-                        tot[t][sb].w = __builtin_fmaf(sc, acc.w, tot[t][sb].w);
+                        scp = __uint_as_float(hi ? (d & 0xFFFF0000u) : (d << 16));
+                        accp = acc;
                     }
+                    tot[TPW - 1][sb].x = __builtin_fmaf(scp, accp.x, tot[TPW - 1][sb].x);
+                    tot[TPW - 1][sb].y = __builtin_fmaf(scp, accp.y, tot[TPW - 1][sb].y);
+                    tot[TPW - 1][sb].z = __builtin_fmaf(scp, accp.z, tot[TPW - 1][sb].z);
+                    tot[TPW - 1][sb].w = __builtin_fmaf(scp, accp.w, tot[TPW - 1][sb].w);
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t)
+                        asm volatile("" : "+v"(tot[t][sb]));
                 }
             }
         };
@@ -936,6 +951,21 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
                 // tile t + 1's codes and scale are read while tile t computes
                 u32x4 w_next = wsrc[0];
                 uint32_t sd_next = __builtin_amdgcn_ds_bpermute(src_lane, (int)((g & 2) ? csc[0].y : csc[0].x));
+                // Tile t's scale FMAs wait for its MFMA chains; they are
+                // issued among tile t + 1's MFMAs (the matrix unit runs
+                // independent VALU work of the same wave alongside), so only
+                // the last tile's FMAs follow the group's last MFMA.
+                floatx4 accp[NSV];
+                float scp = 0.f;
+                auto scale_add = [&](int t) {
+#pragma unroll
+                    for (int sb = 0; sb < NSV; ++sb) {
+                        tot[t][sb].x = __builtin_fmaf(scp, accp[sb].x, tot[t][sb].x);
+                        tot[t][sb].y = __builtin_fmaf(scp, accp[sb].y, tot[t][sb].y);
+                        tot[t][sb].z = __builtin_fmaf(scp, accp[sb].z, tot[t][sb].z);
+                        tot[t][sb].w = __builtin_fmaf(scp, accp[sb].w, tot[t][sb].w);
+                    }
+                };
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
                     const u32x4 w4 = w_next;
@@ -957,14 +987,28 @@ __global__ __launch_bounds__(kTileWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
                         for (int sb = 0; sb < NSV; ++sb)
                             acc[sb] = mfma(a[sb][i], qv[i], acc[sb]);
+                    if (t > 0)
+                        scale_add(t - 1);
+                    // issue order: one MFMA, then up to two VALU instructions
+                    // (the previous tile's FMAs, the next tile's unpack)
 #pragma unroll
-                    for (int sb = 0; sb < NSV; ++sb) {
-                        tot[t][sb].x = __builtin_fmaf(sc, acc[sb].x, tot[t][sb].x);
-                        tot[t][sb].y = __builtin_fmaf(sc, acc[sb].y, tot[t][sb].y);
-                        tot[t][sb].z = __builtin_fmaf(sc, acc[sb].z, tot[t][sb].z);
-                        tot[t][sb].w = __builtin_fmaf(sc, acc[sb].w, tot[t][sb].w);
+                    for (int i = 0; i < 4 * NSV; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
                     }
+#pragma unroll
+                    for (int sb = 0; sb < NSV; ++sb)
+                        accp[sb] = acc[sb];
+                    scp = sc;
                 }
+                scale_add(TPW - 1);
+                // keep the FMAs here, among this group's MFMAs, instead of
+                // letting them sink past the code copies that follow
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int sb = 0; sb < NSV; ++sb)
+                        asm volatile("" : "+v"(tot[t][sb]));
             };
 
             wait_barrier(std::integral_constant<int, 2 * NCOPY + TPW + 2 + NST>());   // group 0 landed
