@@ -321,10 +321,17 @@ __global__ __launch_bounds__(KS * SP * 64) void decode_down_combine_kernel(Decod
                     for (int i = 0; i < 4; ++i) {
                         const u32x4 v = *reinterpret_cast<const u32x4 *>(hrow + g * kGroup + kq * 32 + i * 8);
                         const u32x4 z = {0u, 0u, 0u, 0u};
-                        const u32x4 va = n16 == 0 ? v : z;    // row 0 only: the token's h row
-                        a[i] = p.w_tiled ? va : permute_act(va);
+                        a[i] = n16 == 0 ? v : z;              // row 0 only: the token's h row
                     }
-                    splitk_group(a, wv[u][q], sc[u][q], tot);
+                    // a branch on the layout, not a select (tiled codes: no permutation)
+                    if (p.w_tiled) {
+                        splitk_group(a, wv[u][q], sc[u][q], tot);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            a[i] = permute_act(a[i]);
+                        splitk_group(a, wv[u][q], sc[u][q], tot);
+                    }
                 }
             }
             if (kq == 0)

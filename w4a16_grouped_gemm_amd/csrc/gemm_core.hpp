@@ -161,11 +161,17 @@ __device__ __forceinline__ floatx4 splitk_wave_sum(__amdgpu_buffer_rsrc_t rw, ui
         for (int j = 0; j < GB; ++j) {
             if (gb + j >= g1)
                 break;
-            u32x4 a[4];
+            // a branch on the layout, not a select: with tiled codes the
+            // fragments are used as loaded and no permutation is formed
+            if (w_tiled) {
+                splitk_group(xa[j], wv[j], sc[j], tot);
+            } else {
+                u32x4 a[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = w_tiled ? xa[j][i] : permute_act(xa[j][i]);
-            splitk_group(a, wv[j], sc[j], tot);
+                for (int i = 0; i < 4; ++i)
+                    a[i] = permute_act(xa[j][i]);
+                splitk_group(a, wv[j], sc[j], tot);
+            }
         }
     }
     return tot;

@@ -409,11 +409,27 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         auto write_act = [&](auto bufc) {
             constexpr int buf = decltype(bufc)::value;
             u32x4 *dst = &s_act[buf][0][0][0][0];
+            // a branch on the layout, not a select: with tiled codes the
+            // fragments are stored as loaded and no permutation is formed
+            if (p.w_tiled) {
 #pragma unroll
-            for (int j = 0; j < KSEG; ++j)
+                for (int j = 0; j < KSEG; ++j)
 #pragma unroll
-                for (int sb = 0; sb < NSUB; ++sb)
-                    dst[(j * NSUB + sb) * 256 + st_idx] = p.w_tiled ? xr[j][sb] : permute_act(xr[j][sb]);
+                    for (int sb = 0; sb < NSUB; ++sb)
+                        dst[(j * NSUB + sb) * 256 + st_idx] = xr[j][sb];
+            } else {
+#pragma unroll
+                for (int j = 0; j < KSEG; ++j)
+#pragma unroll
+                    for (int sb = 0; sb < NSUB; ++sb)
+                        xr[j][sb] = permute_act(xr[j][sb]);
+                asm volatile("" ::: "memory");   // keeps the two store sequences apart
+#pragma unroll
+                for (int j = 0; j < KSEG; ++j)
+#pragma unroll
+                    for (int sb = 0; sb < NSUB; ++sb)
+                        dst[(j * NSUB + sb) * 256 + st_idx] = xr[j][sb];
+            }
         };
         auto load_w = [&](int g, int b) {
             const uint32_t oor = g < G ? 0u : kOutOfRange;
