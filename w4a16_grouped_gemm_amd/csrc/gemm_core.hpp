@@ -261,6 +261,21 @@ __device__ __forceinline__ int chunk_expert(const int *s_prefix, int E, int chun
     return lo;
 }
 
+// The same expert found by the whole wave at once (every lane active, chunk
+// uniform): the prefix is non-decreasing, so the experts e >= 1 with
+// s_prefix[e] <= chunk are exactly 1 .. answer, and the lanes count them in
+// one pass of independent LDS reads per 64 experts instead of a chain of
+// log2(E) dependent ones.
+__device__ __forceinline__ int chunk_expert_wave(const int *s_prefix, int E, int chunk, int lane)
+{
+    int n = 0;
+    for (int e0 = 1; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        n += __popcll(__ballot(e < E && s_prefix[e] <= chunk));
+    }
+    return n;
+}
+
 // ---------------------------------------------------------------------------
 // SRC_IDS: the layer's stable expert permutation (moe_permute's result) built
 // by every workgroup in LDS from the routing ids, so that the gate/up GEMM

@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         int e, row0, nvalid;
         uint64_t m0 = 0, m1 = 0;                          // small batch: the expert's slots
         if constexpr (CHUNKED) {
-            e = uniform(chunk_expert(s_prefix, E, chunk));
+            e = uniform(chunk_expert_wave(s_prefix, E, chunk, lane));
             row0 = uniform(s_off[e] + (chunk - s_prefix[e]) * CS);
             nvalid = uniform(min(CS, s_off[e + 1] - row0));
         } else {
@@ -536,17 +536,25 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
                 for (int sb = 0; sb < NSUB; ++sb) {
                     const floatx4 v = tot[t][sb];
                     const float r4[4] = {v.x, v.y, v.z, v.w};
+                    if (SWI) {
+                        // lane n16 < 8 holds the gate row of feature n16 for
+                        // token rows 4 kq + 0..3, lane n16 + 8 the up row: the
+                        // gate lane forms rows 0 and 1 (it receives two up
+                        // values), the up lane rows 2 and 3 (two gate values),
+                        // so every lane stores and none waits on a branch
+                        const bool gl = n16 < 8;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int rr = kq * 4 + i;
-                        if (SWI) {
-                            const float up = row_swap8(r4[i]);     // lane n16 + 8 holds the up row
-                            if (n16 < 8)
-                                so[((t * NSUB + sb) * 16 + rr) * COLS + n16] =
-                                    (uint16_t)f32_to_bf16_rne(silu_fast(r4[i]) * up);
-                        } else {
-                            so[((t * NSUB + sb) * 16 + rr) * COLS + n16] = (uint16_t)f32_to_bf16_rne(r4[i]);
+                        for (int j = 0; j < 2; ++j) {
+                            const float recv = row_swap8(gl ? r4[j + 2] : r4[j]);
+                            const float gate = gl ? r4[j] : recv, up = gl ? recv : r4[j + 2];
+                            const int rr = kq * 4 + (gl ? j : j + 2);
+                            so[((t * NSUB + sb) * 16 + rr) * COLS + (n16 & 7)] =
+                                (uint16_t)f32_to_bf16_rne(silu_fast(gate) * up);
                         }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            so[((t * NSUB + sb) * 16 + kq * 4 + i) * COLS + n16] = (uint16_t)f32_to_bf16_rne(r4[i]);
                     }
                 }
             __builtin_amdgcn_wave_barrier();
@@ -612,7 +620,7 @@ __global__ __launch_bounds__(NWAVES * 64) void gemm_splitk_kernel(GemmArgs p)
     for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
         const int chunk = item / ntiles;
         const int tile = item - chunk * ntiles;
-        const int e = uniform(chunk_expert(s_prefix, E, chunk));
+        const int e = uniform(chunk_expert_wave(s_prefix, E, chunk, lane));
         const int row0 = uniform(expert_offset(p.offsets, p.dense_rows, e) + (chunk - s_prefix[e]) * CS);
         const int nvalid = uniform(min(CS, expert_offset(p.offsets, p.dense_rows, e + 1) - row0));
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(expert_codes(p, e, (uint32_t)p.N * row_bytes), (uint32_t)p.N * row_bytes);
