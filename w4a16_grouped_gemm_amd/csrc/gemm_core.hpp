@@ -269,9 +269,11 @@ __device__ __forceinline__ int chunk_expert(const int *s_prefix, int E, int chun
 __device__ __forceinline__ int chunk_expert_wave(const int *s_prefix, int E, int chunk, int lane)
 {
     int n = 0;
+#pragma unroll 2
     for (int e0 = 1; e0 < E; e0 += 64) {
         const int e = e0 + lane;
-        n += __popcll(__ballot(e < E && s_prefix[e] <= chunk));
+        const int pv = s_prefix[e < E ? e : E];      // entry E exists: no load under a branch
+        n += __popcll(__ballot((e < E) & (pv <= chunk)));
     }
     return n;
 }
