@@ -99,12 +99,35 @@ __device__ __forceinline__ void route_token(const float *__restrict__ row, int E
 #pragma unroll
         for (int i = 0; i < PL; ++i)
             bv = val[i] > bv ? val[i] : bv;
-        const uint32_t m = token_reduce<TL, true>(bv);
-        uint32_t bi = 0xFFFFFFFFu;
+        uint32_t m;
+        int e;
+        if constexpr (TL == 64) {
+            // whole wave: each row's maximum, then rows 1 and 3 take lane
+            // 15's and 47's, rows 2 and 3 lane 31's (DPP row broadcasts), so
+            // lane 63 holds the wave's maximum: one readlane instead of four
+            bv = row_reduce<true>(bv);
+            uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bv, 0x142, 0xA, 0xF, false);   // row_bcast:15
+            bv = o > bv ? o : bv;
+            o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bv, 0x143, 0xC, 0xF, false);            // row_bcast:31
+            bv = o > bv ? o : bv;
+            m = (uint32_t)__builtin_amdgcn_readlane((int)bv, 63);
+            // lowest index holding m: indices q + 64 i ascend with i, then with
+            // the lane, so the first i whose ballot is not empty decides
+            e = -1;
 #pragma unroll
-        for (int i = PL - 1; i >= 0; --i)               // lowest index of this lane holding m
-            bi = val[i] == m ? (uint32_t)(q + TL * i) : bi;
-        const int e = (int)token_reduce<TL, false>(bi);
+            for (int i = PL - 1; i >= 0; --i) {
+                const uint64_t b = __ballot(val[i] == m);
+                if (b)
+                    e = 64 * i + __builtin_ctzll(b);
+            }
+        } else {
+            m = token_reduce<TL, true>(bv);
+            uint32_t bi = 0xFFFFFFFFu;
+#pragma unroll
+            for (int i = PL - 1; i >= 0; --i)           // lowest index of this lane holding m
+                bi = val[i] == m ? (uint32_t)(q + TL * i) : bi;
+            e = (int)token_reduce<TL, false>(bi);
+        }
         if (j == 0)
             l0 = from_ordered_bits(m);
         if (q == j) {
