@@ -113,3 +113,21 @@ def test_shared_many_tokens_sampled(wl, T, S):
     ref = oracle.layer(inp.x, inp.logits, inp.w13_q, inp.s13, inp.w2_q, inp.s2, top_k=inp.workload.top_k,
                        expert_begin=inp.workload.expert_begin, tok_sel=sel, shared=sh)
     assert_layer_close(got[rows], ref["out"][rows], f"shared {wl} T={T}")
+
+
+@pytest.mark.parametrize("wl,T,S", [("tiny", 40, 4), ("qwen3_decode", 64, 1), ("qwen3_decode", 256, 2),
+                                    ("ep_shard_decode", 64, 1)])
+def test_shared_permutation_in_gemm_equals_separate_permutation(wl, T, S):
+    # the layer with shared experts, its permutation (routed rows, then one
+    # T-row segment per shared expert) built inside the gate/up GEMM, against
+    # the same layer with the separate permutation launch: bit for bit
+    from w4a16_grouped_gemm_amd import ops
+    say(f"shared layer, permutation in gemm {wl} T={T} S={S}")
+    inp = make_layer_inputs(wl, T)
+    sh = make_shared_weights(inp.workload, S)
+    with ops.launch_override(perm_in_gemm_max_tokens=4096):
+        fused = _forward(inp, sh)
+    with ops.launch_override(perm_in_gemm_max_tokens=0):
+        separate = _forward(inp, sh)
+    assert np.array_equal(fused, separate)
+    assert np.any(fused != 0)

@@ -489,17 +489,6 @@ static moe_status forward_impl(const moe_shape *shape, int nsh, const uint16_t *
     // (2.2-2.5 us) faster than routing inside the permutation, 64 and 256
     // tokens 2.0-3.3 and 2.6-2.8 us (5.3-7.4 and 1.9-2.6 us) faster than the
     // separate permutation, 512 tokens 1.9 us.
-    const bool perm_in_gemm = nsh == 0 && perm_in_gemm_fits(sh) && gemm_ids_supported(g1, sh.num_tokens);
-    if (perm_in_gemm) {
-        e = launch_route(sh, router_logits, ws.ids, ws.w, s);
-    } else if (route_permute_fusable(sh)) {
-        e = launch_route_permute(sh, router_logits, ws.ids, ws.w, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s,
-                                 nsh);
-    } else {
-        e = launch_route(sh, router_logits, ws.ids, ws.w, s);
-        if (e == hipSuccess)
-            e = launch_permute(sh, ws.ids, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s, nsh, ws.part);
-    }
     auto with_shared = [&](GemmLaunch &g, const uint8_t *wq_sh, const uint16_t *s_sh) {
         if (nsh == 0)
             return;
@@ -510,11 +499,24 @@ static moe_status forward_impl(const moe_shape *shape, int nsh, const uint16_t *
         g.wq_sh = wq_sh;
         g.s_sh = s_sh;
     };
+    with_shared(g1, w13_sh, s13_sh);
+    // (with shared experts the GEMM appends their T-row segments, as the
+    // separate permutation does)
+    const bool perm_in_gemm = perm_in_gemm_fits(sh) && gemm_ids_supported(g1, sh.num_tokens);
+    if (perm_in_gemm) {
+        e = launch_route(sh, router_logits, ws.ids, ws.w, s);
+    } else if (route_permute_fusable(sh)) {
+        e = launch_route_permute(sh, router_logits, ws.ids, ws.w, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s,
+                                 nsh);
+    } else {
+        e = launch_route(sh, router_logits, ws.ids, ws.w, s);
+        if (e == hipSuccess)
+            e = launch_permute(sh, ws.ids, ws.counts, ws.offsets, ws.perm, ws.inv_perm, s, nsh, ws.part);
+    }
     if (e == hipSuccess && perm_in_gemm) {
         IdsSource src{ws.ids, sh.num_tokens, sh.expert_begin, ws.counts, ws.offsets, ws.perm, ws.inv_perm};
         e = launch_gemm_ids(g1, src, s);
     } else if (e == hipSuccess) {
-        with_shared(g1, w13_sh, s13_sh);
         e = launch_grouped_gemm(g1, s);
     }
     // every slot local (and no shared rows): the down GEMM writes y in slot

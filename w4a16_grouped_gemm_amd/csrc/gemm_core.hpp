@@ -298,6 +298,7 @@ struct IdsTables {
     const int32_t *ids;          // [T*k] global expert ids (the routing result)
     int T, k, begin, E;          // tokens, slots per token, global id of local expert 0, local experts
     int32_t *cnt_out, *off_out, *perm_out, *inv_out;   // stored by workgroup 0
+    int nsh;                     // shared experts after the E routed ones (T rows each), as moe_permute appends them
 };
 
 template <int NT>
@@ -330,14 +331,18 @@ __device__ void build_from_ids(const IdsTables &p, int CS, uint32_t *s_bits, int
     __syncthreads();
     // thread e: its row count and word prefixes, then one scan over the
     // experts of (rows, chunks of CS rows)
+    // (experts E .. E + nsh - 1: the shared experts, every token once)
+    const int Et = E + p.nsh;
     int cnt = 0, ch = 0;
     if (tid < E) {
         for (int w = 0; w < words; ++w) {
             s_wpre[tid * words + w] = cnt;
             cnt += __popc(s_bits[tid * words + w]);
         }
-        ch = (cnt + CS - 1) / CS;
+    } else if (tid < Et) {
+        cnt = p.T;
     }
+    ch = (cnt + CS - 1) / CS;
     int tc, tch;
     const int xc = wave_exclusive_scan(cnt, tc);
     const int xch = wave_exclusive_scan(ch, tch);
@@ -354,7 +359,7 @@ __device__ void build_from_ids(const IdsTables &p, int CS, uint32_t *s_bits, int
         ac += s_wtot[w];
         ach += s_wtot[NT / 64 + w];
     }
-    if (tid < E) {
+    if (tid < Et) {
         s_off[tid] = bc + xc;
         s_prefix[tid] = bch + xch;
         if (store) {
@@ -363,12 +368,22 @@ __device__ void build_from_ids(const IdsTables &p, int CS, uint32_t *s_bits, int
         }
     }
     if (tid == 0) {
-        s_off[E] = ac;
-        s_prefix[E] = ach;
+        s_off[Et] = ac;
+        s_prefix[Et] = ach;
         if (store)
-            p.off_out[E] = ac;
+            p.off_out[Et] = ac;
     }
     __syncthreads();
+    // shared rows: row R + s T + t reads token t (slot t k, as moe_permute writes it)
+    if (p.nsh > 0) {
+        const int R = s_off[E];
+        for (int r = tid; r < p.nsh * p.T; r += NT) {
+            const int t = r % p.T;
+            s_row[R + r] = (uint16_t)(t * k);
+            if (store)
+                p.perm_out[R + r] = t * k;
+        }
+    }
     // the row of every slot first (LDS reads only, all independent), then the stores
     int row[kIdsPerThread];
 #pragma unroll

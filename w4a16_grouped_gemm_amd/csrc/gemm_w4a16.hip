@@ -252,7 +252,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p)
         uint32_t *s_bits = reinterpret_cast<uint32_t *>(s_dyn);
         const int words = (p.T + 31) >> 5;
         int *s_wpre = reinterpret_cast<int *>(s_bits + E * words);
-        const IdsTables it{p.ids, p.T, p.top_k, p.begin, E, p.cnt_out, p.off_out, p.perm_out, p.inv_out};
+        // (the shared experts, if any, are the last E - e_routed)
+        const IdsTables it{p.ids,      p.T,        p.top_k,     p.begin,   p.e_routed,
+                           p.cnt_out,  p.off_out,  p.perm_out,  p.inv_out, E - p.e_routed};
         build_from_ids<256>(it, CS, s_bits, s_wpre, s_row, s_prefix, s_off, s_wtot);
         total_items = s_prefix[E] * nblocks;
     } else {
@@ -1237,7 +1239,8 @@ hipError_t launch_stream(const GemmArgs &a, int max_rows, hipStream_t st)
     constexpr int CS = 16 * NSUB;
     auto kernel = gemm_stream_kernel<KIND, TPW, NSUB, KSEG, RING, NT, SRC, PL>;
     const size_t tables = SRC == SRC_OFFSETS ? sizeof(int) * (2 * (a.num_experts + 1) + 4)
-                          : SRC == SRC_IDS   ? sizeof(int) * (2 * (a.num_experts + 1) + 8) + 2 * (size_t)a.T * a.top_k
+                          : SRC == SRC_IDS   ? sizeof(int) * (2 * (a.num_experts + 1) + 8) +
+                                                   2 * (size_t)a.T * (a.top_k + a.num_experts - a.e_routed)
                                              : sizeof(int) * (2 * kDecMaxSlots + 4 + a.num_experts);
     const size_t lds = stream_act_bytes<NSUB, KSEG>() + tables;
     const int per_cu = resident_per_cu(kernel, lds);
@@ -1543,7 +1546,7 @@ static bool ids_instance(const LaunchChoice &c)
 
 bool gemm_ids_supported(const GemmLaunch &g, int T)
 {
-    if (g.kind != MOE_GEMM_W13_SWIGLU || g.wq_sh || g.c_f32 || g.num_experts > 256 || g.offsets == nullptr)
+    if (g.kind != MOE_GEMM_W13_SWIGLU || g.c_f32 || g.num_experts > 256 || g.offsets == nullptr)
         return false;
     const LaunchChoice c = choose_launch(g);
     if (c.mode != 1 || !ids_instance(c) || g.max_rows > kIdsPerThread * 256)
